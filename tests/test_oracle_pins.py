@@ -1,0 +1,340 @@
+"""Pins for the CPU oracle: each test checks it against something other than itself.
+
+- decoders: every code of every format against torch's own casts, plus closed forms;
+- dense GEMM: exact rational / integer brute force on small inputs, identity,
+  permutation and one-hot products, beta = 0 ignoring a NaN C, int32 wrap-around;
+- compressor: the index value the pages print for the {0,2} pattern, hand-worked
+  groups, invariants over an exhaustive small alphabet, round trip;
+- sparse GEMM: equal, bit for bit in fp64, to the dense GEMM on the decompressed A.
+"""
+import itertools
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from oracle import BF16, E4M3, E5M2, F16, I8
+
+TORCH = {F16: torch.float16, BF16: torch.bfloat16, E4M3: torch.float8_e4m3fn, E5M2: torch.float8_e5m2}
+
+
+def torch_decode(bits, t):
+    """Decode raw bits with torch's casts (independent of the oracle's decoders)."""
+    bits = np.ascontiguousarray(bits)
+    if t == I8:
+        return bits.astype(np.float64)
+    if t in (F16, BF16):
+        return torch.from_numpy(bits.view(np.int16)).view(TORCH[t]).to(torch.float64).numpy()
+    return torch.from_numpy(bits.view(np.uint8)).view(TORCH[t]).to(torch.float64).numpy()
+
+
+def same_values(a, b):
+    a, b = np.asarray(a), np.asarray(b)
+    nan_a, nan_b = np.isnan(a), np.isnan(b)
+    assert np.array_equal(nan_a, nan_b)
+    ok = ~nan_a
+    assert np.array_equal(a[ok], b[ok])
+    assert np.array_equal(np.signbit(a[ok]), np.signbit(b[ok]))
+
+
+# ---------------------------------------------------------------- decoders --
+
+@pytest.mark.parametrize("t,n", [(F16, 65536), (BF16, 65536), (E4M3, 256), (E5M2, 256)])
+def test_decode_exhaustive_vs_torch(t, n):
+    bits = np.arange(n, dtype=np.int64).astype(oracle.BITS_DTYPE[t])
+    same_values(oracle.decode(t, bits), torch_decode(bits, t))
+
+
+def test_decode_int8_exhaustive():
+    bits = np.arange(-128, 128, dtype=np.int64).astype(np.int8)
+    assert np.array_equal(oracle.decode(I8, bits), np.arange(-128, 128, dtype=np.float64))
+
+
+def test_decode_closed_forms():
+    d = oracle.decode_one
+    assert d(E4M3, 0x7E) == 448.0 and d(E4M3, 0xFE) == -448.0     # largest finite E4M3
+    assert d(E4M3, 0x01) == 2.0 ** -9                             # smallest subnormal
+    assert np.isnan(d(E4M3, 0x7F)) and np.isnan(d(E4M3, 0xFF))    # S.1111.111 only NaN
+    assert d(E4M3, 0x78) == 256.0                                 # exponent field 15 is finite
+    assert d(E5M2, 0x7B) == 57344.0 and d(E5M2, 0x01) == 2.0 ** -16
+    assert d(E5M2, 0x7C) == float("inf") and d(E5M2, 0xFC) == float("-inf")
+    assert np.isnan(d(E5M2, 0x7D))
+    assert d(F16, 0x7BFF) == 65504.0 and d(F16, 0x0001) == 2.0 ** -24 and d(F16, 0x3C00) == 1.0
+    assert d(BF16, 0x3F80) == 1.0 and d(BF16, 0xC000) == -2.0 and d(BF16, 0x0001) == 2.0 ** -133
+    assert d(I8, 0x80) == -128.0 and d(I8, 0x7F) == 127.0
+
+
+# ------------------------------------------------------------- dense GEMM --
+
+PAIRS = [(BF16, BF16), (F16, F16), (E4M3, E5M2), (E5M2, E4M3), (E4M3, E4M3), (E5M2, E5M2)]
+
+
+def random_bits(shape, t, seed):
+    g = np.random.default_rng(seed)
+    if t == I8:
+        return g.integers(-128, 128, size=shape).astype(np.int8)
+    return W.to_bits(g.standard_normal(shape) * 2.0, t)
+
+
+@pytest.mark.parametrize("ta,tb", PAIRS)
+@pytest.mark.parametrize("M,N,K", [(4, 4, 4), (7, 5, 9), (32, 32, 32), (3, 17, 64)])
+def test_dense_vs_exact_rational(ta, tb, M, N, K):
+    seed = M * 1000 + N * 10 + K + 7 * ta + tb
+    A, B = random_bits((M, K), ta, seed), random_bits((N, K), tb, seed + 1)
+    C = np.random.default_rng(seed + 2).standard_normal((M, N)).astype(np.float32)
+    alpha, beta = 0.75, -1.25
+    D, S = oracle.gemm_dense(ta, tb, A, B, alpha, beta, C)
+    Ad, Bd = torch_decode(A, ta), torch_decode(B, tb)
+    for i in range(M):
+        for j in range(N):
+            exact = Fraction(0)
+            for k in range(K):
+                exact += Fraction(Ad[i, k]) * Fraction(Bd[j, k])
+            exact = Fraction(alpha) * exact + Fraction(beta) * Fraction(float(C[i, j]))
+            bound = (K + 3) * 2.0 ** -52 * (abs(alpha) * S[i, j] + abs(beta) * abs(float(C[i, j]))) + 1e-300
+            assert abs(D[i, j] - float(exact)) <= bound, (i, j)
+            assert S[i, j] == pytest.approx(float(sum(abs(Fraction(Ad[i, k]) * Fraction(Bd[j, k]))
+                                                       for k in range(K))), rel=1e-12, abs=0)
+
+
+@pytest.mark.parametrize("M,N,K", [(4, 4, 4), (9, 6, 33), (32, 32, 32)])
+def test_dense_int8_vs_python_ints(M, N, K):
+    A, B = random_bits((M, K), I8, M + K), random_bits((N, K), I8, N + K + 1)
+    C = np.random.default_rng(3).integers(-1000, 1001, size=(M, N)).astype(np.int32)
+    D, oor = oracle.gemm_dense(I8, I8, A, B, 3, -2, C)
+    assert not oor
+    for i in range(M):
+        for j in range(N):
+            v = 3 * sum(int(A[i, k]) * int(B[j, k]) for k in range(K)) - 2 * int(C[i, j])
+            assert D[i, j] == v
+
+
+def test_int8_wraps_mod_2_32():
+    K = 64
+    A = np.full((1, K), -128, np.int8)
+    B = np.full((1, K), -128, np.int8)
+    C = np.array([[2 ** 31 - 1]], np.int32)
+    alpha, beta = 1000, 1
+    exact = alpha * K * 128 * 128 + (2 ** 31 - 1)        # 1,048,576,000 + 2,147,483,647 > 2^31
+    D, oor = oracle.gemm_dense(I8, I8, A, B, alpha, beta, C)
+    assert oor
+    wrapped = (exact + 2 ** 31) % 2 ** 32 - 2 ** 31
+    assert int(D[0, 0]) == wrapped and wrapped < 0
+
+
+@pytest.mark.parametrize("t", [BF16, F16, E4M3, E5M2])
+def test_identity_permutation_onehot(t):
+    n = 24
+    one = W.to_bits(np.ones(1), t)[0]
+    zero = W.zero_bits(t)
+    B = random_bits((n, n), t, 11)             # B column-major: B[k, j] = Bst[j, k]
+    Bd = torch_decode(B, t)
+    # A = I  =>  D[i, j] = B[i, j] = Bst[j, i]
+    A = np.full((n, n), zero, oracle.BITS_DTYPE[t])
+    np.fill_diagonal(A, one)
+    D, _ = oracle.gemm_dense(t, t, A, B)
+    assert np.array_equal(D, Bd.T)
+    # A = permutation P (row i picks column perm[i])  =>  D[i, :] = B[perm[i], :]
+    perm = np.random.default_rng(5).permutation(n)
+    P = np.full((n, n), zero, oracle.BITS_DTYPE[t])
+    P[np.arange(n), perm] = one
+    D, _ = oracle.gemm_dense(t, t, P, B)
+    assert np.array_equal(D, Bd.T[perm, :])
+    # one-hot A[2, 5] and B[5, 7] (i.e. Bst[7, 5])  =>  a single one at D[2, 7]
+    A1 = np.full((n, n), zero, oracle.BITS_DTYPE[t]); A1[2, 5] = one
+    B1 = np.full((n, n), zero, oracle.BITS_DTYPE[t]); B1[7, 5] = one
+    D, _ = oracle.gemm_dense(t, t, A1, B1)
+    expect = np.zeros((n, n)); expect[2, 7] = 1.0
+    assert np.array_equal(D, expect)
+
+
+def test_b_identity_and_alpha_beta():
+    n = 16
+    one, zero = W.to_bits(np.ones(1), BF16)[0], W.zero_bits(BF16)
+    A = random_bits((n, n), BF16, 21)
+    Bi = np.full((n, n), zero, np.uint16); np.fill_diagonal(Bi, one)
+    C = np.random.default_rng(1).standard_normal((n, n)).astype(np.float32)
+    D, _ = oracle.gemm_dense(BF16, BF16, A, Bi, 2.0, 0.5, C)
+    assert np.array_equal(D, 2.0 * torch_decode(A, BF16) + 0.5 * C.astype(np.float64))
+
+
+def test_beta_zero_ignores_nan_c():
+    A, B = random_bits((8, 8), BF16, 1), random_bits((8, 8), BF16, 2)
+    Cnan = np.full((8, 8), np.nan, np.float32)
+    D0, _ = oracle.gemm_dense(BF16, BF16, A, B, 1.0, 0.0, None)
+    D1, _ = oracle.gemm_dense(BF16, BF16, A, B, 1.0, 0.0, Cnan)
+    assert np.isfinite(D1).all() and np.array_equal(D0, D1)
+
+
+def test_row_ranges_and_entries_agree_with_full():
+    A, B = random_bits((40, 48), E4M3, 3), random_bits((36, 48), E5M2, 4)
+    C = np.random.default_rng(2).standard_normal((40, 36)).astype(np.float32)
+    D, S = oracle.gemm_dense(E4M3, E5M2, A, B, 1.5, 0.5, C)
+    Dr, Sr = oracle.gemm_dense(E4M3, E5M2, A, B, 1.5, 0.5, C, rows=(7, 19))
+    assert np.array_equal(D[7:19], Dr) and np.array_equal(S[7:19], Sr)
+    ii = np.array([0, 39, 13, 7]); jj = np.array([35, 0, 17, 7])
+    De, Se = oracle.gemm_dense_entries(E4M3, E5M2, A, B, ii, jj, 1.5, 0.5, C)
+    assert np.array_equal(De, D[ii, jj]) and np.array_equal(Se, S[ii, jj])
+
+
+# ------------------------------------------------------------- compressor --
+
+def test_index_value_printed_on_pages():
+    """Keeping positions {0,2} of every group gives 0x88 for two groups and 0x8888 for four
+    (the pages' fixed-pattern examples); a 32-wide span is then 0x88888888."""
+    fixture = {}
+    for line in open(__file__.replace("test_oracle_pins.py", "golden/sparsity_index.txt")):
+        if line.strip() and not line.startswith("#"):
+            g, v = line.split()
+            fixture[int(g)] = int(v, 16)
+    for t in (F16, E4M3):
+        one = W.to_bits(np.ones(1), t)[0]
+        for groups, value in fixture.items():
+            K = 4 * groups
+            A = np.full((3, K), W.zero_bits(t), oracle.BITS_DTYPE[t])
+            A[:, 0::4] = one
+            A[:, 2::4] = one
+            Ac, idx, bad = oracle.compress24(t, A)
+            assert bad == 0 and idx.shape == (3, 1)
+            assert (idx[:, 0] == value).all()
+            assert (Ac == one).all()
+        A = np.full((2, 64), W.zero_bits(t), oracle.BITS_DTYPE[t])
+        A[:, 0::4] = one
+        A[:, 2::4] = one
+        _, idx, _ = oracle.compress24(t, A)
+        assert (idx == 0x88888888).all()
+
+
+# hand-worked groups: (values as floats, expected kept positions, expected violation)
+HAND = [
+    ([0.0, 5.0, 0.0, 7.0], (1, 3), 0),
+    ([2.0, 0.0, 0.0, -3.0], (0, 3), 0),
+    ([0.0, 0.0, 1.5, 2.5], (2, 3), 0),
+    ([4.0, 1.0, 0.0, 0.0], (0, 1), 0),
+    ([0.0, 6.0, 8.0, 0.0], (1, 2), 0),
+    ([0.0, 0.0, 0.0, 0.0], (0, 1), 0),       # no non-zero: pad with the two lowest
+    ([0.0, 0.0, 0.0, 9.0], (0, 3), 0),       # one non-zero at 3: pad with 0
+    ([0.0, 9.0, 0.0, 0.0], (0, 1), 0),       # one non-zero at 1: pad with 0
+    ([0.0, 0.0, 9.0, 0.0], (0, 2), 0),
+    ([1.0, 2.0, 3.0, 0.0], (0, 1), 1),       # three non-zeros: violation, keep lowest two
+    ([1.0, 2.0, 3.0, 4.0], (0, 1), 1),
+    ([0.0, 2.0, 3.0, 4.0], (1, 2), 1),
+]
+NIBBLE = {(0, 1): 0x4, (0, 2): 0x8, (0, 3): 0xC, (1, 2): 0x9, (1, 3): 0xD, (2, 3): 0xE}
+
+
+@pytest.mark.parametrize("t", [F16, BF16, E4M3, E5M2])
+def test_compress_hand_worked_groups(t):
+    vals = np.array([v for g in HAND for v in g[0]])
+    A = W.to_bits(vals, t).reshape(1, -1)
+    Ac, idx, bad = oracle.compress24(t, A)
+    assert bad == sum(g[2] for g in HAND)
+    for g, (v, (p0, p1), _) in enumerate(HAND):
+        nib = (int(idx[0, g // 8]) >> (4 * (g % 8))) & 0xF
+        assert nib == NIBBLE[(p0, p1)], (g, v)
+        assert Ac[0, 2 * g] == A[0, 4 * g + p0] and Ac[0, 2 * g + 1] == A[0, 4 * g + p1]
+
+
+def test_compress_int8_minus128_is_nonzero():
+    A = np.array([[0, -128, 0, 1]], np.int8)
+    Ac, idx, bad = oracle.compress24(I8, A)
+    assert bad == 0 and (int(idx[0, 0]) & 0xF) == NIBBLE[(1, 3)] and list(Ac[0]) == [-128, 1]
+
+
+@pytest.mark.parametrize("t", [F16, E4M3])
+def test_compress_exhaustive_small_alphabet(t):
+    """All 625 groups over {+0, -0, 1, -1, NaN}: invariants of the compressor."""
+    if t == F16:
+        alphabet = [0x0000, 0x8000, 0x3C00, 0xBC00, 0x7E00]
+    else:
+        alphabet = [0x00, 0x80, 0x38, 0xB8, 0x7F]
+    groups = list(itertools.product(range(5), repeat=4))
+    A = np.array([[alphabet[s] for g in groups for s in g]], oracle.BITS_DTYPE[t])
+    Ac, idx, bad = oracle.compress24(t, A)
+    n_viol = 0
+    for g, sym in enumerate(groups):
+        nz = [p for p in range(4) if sym[p] not in (0, 1)]
+        nib = (int(idx[0, g // 8]) >> (4 * (g % 8))) & 0xF
+        p0, p1 = nib & 3, nib >> 2
+        assert p0 < p1
+        if len(nz) <= 2:
+            assert set(nz) <= {p0, p1}          # every non-zero is kept
+        else:
+            n_viol += 1
+            assert (p0, p1) == (nz[0], nz[1])   # the two lowest non-zeros
+        assert Ac[0, 2 * g] == A[0, 4 * g + p0] and Ac[0, 2 * g + 1] == A[0, 4 * g + p1]
+    assert bad == n_viol
+    # the ragged index word: 625 groups -> 79 words, the last holds 1 group
+    assert idx.shape == (1, 79) and (int(idx[0, 78]) >> 4) == 0
+
+
+@pytest.mark.parametrize("t", [F16, BF16, E4M3, E5M2, I8])
+def test_compress_matches_generator_pattern_and_round_trips(t):
+    M, K = 13, 72                      # ragged: 72 = 2 full index words + 8 of 32
+    pats = np.random.default_rng(9).integers(0, 6, size=(M, K // 4))
+    keep = W.prune_mask(M, K, 0, patterns=pats)
+    if t == I8:
+        dense = np.random.default_rng(4).integers(1, 128, size=(M, K)).astype(np.int8)
+        dense *= np.where(np.random.default_rng(5).random((M, K)) < 0.5, -1, 1).astype(np.int8)
+        A = np.where(keep, dense, np.int8(0))
+    else:
+        dense = np.abs(np.random.default_rng(4).standard_normal((M, K))) + 0.5
+        A = np.where(keep, W.to_bits(dense, t), W.zero_bits(t))
+    Ac, idx, bad = oracle.compress24(t, A)
+    assert bad == 0
+    # compressed values are the kept ones in row order, nibbles name the drawn pattern
+    assert np.array_equal(Ac, A[keep].reshape(M, K // 2))
+    for i in range(M):
+        for g in range(K // 4):
+            nib = (int(idx[i, g // 8]) >> (4 * (g % 8))) & 0xF
+            assert nib == NIBBLE[W.PATTERNS[pats[i, g]]]
+    assert np.array_equal(oracle.decompress24(t, Ac, idx, K), A)
+
+
+# ------------------------------------------------------------ sparse GEMM --
+
+@pytest.mark.parametrize("ta,tb", [(F16, F16), (BF16, BF16), (E4M3, E5M2), (E5M2, E5M2)])
+def test_sparse_equals_dense_on_decompressed(ta, tb):
+    M, N, K = 19, 23, 136
+    A = W.sparse24_normal(M, K, ta, 77, exact_two=False)
+    A[0, :8] = W.to_bits(np.array([1, 2, 3, 0, 0, 0, 0, 0.0]), ta)   # one violating group
+    B = random_bits((N, K), tb, 5)
+    C = np.random.default_rng(8).standard_normal((M, N)).astype(np.float32)
+    Ac, idx, bad = oracle.compress24(ta, A)
+    assert bad == 1
+    Ad = oracle.decompress24(ta, Ac, idx, K)       # the 4:2 matrix the sparse path sees
+    Ds, Ss = oracle.gemm_sparse24(ta, tb, Ac, idx, B, 1.25, -0.5, C)
+    Dd, Sd = oracle.gemm_dense(ta, tb, Ad, B, 1.25, -0.5, C)
+    assert np.array_equal(Ds, Dd) and np.array_equal(Ss, Sd)
+    ii = np.array([0, 18, 5]); jj = np.array([22, 0, 11])
+    De, Se = oracle.gemm_sparse24_entries(ta, tb, Ac, idx, B, ii, jj, 1.25, -0.5, C)
+    assert np.array_equal(De, Ds[ii, jj]) and np.array_equal(Se, Ss[ii, jj])
+
+
+def test_sparse_int8_equals_dense_on_decompressed():
+    M, N, K = 11, 9, 96
+    pats = np.random.default_rng(1).integers(0, 6, size=(M, K // 4))
+    keep = W.prune_mask(M, K, 0, patterns=pats)
+    A = np.where(keep, random_bits((M, K), I8, 2), np.int8(0))
+    B = random_bits((N, K), I8, 3)
+    C = np.random.default_rng(4).integers(-1000, 1001, size=(M, N)).astype(np.int32)
+    Ac, idx, _ = oracle.compress24(I8, A)
+    Ds, o1 = oracle.gemm_sparse24(I8, I8, Ac, idx, B, 2, 3, C)
+    Dd, o2 = oracle.gemm_dense(I8, I8, oracle.decompress24(I8, Ac, idx, K), B, 2, 3, C)
+    assert np.array_equal(Ds, Dd) and o1 == o2
+
+
+def test_sparse_rejects_invalid_nibble():
+    Ac = np.zeros((1, 2), np.uint16)
+    idx = np.array([[0x5]], np.uint32)          # p0 = 1, p1 = 1: not a pair
+    B = np.zeros((1, 4), np.uint16)
+    with pytest.raises(ValueError):
+        oracle.gemm_sparse24(F16, F16, Ac, idx, B)
+
+
+def test_normwise_error_metric():
+    D = np.array([[1.0, 2.0]]); S = np.array([[3.0, 4.0]])
+    assert oracle.normwise_error(D + np.array([[0.0, 0.5]]), D, S, 1.0, 0.0) == pytest.approx(0.1)
