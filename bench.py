@@ -1,6 +1,227 @@
-"""Benchmark harness (being written)."""
+"""Benchmark: dense bf16, dense fp8 and 4:2-sparse fp8 GEMM at 8192^3 on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input:
+  1. 4:2 compression of the pruned fp8 A (mmac_sparse24_compress),
+  2. sparse fp8 x bf8 GEMM on it (mmac_gemm_sparse24),
+  3. dense bf16 GEMM, D = A*B + C (mmac_gemm_dense),
+  4. dense fp8 E4M3 x bf8 E5M2 GEMM (mmac_gemm_dense).
+The inputs are resident in HBM before timing starts.  `value` is the step's
+work (2*M*N*K per GEMM, dense-equivalent K for the sparse one) divided by the
+wall time of the step.  Each kernel is also timed with HIP events on the
+stream it runs on, and the slowest one is reported against its roofline.  The
+CPU oracle is timed on a bounded slice of the bf16 GEMM for scale.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-check]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOP/s + % MFMA peak, bf16/fp8 dense and 4:2 sparse at 8192³, 1 GPU"
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp8": 5000.0, "int8": 5000.0}
+PEAK_HBM_GBS = 8000.0
 
 
 def gemm_flops(M, N, K):
     """Work of one GEMM: 2*M*N*K operations (for a 4:2-sparse A, K is the dense K)."""
     return 2 * int(M) * int(N) * int(K)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0, help="rows of the oracle slice (0 = calibrate)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_matrix_multiply_amd as mm
+    import workloads as W
+
+    mm.lib()                                  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    F16, BF16, I8, E4M3, E5M2 = W.F16, W.BF16, W.I8, W.E4M3, W.E5M2
+
+    def to_dev(bits, t):
+        host = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16 if bits.dtype == np.uint16 else np.int8))
+        x = host.to(dev)
+        return x.view({BF16: torch.bfloat16, F16: torch.float16, E4M3: torch.float8_e4m3fn,
+                       E5M2: torch.float8_e5m2}[t])
+
+    t_gen = time.perf_counter()
+    wb = W.workload("bf16_8192")
+    w8 = W.workload("fp8_8192")
+    ws = W.workload("fp8_8192_sparse")
+    M = N = K = 8192
+    Ab, Bb, Cb = to_dev(wb["A"], BF16), to_dev(wb["B"], BF16), torch.from_numpy(wb["C"]).to(dev)
+    A8, B8 = to_dev(w8["A"], E4M3), to_dev(w8["B"], E5M2)
+    As = to_dev(ws["A"], E4M3)
+    Db = torch.empty((M, N), dtype=torch.float32, device=dev)
+    D8 = torch.empty((M, N), dtype=torch.float32, device=dev)
+    Ds = torch.empty((M, N), dtype=torch.float32, device=dev)
+    Ac = torch.empty((M, K // 2), dtype=torch.float8_e4m3fn, device=dev)
+    idx = torch.empty((M, K // 32), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    print(f"# inputs ready in {t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    parts = ["compress_fp8", "sparse_fp8", "dense_bf16", "dense_fp8"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        mm.sparse24_compress(As, Ac, idx, a_type=E4M3, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        mm.gemm_sparse24(Ac, idx, B8, Ds, K=K, alpha=1.0, beta=0.0, a_type=E4M3, b_type=E5M2, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        mm.gemm_dense(Ab, Bb, Db, 1.0, 1.0, Cb, a_type=BF16, b_type=BF16, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+        mm.gemm_dense(A8, B8, D8, 1.0, 0.0, None, a_type=E4M3, b_type=E5M2, stream=stream)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    part_ms = {p: 0.0 for p in parts}
+    for ev in events:
+        for q, p in enumerate(parts):
+            part_ms[p] += ev[q].elapsed_time(ev[q + 1]) / args.steps
+
+    flops = {"compress_fp8": 0, "sparse_fp8": gemm_flops(M, N, K), "dense_bf16": gemm_flops(M, N, K),
+             "dense_fp8": gemm_flops(M, N, K)}
+    step_flops = sum(flops.values())
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    # sparse: dense-equivalent FLOP against 2x the dense peak == effective FLOP against the dense peak
+    peak = {"sparse_fp8": 2 * PEAK_TFLOPS["fp8"], "dense_bf16": PEAK_TFLOPS["bf16"], "dense_fp8": PEAK_TFLOPS["fp8"]}
+    comp_bytes = M * K + M * (K // 2) + M * (K // 32) * 4        # read A, write Ac + idx
+    report = {}
+    for p in parts:
+        t = part_ms[p] * 1e-3
+        if p == "compress_fp8":
+            report[p] = {"ms": round(part_ms[p], 4), "GB/s": round(comp_bytes / t / 1e9, 1),
+                         "frac_hbm_peak": round(comp_bytes / t / 1e9 / PEAK_HBM_GBS, 4)}
+        else:
+            tf = flops[p] / t / 1e12
+            r = {"ms": round(part_ms[p], 4), "TFLOP/s": round(tf, 1), "frac_peak": round(tf / peak[p], 4)}
+            if p == "sparse_fp8":
+                r["TFLOP/s_dense_equivalent"] = r.pop("TFLOP/s")
+                r["TFLOP/s_effective"] = round(tf / 2, 1)
+            report[p] = r
+
+    dominant = max(parts, key=lambda p: part_ms[p])
+    if dominant == "compress_fp8":
+        roof = {"bound": "hbm", "achieved": round(comp_bytes / (part_ms[dominant] * 1e-3) / 1e9, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        ach = flops[dominant] / (part_ms[dominant] * 1e-3) / 1e12
+        if dominant == "sparse_fp8":
+            ach /= 2                                  # effective FLOP vs the dense fp8 peak
+        pk = PEAK_TFLOPS["bf16" if dominant == "dense_bf16" else "fp8"]
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": pk, "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["kernel"] = dominant
+    roof["traffic"] = None
+
+    check = None
+    if not args.no_check:
+        check = spot_check(wb, w8, ws, Db, D8, Ds, Ac, idx, dev)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wb, args.cpu_rows)
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16,fp8e4m3xbf8e5m2", "data": "synthetic",
+        "config": {"workload": "8192^3: 4:2 compress fp8 A + sparse fp8xbf8 GEMM + dense bf16 GEMM "
+                               "(beta=1) + dense fp8xbf8 GEMM, fp32 out", "M": M, "N": N, "K": K},
+        "parts": report, "roofline": roof, "cpu_baseline": cpu, "check": check,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def spot_check(wb, w8, ws, Db, D8, Ds, Ac, idx, dev):
+    """Compare 512 sampled outputs of each GEMM (and the index words) with the oracle."""
+    import numpy as np
+    import torch
+    import oracle
+
+    g = np.random.default_rng(1)
+    ii = g.integers(0, 8192, 512)
+    jj = g.integers(0, 8192, 512)
+    it, jt = torch.from_numpy(ii).to(dev), torch.from_numpy(jj).to(dev)
+    out = {}
+    for name, w, D in (("dense_bf16", wb, Db), ("dense_fp8", w8, D8)):
+        ref, S = oracle.gemm_dense_entries(w["ta"], w["tb"], w["A"], w["B"], ii, jj, w["alpha"], w["beta"], w["C"])
+        C = w["C"][ii, jj] if w["beta"] != 0 else None
+        e = oracle.normwise_error(D[it, jt].cpu().numpy(), ref, S, w["alpha"], w["beta"], C)
+        out[name] = float(f"{e:.3e}")
+    Ac_ref, idx_ref, _ = oracle.compress24(ws["ta"], ws["A"])
+    out["index_words_match"] = bool(np.array_equal(idx.cpu().numpy().view(np.uint32), idx_ref))
+    out["compressed_values_match"] = bool(np.array_equal(
+        Ac.view(torch.int8).cpu().numpy().view(np.uint8), Ac_ref))
+    ref, S = oracle.gemm_sparse24_entries(ws["ta"], ws["tb"], Ac_ref, idx_ref, ws["B"], ii, jj)
+    e = oracle.normwise_error(Ds[it, jt].cpu().numpy(), ref, S, 1.0, 0.0)
+    out["sparse_fp8"] = float(f"{e:.3e}")
+    out["index_words_match"] = idx_ok
+    return out
+
+
+def cpu_baseline(wb, rows):
+    """Time the oracle on a slice of the bf16 8192^3 GEMM's output rows (all 8192 columns)."""
+    import oracle
+    threads = oracle.num_threads()
+    if rows <= 0:
+        # calibrate: about 15 s of CPU work from a 2-row probe
+        t = time.perf_counter()
+        oracle.gemm_dense(wb["ta"], wb["tb"], wb["A"], wb["B"], wb["alpha"], wb["beta"], wb["C"], rows=(0, 2))
+        per_row = max((time.perf_counter() - t) / 2, 1e-4)
+        rows = int(min(512, max(threads, 15.0 / per_row)))
+    t = time.perf_counter()
+    oracle.gemm_dense(wb["ta"], wb["tb"], wb["A"], wb["B"], wb["alpha"], wb["beta"], wb["C"], rows=(0, rows))
+    dt = time.perf_counter() - t
+    return {"value": round(gemm_flops(rows, 8192, 8192) / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"bf16 GEMM, output rows 0..{rows - 1} of 8192x8192x8192 (fp64 accumulation), {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,143 @@
+/*
+ * mmac -- tiled matrix multiply-accumulate on AMD Instinct MI355X (gfx950).
+ *
+ * Computes D = alpha * A*B + beta * C on one GPU, with A either dense or 4:2
+ * structured-sparse (stored as its non-zeros plus a per-group index), using
+ * the gfx950 dense MFMA and sparse SMFMAC matrix instructions.
+ *
+ * Operation (ROCm handbook, "CDNA dense MFMA builtins", section "Naming
+ * convention"): a matrix instruction adds the contribution of a K-wide panel of
+ * A (M x K) and of B (K x N) to an M x N tile of C, and the caller loops over K
+ * to form the full product.  Each call below is that full product over a whole
+ * matrix, scaled by alpha, plus beta * C.
+ *
+ * Sparse form ("CDNA3 sparse MFMA builtins", section "Structured sparsity (4:2
+ * pattern)"): in every contiguous group of four elements of A along K at most
+ * two are non-zero; the compressed A stores the two kept values of each group
+ * in ascending position, half the K length, and the index gives their
+ * positions p0 < p1 as the nibble p0 | (p1 << 2) (keeping positions {0,2} of a
+ * group gives 0x8, as the page's 0x88 / 0x8888 examples show).
+ *
+ * Conventions shared by every call
+ *   - Element types: see mmac_dtype_t.  FP8 and BF8 use the OCP encodings
+ *     (E4M3 and E5M2), which gfx950 uses ("CDNA3 sparse MFMA builtins", note
+ *     under "FP8 16x16 sparse kernel").
+ *   - Layouts (all strides in elements):
+ *       A   row-major    M x K :  A[i*lda + k],   lda >= K
+ *       B   column-major K x N :  B[j*ldb + k],   ldb >= K
+ *       C,D row-major    M x N :  D[i*ldd + j],   ldd >= N (ldc >= N)
+ *       Ac  row-major    M x K/2: compressed A, ldac >= K/2
+ *       idx row-major    M x ceil(K/32) 32-bit words, ldidx >= ceil(K/32);
+ *           group g of row i (elements 4g..4g+3) is the nibble at bits
+ *           4*(g mod 8) of word g/8; bits of groups at or past K/4 are zero.
+ *   - Output type: float (fp32) for floating inputs, int32 for int8 inputs;
+ *     C has the output type.  Floating results are accumulated in fp32; int8
+ *     results are exact modulo 2^32 (two's complement wrap, no saturation).
+ *   - beta == 0 means C is not read (C may be NULL; NaNs in C do not leak).
+ *     D may be the same buffer as C when ldd == ldc; other overlaps between
+ *     outputs and inputs are not allowed.
+ *   - int8: alpha and beta must be integers that fit in int32.
+ *   - M == 0 or N == 0: nothing is done.  K == 0: D = beta * C.
+ *   - Alignment: A, B, Ac must start on a 16-byte boundary and their row
+ *     pitch in bytes (ld * element size) must be a multiple of 16.  C, D and
+ *     idx need only their natural 4-byte alignment.
+ *   - Sizes: M, N, K must be below 2^31 (MMAC_ERR_INVALID_ARG otherwise); the
+ *     row pitch of A, B and Ac must be at most 8 MiB and that of idx at most
+ *     8 MiB / 4 words (MMAC_ERR_UNSUPPORTED otherwise).
+ *   - Memory: every pointer is device memory on the current HIP device, owned
+ *     by the caller; the library never allocates, frees or keeps a pointer.
+ *     Buffers must stay valid until the work on `stream` has finished.
+ *   - Asynchrony: each call validates its arguments on the host, then enqueues
+ *     kernels on `stream` (a hipStream_t; NULL is the default stream) and
+ *     returns without synchronising.  A kernel fault shows up at the caller's
+ *     next synchronisation.
+ *   - Errors: no exception crosses this interface.  Argument errors are
+ *     detected before any GPU work is enqueued; nothing is written then.
+ *   - Thread safety: calls are re-entrant; the library keeps no mutable state
+ *     besides a per-device cache of device properties, filled once.
+ */
+#ifndef MMAC_H
+#define MMAC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MMAC_OK = 0,
+    MMAC_ERR_INVALID_ARG = 1, /* negative or oversized dims, bad ld, NULL pointer, bad alpha/beta */
+    MMAC_ERR_UNSUPPORTED = 2, /* element-type pair not supported */
+    MMAC_ERR_MISALIGNED = 3,  /* alignment rule above broken */
+    MMAC_ERR_HIP = 4          /* the HIP runtime refused the launch */
+} mmac_status_t;
+
+typedef enum {
+    MMAC_F16 = 1,      /* IEEE binary16 */
+    MMAC_BF16 = 2,     /* bfloat16 */
+    MMAC_I8 = 3,       /* signed 8-bit integer */
+    MMAC_FP8_E4M3 = 4, /* OCP FP8 E4M3 */
+    MMAC_BF8_E5M2 = 5  /* OCP BF8 E5M2 */
+} mmac_dtype_t;
+
+/*
+ * Dense GEMM: D = alpha * A*B + beta * C.
+ * Supported (a_type, b_type): (F16, F16), (BF16, BF16), (I8, I8), and every
+ * pair of FP8_E4M3 / BF8_E5M2 (the page "CDNA3 sparse MFMA builtins" lists all
+ * four FP8 x BF8 combinations).  Other pairs return MMAC_ERR_UNSUPPORTED.
+ */
+mmac_status_t mmac_gemm_dense(mmac_dtype_t a_type, mmac_dtype_t b_type,
+                              int64_t M, int64_t N, int64_t K, double alpha,
+                              const void *A, int64_t lda,
+                              const void *B, int64_t ldb,
+                              double beta, const void *C, int64_t ldc,
+                              void *D, int64_t ldd, void *stream);
+
+/*
+ * 4:2 compression of a dense A ("CDNA3 sparse MFMA builtins", "Structured
+ * sparsity (4:2 pattern)": walk K in groups of four and pack the two non-zeros
+ * of each group one after the other).
+ *   A    dense row-major M x K of a_type (any of the five types), K % 4 == 0.
+ *   Ac   output, row-major M x K/2 of a_type.
+ *   idx  output, row-major M x ceil(K/32) words (layout above).
+ *   bad_groups  device pointer to one uint32 or NULL; if given, the number of
+ *        groups with more than two non-zeros is atomically added to it (the
+ *        caller clears it).
+ * Rules per group: a non-zero is any element other than +0/-0 (floating) or 0
+ * (int8); a NaN counts as non-zero.  More than two non-zeros: the two lowest
+ * positions are kept and the group is counted in bad_groups.  Fewer than two:
+ * the lowest unused positions fill the pair (their stored value is the zero
+ * found there, bit for bit).  The output is bit-exact and deterministic.
+ */
+mmac_status_t mmac_sparse24_compress(mmac_dtype_t a_type, int64_t M, int64_t K,
+                                     const void *A, int64_t lda,
+                                     void *Ac, int64_t ldac,
+                                     uint32_t *idx, int64_t ldidx,
+                                     uint32_t *bad_groups, void *stream);
+
+/*
+ * Sparse GEMM with a compressed 4:2 A: D = alpha * A*B + beta * C, where A is
+ * the dense M x K matrix described by (Ac, idx) and B, C, D are as in
+ * mmac_gemm_dense.  K is the dense K and must be a multiple of 4.  Supported
+ * pairs are those of mmac_gemm_dense.  Every index nibble must name a pair
+ * p0 < p1 (the compressor only writes such nibbles); other nibble values give
+ * unspecified results.  Floating work is counted with the dense K
+ * ("dense-equivalent": 2*M*N*K), as the page's sparse instruction table does.
+ */
+mmac_status_t mmac_gemm_sparse24(mmac_dtype_t a_type, mmac_dtype_t b_type,
+                                 int64_t M, int64_t N, int64_t K, double alpha,
+                                 const void *Ac, int64_t ldac,
+                                 const uint32_t *idx, int64_t ldidx,
+                                 const void *B, int64_t ldb,
+                                 double beta, const void *C, int64_t ldc,
+                                 void *D, int64_t ldd, void *stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *mmac_status_string(mmac_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MMAC_H */

@@ -50,8 +50,14 @@ def lib():
                                                        i64, dbl, vp, i64, i64, vp, vp, vp, vp]
         L.oracle_gemm_sparse24_i8.argtypes = [i64, i64, i64, i64, vp, i64, vp, i64, vp, i64, i64, vp, i64,
                                               i64, i64, vp, i64, vp]
+        L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
+
+
+def num_threads():
+    """Threads the oracle's OpenMP loops use."""
+    return int(lib().oracle_num_threads())
 
 
 def _p(a):

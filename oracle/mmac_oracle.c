@@ -36,6 +36,7 @@
  * 4*(g mod 8) of word g/8.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -425,3 +426,6 @@ int oracle_gemm_sparse24_i8(int64_t M, int64_t N, int64_t K, int64_t alpha,
 
 /* Tell the caller whether a type code is a floating type (used by the wrapper). */
 int oracle_is_float_type(int t) { return is_float_type(t); }
+
+/* Number of threads the oracle's parallel loops use. */
+int oracle_num_threads(void) { return omp_get_max_threads(); }

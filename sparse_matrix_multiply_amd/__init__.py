@@ -1,0 +1,126 @@
+"""Python binding of libmmac: tiled dense and 4:2-sparse GEMM for MI355X (gfx950).
+
+Thin ctypes layer over the C ABI in include/mmac.h, with the same three entry
+points.  It only marshals arguments: torch tensors provide device memory and
+the current HIP stream; every step of the computation runs in the library's
+HIP kernels.  If libmmac.so is missing, importing the binding succeeds but the
+first call raises -- there is no fallback path.
+
+Tensor conventions (element strides; the last dimension must be contiguous):
+    A   M x K  row-major             (torch dtype gives the element type)
+    B   N x K  (the K x N matrix B stored column-major)
+    C,D M x N  float32 (int32 for int8 inputs)
+    Ac  M x K/2, idx M x ceil(K/32) int32/uint32 words
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmmac.so")
+
+F16, BF16, I8, FP8_E4M3, BF8_E5M2 = 1, 2, 3, 4, 5
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_HIP = 0, 1, 2, 3, 4
+
+DTYPE_OF = {torch.float16: F16, torch.bfloat16: BF16, torch.int8: I8,
+            torch.float8_e4m3fn: FP8_E4M3, torch.float8_e5m2: BF8_E5M2}
+TORCH_OF = {v: k for k, v in DTYPE_OF.items()}
+
+_lib = None
+
+
+class MmacError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {string(status)}")
+
+
+def lib():
+    """The loaded libmmac.so (raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run `python -m sparse_matrix_multiply_amd.build` first")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, dbl, vp, i32 = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p, ctypes.c_int
+        L.mmac_gemm_dense.restype = i32
+        L.mmac_gemm_dense.argtypes = [i32, i32, i64, i64, i64, dbl, vp, i64, vp, i64, dbl, vp, i64, vp, i64, vp]
+        L.mmac_sparse24_compress.restype = i32
+        L.mmac_sparse24_compress.argtypes = [i32, i64, i64, vp, i64, vp, i64, vp, i64, vp, vp]
+        L.mmac_gemm_sparse24.restype = i32
+        L.mmac_gemm_sparse24.argtypes = [i32, i32, i64, i64, i64, dbl, vp, i64, vp, i64, vp, i64, dbl, vp, i64,
+                                         vp, i64, vp]
+        L.mmac_status_string.restype = ctypes.c_char_p
+        L.mmac_status_string.argtypes = [i32]
+        _lib = L
+    return _lib
+
+
+def string(status):
+    return lib().mmac_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _ld(t):
+    """Row pitch (elements) of a 2-D tensor whose last dimension is contiguous."""
+    if t.dim() != 2 or (t.stride(1) != 1 and t.shape[1] > 1):
+        raise ValueError("expected a 2-D tensor with a contiguous last dimension")
+    return max(t.stride(0), t.shape[1], 1)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype(t, given):
+    return given if given is not None else DTYPE_OF[t.dtype]
+
+
+def _check(status, what):
+    if status != OK:
+        raise MmacError(status, what)
+
+
+def gemm_dense(A, B, D, alpha=1.0, beta=0.0, C=None, a_type=None, b_type=None, stream=None):
+    """D = alpha * A @ B + beta * C with A M x K (row-major) and B given as its N x K transpose."""
+    M, K = A.shape
+    N = B.shape[0]
+    ta, tb = _dtype(A, a_type), _dtype(B, b_type)
+    st = lib().mmac_gemm_dense(ta, tb, M, N, K, float(alpha), _ptr(A), _ld(A), _ptr(B), _ld(B), float(beta),
+                               _ptr(C), _ld(C) if C is not None else 0, _ptr(D), _ld(D), _stream(stream))
+    _check(st, "mmac_gemm_dense")
+    return D
+
+
+def sparse24_compress(A, Ac, idx, bad_groups=None, a_type=None, stream=None):
+    """Compress a 4:2 A (M x K) into Ac (M x K/2) and idx (M x ceil(K/32) words)."""
+    M, K = A.shape
+    ta = _dtype(A, a_type)
+    st = lib().mmac_sparse24_compress(ta, M, K, _ptr(A), _ld(A), _ptr(Ac), _ld(Ac), _ptr(idx), _ld(idx),
+                                      _ptr(bad_groups), _stream(stream))
+    _check(st, "mmac_sparse24_compress")
+    return Ac, idx
+
+
+def gemm_sparse24(Ac, idx, B, D, K=None, alpha=1.0, beta=0.0, C=None, a_type=None, b_type=None, stream=None):
+    """D = alpha * A @ B + beta * C with A given compressed (Ac, idx); K is the dense K."""
+    M = Ac.shape[0]
+    N, KB = B.shape
+    K = KB if K is None else K
+    ta, tb = _dtype(Ac, a_type), _dtype(B, b_type)
+    st = lib().mmac_gemm_sparse24(ta, tb, M, N, K, float(alpha), _ptr(Ac), _ld(Ac), _ptr(idx), _ld(idx),
+                                  _ptr(B), _ld(B), float(beta), _ptr(C), _ld(C) if C is not None else 0,
+                                  _ptr(D), _ld(D), _stream(stream))
+    _check(st, "mmac_gemm_sparse24")
+    return D
+
+
+def raw_call(name, *args):
+    """Call a C entry point with raw arguments (pointers as ints); returns the status."""
+    return getattr(lib(), name)(*args)

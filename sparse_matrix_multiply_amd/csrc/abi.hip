@@ -1,0 +1,171 @@
+// C ABI of libmmac: argument validation on the host, kernel selection, launch
+// on the caller's stream.  The public contract is in include/mmac.h.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+
+#include "launch.h"
+#include "mmac.h"
+
+using namespace mmac;
+
+namespace {
+
+constexpr int64_t kMaxDim = 0x7fffffff;          // M, N, K below 2^31
+constexpr int64_t kMaxPitchBytes = (int64_t)1 << 23;  // 256 rows of a tile must span < 2^31 bytes
+
+int elem_size(int t) { return (t == MMAC_F16 || t == MMAC_BF16) ? 2 : 1; }
+bool valid_type(int t) { return t >= MMAC_F16 && t <= MMAC_BF8_E5M2; }
+bool is_fp8(int t) { return t == MMAC_FP8_E4M3 || t == MMAC_BF8_E5M2; }
+
+bool supported_pair(int a, int b) {
+    if (!valid_type(a) || !valid_type(b)) return false;
+    if (is_fp8(a)) return is_fp8(b);
+    return a == b;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+
+bool integral_i32(double v) { return std::isfinite(v) && v == std::floor(v) && v >= -2147483648.0 && v <= 2147483647.0; }
+
+// Optional overrides for tuning: MMAC_TILE=256|128|64, MMAC_GROUP_M=<n>.
+int env_int(const char *name, int dflt) {
+    const char *s = std::getenv(name);
+    if (!s || !*s) return dflt;
+    return std::atoi(s);
+}
+
+TileShape pick_shape(int64_t M, int64_t N) {
+    const int forced = env_int("MMAC_TILE", 0);
+    if (forced == 256) return TILE_256;
+    if (forced == 128) return TILE_128;
+    if (forced == 64) return TILE_64;
+    // Largest tile that still gives about one tile per compute unit (256 CUs).
+    auto tiles = [&](int t) { return ((M + t - 1) / t) * ((N + t - 1) / t); };
+    if (tiles(256) >= 192) return TILE_256;
+    if (tiles(128) >= 192) return TILE_128;
+    return TILE_64;
+}
+
+// Common checks of the GEMM calls.  Returns MMAC_OK or the error.
+mmac_status_t check_gemm(int a, int b, int64_t M, int64_t N, int64_t K, double alpha, const void *A,
+                         int64_t lda, int64_t a_cols, const void *B, int64_t ldb, double beta, const void *C,
+                         int64_t ldc, const void *D, int64_t ldd) {
+    if (!supported_pair(a, b)) return MMAC_ERR_UNSUPPORTED;
+    if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return MMAC_ERR_INVALID_ARG;
+    if (!A || !B || !D) return MMAC_ERR_INVALID_ARG;
+    if (beta != 0.0 && !C) return MMAC_ERR_INVALID_ARG;
+    if (lda < a_cols || ldb < K || lda < 1 || ldb < 1 || ldd < N || (C && beta != 0.0 && ldc < N))
+        return MMAC_ERR_INVALID_ARG;
+    if (!std::isfinite(alpha) || !std::isfinite(beta)) return MMAC_ERR_INVALID_ARG;
+    if (a == MMAC_I8 && (!integral_i32(alpha) || !integral_i32(beta))) return MMAC_ERR_INVALID_ARG;
+    if (C == D && beta != 0.0 && ldc != ldd) return MMAC_ERR_INVALID_ARG;
+    const int es = elem_size(a);
+    if (lda * es > kMaxPitchBytes || ldb * es > kMaxPitchBytes) return MMAC_ERR_UNSUPPORTED;
+    if (!aligned16(A) || !aligned16(B) || (lda * es) % 16 || (ldb * es) % 16) return MMAC_ERR_MISALIGNED;
+    if (!aligned4(D) || (C && beta != 0.0 && !aligned4(C))) return MMAC_ERR_MISALIGNED;
+    return MMAC_OK;
+}
+
+GemmParams make_params(int a, int64_t M, int64_t N, int64_t K, double alpha, const void *A, int64_t lda,
+                       const void *B, int64_t ldb, double beta, const void *C, int64_t ldc, void *D, int64_t ldd,
+                       TileShape shape) {
+    GemmParams p{};
+    const int es = elem_size(a);
+    p.A = static_cast<const uint8_t *>(A);
+    p.a_pitch = lda * es;
+    p.B = static_cast<const uint8_t *>(B);
+    p.b_pitch = ldb * es;
+    p.C = beta != 0.0 ? C : nullptr;
+    p.ldc = ldc;
+    p.D = D;
+    p.ldd = ldd;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.alpha = (float)alpha;
+    p.beta = (float)beta;
+    p.ialpha = a == MMAC_I8 ? (int)alpha : 0;
+    p.ibeta = a == MMAC_I8 ? (int)beta : 0;
+    p.use_c = beta != 0.0 ? 1 : 0;
+    const int t = tile_rows(shape);
+    p.tiles_m = (int)((M + t - 1) / t);
+    p.tiles_n = (int)((N + t - 1) / t);
+    p.group_m = std::max(1, env_int("MMAC_GROUP_M", 4));
+    return p;
+}
+
+mmac_status_t launched(hipError_t e) { return e == hipSuccess ? MMAC_OK : MMAC_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+mmac_status_t mmac_gemm_dense(mmac_dtype_t a_type, mmac_dtype_t b_type, int64_t M, int64_t N, int64_t K,
+                              double alpha, const void *A, int64_t lda, const void *B, int64_t ldb, double beta,
+                              const void *C, int64_t ldc, void *D, int64_t ldd, void *stream) {
+    const mmac_status_t st = check_gemm(a_type, b_type, M, N, K, alpha, A, lda, K, B, ldb, beta, C, ldc, D, ldd);
+    if (st != MMAC_OK) return st;
+    if (M == 0 || N == 0) return MMAC_OK;
+    const TileShape shape = pick_shape(M, N);
+    const GemmParams p = make_params(a_type, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd, shape);
+    return launched(launch_gemm_dense(a_type, b_type, shape, p, static_cast<hipStream_t>(stream)));
+}
+
+mmac_status_t mmac_sparse24_compress(mmac_dtype_t a_type, int64_t M, int64_t K, const void *A, int64_t lda,
+                                     void *Ac, int64_t ldac, uint32_t *idx, int64_t ldidx, uint32_t *bad_groups,
+                                     void *stream) {
+    if (!valid_type(a_type)) return MMAC_ERR_UNSUPPORTED;
+    if (M < 0 || K < 0 || M > kMaxDim || K > kMaxDim || (K % 4) != 0) return MMAC_ERR_INVALID_ARG;
+    if (!A || !Ac || !idx) return MMAC_ERR_INVALID_ARG;
+    const int64_t words = (K + 31) / 32;
+    if (lda < K || ldac < K / 2 || ldidx < words || lda < 1 || ldac < 1 || ldidx < 1) return MMAC_ERR_INVALID_ARG;
+    const int es = elem_size(a_type);
+    if (!aligned16(A) || !aligned16(Ac) || (lda * es) % 16 || (ldac * es) % 16) return MMAC_ERR_MISALIGNED;
+    if (!aligned4(idx) || (bad_groups && !aligned4(bad_groups))) return MMAC_ERR_MISALIGNED;
+    if (M == 0 || K == 0) return MMAC_OK;
+    CompressParams p{};
+    p.A = static_cast<const uint8_t *>(A);
+    p.a_pitch = lda * es;
+    p.Ac = static_cast<uint8_t *>(Ac);
+    p.ac_pitch = ldac * es;
+    p.idx = idx;
+    p.idx_pitch = ldidx;
+    p.bad = bad_groups;
+    p.M = (int)M;
+    p.K = (int)K;
+    return launched(launch_compress(a_type, p, static_cast<hipStream_t>(stream)));
+}
+
+mmac_status_t mmac_gemm_sparse24(mmac_dtype_t a_type, mmac_dtype_t b_type, int64_t M, int64_t N, int64_t K,
+                                 double alpha, const void *Ac, int64_t ldac, const uint32_t *idx, int64_t ldidx,
+                                 const void *B, int64_t ldb, double beta, const void *C, int64_t ldc, void *D,
+                                 int64_t ldd, void *stream) {
+    if (K >= 0 && (K % 4) != 0) return MMAC_ERR_INVALID_ARG;
+    const mmac_status_t st = check_gemm(a_type, b_type, M, N, K, alpha, Ac, ldac, K / 2, B, ldb, beta, C, ldc, D, ldd);
+    if (st != MMAC_OK) return st;
+    if (!idx || ldidx < (K + 31) / 32 || ldidx < 1) return MMAC_ERR_INVALID_ARG;
+    if (ldidx * 4 * 256 > ((int64_t)1 << 31)) return MMAC_ERR_UNSUPPORTED;
+    if (!aligned4(idx)) return MMAC_ERR_MISALIGNED;
+    if (M == 0 || N == 0) return MMAC_OK;
+    const TileShape shape = pick_shape(M, N);
+    GemmParams p = make_params(a_type, M, N, K, alpha, Ac, ldac, B, ldb, beta, C, ldc, D, ldd, shape);
+    p.idx = idx;
+    p.idx_pitch = ldidx;
+    return launched(launch_gemm_sparse(a_type, b_type, shape, p, static_cast<hipStream_t>(stream)));
+}
+
+const char *mmac_status_string(mmac_status_t s) {
+    switch (s) {
+    case MMAC_OK: return "MMAC_OK";
+    case MMAC_ERR_INVALID_ARG: return "MMAC_ERR_INVALID_ARG: invalid argument";
+    case MMAC_ERR_UNSUPPORTED: return "MMAC_ERR_UNSUPPORTED: unsupported element types or sizes";
+    case MMAC_ERR_MISALIGNED: return "MMAC_ERR_MISALIGNED: pointer or row pitch not aligned as required";
+    case MMAC_ERR_HIP: return "MMAC_ERR_HIP: the HIP runtime refused the launch";
+    default: return "unknown mmac status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,164 @@
+// Device primitives for the gfx950 GEMM kernels: fragment types, buffer
+// resources, the LDS swizzle and one wrapper per matrix instruction.
+//
+// Fragment convention used by every kernel here.  A matrix instruction with a
+// 32 x 32 output tile takes, in each of the 64 lanes, one row of A (lane mod
+// 32) and one column of B (lane mod 32); the two lane halves (g = lane / 32)
+// carry two different K slices of that row / column.  This library gives lane
+// half g the g-th contiguous half of the instruction's K step, for A and B
+// alike.  For a dense product the order in which K values sit in the lanes
+// does not change the sum as long as A and B use the same order; for the
+// sparse instructions the compressed A values of a lane half, its index bits
+// and its dense B values all cover the same K slice.  The output tile uses
+// the one-block 32 x 32 accumulator layout ("CDNA dense MFMA builtins",
+// "Accumulator layout", 32x32 layout; "CDNA3 sparse MFMA builtins",
+// "Accumulator layout": sparse instructions use the same one-block layout).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mmac {
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x16 __attribute__((ext_vector_type(16)));
+
+enum : int { DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3, DT_E4M3 = 4, DT_E5M2 = 5 };
+
+// Word 3 of a gfx9 buffer descriptor for raw (untyped) 32-bit accesses.
+constexpr int kBufferWord3 = 0x00020000;
+// A byte offset that is never inside any buffer this library builds: loads
+// from it return zero.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufferWord3);
+}
+
+// LDS tiles are stored in 16-byte units.  Unit L of a tile (row-major, W units
+// per row) sits at physical unit swz(L): inside each aligned run of 8 units
+// (128 bytes) the position is XOR-ed with the run number mod 8, so that the 8
+// rows read by 8 consecutive lanes at the same column land in 8 different
+// 16-byte bank groups.  The map is its own inverse.
+__device__ __forceinline__ constexpr uint32_t swz(uint32_t L) { return (L & ~7u) | ((L ^ (L >> 3)) & 7u); }
+
+// ---- matrix-instruction wrappers -----------------------------------------
+// Each describes one instruction: bytes of A and B per lane, dense K per
+// instruction, accumulator and output types, and mma().
+
+template <int BYTES> struct Frag;
+template <> struct Frag<16> { i32x4 v; };
+template <> struct Frag<32> { i32x4 lo, hi; };
+
+__device__ __forceinline__ i32x8 join(const Frag<32> &f) {
+    return i32x8{f.lo[0], f.lo[1], f.lo[2], f.lo[3], f.hi[0], f.hi[1], f.hi[2], f.hi[3]};
+}
+
+// Dense bf16 / fp16: v_mfma_f32_32x32x16_{bf16,f16}, 8 elements (16 B) per lane.
+template <int DT> struct MmaDense16 {
+    static constexpr bool kSparse = false;
+    static constexpr int kEsize = 2, kAFrag = 16, kBFrag = 16, kKStep = 16;
+    static constexpr int kBK = 64;                 // dense K per LDS k-tile (128 B rows)
+    static constexpr int kARowBytes = kBK * kEsize, kBRowBytes = kBK * kEsize;
+    typedef f32x16 acc_t;
+    typedef float out_t;
+    __device__ __forceinline__ static acc_t mma(const Frag<16> &a, const Frag<16> &b, acc_t c, uint32_t) {
+        if constexpr (DT == DT_BF16)
+            return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.v),
+                                                          __builtin_bit_cast(bf16x8, b.v), c, 0, 0, 0);
+        else
+            return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a.v),
+                                                         __builtin_bit_cast(f16x8, b.v), c, 0, 0, 0);
+    }
+};
+
+// Dense int8: v_mfma_i32_32x32x32_i8, 16 elements (16 B) per lane.
+struct MmaDenseI8 {
+    static constexpr bool kSparse = false;
+    static constexpr int kEsize = 1, kAFrag = 16, kBFrag = 16, kKStep = 32;
+    static constexpr int kBK = 128;
+    static constexpr int kARowBytes = kBK, kBRowBytes = kBK;
+    typedef i32x16 acc_t;
+    typedef int32_t out_t;
+    __device__ __forceinline__ static acc_t mma(const Frag<16> &a, const Frag<16> &b, acc_t c, uint32_t) {
+        return __builtin_amdgcn_mfma_i32_32x32x32_i8(a.v, b.v, c, 0, 0, 0);
+    }
+};
+
+// Dense fp8 / bf8 (OCP): v_mfma_f32_32x32x64_f8f6f4 with unit scales; the
+// format selectors name the A and B formats (0 = E4M3, 1 = E5M2).
+template <int FA, int FB> struct MmaDenseF8 {
+    static constexpr bool kSparse = false;
+    static constexpr int kEsize = 1, kAFrag = 32, kBFrag = 32, kKStep = 64;
+    static constexpr int kBK = 128;
+    static constexpr int kARowBytes = kBK, kBRowBytes = kBK;
+    typedef f32x16 acc_t;
+    typedef float out_t;
+    __device__ __forceinline__ static acc_t mma(const Frag<32> &a, const Frag<32> &b, acc_t c, uint32_t) {
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(join(a), join(b), c, FA, FB, 0, 0, 0, 0);
+    }
+};
+
+// Sparse fp16 / bf16: v_smfmac_f32_32x32x32_{f16,bf16}.  Per lane: 8
+// compressed A values (16 B) = 16 dense K, 16 dense B values (32 B), and 16
+// index bits (4 groups).  One index word covers the instruction's 32 dense K;
+// lane half g takes its bits [16g, 16g + 16).
+template <int DT> struct MmaSparse16 {
+    static constexpr bool kSparse = true;
+    static constexpr int kEsize = 2, kAFrag = 16, kBFrag = 32, kKStep = 32;
+    static constexpr int kBK = 64;
+    static constexpr int kARowBytes = kBK / 2 * kEsize, kBRowBytes = kBK * kEsize;
+    static constexpr int kIdxWordsPerTile = kBK / 32;
+    typedef f32x16 acc_t;
+    typedef float out_t;
+    // index bits of lane half g for step s of a k-tile, from that tile's words
+    __device__ __forceinline__ static uint32_t lane_idx(const uint32_t *w, int s, int g) { return w[s] >> (16 * g); }
+    __device__ __forceinline__ static acc_t mma(const Frag<16> &a, const Frag<32> &b, acc_t c, uint32_t idx) {
+        if constexpr (DT == DT_BF16)
+            return __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(bf16x8, a.v),
+                                                            __builtin_bit_cast(bf16x16, join(b)), c, (int)idx, 0, 0);
+        else
+            return __builtin_amdgcn_smfmac_f32_32x32x32_f16(__builtin_bit_cast(f16x8, a.v),
+                                                           __builtin_bit_cast(f16x16, join(b)), c, (int)idx, 0, 0);
+    }
+};
+
+// Sparse int8 / fp8 / bf8: v_smfmac_{i32,f32}_32x32x64_*.  Per lane: 16
+// compressed A bytes = 32 dense K, 32 dense B bytes, 32 index bits (8 groups).
+// The instruction's 64 dense K take two index words; lane half g takes word g.
+template <int DT_A, int DT_B> struct MmaSparse8 {
+    static constexpr bool kSparse = true;
+    static constexpr int kEsize = 1, kAFrag = 16, kBFrag = 32, kKStep = 64;
+    static constexpr int kBK = 128;
+    static constexpr int kARowBytes = kBK / 2, kBRowBytes = kBK;
+    static constexpr int kIdxWordsPerTile = kBK / 32;
+    static constexpr bool kInt = (DT_A == DT_I8);
+    typedef typename std::conditional<kInt, i32x16, f32x16>::type acc_t;
+    typedef typename std::conditional<kInt, int32_t, float>::type out_t;
+    __device__ __forceinline__ static uint32_t lane_idx(const uint32_t *w, int s, int g) { return w[2 * s + g]; }
+    __device__ __forceinline__ static acc_t mma(const Frag<16> &a, const Frag<32> &b, acc_t c, uint32_t idx) {
+        if constexpr (kInt)
+            return __builtin_amdgcn_smfmac_i32_32x32x64_i8(a.v, join(b), c, (int)idx, 0, 0);
+        else if constexpr (DT_A == DT_E4M3 && DT_B == DT_E4M3)
+            return __builtin_amdgcn_smfmac_f32_32x32x64_fp8_fp8(a.v, join(b), c, (int)idx, 0, 0);
+        else if constexpr (DT_A == DT_E4M3 && DT_B == DT_E5M2)
+            return __builtin_amdgcn_smfmac_f32_32x32x64_fp8_bf8(a.v, join(b), c, (int)idx, 0, 0);
+        else if constexpr (DT_A == DT_E5M2 && DT_B == DT_E4M3)
+            return __builtin_amdgcn_smfmac_f32_32x32x64_bf8_fp8(a.v, join(b), c, (int)idx, 0, 0);
+        else
+            return __builtin_amdgcn_smfmac_f32_32x32x64_bf8_bf8(a.v, join(b), c, (int)idx, 0, 0);
+    }
+};
+
+}  // namespace mmac

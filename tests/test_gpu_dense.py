@@ -1,0 +1,137 @@
+"""GPU parity of mmac_gemm_dense against the CPU oracle (small and ragged shapes).
+
+Every supported element-type pair, every tile shape the library can pick,
+shapes that span several tiles with ragged M, N and K tails (including K tails
+that cut a 16-byte unit), exact small-integer inputs (bit-exact whatever the
+summation order), the beta = 0 / NaN-C rule, in-place C == D, K == 0, and
+run-to-run determinism.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_matrix_multiply_amd as mm
+import workloads as W
+from gpu_helpers import (FP8, assert_close, dev, out_tensor, run_dense, tile_shape, to_dev_bits)
+from oracle import BF16, E4M3, E5M2, F16, I8
+
+pytestmark = pytest.mark.gpu
+
+PAIRS = [(BF16, BF16), (F16, F16), (I8, I8), (E4M3, E4M3), (E4M3, E5M2), (E5M2, E4M3), (E5M2, E5M2)]
+SHAPES = [(64, 64, 64), (100, 77, 200), (257, 130, 333), (33, 300, 1000), (300, 260, 128), (1, 1, 1)]
+
+
+def inputs(ta, tb, M, N, K, seed):
+    g = np.random.default_rng(seed)
+    if ta == I8:
+        A = g.integers(-128, 128, size=(M, K)).astype(np.int8)
+        B = g.integers(-128, 128, size=(N, K)).astype(np.int8)
+        C = g.integers(-1000, 1001, size=(M, N)).astype(np.int32)
+        return A, B, C, 3, -2
+    A = W.to_bits(g.standard_normal((M, K)), ta)
+    B = W.to_bits(g.standard_normal((N, K)), tb)
+    C = g.standard_normal((M, N)).astype(np.float32)
+    return A, B, C, 1.5, -0.75
+
+
+@pytest.mark.parametrize("tile", [256, 128, 64])
+@pytest.mark.parametrize("ta,tb", PAIRS)
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_dense_matches_oracle(ta, tb, M, N, K, tile):
+    A, B, C, alpha, beta = inputs(ta, tb, M, N, K, M * 7 + N * 3 + K + ta * 11 + tb)
+    with tile_shape(tile):
+        D = run_dense(ta, tb, A, B, alpha, beta, C)
+    Dref, aux = oracle.gemm_dense(ta, tb, A, B, alpha, beta, C)
+    if ta == I8:
+        assert np.array_equal(D, Dref), f"int8 mismatch at {np.argwhere(D != Dref)[:5]}"
+    else:
+        assert_close(D, Dref, aux, ta, K, alpha, beta, C, f"{ta},{tb} {M}x{N}x{K} tile {tile}")
+
+
+@pytest.mark.parametrize("ta,tb", [(BF16, BF16), (F16, F16), (E4M3, E5M2), (E5M2, E5M2)])
+def test_small_integers_are_exact(ta, tb):
+    """|a|, |b| <= 4 integers with K = 520: every partial sum is an integer below 2^24,
+    so the fp32 result is exact whatever the order of summation."""
+    M, N, K = 130, 70, 520
+    g = np.random.default_rng(5)
+    A = W.to_bits(g.integers(-4, 5, size=(M, K)).astype(np.float64), ta)
+    B = W.to_bits(g.integers(-4, 5, size=(N, K)).astype(np.float64), tb)
+    C = g.integers(-50, 51, size=(M, N)).astype(np.float32)
+    for tile in (256, 64):
+        with tile_shape(tile):
+            D = run_dense(ta, tb, A, B, 1.0, 1.0, C)
+        Dref, _ = oracle.gemm_dense(ta, tb, A, B, 1.0, 1.0, C)
+        assert np.array_equal(D.astype(np.float64), Dref)
+
+
+@pytest.mark.parametrize("t", [BF16, E4M3])
+def test_identity_and_permutation(t):
+    n = 160
+    one, zero = W.to_bits(np.ones(1), t)[0], W.zero_bits(t)
+    g = np.random.default_rng(3)
+    B = W.to_bits(g.standard_normal((n, n)), t)
+    perm = g.permutation(n)
+    P = np.full((n, n), zero, oracle.BITS_DTYPE[t])
+    P[np.arange(n), perm] = one
+    D = run_dense(t, t, P, B, 1.0, 0.0, None)
+    Bf = W.from_bits(B, t).astype(np.float64)          # Bf[j, k] = B[k, j]
+    assert np.array_equal(D.astype(np.float64), Bf.T[perm, :])
+
+
+def test_beta_zero_never_reads_c():
+    M, N, K = 96, 96, 64
+    A, B, _, _, _ = inputs(BF16, BF16, M, N, K, 1)
+    Cnan = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev())
+    D = run_dense(BF16, BF16, A, B, 1.0, 0.0, None, C_dev=Cnan)
+    assert np.isfinite(D).all()
+    Dref, S = oracle.gemm_dense(BF16, BF16, A, B)
+    assert_close(D, Dref, S, BF16, K, 1.0, 0.0)
+
+
+@pytest.mark.parametrize("ta", [BF16, I8])
+def test_in_place_c_equals_d(ta):
+    M, N, K = 200, 144, 96
+    A, B, C, alpha, beta = inputs(ta, ta, M, N, K, 2)
+    Cd = torch.from_numpy(C).to(dev())
+    mm.gemm_dense(to_dev_bits(A, ta), to_dev_bits(B, ta), Cd, alpha, beta, Cd, a_type=ta, b_type=ta)
+    torch.cuda.synchronize()
+    Dref, aux = oracle.gemm_dense(ta, ta, A, B, alpha, beta, C)
+    if ta == I8:
+        assert np.array_equal(Cd.cpu().numpy(), Dref)
+    else:
+        assert_close(Cd.cpu().numpy(), Dref, aux, ta, K, alpha, beta, C)
+
+
+def test_k_zero_gives_beta_c():
+    M, N = 70, 90
+    C = np.random.default_rng(1).standard_normal((M, N)).astype(np.float32)
+    Ad = to_dev_bits(np.zeros((M, 8), np.uint16), BF16)[:, :0]
+    Bd = to_dev_bits(np.zeros((N, 8), np.uint16), BF16)[:, :0]
+    D = out_tensor(M, N, False)
+    mm.gemm_dense(Ad, Bd, D, 2.0, 0.5, torch.from_numpy(C).to(dev()), a_type=BF16, b_type=BF16)
+    torch.cuda.synchronize()
+    assert np.array_equal(D.cpu().numpy(), (np.float32(0.5) * C))
+
+
+def test_output_pitch_and_untouched_padding():
+    M, N, K = 65, 33, 100
+    A, B, C, alpha, beta = inputs(F16, F16, M, N, K, 9)
+    ldd = 50
+    Ad, Bd = to_dev_bits(A, F16), to_dev_bits(B, F16)
+    buf = torch.full((M, ldd), 123.0, dtype=torch.float32, device=dev())
+    mm.gemm_dense(Ad, Bd, buf[:, :N], alpha, beta, torch.from_numpy(C).to(dev()), a_type=F16, b_type=F16)
+    torch.cuda.synchronize()
+    out = buf.cpu().numpy()
+    assert (out[:, N:] == 123.0).all()
+    Dref, S = oracle.gemm_dense(F16, F16, A, B, alpha, beta, C)
+    assert_close(out[:, :N], Dref, S, F16, K, alpha, beta, C)
+
+
+@pytest.mark.parametrize("ta,tb", [(BF16, BF16), (E4M3, E5M2)])
+def test_deterministic(ta, tb):
+    M, N, K = 512, 512, 1024
+    A, B, C, alpha, beta = inputs(ta, tb, M, N, K, 4)
+    D1 = run_dense(ta, tb, A, B, alpha, beta, C)
+    D2 = run_dense(ta, tb, A, B, alpha, beta, C)
+    assert np.array_equal(D1, D2)

@@ -1,0 +1,79 @@
+"""GPU parity at the full sizes of the benchmark workloads, in the launch configuration
+the benchmark times (the library's default tile choice).
+
+Small workloads are checked against the full oracle; the large ones against
+oracle rows and entries that the CPU computes in seconds: two whole 256 x 256
+output tiles (every wave, lane and register position of a workgroup) plus
+random entries.  Compressor output is always compared in full, bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_matrix_multiply_amd as mm
+import workloads as W
+from gpu_helpers import (assert_close, compress_dev, dev, dev_bits_to_host, out_tensor, sample_entries,
+                         to_dev_bits, tolerance)
+
+pytestmark = pytest.mark.gpu
+
+
+def dense_on_gpu(w):
+    Ad, Bd = to_dev_bits(w["A"], w["ta"]), to_dev_bits(w["B"], w["tb"])
+    integer = w["ta"] == oracle.I8
+    D = out_tensor(w["M"], w["N"], integer)
+    Cd = torch.from_numpy(w["C"]).to(dev()) if w["beta"] != 0 else None
+    mm.gemm_dense(Ad, Bd, D, w["alpha"], w["beta"], Cd, a_type=w["ta"], b_type=w["tb"])
+    torch.cuda.synchronize()
+    return D
+
+
+def check_sampled(D, w, fn_entries, seed):
+    M, N, K = w["M"], w["N"], w["K"]
+    ii, jj = sample_entries(M, N, 20000, seed, tiles=((0, 0), ((M - 1) // 256, (N - 1) // 256)))
+    ref, S = fn_entries(ii, jj)
+    got = D[torch.from_numpy(ii).to(dev()), torch.from_numpy(jj).to(dev())].cpu().numpy()
+    C = w["C"][ii, jj] if w["beta"] != 0 else None
+    return assert_close(got, ref, S, w["ta"], K, w["alpha"], w["beta"], C, "sampled")
+
+
+@pytest.mark.parametrize("name", ["bf16_256", "i8_1024", "bf16_skinny"])
+def test_small_workloads_full_oracle(name):
+    w = W.workload(name)
+    D = dense_on_gpu(w).cpu().numpy()
+    Dref, aux = oracle.gemm_dense(w["ta"], w["tb"], w["A"], w["B"], w["alpha"], w["beta"], w["C"])
+    if w["ta"] == oracle.I8:
+        assert not aux                     # no int32 overflow in this workload
+        assert np.array_equal(D, Dref)
+    else:
+        assert_close(D, Dref, aux, w["ta"], w["K"], w["alpha"], w["beta"], w["C"], name)
+
+
+@pytest.mark.parametrize("name", ["bf16_4096", "bf16_8192", "fp8_8192"])
+def test_large_dense_workloads_sampled(name):
+    w = W.workload(name)
+    D = dense_on_gpu(w)
+    fn = lambda ii, jj: oracle.gemm_dense_entries(w["ta"], w["tb"], w["A"], w["B"], ii, jj, w["alpha"],
+                                                  w["beta"], w["C"])
+    check_sampled(D, w, fn, 7)
+
+
+@pytest.mark.parametrize("name", ["f16_sparse", "fp8_8192_sparse"])
+def test_sparse_workloads(name):
+    w = W.workload(name)
+    ta, tb, M, N, K = w["ta"], w["tb"], w["M"], w["N"], w["K"]
+    Ac_ref, idx_ref, bad_ref = oracle.compress24(ta, w["A"])
+    assert bad_ref == 0
+    Acd, idxd, bad = compress_dev(ta, to_dev_bits(w["A"], ta), M, K)
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 0
+    assert np.array_equal(dev_bits_to_host(Acd, ta), Ac_ref)
+    assert np.array_equal(idxd.cpu().numpy().view(np.uint32), idx_ref)
+    D = out_tensor(M, N, False)
+    mm.gemm_sparse24(Acd, idxd, to_dev_bits(w["B"], tb), D, K=K, alpha=w["alpha"], beta=w["beta"],
+                     a_type=ta, b_type=tb)
+    torch.cuda.synchronize()
+    fn = lambda ii, jj: oracle.gemm_sparse24_entries(ta, tb, Ac_ref, idx_ref, w["B"], ii, jj, w["alpha"],
+                                                     w["beta"], w["C"])
+    check_sampled(D, w, fn, 8)
