@@ -37,7 +37,8 @@
  *     D may be the same buffer as C when ldd == ldc; other overlaps between
  *     outputs and inputs are not allowed.
  *   - int8: alpha and beta must be integers that fit in int32.
- *   - M == 0 or N == 0: nothing is done.  K == 0: D = beta * C.
+ *   - M == 0 or N == 0: nothing is done.  K == 0: D = beta * C (A, B, Ac and
+ *     idx are not read and may be NULL).
  *   - Alignment: A, B, Ac must start on a 16-byte boundary and their row
  *     pitch in bytes (ld * element size) must be a multiple of 16.  C, D and
  *     idx need only their natural 4-byte alignment.

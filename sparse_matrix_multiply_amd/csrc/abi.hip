@@ -55,7 +55,7 @@ mmac_status_t check_gemm(int a, int b, int64_t M, int64_t N, int64_t K, double a
                          int64_t ldc, const void *D, int64_t ldd) {
     if (!supported_pair(a, b)) return MMAC_ERR_UNSUPPORTED;
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return MMAC_ERR_INVALID_ARG;
-    if (!A || !B || !D) return MMAC_ERR_INVALID_ARG;
+    if ((K > 0 && (!A || !B)) || !D) return MMAC_ERR_INVALID_ARG;
     if (beta != 0.0 && !C) return MMAC_ERR_INVALID_ARG;
     if (lda < a_cols || ldb < K || lda < 1 || ldb < 1 || ldd < N || (C && beta != 0.0 && ldc < N))
         return MMAC_ERR_INVALID_ARG;
@@ -146,7 +146,7 @@ mmac_status_t mmac_gemm_sparse24(mmac_dtype_t a_type, mmac_dtype_t b_type, int64
     if (K >= 0 && (K % 4) != 0) return MMAC_ERR_INVALID_ARG;
     const mmac_status_t st = check_gemm(a_type, b_type, M, N, K, alpha, Ac, ldac, K / 2, B, ldb, beta, C, ldc, D, ldd);
     if (st != MMAC_OK) return st;
-    if (!idx || ldidx < (K + 31) / 32 || ldidx < 1) return MMAC_ERR_INVALID_ARG;
+    if ((K > 0 && !idx) || ldidx < (K + 31) / 32 || ldidx < 1) return MMAC_ERR_INVALID_ARG;
     if (ldidx * 4 * 256 > ((int64_t)1 << 31)) return MMAC_ERR_UNSUPPORTED;
     if (!aligned4(idx)) return MMAC_ERR_MISALIGNED;
     if (M == 0 || N == 0) return MMAC_OK;

@@ -4,12 +4,12 @@
 // Fragment convention used by every kernel here.  A matrix instruction with a
 // 32 x 32 output tile takes, in each of the 64 lanes, one row of A (lane mod
 // 32) and one column of B (lane mod 32); the two lane halves (g = lane / 32)
-// carry two different K slices of that row / column.  This library gives lane
-// half g the g-th contiguous half of the instruction's K step, for A and B
-// alike.  For a dense product the order in which K values sit in the lanes
-// does not change the sum as long as A and B use the same order; for the
-// sparse instructions the compressed A values of a lane half, its index bits
-// and its dense B values all cover the same K slice.  The output tile uses
+// carry two different K slices of that row / column.  For a dense product the
+// order in which K values sit in the lanes does not change the sum as long as
+// A and B use the same order, and this library gives lane half g the g-th
+// contiguous half of the instruction's K step for both.  The sparse
+// instructions fix the pairing of compressed A, index and dense B (described
+// above their wrappers below).  The output tile uses
 // the one-block 32 x 32 accumulator layout ("CDNA dense MFMA builtins",
 // "Accumulator layout", 32x32 layout; "CDNA3 sparse MFMA builtins",
 // "Accumulator layout": sparse instructions use the same one-block layout).
@@ -73,6 +73,9 @@ template <int DT> struct MmaDense16 {
     static constexpr int kARowBytes = kBK * kEsize, kBRowBytes = kBK * kEsize;
     typedef f32x16 acc_t;
     typedef float out_t;
+    // 16-byte unit (within a k-tile row) of half h of the fragment of lane half g, step s
+    __device__ __forceinline__ static constexpr int a_unit(int s, int g, int) { return 2 * s + g; }
+    __device__ __forceinline__ static constexpr int b_unit(int s, int g, int) { return 2 * s + g; }
     __device__ __forceinline__ static acc_t mma(const Frag<16> &a, const Frag<16> &b, acc_t c, uint32_t) {
         if constexpr (DT == DT_BF16)
             return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.v),
@@ -91,6 +94,8 @@ struct MmaDenseI8 {
     static constexpr int kARowBytes = kBK, kBRowBytes = kBK;
     typedef i32x16 acc_t;
     typedef int32_t out_t;
+    __device__ __forceinline__ static constexpr int a_unit(int s, int g, int) { return 2 * s + g; }
+    __device__ __forceinline__ static constexpr int b_unit(int s, int g, int) { return 2 * s + g; }
     __device__ __forceinline__ static acc_t mma(const Frag<16> &a, const Frag<16> &b, acc_t c, uint32_t) {
         return __builtin_amdgcn_mfma_i32_32x32x32_i8(a.v, b.v, c, 0, 0, 0);
     }
@@ -105,11 +110,22 @@ template <int FA, int FB> struct MmaDenseF8 {
     static constexpr int kARowBytes = kBK, kBRowBytes = kBK;
     typedef f32x16 acc_t;
     typedef float out_t;
+    __device__ __forceinline__ static constexpr int a_unit(int s, int g, int h) { return 4 * s + 2 * g + h; }
+    __device__ __forceinline__ static constexpr int b_unit(int s, int g, int h) { return 4 * s + 2 * g + h; }
     __device__ __forceinline__ static acc_t mma(const Frag<32> &a, const Frag<32> &b, acc_t c, uint32_t) {
         return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(join(a), join(b), c, FA, FB, 0, 0, 0, 0);
     }
 };
 
+// Sparse instructions, A side: lane half g holds the compressed values of
+// the g-th contiguous half of the instruction's dense K (in ascending order)
+// and the index nibbles of those groups.  B side: the 64-byte K step of a B
+// column splits into four 16-byte quarters; lane half g takes quarters g and
+// 2 + g (registers 0-3 and 4-7).  This pairing was established on gfx950
+// with one-hot products through this library (each compressed slot against
+// an identity B, for all six index nibbles); it is what the parity tests
+// against the oracle check on every run.
+//
 // Sparse fp16 / bf16: v_smfmac_f32_32x32x32_{f16,bf16}.  Per lane: 8
 // compressed A values (16 B) = 16 dense K, 16 dense B values (32 B), and 16
 // index bits (4 groups).  One index word covers the instruction's 32 dense K;
@@ -122,6 +138,8 @@ template <int DT> struct MmaSparse16 {
     static constexpr int kIdxWordsPerTile = kBK / 32;
     typedef f32x16 acc_t;
     typedef float out_t;
+    __device__ __forceinline__ static constexpr int a_unit(int s, int g, int) { return 2 * s + g; }
+    __device__ __forceinline__ static constexpr int b_unit(int s, int g, int h) { return 4 * s + g + 2 * h; }
     // index bits of lane half g for step s of a k-tile, from that tile's words
     __device__ __forceinline__ static uint32_t lane_idx(const uint32_t *w, int s, int g) { return w[s] >> (16 * g); }
     __device__ __forceinline__ static acc_t mma(const Frag<16> &a, const Frag<32> &b, acc_t c, uint32_t idx) {
@@ -146,6 +164,8 @@ template <int DT_A, int DT_B> struct MmaSparse8 {
     static constexpr bool kInt = (DT_A == DT_I8);
     typedef typename std::conditional<kInt, i32x16, f32x16>::type acc_t;
     typedef typename std::conditional<kInt, int32_t, float>::type out_t;
+    __device__ __forceinline__ static constexpr int a_unit(int s, int g, int) { return 2 * s + g; }
+    __device__ __forceinline__ static constexpr int b_unit(int s, int g, int h) { return 4 * s + g + 2 * h; }
     __device__ __forceinline__ static uint32_t lane_idx(const uint32_t *w, int s, int g) { return w[2 * s + g]; }
     __device__ __forceinline__ static acc_t mma(const Frag<16> &a, const Frag<32> &b, acc_t c, uint32_t idx) {
         if constexpr (kInt)

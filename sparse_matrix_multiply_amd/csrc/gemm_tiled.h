@@ -47,13 +47,14 @@ __device__ __forceinline__ void tile_coords(int wg, const GemmParams &p, int &tm
 // s_waitcnt with vmcnt = 0 (expcnt and lgkmcnt left at their maxima).
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// One fragment from LDS: 16-byte units u0 (and u1 for 32-byte fragments) of a tile.
 template <int BYTES>
-__device__ __forceinline__ void lds_frag(Frag<BYTES> &f, const uint8_t *base, uint32_t unit) {
+__device__ __forceinline__ void lds_frag(Frag<BYTES> &f, const uint8_t *base, uint32_t u0, uint32_t u1) {
     if constexpr (BYTES == 16) {
-        f.v = *reinterpret_cast<const i32x4 *>(base + swz(unit) * 16);
+        f.v = *reinterpret_cast<const i32x4 *>(base + swz(u0) * 16);
     } else {
-        f.lo = *reinterpret_cast<const i32x4 *>(base + swz(unit) * 16);
-        f.hi = *reinterpret_cast<const i32x4 *>(base + swz(unit + 1) * 16);
+        f.lo = *reinterpret_cast<const i32x4 *>(base + swz(u0) * 16);
+        f.hi = *reinterpret_cast<const i32x4 *>(base + swz(u1) * 16);
     }
 }
 
@@ -92,7 +93,6 @@ struct TiledGemm {
     static_assert(AQ * NT == BM * AW && BQ * NT == BN * BW, "tile not a whole number of DMA passes");
     static constexpr int A_BYTES = BM * AW * 16, B_BYTES = BN * BW * 16, STAGE = A_BYTES + B_BYTES;
     static constexpr int STEPS = Op::kBK / Op::kKStep;
-    static constexpr int A_STEP = 2 * Op::kAFrag, B_STEP = 2 * Op::kBFrag;     // row bytes per instruction
     static constexpr int IW = Op::kSparse ? Op::kBK / 32 : 1;                   // index words per k-tile row
 
     const GemmParams &p;
@@ -181,26 +181,33 @@ struct TiledGemm {
         }
     }
 
-    // All matrix instructions of one k-tile held in LDS stage `st`.
-    __device__ __forceinline__ void compute(const uint8_t *st, const uint32_t (&w)[TM][IW]) {
+    typedef Frag<Op::kAFrag> FragA;
+    typedef Frag<Op::kBFrag> FragB;
+
+    // Fragments of step s of the k-tile held in LDS stage `st`.
+    __device__ __forceinline__ void load_frags(FragA (&a)[TM], FragB (&b)[TN], const uint8_t *st, int s) {
         const uint8_t *sa = st, *sb = st + A_BYTES;
 #pragma unroll
-        for (int s = 0; s < STEPS; ++s) {
-            Frag<Op::kAFrag> a[TM];
-            Frag<Op::kBFrag> b[TN];
+        for (int i = 0; i < TM; ++i) {
+            const uint32_t r = (wm * WTM + i * 32 + l32) * AW;
+            lds_frag(a[i], sa, r + Op::a_unit(s, g, 0), r + Op::a_unit(s, g, 1));
+        }
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
-                lds_frag(a[i], sa, (wm * WTM + i * 32 + l32) * AW + (s * A_STEP + g * Op::kAFrag) / 16);
+        for (int j = 0; j < TN; ++j) {
+            const uint32_t r = (wn * WTN + j * 32 + l32) * BW;
+            lds_frag(b[j], sb, r + Op::b_unit(s, g, 0), r + Op::b_unit(s, g, 1));
+        }
+    }
+
+    // The TM x TN matrix instructions of step s.
+    __device__ __forceinline__ void mma_step(const FragA (&a)[TM], const FragB (&b)[TN], const uint32_t (&w)[TM][IW],
+                                             int s) {
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                lds_frag(b[j], sb, (wn * WTN + j * 32 + l32) * BW + (s * B_STEP + g * Op::kBFrag) / 16);
+        for (int i = 0; i < TM; ++i) {
+            uint32_t ix = 0;
+            if constexpr (Op::kSparse) ix = Op::lane_idx(w[i], s, g);
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                uint32_t ix = 0;
-                if constexpr (Op::kSparse) ix = Op::lane_idx(w[i], s, g);
-#pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j] = Op::mma(a[i], b[j], acc[i][j], ix);
-            }
+            for (int j = 0; j < TN; ++j) acc[i][j] = Op::mma(a[i], b[j], acc[i][j], ix);
         }
     }
 
@@ -248,26 +255,45 @@ void gemm_tiled_kernel(GemmParams p) {
 
     const int nk = p.K / Op::kBK;                        // whole k-tiles
     const int nkt = nk + (p.K > nk * Op::kBK ? 1 : 0);   // plus a ragged one
+    constexpr int STEPS = T::STEPS;
+    static_assert(STEPS % 2 == 0, "fragment double buffering assumes an even number of steps");
     uint32_t ixc[TM][IW], ixn[TM][IW];
+    typename T::FragA a[2][TM];
+    typename T::FragB b[2][T::TN];
 
+    // Software pipeline: the fragments of step s + 1 are read from LDS while the
+    // matrix instructions of step s run; the block barrier that hands over the
+    // next LDS stage sits before the last step's instructions, so the first
+    // reads of the next k-tile overlap them.  The copy of k-tile kt + 1 into the
+    // other stage is in flight during the whole of k-tile kt.
     if (nkt > 0) {
         if (0 < nk) t.dma(st0, 0);
         else t.fill_masked(st0, 0);
         t.load_idx(ixc, 0);
+        wait_vmem_all();
+        __syncthreads();
+        t.load_frags(a[0], b[0], st0, 0);
     }
-    wait_vmem_all();
-    __syncthreads();
     for (int kt = 0; kt < nkt; ++kt) {
-        uint8_t *cur = (kt & 1) ? st1 : st0;
+        const uint8_t *cur = (kt & 1) ? st1 : st0;
         uint8_t *nxt = (kt & 1) ? st0 : st1;
         if (kt + 1 < nkt) {
             if (kt + 1 < nk) t.dma(nxt, kt + 1);
             else t.fill_masked(nxt, kt + 1);
             t.load_idx(ixn, kt + 1);
         }
-        t.compute(cur, ixc);
-        wait_vmem_all();
-        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s) {
+            const int cb = s & 1;
+            if (s + 1 < STEPS) {
+                t.load_frags(a[cb ^ 1], b[cb ^ 1], cur, s + 1);
+            } else {
+                wait_vmem_all();
+                __syncthreads();
+                if (kt + 1 < nkt) t.load_frags(a[cb ^ 1], b[cb ^ 1], nxt, 0);
+            }
+            t.mma_step(a[cb], b[cb], ixc, s);
+        }
         if constexpr (Op::kSparse) {
 #pragma unroll
             for (int i = 0; i < TM; ++i)
