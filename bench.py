@@ -209,11 +209,14 @@ def cpu_baseline(wb, rows):
     import oracle
     threads = oracle.num_threads()
     if rows <= 0:
-        # calibrate: about 15 s of CPU work from a 2-row probe
-        t = time.perf_counter()
-        oracle.gemm_dense(wb["ta"], wb["tb"], wb["A"], wb["B"], wb["alpha"], wb["beta"], wb["C"], rows=(0, 2))
-        per_row = max((time.perf_counter() - t) / 2, 1e-4)
-        rows = int(min(512, max(threads, 15.0 / per_row)))
+        # calibrate to about 15 s of CPU work: two probes, so the fixed cost (decoding B) cancels
+        def timed(r):
+            t = time.perf_counter()
+            oracle.gemm_dense(wb["ta"], wb["tb"], wb["A"], wb["B"], wb["alpha"], wb["beta"], wb["C"], rows=(0, r))
+            return time.perf_counter() - t
+        r1, r2 = threads, 3 * threads
+        per_row = max((timed(r2) - timed(r1)) / (r2 - r1), 1e-4)
+        rows = int(min(8192, max(threads, 15.0 / per_row)))
     t = time.perf_counter()
     oracle.gemm_dense(wb["ta"], wb["tb"], wb["A"], wb["B"], wb["alpha"], wb["beta"], wb["C"], rows=(0, rows))
     dt = time.perf_counter() - t
