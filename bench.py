@@ -42,11 +42,28 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="rows of the oracle slice (0 = calibrate)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain elementwise copy of this many MiB (fp32) three times: the known-size "
+                         "kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+def copy_probe(mib):
+    import torch
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.mul(x, 2.0, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe": {"bytes_read": n * 4, "bytes_written": n * 4, "launches": 3}}))
 
 
 def main():
     args = parse()
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)

@@ -30,21 +30,25 @@ bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 
 bool integral_i32(double v) { return std::isfinite(v) && v == std::floor(v) && v >= -2147483648.0 && v <= 2147483647.0; }
 
-// Optional overrides for tuning: MMAC_TILE=256|128|64, MMAC_GROUP_M=<n>.
+// Optional overrides for tuning: MMAC_TILE=256|128|64|16 (16 = skinny, M <= 32), MMAC_WAVES=4|8 (waves of
+// a 256 x 256 tile), MMAC_GROUP_M=<n>.
 int env_int(const char *name, int dflt) {
     const char *s = std::getenv(name);
     if (!s || !*s) return dflt;
     return std::atoi(s);
 }
 
-TileShape pick_shape(int64_t M, int64_t N) {
+TileShape pick_shape(int64_t M, int64_t N, bool sparse = false) {
     const int forced = env_int("MMAC_TILE", 0);
-    if (forced == 256) return TILE_256;
+    if (forced == 256) return env_int("MMAC_WAVES", 4) == 8 ? TILE_256_W8 : TILE_256;
     if (forced == 128) return TILE_128;
     if (forced == 64) return TILE_64;
+    if (forced == 16 && !sparse && M <= 32) return TILE_SKINNY;
+    // At most 32 rows: stream B once with the skinny kernel (dense A only).
+    if (!sparse && M <= 32) return TILE_SKINNY;
     // Largest tile that still gives about one tile per compute unit (256 CUs).
     auto tiles = [&](int t) { return ((M + t - 1) / t) * ((N + t - 1) / t); };
-    if (tiles(256) >= 192) return TILE_256;
+    if (tiles(256) >= 192) return env_int("MMAC_WAVES", 4) == 8 ? TILE_256_W8 : TILE_256;
     if (tiles(128) >= 192) return TILE_128;
     return TILE_64;
 }
@@ -111,6 +115,8 @@ mmac_status_t mmac_gemm_dense(mmac_dtype_t a_type, mmac_dtype_t b_type, int64_t 
     if (M == 0 || N == 0) return MMAC_OK;
     const TileShape shape = pick_shape(M, N);
     const GemmParams p = make_params(a_type, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd, shape);
+    if (shape == TILE_SKINNY)
+        return launched(launch_gemm_skinny(a_type, b_type, p, static_cast<hipStream_t>(stream)));
     return launched(launch_gemm_dense(a_type, b_type, shape, p, static_cast<hipStream_t>(stream)));
 }
 
@@ -150,7 +156,7 @@ mmac_status_t mmac_gemm_sparse24(mmac_dtype_t a_type, mmac_dtype_t b_type, int64
     if (ldidx * 4 * 256 > ((int64_t)1 << 31)) return MMAC_ERR_UNSUPPORTED;
     if (!aligned4(idx)) return MMAC_ERR_MISALIGNED;
     if (M == 0 || N == 0) return MMAC_OK;
-    const TileShape shape = pick_shape(M, N);
+    const TileShape shape = pick_shape(M, N, true);
     GemmParams p = make_params(a_type, M, N, K, alpha, Ac, ldac, B, ldb, beta, C, ldc, D, ldd, shape);
     p.idx = idx;
     p.idx_pitch = ldidx;

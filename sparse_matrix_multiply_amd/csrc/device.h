@@ -46,12 +46,20 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufferWord3);
 }
 
-// LDS tiles are stored in 16-byte units.  Unit L of a tile (row-major, W units
-// per row) sits at physical unit swz(L): inside each aligned run of 8 units
-// (128 bytes) the position is XOR-ed with the run number mod 8, so that the 8
-// rows read by 8 consecutive lanes at the same column land in 8 different
-// 16-byte bank groups.  The map is its own inverse.
-__device__ __forceinline__ constexpr uint32_t swz(uint32_t L) { return (L & ~7u) | ((L ^ (L >> 3)) & 7u); }
+// LDS tiles are stored in 16-byte units, W units per row (row-major).  The
+// LDS of gfx950 serves 16 lanes' 16-byte reads per cycle from 64 banks (256
+// bytes); the fragment reads of the kernels have 16 consecutive lanes read
+// the same unit c of 16 consecutive rows.  Unit c of row r is therefore stored
+// at c ^ ((r / (16 / W)) mod W) of its row: the 16/W rows that share one
+// 256-byte bank row keep distinct positions, and successive bank rows are
+// XOR-rotated, so those 16 reads hit 16 different 16-byte bank groups.  The
+// map keeps the row and is its own inverse.
+template <int W>
+__device__ __forceinline__ constexpr uint32_t swz(uint32_t L) {
+    static_assert(W == 2 || W == 4 || W == 8, "rows of 2, 4 or 8 units");
+    const uint32_t r = L / W;
+    return r * W + ((L % W) ^ ((r / (16 / W)) % W));
+}
 
 // ---- matrix-instruction wrappers -----------------------------------------
 // Each describes one instruction: bytes of A and B per lane, dense K per
@@ -69,7 +77,7 @@ __device__ __forceinline__ i32x8 join(const Frag<32> &f) {
 template <int DT> struct MmaDense16 {
     static constexpr bool kSparse = false;
     static constexpr int kEsize = 2, kAFrag = 16, kBFrag = 16, kKStep = 16;
-    static constexpr int kBK = 64;                 // dense K per LDS k-tile (128 B rows)
+    static constexpr int kBK = 32;                 // dense K per LDS k-tile (64-byte rows)
     static constexpr int kARowBytes = kBK * kEsize, kBRowBytes = kBK * kEsize;
     typedef f32x16 acc_t;
     typedef float out_t;
@@ -90,7 +98,7 @@ template <int DT> struct MmaDense16 {
 struct MmaDenseI8 {
     static constexpr bool kSparse = false;
     static constexpr int kEsize = 1, kAFrag = 16, kBFrag = 16, kKStep = 32;
-    static constexpr int kBK = 128;
+    static constexpr int kBK = 64;
     static constexpr int kARowBytes = kBK, kBRowBytes = kBK;
     typedef i32x16 acc_t;
     typedef int32_t out_t;
@@ -106,7 +114,7 @@ struct MmaDenseI8 {
 template <int FA, int FB> struct MmaDenseF8 {
     static constexpr bool kSparse = false;
     static constexpr int kEsize = 1, kAFrag = 32, kBFrag = 32, kKStep = 64;
-    static constexpr int kBK = 128;
+    static constexpr int kBK = 64;
     static constexpr int kARowBytes = kBK, kBRowBytes = kBK;
     typedef f32x16 acc_t;
     typedef float out_t;
@@ -133,7 +141,7 @@ template <int FA, int FB> struct MmaDenseF8 {
 template <int DT> struct MmaSparse16 {
     static constexpr bool kSparse = true;
     static constexpr int kEsize = 2, kAFrag = 16, kBFrag = 32, kKStep = 32;
-    static constexpr int kBK = 64;
+    static constexpr int kBK = 32;
     static constexpr int kARowBytes = kBK / 2 * kEsize, kBRowBytes = kBK * kEsize;
     static constexpr int kIdxWordsPerTile = kBK / 32;
     typedef f32x16 acc_t;
@@ -158,7 +166,7 @@ template <int DT> struct MmaSparse16 {
 template <int DT_A, int DT_B> struct MmaSparse8 {
     static constexpr bool kSparse = true;
     static constexpr int kEsize = 1, kAFrag = 16, kBFrag = 32, kKStep = 64;
-    static constexpr int kBK = 128;
+    static constexpr int kBK = 64;
     static constexpr int kARowBytes = kBK / 2, kBRowBytes = kBK;
     static constexpr int kIdxWordsPerTile = kBK / 32;
     static constexpr bool kInt = (DT_A == DT_I8);

@@ -2,13 +2,16 @@
 //
 // One workgroup computes a BM x BN tile of D; its WM x WN waves each own a
 // (BM/WM) x (BN/WN) sub-tile made of 32 x 32 instruction tiles.  K is walked
-// in k-tiles of Op::kBK dense elements (one 128-byte LDS row for B; 128 or 64
-// bytes for A, which is half as long when compressed).  Each k-tile of A and B
-// is copied from HBM straight into LDS by buffer loads with an LDS
-// destination (no register staging), into one of two LDS stages, while the
-// waves run the matrix instructions on the other stage.  Rows past M and
-// columns past N read as zero through the buffer descriptor's range check; a
-// ragged last k-tile is filled through registers with explicit zero masking.
+// in k-tiles of Op::kBK dense elements.  Each k-tile of A (or compressed A),
+// B and, for sparse A, the index words is copied from memory straight into
+// LDS by buffer loads with an LDS destination (no register staging).  There
+// are STAGES LDS stages: while the waves run the matrix instructions of
+// k-tile kt, the copies of k-tiles kt+1 .. kt+STAGES-1 are in flight, and the
+// wait at the end of an iteration only drains the copy of k-tile kt+1
+// (counted vmcnt), so several k-tiles' worth of memory latency is hidden.
+// Rows past M and columns past N read as zero through the buffer descriptor's
+// range check; a ragged last k-tile is filled through registers with explicit
+// zero masking.
 //
 // The multiply-accumulate follows "CDNA dense MFMA builtins", section
 // "Naming convention" (each instruction adds one K panel; the kernel loops
@@ -44,19 +47,40 @@ __device__ __forceinline__ void tile_coords(int wg, const GemmParams &p, int &tm
     tn = in / gsz;
 }
 
-// s_waitcnt with vmcnt = 0 (expcnt and lgkmcnt left at their maxima).
-__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt encoding on gfx9: vmcnt in bits [3:0] and [15:14], expcnt [6:4],
+// lgkmcnt [11:8].  Waits for vmcnt <= VM and lgkmcnt == 0.
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    __builtin_amdgcn_sched_barrier(0);   // keep the instruction order across the wait
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));
+    asm volatile("" ::: "memory");
+}
 
-// One fragment from LDS: 16-byte units u0 (and u1 for 32-byte fragments) of a tile.
-template <int BYTES>
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// wait for every outstanding copy); the waits that are needed are explicit.
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// One fragment from LDS: 16-byte units u0 (and u1 for 32-byte fragments) of a
+// tile with W units per row.
+template <int W, int BYTES>
 __device__ __forceinline__ void lds_frag(Frag<BYTES> &f, const uint8_t *base, uint32_t u0, uint32_t u1) {
     if constexpr (BYTES == 16) {
-        f.v = *reinterpret_cast<const i32x4 *>(base + swz(u0) * 16);
+        f.v = *reinterpret_cast<const i32x4 *>(base + swz<W>(u0) * 16);
     } else {
-        f.lo = *reinterpret_cast<const i32x4 *>(base + swz(u0) * 16);
-        f.hi = *reinterpret_cast<const i32x4 *>(base + swz(u1) * 16);
+        f.lo = *reinterpret_cast<const i32x4 *>(base + swz<W>(u0) * 16);
+        f.hi = *reinterpret_cast<const i32x4 *>(base + swz<W>(u1) * 16);
     }
 }
+
+// Instruction classes for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
 
 // 16 bytes of one row starting at element e0 of that row, keeping only the
 // elements below `limit` (the rest become zero).  Used for the ragged k-tile.
@@ -79,31 +103,48 @@ __device__ __forceinline__ i32x4 masked_unit(rsrc_t r, uint32_t off, int e0, int
     return v;
 }
 
-template <class Op, int BM, int BN, int WM, int WN>
+// Wait until at most n * LPT copy instructions of this wave are outstanding
+// (and every LDS access has completed); n is in [0, MAXN].
+template <int LPT, int MAXN>
+__device__ __forceinline__ void wait_copies(int n) {
+    if constexpr (MAXN <= 0) {
+        wait_vm_lgkm0<0>();
+    } else {
+        if (n >= MAXN) wait_vm_lgkm0<MAXN * LPT>();
+        else wait_copies<LPT, MAXN - 1>(n);
+    }
+}
+
+template <class Op, int BM, int BN, int WM, int WN, int STAGES_>
 struct TiledGemm {
     typedef typename Op::acc_t acc_t;
     typedef typename Op::out_t out_t;
-    static constexpr int NT = WM * WN * 64;
+    static constexpr int NW = WM * WN, NT = NW * 64, STAGES = STAGES_;
     static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 tiles");
     static constexpr int AW = Op::kARowBytes / 16, BW = Op::kBRowBytes / 16;  // 16-byte units per LDS row
-    static_assert(AW == 4 || AW == 8, "LDS rows of 64 or 128 bytes");
-    static_assert(BW == 8, "B LDS rows of 128 bytes");
-    static constexpr int AQ = BM * AW / NT, BQ = BN * BW / NT;                  // DMA units per thread
-    static_assert(AQ * NT == BM * AW && BQ * NT == BN * BW, "tile not a whole number of DMA passes");
-    static constexpr int A_BYTES = BM * AW * 16, B_BYTES = BN * BW * 16, STAGE = A_BYTES + B_BYTES;
+    static_assert(AW == 2 || AW == 4 || AW == 8, "A LDS rows of 32, 64 or 128 bytes");
+    static_assert(BW == 4 || BW == 8, "B LDS rows of 64 or 128 bytes");
+    static constexpr int IW = Op::kSparse ? Op::kBK / 32 : 0;                  // index words per row
+    // copy units per wave: 16-byte units of A and B, 4-byte words of the index
+    static constexpr int AUPW = BM * AW / NW, BUPW = BN * BW / NW, IUPW = BM * IW / NW;
+    static_assert(AUPW * NW == BM * AW && BUPW * NW == BN * BW && IUPW * NW == BM * IW, "uneven copy split");
+    static constexpr int AP = (AUPW + 63) / 64, BP = (BUPW + 63) / 64, IP = (IUPW + 63) / 64;  // passes
+    static constexpr int LPT = AP + BP + IP;        // copy instructions per wave per k-tile
+    static constexpr int A_BYTES = BM * AW * 16, B_BYTES = BN * BW * 16, I_BYTES = BM * IW * 4;
+    static constexpr int STAGE = A_BYTES + B_BYTES + I_BYTES;
     static constexpr int STEPS = Op::kBK / Op::kKStep;
-    static constexpr int IW = Op::kSparse ? Op::kBK / 32 : 1;                   // index words per k-tile row
+    static constexpr int LDS_BYTES = STAGES * STAGE;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 workgroup");
 
     const GemmParams &p;
-    int tid, wave, g, l32, wm, wn, row0, col0, arows, bcols;
+    int wave, lane, g, l32, wm, wn, row0, col0;
     rsrc_t ra, rb, rx;
-    uint32_t a_off[AQ], b_off[BQ];   // byte offset (k-tile 0) of the unit copied in DMA pass q
     acc_t acc[TM][TN];
 
     __device__ __forceinline__ TiledGemm(const GemmParams &p_) : p(p_) {
-        tid = threadIdx.x;
-        const int lane = tid & 63;
+        const int tid = threadIdx.x;
+        lane = tid & 63;
         wave = tid >> 6;
         g = lane >> 5;
         l32 = lane & 31;
@@ -113,101 +154,179 @@ struct TiledGemm {
         tile_coords(blockIdx.x, p, tm, tn);
         row0 = tm * BM;
         col0 = tn * BN;
-        arows = min(BM, p.M - row0);
-        bcols = min(BN, p.N - col0);
+        const int arows = min(BM, p.M - row0), bcols = min(BN, p.N - col0);
         ra = make_rsrc(p.A + (int64_t)row0 * p.a_pitch, (uint32_t)(arows * p.a_pitch));
         rb = make_rsrc(p.B + (int64_t)col0 * p.b_pitch, (uint32_t)(bcols * p.b_pitch));
         if constexpr (Op::kSparse)
             rx = make_rsrc(p.idx + (int64_t)row0 * p.idx_pitch, (uint32_t)(arows * p.idx_pitch * 4));
-#pragma unroll
-        for (int q = 0; q < AQ; ++q) {
-            const uint32_t L = swz(tid + q * NT);
-            a_off[q] = (L / AW) * (uint32_t)p.a_pitch + (L % AW) * 16;
-        }
-#pragma unroll
-        for (int q = 0; q < BQ; ++q) {
-            const uint32_t L = swz(tid + q * NT);
-            b_off[q] = (L / BW) * (uint32_t)p.b_pitch + (L % BW) * 16;
-        }
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j) acc[i][j] = acc_t{};
     }
 
-    // Copy k-tile kt of A and B into the LDS stage `st` (asynchronous; rows past M / N read as zero).
-    __device__ __forceinline__ void dma(uint8_t *st, int kt) {
-        const uint32_t ka = kt * Op::kARowBytes, kb = kt * Op::kBRowBytes;
-#pragma unroll
-        for (int q = 0; q < AQ; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(st + (q * NT + wave * 64) * 16), 16,
-                                                     a_off[q] + ka, 0, 0, 0);
-#pragma unroll
-        for (int q = 0; q < BQ; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(st + A_BYTES + (q * NT + wave * 64) * 16), 16,
-                                                     b_off[q] + kb, 0, 0, 0);
+    // Physical LDS unit P of a W-unit-wide tile -> byte offset of its source in
+    // the row-major source buffer at k-tile kt.
+    template <int W>
+    __device__ __forceinline__ uint32_t src_off(uint32_t P, int64_t pitch, int kt) const {
+        const uint32_t L = swz<W>(P);
+        return (L / W) * (uint32_t)pitch + (uint32_t)(kt * W * 16) + (L % W) * 16;
     }
 
-    // The ragged last k-tile, filled through registers with elements past K set to zero.
-    __device__ __forceinline__ void fill_masked(uint8_t *st, int kt) {
-        const int climit = Op::kSparse ? p.K / 2 : p.K;      // elements of A per row
-#pragma unroll
-        for (int q = 0; q < AQ; ++q) {
-            const uint32_t P = tid + q * NT, L = swz(P);
-            const int e0 = (kt * Op::kARowBytes + (int)(L % AW) * 16) / Op::kEsize;
-            *reinterpret_cast<i32x4 *>(st + P * 16) =
-                masked_unit<Op::kEsize>(ra, a_off[q] + kt * Op::kARowBytes, e0, climit);
-        }
-#pragma unroll
-        for (int q = 0; q < BQ; ++q) {
-            const uint32_t P = tid + q * NT, L = swz(P);
-            const int e0 = (kt * Op::kBRowBytes + (int)(L % BW) * 16) / Op::kEsize;
-            *reinterpret_cast<i32x4 *>(st + A_BYTES + P * 16) =
-                masked_unit<Op::kEsize>(rb, b_off[q] + kt * Op::kBRowBytes, e0, p.K);
-        }
+    // Byte offset of word d (= row * IW + w) of the index tile at k-tile kt.
+    __device__ __forceinline__ uint32_t idx_off(uint32_t d, int kt) const {
+        return ((d / IW) * (uint32_t)p.idx_pitch + kt * IW + d % IW) * 4;
     }
 
-    // Sparse index words of this lane's rows for k-tile kt.
-    __device__ __forceinline__ void load_idx(uint32_t (&w)[TM][IW], int kt) {
+    __device__ __forceinline__ void copy_index(uint8_t *st, int kt) const {
         if constexpr (Op::kSparse) {
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const uint32_t r = wm * WTM + i * 32 + l32;
-#pragma unroll
-                for (int q = 0; q < IW; ++q)
-                    w[i][q] = __builtin_amdgcn_raw_buffer_load_b32(rx, (r * (uint32_t)p.idx_pitch + kt * IW + q) * 4,
-                                                                   0, 0);
+            for (int q = 0; q < IP; ++q) {
+                const int u = q * 64 + lane;
+                if (IUPW % 64 == 0 || u < IUPW)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rx, (lds_void *)(st + A_BYTES + B_BYTES + (wave * IUPW + q * 64) * 4), 4,
+                        idx_off(wave * IUPW + u, kt), 0, 0, 0);
             }
         }
+    }
+
+    // Start the copy of k-tile kt into LDS stage `st` (every wave issues LPT
+    // instructions; each writes one contiguous run of LDS).
+    __device__ __forceinline__ void dma(uint8_t *st, int kt) const {
+#pragma unroll
+        for (int q = 0; q < AP; ++q) {
+            const int u = q * 64 + lane;
+            if (AUPW % 64 == 0 || u < AUPW)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(st + (wave * AUPW + q * 64) * 16), 16,
+                                                         src_off<AW>(wave * AUPW + u, p.a_pitch, kt), 0, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < BP; ++q) {
+            const int u = q * 64 + lane;
+            if (BUPW % 64 == 0 || u < BUPW)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(st + A_BYTES + (wave * BUPW + q * 64) * 16),
+                                                         16, src_off<BW>(wave * BUPW + u, p.b_pitch, kt), 0, 0, 0);
+        }
+        copy_index(st, kt);
+    }
+
+    // The ragged last k-tile: A and B through registers with elements past K set
+    // to zero (the index words, if any, still by copy).
+    __device__ __forceinline__ void fill_masked(uint8_t *st, int kt) const {
+        const int climit = Op::kSparse ? p.K / 2 : p.K;      // elements of A per row
+#pragma unroll
+        for (int q = 0; q < AP; ++q) {
+            const int u = q * 64 + lane;
+            const uint32_t P = wave * AUPW + u;
+            if (AUPW % 64 == 0 || u < AUPW) {
+                const int e0 = (kt * AW * 16 + (int)(swz<AW>(P) % AW) * 16) / Op::kEsize;
+                *reinterpret_cast<i32x4 *>(st + P * 16) =
+                    masked_unit<Op::kEsize>(ra, src_off<AW>(P, p.a_pitch, kt), e0, climit);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < BP; ++q) {
+            const int u = q * 64 + lane;
+            const uint32_t P = wave * BUPW + u;
+            if (BUPW % 64 == 0 || u < BUPW) {
+                const int e0 = (kt * BW * 16 + (int)(swz<BW>(P) % BW) * 16) / Op::kEsize;
+                *reinterpret_cast<i32x4 *>(st + A_BYTES + P * 16) =
+                    masked_unit<Op::kEsize>(rb, src_off<BW>(P, p.b_pitch, kt), e0, p.K);
+            }
+        }
+        copy_index(st, kt);
     }
 
     typedef Frag<Op::kAFrag> FragA;
     typedef Frag<Op::kBFrag> FragB;
 
-    // Fragments of step s of the k-tile held in LDS stage `st`.
-    __device__ __forceinline__ void load_frags(FragA (&a)[TM], FragB (&b)[TN], const uint8_t *st, int s) {
+    // Fragments (and index bits) of step s of the k-tile held in LDS stage `st`.
+    __device__ __forceinline__ void load_frags(FragA (&a)[TM], FragB (&b)[TN], uint32_t (&ix)[TM], const uint8_t *st,
+                                               int s) const {
         const uint8_t *sa = st, *sb = st + A_BYTES;
+        const uint32_t *sx = reinterpret_cast<const uint32_t *>(st + A_BYTES + B_BYTES);
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            const uint32_t r = (wm * WTM + i * 32 + l32) * AW;
-            lds_frag(a[i], sa, r + Op::a_unit(s, g, 0), r + Op::a_unit(s, g, 1));
+            const uint32_t r = wm * WTM + i * 32 + l32;
+            lds_frag<AW>(a[i], sa, r * AW + Op::a_unit(s, g, 0), r * AW + Op::a_unit(s, g, 1));
+            if constexpr (Op::kSparse) ix[i] = Op::lane_idx(sx + r * IW, s, g);
+            else ix[i] = 0;
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const uint32_t r = (wn * WTN + j * 32 + l32) * BW;
-            lds_frag(b[j], sb, r + Op::b_unit(s, g, 0), r + Op::b_unit(s, g, 1));
+            lds_frag<BW>(b[j], sb, r + Op::b_unit(s, g, 0), r + Op::b_unit(s, g, 1));
         }
     }
 
-    // The TM x TN matrix instructions of step s.
-    __device__ __forceinline__ void mma_step(const FragA (&a)[TM], const FragB (&b)[TN], const uint32_t (&w)[TM][IW],
-                                             int s) {
+    // Instruction counts of one step, for the interleaving below.
+    static constexpr int NMMA = TM * TN;
+    static constexpr int NREAD = TM * (Op::kAFrag / 16) + TN * (Op::kBFrag / 16) + (Op::kSparse ? TM : 0);
+
+    // The TM x TN matrix instructions of one step, interleaved by the scheduler
+    // with the LDS reads (next step's fragments) and copy instructions issued
+    // before them in the same region: one matrix instruction, then one read,
+    // then one copy, so the reads and copies go out while the matrix unit works.
+    __device__ __forceinline__ void mma_step(const FragA (&a)[TM], const FragB (&b)[TN], const uint32_t (&ix)[TM],
+                                             int ncopies) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            uint32_t ix = 0;
-            if constexpr (Op::kSparse) ix = Op::lane_idx(w[i], s, g);
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] = Op::mma(a[i], b[j], acc[i][j], ix);
+            for (int j = 0; j < TN; ++j) acc[i][j] = Op::mma(a[i], b[j], acc[i][j], ix[i]);
+#pragma unroll
+        for (int k = 0; k < NMMA; ++k) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            if (k < NREAD) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            if (k < ncopies) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+        }
+    }
+
+    // Fragment double buffer: a0/b0/x0 feed the current step, a1/b1/x1 receive the next.
+    FragA a0[TM], a1[TM];
+    FragB b0[TN], b1[TN];
+    uint32_t x0[TM], x1[TM];
+
+    // One k-tile: start the copy of k-tile kt + STAGES - 1 into the stage that
+    // k-tile kt - 1 freed, then the STEPS steps of k-tile kt (in stage `cur`).
+    // The barrier that hands over k-tile kt + 1 sits before the last step, so
+    // the first fragments of k-tile kt + 1 are read while that step runs; every
+    // read of a stage completes before the barrier that precedes the copy into
+    // it.  STEADY: every k-tile up to kt + STAGES - 1 is whole (no branches).
+    template <bool STEADY>
+    __device__ __forceinline__ void iteration(uint8_t *smem, int kt, int cur, int nk, int nkt) {
+        const int pre = kt + STAGES - 1;
+        uint8_t *st_pre = smem + (cur == 0 ? STAGES - 1 : cur - 1) * STAGE;
+        if constexpr (STEADY) {
+            dma(st_pre, pre);
+        } else if (pre < nkt) {
+            if (pre < nk) dma(st_pre, pre);
+            else fill_masked(st_pre, pre);
+        }
+        const uint8_t *sc = smem + cur * STAGE;
+        const uint8_t *sn = smem + (cur + 1 == STAGES ? 0 : cur + 1) * STAGE;
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s) {
+            if (s + 1 < STEPS) {
+                load_frags(a1, b1, x1, sc, s + 1);
+            } else {
+                if constexpr (STEADY) {
+                    wait_vm_lgkm0<(STAGES - 2) * LPT>();
+                } else {
+                    const int after = min(STAGES - 2, nkt - 2 - kt);
+                    wait_copies<LPT, STAGES - 2>(after <= 0 || kt + 1 + after >= nk ? 0 : after);
+                }
+                block_barrier();
+                load_frags(a1, b1, x1, sn, 0);   // past the last k-tile this reads a stale stage, unused
+            }
+            mma_step(a0, b0, x0, (STEADY && s == 0) ? LPT : 0);
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                a0[i] = a1[i];
+                x0[i] = x1[i];
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) b0[j] = b1[j];
         }
     }
 
@@ -244,62 +363,44 @@ struct TiledGemm {
     }
 };
 
-template <class Op, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// One workgroup per CU: with WM*WN/4 waves on each SIMD every wave may use
+// 512 / (WM*WN/4) registers.
+template <class Op, int BM, int BN, int WM, int WN, int STAGES>
+__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
 void gemm_tiled_kernel(GemmParams p) {
-    typedef TiledGemm<Op, BM, BN, WM, WN> T;
-    constexpr int IW = T::IW, TM = T::TM;
-    __shared__ __attribute__((aligned(16))) uint8_t st0[T::STAGE];
-    __shared__ __attribute__((aligned(16))) uint8_t st1[T::STAGE];
+    typedef TiledGemm<Op, BM, BN, WM, WN, STAGES> T;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[T::LDS_BYTES];
     T t(p);
 
     const int nk = p.K / Op::kBK;                        // whole k-tiles
     const int nkt = nk + (p.K > nk * Op::kBK ? 1 : 0);   // plus a ragged one
-    constexpr int STEPS = T::STEPS;
-    static_assert(STEPS % 2 == 0, "fragment double buffering assumes an even number of steps");
-    uint32_t ixc[TM][IW], ixn[TM][IW];
-    typename T::FragA a[2][TM];
-    typename T::FragB b[2][T::TN];
 
-    // Software pipeline: the fragments of step s + 1 are read from LDS while the
-    // matrix instructions of step s run; the block barrier that hands over the
-    // next LDS stage sits before the last step's instructions, so the first
-    // reads of the next k-tile overlap them.  The copy of k-tile kt + 1 into the
-    // other stage is in flight during the whole of k-tile kt.
-    if (nkt > 0) {
-        if (0 < nk) t.dma(st0, 0);
-        else t.fill_masked(st0, 0);
-        t.load_idx(ixc, 0);
-        wait_vmem_all();
-        __syncthreads();
-        t.load_frags(a[0], b[0], st0, 0);
+    // prologue: start k-tiles 0 .. STAGES-2
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) {
+        if (s < nkt) {
+            if (s < nk) t.dma(smem + s * T::STAGE, s);
+            else t.fill_masked(smem + s * T::STAGE, s);
+        }
     }
-    for (int kt = 0; kt < nkt; ++kt) {
-        const uint8_t *cur = (kt & 1) ? st1 : st0;
-        uint8_t *nxt = (kt & 1) ? st0 : st1;
-        if (kt + 1 < nkt) {
-            if (kt + 1 < nk) t.dma(nxt, kt + 1);
-            else t.fill_masked(nxt, kt + 1);
-            t.load_idx(ixn, kt + 1);
-        }
-#pragma unroll
-        for (int s = 0; s < STEPS; ++s) {
-            const int cb = s & 1;
-            if (s + 1 < STEPS) {
-                t.load_frags(a[cb ^ 1], b[cb ^ 1], cur, s + 1);
-            } else {
-                wait_vmem_all();
-                __syncthreads();
-                if (kt + 1 < nkt) t.load_frags(a[cb ^ 1], b[cb ^ 1], nxt, 0);
-            }
-            t.mma_step(a[cb], b[cb], ixc, s);
-        }
-        if constexpr (Op::kSparse) {
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int q = 0; q < IW; ++q) ixc[i][q] = ixn[i][q];
-        }
+    // Copies are counted per wave in issue order.  Before using k-tile kt + 1 the
+    // copies of the later k-tiles may stay in flight, provided they are all
+    // whole k-tiles (the ragged one issues fewer copy instructions); otherwise
+    // wait for everything.
+    {
+        const int after = min(STAGES - 2, nkt - 1);
+        wait_copies<T::LPT, STAGES - 2>(after <= 0 || after >= nk ? 0 : after);
+        block_barrier();
+    }
+    if (nkt > 0) t.load_frags(t.a0, t.b0, t.x0, smem, 0);
+    int kt = 0, cur = 0;
+    for (; kt + STAGES - 1 < nk; ++kt) {
+        t.template iteration<true>(smem, kt, cur, nk, nkt);
+        cur = (cur + 1 == STAGES) ? 0 : cur + 1;
+    }
+    for (; kt < nkt; ++kt) {
+        t.template iteration<false>(smem, kt, cur, nk, nkt);
+        cur = (cur + 1 == STAGES) ? 0 : cur + 1;
     }
     t.epilogue();
 }

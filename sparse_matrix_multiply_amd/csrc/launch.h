@@ -38,7 +38,7 @@ struct CompressParams {
 };
 
 // Tile shapes the host can pick from.
-enum TileShape : int { TILE_256 = 0, TILE_128 = 1, TILE_64 = 2, TILE_SKINNY = 3 };
+enum TileShape : int { TILE_256 = 0, TILE_128 = 1, TILE_64 = 2, TILE_SKINNY = 3, TILE_256_W8 = 4 };
 
 // Launchers (defined in the kernel files).  `dt_a`/`dt_b` use the public
 // mmac_dtype_t codes.  They return hipSuccess or the launch error.
@@ -48,6 +48,8 @@ hipError_t launch_gemm_skinny(int dt_a, int dt_b, GemmParams p, hipStream_t s);
 hipError_t launch_compress(int dt, CompressParams p, hipStream_t s);
 
 // Geometry of a tile shape.
-inline int tile_rows(TileShape t) { return t == TILE_256 ? 256 : t == TILE_128 ? 128 : 64; }
+inline int tile_rows(TileShape t) {
+    return (t == TILE_256 || t == TILE_256_W8) ? 256 : t == TILE_128 ? 128 : t == TILE_64 ? 64 : 32;
+}
 
 }  // namespace mmac

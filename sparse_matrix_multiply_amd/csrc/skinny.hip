@@ -1,0 +1,199 @@
+// Skinny dense GEMM (M <= 32): D = alpha * A*B + beta * C streaming B once.
+//
+// With at most 32 rows of A the product does 2*M flops per byte of B, far
+// below the chip's flop/byte ridge, so the time is set by reading B from HBM.
+// Each workgroup owns 16*CB columns of D and all M rows; its WK waves split K
+// (a fixed, contiguous range each), read their A and B fragments straight
+// from memory into registers with 128-bit buffer loads (B exactly once, A from
+// L2), run 16 x 16 matrix instructions, and combine their partial tiles in LDS
+// in a fixed wave order, so the result does not depend on timing.
+//
+// The 16 x 16 accumulator follows the one-block 16x16 layout of "CDNA dense
+// MFMA builtins", "Accumulator layout": element (i, j) is register i mod 4 of
+// lane 16*floor(i/4) + j.  Within an instruction's K step, lane quarter
+// q = lane / 16 takes the q-th quarter of the step for A and B alike.
+#include "device.h"
+#include "launch.h"
+
+namespace mmac {
+
+// 16 x 16 dense instructions of gfx950, one per element type.
+template <int DT_A, int DT_B> struct Mma16;
+template <int DT> struct Mma16Half {
+    static constexpr int kEsize = 2, kFrag = 16, kKStep = 32;   // 8 elements per lane
+    typedef i32x4 frag_t;
+    typedef f32x4 acc_t;
+    typedef float out_t;
+    __device__ __forceinline__ static acc_t mma(const i32x4 &a, const i32x4 &b, acc_t c) {
+        if constexpr (DT == DT_BF16)
+            return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                          c, 0, 0, 0);
+        else
+            return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                         c, 0, 0, 0);
+    }
+};
+template <> struct Mma16<DT_BF16, DT_BF16> : Mma16Half<DT_BF16> {};
+template <> struct Mma16<DT_F16, DT_F16> : Mma16Half<DT_F16> {};
+template <> struct Mma16<DT_I8, DT_I8> {
+    static constexpr int kEsize = 1, kFrag = 16, kKStep = 64;    // 16 elements per lane
+    typedef i32x4 frag_t;
+    typedef i32x4 acc_t;
+    typedef int32_t out_t;
+    __device__ __forceinline__ static acc_t mma(const i32x4 &a, const i32x4 &b, acc_t c) {
+        return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+    }
+};
+template <int FA, int FB> struct Mma16F8 {
+    static constexpr int kEsize = 1, kFrag = 32, kKStep = 128;   // 32 elements per lane
+    typedef Frag<32> frag_t;
+    typedef f32x4 acc_t;
+    typedef float out_t;
+    __device__ __forceinline__ static acc_t mma(const Frag<32> &a, const Frag<32> &b, acc_t c) {
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(join(a), join(b), c, FA, FB, 0, 0, 0, 0);
+    }
+};
+template <> struct Mma16<DT_E4M3, DT_E4M3> : Mma16F8<0, 0> {};
+template <> struct Mma16<DT_E4M3, DT_E5M2> : Mma16F8<0, 1> {};
+template <> struct Mma16<DT_E5M2, DT_E4M3> : Mma16F8<1, 0> {};
+template <> struct Mma16<DT_E5M2, DT_E5M2> : Mma16F8<1, 1> {};
+
+// 16 bytes of a row at byte offset `off`, elements at or past `limit` (element
+// index e0 is the first) read as zero.
+template <int ES>
+__device__ __forceinline__ i32x4 load_unit(rsrc_t r, uint32_t off, int e0, int limit) {
+    constexpr int PER = 16 / ES;
+    if (e0 + PER <= limit) return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    uint32_t w[4] = {0, 0, 0, 0};
+    for (int e = 0; e < PER; ++e) {
+        if (e0 + e < limit) {
+            uint32_t x;
+            if constexpr (ES == 2) x = __builtin_amdgcn_raw_buffer_load_b16(r, off + 2 * e, 0, 0);
+            else x = __builtin_amdgcn_raw_buffer_load_b8(r, off + e, 0, 0);
+            w[(e * ES) / 4] |= x << (8 * ((e * ES) % 4));
+        }
+    }
+    return i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+}
+
+template <class Op>
+__device__ __forceinline__ void load_frag16(typename Op::frag_t &f, rsrc_t r, uint32_t row_off, int k0, int K,
+                                            int q) {
+    constexpr int ES = Op::kEsize;
+    if constexpr (Op::kFrag == 16) {
+        const int e0 = k0 + q * (16 / ES);
+        f = load_unit<ES>(r, row_off + (uint32_t)e0 * ES, e0, K);
+    } else {
+        const int e0 = k0 + q * 32;
+        f.lo = load_unit<ES>(r, row_off + (uint32_t)e0, e0, K);
+        f.hi = load_unit<ES>(r, row_off + (uint32_t)e0 + 16, e0 + 16, K);
+    }
+}
+
+// MB row blocks of 16 (M <= 16*MB), CB column blocks of 16 per workgroup, WK waves along K,
+// U instruction steps per batch of loads.
+template <class Op, int MB, int CB, int WK, int U>
+__global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(GemmParams p) {
+    typedef typename Op::acc_t acc_t;
+    typedef typename Op::out_t out_t;
+    typedef typename Op::frag_t frag_t;
+    constexpr int KS = Op::kKStep;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r16 = lane & 15, q = lane >> 4;
+    const int col0 = blockIdx.x * 16 * CB;
+    const int bcols = min(16 * CB, p.N - col0);
+    const rsrc_t ra = make_rsrc(p.A, (uint32_t)(p.M * p.a_pitch));
+    const rsrc_t rb = make_rsrc(p.B + (int64_t)col0 * p.b_pitch, (uint32_t)(bcols * p.b_pitch));
+
+    // contiguous range of K steps for this wave
+    const int nsteps = (p.K + KS - 1) / KS;
+    const int per_wave = (nsteps + WK - 1) / WK;
+    const int s0 = wave * per_wave, s1 = min(s0 + per_wave, nsteps);
+
+    acc_t acc[MB][CB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int c = 0; c < CB; ++c) acc[m][c] = acc_t{};
+
+    uint32_t aoff[MB], boff[CB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) aoff[m] = (uint32_t)(m * 16 + r16) * (uint32_t)p.a_pitch;
+#pragma unroll
+    for (int c = 0; c < CB; ++c) boff[c] = (uint32_t)(c * 16 + r16) * (uint32_t)p.b_pitch;
+
+    for (int s = s0; s < s1; s += U) {
+        frag_t a[U][MB], b[U][CB];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k0 = (s + u < s1) ? (s + u) * KS : p.K;   // past this wave's range: all zero
+#pragma unroll
+            for (int m = 0; m < MB; ++m) load_frag16<Op>(a[u][m], ra, aoff[m], k0, p.K, q);
+#pragma unroll
+            for (int c = 0; c < CB; ++c) load_frag16<Op>(b[u][c], rb, boff[c], k0, p.K, q);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int m = 0; m < MB; ++m)
+#pragma unroll
+                for (int c = 0; c < CB; ++c) acc[m][c] = Op::mma(a[u][m], b[u][c], acc[m][c]);
+    }
+
+    // combine the WK partial tiles in LDS, in wave order
+    __shared__ out_t red[WK][MB][CB][4][64];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave][m][c][r][lane] = acc[m][c][r];
+    __syncthreads();
+    constexpr int OUTS = MB * CB * 4 * 64;
+    for (int o = threadIdx.x; o < OUTS; o += WK * 64) {
+        const int ln = o & 63, r = (o >> 6) & 3, c = (o >> 8) % CB, m = (o >> 8) / CB;
+        out_t v = red[0][m][c][r][ln];
+        for (int w = 1; w < WK; ++w) {
+            if constexpr (std::is_same<out_t, float>::value) v += red[w][m][c][r][ln];
+            else v = (out_t)((uint32_t)v + (uint32_t)red[w][m][c][r][ln]);
+        }
+        const int row = m * 16 + 4 * (ln >> 4) + r;
+        const int col = col0 + c * 16 + (ln & 15);
+        if (row < p.M && col < p.N) {
+            out_t *d = reinterpret_cast<out_t *>(p.D) + (int64_t)row * p.ldd + col;
+            if constexpr (std::is_same<out_t, float>::value) {
+                float x = p.alpha * v;
+                if (p.use_c) x = fmaf(p.beta, reinterpret_cast<const float *>(p.C)[(int64_t)row * p.ldc + col], x);
+                *d = x;
+            } else {
+                uint32_t x = (uint32_t)p.ialpha * (uint32_t)v;
+                if (p.use_c)
+                    x += (uint32_t)p.ibeta * (uint32_t)reinterpret_cast<const int32_t *>(p.C)[(int64_t)row * p.ldc + col];
+                *d = (int32_t)x;
+            }
+        }
+    }
+}
+
+template <int DA, int DB>
+static hipError_t launch_types(const GemmParams &p, hipStream_t s) {
+    typedef Mma16<DA, DB> Op;
+    constexpr int CB = 1, WK = 4, U = 4;
+    const dim3 grid((p.N + 16 * CB - 1) / (16 * CB)), block(WK * 64);
+    if (p.M <= 16) hipLaunchKernelGGL((gemm_skinny_kernel<Op, 1, CB, WK, U>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((gemm_skinny_kernel<Op, 2, CB, WK, U>), grid, block, 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_skinny(int a, int b, GemmParams p, hipStream_t s) {
+    if (p.M > 32) return hipErrorInvalidValue;
+    if (a == DT_BF16 && b == DT_BF16) return launch_types<DT_BF16, DT_BF16>(p, s);
+    if (a == DT_F16 && b == DT_F16) return launch_types<DT_F16, DT_F16>(p, s);
+    if (a == DT_I8 && b == DT_I8) return launch_types<DT_I8, DT_I8>(p, s);
+    if (a == DT_E4M3 && b == DT_E4M3) return launch_types<DT_E4M3, DT_E4M3>(p, s);
+    if (a == DT_E4M3 && b == DT_E5M2) return launch_types<DT_E4M3, DT_E5M2>(p, s);
+    if (a == DT_E5M2 && b == DT_E4M3) return launch_types<DT_E5M2, DT_E4M3>(p, s);
+    if (a == DT_E5M2 && b == DT_E5M2) return launch_types<DT_E5M2, DT_E5M2>(p, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace mmac

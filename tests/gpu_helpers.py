@@ -67,17 +67,23 @@ def out_tensor(M, N, integer, ld=None, fill=float("nan")):
 
 
 @contextlib.contextmanager
-def tile_shape(t):
-    """Force the library's tile shape (MMAC_TILE) for the calls inside the block."""
-    old = os.environ.get("MMAC_TILE")
-    os.environ["MMAC_TILE"] = str(t)
+def env(**kv):
+    """Set the library's tuning variables (read on every call) inside the block."""
+    old = {k: os.environ.get(k) for k in kv}
+    os.environ.update({k: str(v) for k, v in kv.items()})
     try:
         yield
     finally:
-        if old is None:
-            del os.environ["MMAC_TILE"]
-        else:
-            os.environ["MMAC_TILE"] = old
+        for k, v in old.items():
+            if v is None:
+                del os.environ[k]
+            else:
+                os.environ[k] = v
+
+
+def tile_shape(t, waves=4):
+    """Force the library's tile shape (MMAC_TILE) and, for 256 x 256 tiles, its wave count."""
+    return env(MMAC_TILE=t, MMAC_WAVES=waves)
 
 
 def assert_close(D_gpu, D_ref, S, t, K, alpha, beta, C=None, what=""):

@@ -35,12 +35,12 @@ def inputs(ta, tb, M, N, K, seed):
     return A, B, C, 1.5, -0.75
 
 
-@pytest.mark.parametrize("tile", [256, 128, 64])
+@pytest.mark.parametrize("tile,waves", [(256, 4), (256, 8), (128, 4), (64, 4)])
 @pytest.mark.parametrize("ta,tb", PAIRS)
 @pytest.mark.parametrize("M,N,K", SHAPES)
-def test_dense_matches_oracle(ta, tb, M, N, K, tile):
+def test_dense_matches_oracle(ta, tb, M, N, K, tile, waves):
     A, B, C, alpha, beta = inputs(ta, tb, M, N, K, M * 7 + N * 3 + K + ta * 11 + tb)
-    with tile_shape(tile):
+    with tile_shape(tile, waves):
         D = run_dense(ta, tb, A, B, alpha, beta, C)
     Dref, aux = oracle.gemm_dense(ta, tb, A, B, alpha, beta, C)
     if ta == I8:
@@ -135,3 +135,19 @@ def test_deterministic(ta, tb):
     D1 = run_dense(ta, tb, A, B, alpha, beta, C)
     D2 = run_dense(ta, tb, A, B, alpha, beta, C)
     assert np.array_equal(D1, D2)
+
+
+@pytest.mark.parametrize("ta,tb", PAIRS)
+@pytest.mark.parametrize("M,N,K", [(1, 64, 64), (5, 100, 333), (16, 130, 1000), (17, 77, 200), (32, 300, 4100)])
+def test_skinny_path_matches_oracle(ta, tb, M, N, K):
+    """M <= 32 runs the skinny kernel (B streamed once, split K, fixed-order reduction)."""
+    A, B, C, alpha, beta = inputs(ta, tb, M, N, K, M * 5 + N + K + ta + tb)
+    with tile_shape(16):
+        D = run_dense(ta, tb, A, B, alpha, beta, C)
+    Dref, aux = oracle.gemm_dense(ta, tb, A, B, alpha, beta, C)
+    if ta == I8:
+        assert np.array_equal(D, Dref)
+    else:
+        assert_close(D, Dref, aux, ta, K, alpha, beta, C, f"skinny {ta},{tb} {M}x{N}x{K}")
+    D2 = run_dense(ta, tb, A, B, alpha, beta, C)        # default choice, same kernel: same bits
+    assert np.array_equal(D, D2)
