@@ -43,8 +43,8 @@
  *     pitch in bytes (ld * element size) must be a multiple of 16.  C, D and
  *     idx need only their natural 4-byte alignment.
  *   - Sizes: M, N, K must be below 2^31 (MMAC_ERR_INVALID_ARG otherwise); the
- *     row pitch of A, B and Ac must be at most 8 MiB and that of idx at most
- *     8 MiB / 4 words (MMAC_ERR_UNSUPPORTED otherwise).
+ *     row pitch of A, B, Ac, C and D must be at most 8 MiB and that of idx
+ *     at most 8 MiB / 4 words (MMAC_ERR_UNSUPPORTED otherwise).
  *   - Memory: every pointer is device memory on the current HIP device, owned
  *     by the caller; the library never allocates, frees or keeps a pointer.
  *     Buffers must stay valid until the work on `stream` has finished.

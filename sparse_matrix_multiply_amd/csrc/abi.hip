@@ -40,7 +40,7 @@ int env_int(const char *name, int dflt) {
 
 TileShape pick_shape(int64_t M, int64_t N, bool sparse = false) {
     const int forced = env_int("MMAC_TILE", 0);
-    if (forced == 256) return env_int("MMAC_WAVES", 4) == 8 ? TILE_256_W8 : TILE_256;
+    if (forced == 256) return env_int("MMAC_WAVES", 8) == 4 ? TILE_256 : TILE_256_W8;
     if (forced == 128) return TILE_128;
     if (forced == 64) return TILE_64;
     if (forced == 16 && !sparse && M <= 32) return TILE_SKINNY;
@@ -48,7 +48,7 @@ TileShape pick_shape(int64_t M, int64_t N, bool sparse = false) {
     if (!sparse && M <= 32) return TILE_SKINNY;
     // Largest tile that still gives about one tile per compute unit (256 CUs).
     auto tiles = [&](int t) { return ((M + t - 1) / t) * ((N + t - 1) / t); };
-    if (tiles(256) >= 192) return env_int("MMAC_WAVES", 4) == 8 ? TILE_256_W8 : TILE_256;
+    if (tiles(256) >= 192) return env_int("MMAC_WAVES", 8) == 4 ? TILE_256 : TILE_256_W8;
     if (tiles(128) >= 192) return TILE_128;
     return TILE_64;
 }
@@ -68,6 +68,7 @@ mmac_status_t check_gemm(int a, int b, int64_t M, int64_t N, int64_t K, double a
     if (C == D && beta != 0.0 && ldc != ldd) return MMAC_ERR_INVALID_ARG;
     const int es = elem_size(a);
     if (lda * es > kMaxPitchBytes || ldb * es > kMaxPitchBytes) return MMAC_ERR_UNSUPPORTED;
+    if (ldd * 4 > kMaxPitchBytes || (C && beta != 0.0 && ldc * 4 > kMaxPitchBytes)) return MMAC_ERR_UNSUPPORTED;
     if (!aligned16(A) || !aligned16(B) || (lda * es) % 16 || (ldb * es) % 16) return MMAC_ERR_MISALIGNED;
     if (!aligned4(D) || (C && beta != 0.0 && !aligned4(C))) return MMAC_ERR_MISALIGNED;
     return MMAC_OK;

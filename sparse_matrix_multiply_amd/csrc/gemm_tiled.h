@@ -330,32 +330,65 @@ struct TiledGemm {
         }
     }
 
-    // D = alpha * acc + beta * C, element (i, j) of a 32 x 32 tile being
-    // register G of lane L with i = 8*floor(G/4) + 4*floor(L/32) + (G mod 4),
-    // j = L mod 32 (lanes 0-31 and 32-63 each write 32 consecutive floats of a row).
+    // D = alpha * acc + beta * C.  Element (i, j) of a 32 x 32 instruction tile
+    // is register G of lane L with i = 8*floor(G/4) + 4*floor(L/32) + (G mod 4),
+    // j = L mod 32, so for each register lanes 0-31 and 32-63 each cover 32
+    // consecutive elements of a row.  C and D are accessed with buffer
+    // instructions over this tile's rows: elements outside M x N get an offset
+    // past the end of the buffer, where loads return zero and stores are
+    // dropped, so there are no branches and all loads of a row of instruction
+    // tiles are in flight together.
     __device__ __forceinline__ void epilogue() {
+        const int rows = min(BM, p.M - row0);
+        const rsrc_t rd = make_rsrc(reinterpret_cast<out_t *>(p.D) + (int64_t)row0 * p.ldd,
+                                    (uint32_t)(rows * p.ldd * sizeof(out_t)));
+        if (p.use_c) {
+            const rsrc_t rc = make_rsrc(reinterpret_cast<const out_t *>(p.C) + (int64_t)row0 * p.ldc,
+                                        (uint32_t)(rows * p.ldc * sizeof(out_t)));
+            store_tiles<true>(rd, rc);
+        } else {
+            store_tiles<false>(rd, rd);
+        }
+    }
+
+    template <bool USE_C>
+    __device__ __forceinline__ void store_tiles(rsrc_t rd, rsrc_t rc) {
+        constexpr int JB = TN < 2 ? TN : 2;             // instruction tiles per batch of loads
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int col = col0 + wn * WTN + j * 32 + l32;
+            for (int j0 = 0; j0 < TN; j0 += JB) {
+                uint32_t c[JB][16];
+                uint32_t od[JB][16];
 #pragma unroll
-                for (int G = 0; G < 16; ++G) {
-                    const int row = row0 + wm * WTM + i * 32 + 8 * (G / 4) + 4 * g + (G % 4);
-                    if (row < p.M && col < p.N) {
-                        out_t *d = reinterpret_cast<out_t *>(p.D) + (int64_t)row * p.ldd + col;
-                        if constexpr (std::is_same<out_t, float>::value) {
-                            float v = p.alpha * acc[i][j][G];
-                            if (p.use_c)
-                                v = fmaf(p.beta, reinterpret_cast<const float *>(p.C)[(int64_t)row * p.ldc + col], v);
-                            *d = v;
-                        } else {
-                            uint32_t v = (uint32_t)p.ialpha * (uint32_t)acc[i][j][G];
-                            if (p.use_c)
-                                v += (uint32_t)p.ibeta *
-                                     (uint32_t)reinterpret_cast<const int32_t *>(p.C)[(int64_t)row * p.ldc + col];
-                            *d = (int32_t)v;
+                for (int jj = 0; jj < JB; ++jj) {
+                    const int col = col0 + wn * WTN + (j0 + jj) * 32 + l32;
+#pragma unroll
+                    for (int G = 0; G < 16; ++G) {
+                        const int r = wm * WTM + i * 32 + 8 * (G / 4) + 4 * g + (G % 4);   // row within the tile
+                        const bool in = (row0 + r < p.M) && (col < p.N);
+                        od[jj][G] = in ? (uint32_t)((r * p.ldd + col) * sizeof(out_t)) : kOutOfRange;
+                        if constexpr (USE_C) {
+                            const uint32_t oc = in ? (uint32_t)((r * p.ldc + col) * sizeof(out_t)) : kOutOfRange;
+                            c[jj][G] = __builtin_amdgcn_raw_buffer_load_b32(rc, oc, 0, 0);
                         }
+                    }
+                }
+#pragma unroll
+                for (int jj = 0; jj < JB; ++jj) {
+#pragma unroll
+                    for (int G = 0; G < 16; ++G) {
+                        uint32_t bits;
+                        if constexpr (std::is_same<out_t, float>::value) {
+                            float v = p.alpha * acc[i][j0 + jj][G];
+                            if constexpr (USE_C) v = fmaf(p.beta, __builtin_bit_cast(float, c[jj][G]), v);
+                            bits = __builtin_bit_cast(uint32_t, v);
+                        } else {
+                            uint32_t v = (uint32_t)p.ialpha * (uint32_t)acc[i][j0 + jj][G];
+                            if constexpr (USE_C) v += (uint32_t)p.ibeta * c[jj][G];
+                            bits = v;
+                        }
+                        __builtin_amdgcn_raw_buffer_store_b32(bits, rd, od[jj][G], 0, 0);
                     }
                 }
             }
