@@ -29,6 +29,45 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp8": 5000.0, "int8": 5000.0}
 PEAK_HBM_GBS = 8000.0
 
 
+# Source files each kernel is built from: the HBM traffic recorded in profiles/traffic_8192.json
+# applies only while their hash is the one recorded there.
+_KSRC = {
+    "dense": ["include/mmac.h", "sparse_matrix_multiply_amd/csrc/device.h", "sparse_matrix_multiply_amd/csrc/gemm_tiled.h",
+              "sparse_matrix_multiply_amd/csrc/launch.h", "sparse_matrix_multiply_amd/csrc/gemm_dense.hip",
+              "sparse_matrix_multiply_amd/csrc/abi.hip"],
+    "sparse": ["include/mmac.h", "sparse_matrix_multiply_amd/csrc/device.h", "sparse_matrix_multiply_amd/csrc/gemm_tiled.h",
+               "sparse_matrix_multiply_amd/csrc/launch.h", "sparse_matrix_multiply_amd/csrc/gemm_sparse.hip",
+               "sparse_matrix_multiply_amd/csrc/abi.hip"],
+    "compress": ["include/mmac.h", "sparse_matrix_multiply_amd/csrc/device.h", "sparse_matrix_multiply_amd/csrc/launch.h",
+                 "sparse_matrix_multiply_amd/csrc/compress.hip", "sparse_matrix_multiply_amd/csrc/abi.hip"],
+}
+# kernel names of the launches this benchmark makes (default tile choice at 8192^3)
+_KNAME = {"dense_bf16": ("dense", "gemm_tiled_kernel<mmac::MmaDense16<2>, 256, 256, 2, 4, 4>"),
+          "dense_fp8": ("dense", "gemm_tiled_kernel<mmac::MmaDenseF8<0, 1>, 256, 256, 2, 4, 4>"),
+          "sparse_fp8": ("sparse", "gemm_tiled_kernel<mmac::MmaSparse8<4, 5>, 256, 256, 2, 4, 6>"),
+          "compress_fp8": ("compress", "compress_kernel<4>")}
+
+
+def measured_traffic(part):
+    """HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE) recorded by the last counter runs,
+    or None when the kernel's sources changed since (or nothing was recorded)."""
+    import hashlib
+    kind, name = _KNAME[part]
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "traffic_8192.json")))["kernels"][name]
+    except (OSError, KeyError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in _KSRC[kind]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != rec["source_hash"]:
+        return None
+    return {"bytes": rec["fetch_bytes"] + rec["write_bytes"], "read_bytes": rec["fetch_bytes"],
+            "write_bytes": rec["write_bytes"],
+            "algorithmic_bytes": rec["algorithmic_read_bytes"] + rec["algorithmic_write_bytes"]}
+
+
 def gemm_flops(M, N, K):
     """Work of one GEMM: 2*M*N*K operations (for a 4:2-sparse A, K is the dense K)."""
     return 2 * int(M) * int(N) * int(K)
@@ -173,7 +212,10 @@ def main():
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": pk, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["kernel"] = dominant
-    roof["traffic"] = None
+    tr = measured_traffic(dominant)
+    roof["traffic"] = tr["bytes"] if tr else None
+    if tr:
+        roof["traffic_detail"] = tr
 
     check = None
     if not args.no_check:

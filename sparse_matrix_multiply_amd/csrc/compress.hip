@@ -6,14 +6,17 @@
 // nibble p0 | (p1 << 2) with p0 < p1 (positions {0,2} -> 0x8, as the page's
 // 0x88 / 0x8888 examples show).
 //
-// The work is a streaming copy, bound by HBM bandwidth: each thread owns one
-// 16-byte chunk of a dense row (8 fp16/bf16 = 2 groups, or 16 one-byte
-// elements = 4 groups), reads it with one 128-bit load and writes its 8
-// compressed bytes with one 64-bit store; consecutive threads own consecutive
-// chunks of a row, so both the loads and the stores of a wave are contiguous.
-// The index bits of the 4 (two-byte types) or 2 (one-byte types) chunks that
-// share one 32-bit word are gathered with lane shuffles and written by the
-// first of those lanes.
+// The work is a streaming copy, bound by HBM bandwidth, so the per-element
+// work is kept to a few instructions: each thread owns one 16-byte chunk of a
+// dense row (8 two-byte or 16 one-byte elements = 2 or 4 groups), reads it
+// with one 128-bit load, finds the non-zero masks of its groups with packed
+// word arithmetic, looks the kept pair up in a 16-entry table, gathers the
+// kept elements with byte permutes, and writes its 8 compressed bytes with one
+// 64-bit store.  Consecutive threads own consecutive chunks of a row (the grid
+// is chunks x rows), so both the loads and the stores of a wave are
+// contiguous.  The index bits of the 4 (two-byte types) or 2 (one-byte types)
+// chunks that share a 32-bit word are gathered with lane shuffles and written
+// by the first of those lanes.
 #include <algorithm>
 
 #include "device.h"
@@ -21,98 +24,104 @@
 
 namespace mmac {
 
-// Nonzero test on raw bits: both signed zeros count as zero for the floating
-// types; int8 has a single zero.  NaN is non-zero.
-template <int DT>
-__device__ __forceinline__ uint32_t nonzero(uint32_t x) {
-    if constexpr (DT == DT_F16 || DT == DT_BF16) return (x & 0x7fffu) != 0u;
-    else if constexpr (DT == DT_I8) return (x & 0xffu) != 0u;
-    else return (x & 0x7fu) != 0u;
-}
-
-// Positions kept for a group whose non-zero mask is m (bit p = element p):
-// the non-zero positions; if more than two, the two lowest (a violation); if
-// fewer, topped up with the lowest positions not yet taken.  Returns the
-// nibble p0 | (p1 << 2) and sets *viol.
-__device__ __forceinline__ uint32_t pick_pair(uint32_t m, uint32_t *viol) {
-    *viol = __builtin_popcount(m) > 2 ? 1u : 0u;
+// Kept positions for a group whose non-zero mask is m (bit p = element p):
+// the non-zero positions; if more than two, the two lowest; if fewer, topped
+// up with the lowest positions not yet taken.  Returns p0 | (p1 << 2).
+constexpr uint32_t kept_pair(uint32_t m) {
     uint32_t k = m;
     while (__builtin_popcount(k) < 2) k |= ~k & (k + 1u);   // add the lowest clear bit
-    const uint32_t p0 = __builtin_ctz(k);
-    const uint32_t p1 = __builtin_ctz(k & (k - 1u));
-    return p0 | (p1 << 2);
+    return (uint32_t)__builtin_ctz(k) | ((uint32_t)__builtin_ctz(k & (k - 1u)) << 2);
+}
+constexpr uint64_t pair_table() {
+    uint64_t t = 0;
+    for (uint32_t m = 0; m < 16; ++m) t |= (uint64_t)kept_pair(m) << (4 * m);
+    return t;
+}
+constexpr uint64_t kPairTable = pair_table();
+// masks with more than two non-zeros: 0b0111, 0b1011, 0b1101, 0b1110, 0b1111
+constexpr uint32_t kViolations = (1u << 7) | (1u << 11) | (1u << 13) | (1u << 14) | (1u << 15);
+
+// Non-zero mask of the 4-element group held in one word (one-byte types):
+// floating types treat both signed zeros as zero (bit 7 ignored), int8 has one zero.
+template <int DT>
+__device__ __forceinline__ uint32_t group_mask8(uint32_t w) {
+    uint32_t nz;
+    if constexpr (DT == DT_I8) nz = (((w & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w) & 0x80808080u;
+    else nz = ((w & 0x7f7f7f7fu) + 0x7f7f7f7fu) & 0x80808080u;
+    return ((nz >> 7) & 1u) | ((nz >> 14) & 2u) | ((nz >> 21) & 4u) | ((nz >> 28) & 8u);
+}
+
+// Non-zero mask of the 4-element group held in two words (two-byte floating types).
+__device__ __forceinline__ uint32_t group_mask16(uint32_t w0, uint32_t w1) {
+    const uint32_t n0 = ((w0 & 0x7fff7fffu) + 0x7fff7fffu) & 0x80008000u;
+    const uint32_t n1 = ((w1 & 0x7fff7fffu) + 0x7fff7fffu) & 0x80008000u;
+    return ((n0 >> 15) & 1u) | ((n0 >> 30) & 2u) | ((n1 >> 13) & 4u) | ((n1 >> 28) & 8u);
 }
 
 template <int DT>
-__global__ __launch_bounds__(256) void compress_kernel(CompressParams p, int cpr, int cpr_pad, int64_t total,
-                                                       int64_t iters) {
+__global__ __launch_bounds__(256) void compress_kernel(CompressParams p, int cpr) {
     constexpr int ES = (DT == DT_F16 || DT == DT_BF16) ? 2 : 1;
     constexpr int PER = 16 / ES;         // elements per chunk
     constexpr int GROUPS = PER / 4;      // groups per chunk
     constexpr int LPW = 8 / GROUPS;      // chunks (lanes) per index word
+    const int ch = blockIdx.x * 256 + threadIdx.x;      // chunk within the row
     const int words = (p.K + 31) / 32;
+    const int e0 = ch * PER;
+    const int ngroups = ch < cpr ? min(GROUPS, (p.K - e0) / 4) : 0;   // K % 4 == 0
     uint32_t bad = 0;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t it = 0; it < iters; ++it) {
-        const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x + it * stride;
-        const int64_t row = t / cpr_pad;
-        const int ch = (int)(t - row * cpr_pad);
+    for (int row = blockIdx.y; row < p.M; row += gridDim.y) {
+        const uint8_t *src = p.A + (int64_t)row * p.a_pitch + (int64_t)e0 * ES;
+        uint8_t *dst = p.Ac + (int64_t)row * p.ac_pitch + (int64_t)(e0 / 2) * ES;
         uint32_t bits = 0;
-        if (t < total && ch < cpr) {
-            const int e0 = ch * PER;
-            const int ngroups = min(GROUPS, (p.K - e0) / 4);        // K % 4 == 0
-            const uint8_t *src = p.A + row * p.a_pitch + (int64_t)e0 * ES;
-            uint8_t *dst = p.Ac + row * p.ac_pitch + (int64_t)(e0 / 2) * ES;
-            // chunk as 4 words; group q is word q (1-byte types) or words 2q, 2q+1 (2-byte types)
-            uint32_t w[4] = {0, 0, 0, 0};
+        if (ngroups > 0) {
+            uint32_t w[4] = {0, 0, 0, 0};   // the chunk; group q is word q (1-byte) or words 2q, 2q+1
             if (ngroups == GROUPS) {
                 const i32x4 v = *reinterpret_cast<const i32x4 *>(src);
                 w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
             } else {
-                for (int q = 0; q < ngroups * 4 * ES / 4; ++q) w[q] = reinterpret_cast<const uint32_t *>(src)[q];
+                for (int q = 0; q < ngroups * ES; ++q) w[q] = reinterpret_cast<const uint32_t *>(src)[q];
             }
             uint32_t out[2] = {0, 0};     // 8 compressed bytes
+            uint32_t nib[4];
 #pragma unroll
             for (int q = 0; q < GROUPS; ++q) {
+                const uint32_t m = (ES == 2) ? group_mask16(w[2 * q], w[2 * q + 1]) : group_mask8<DT>(w[q]);
+                nib[q] = (uint32_t)(kPairTable >> (4 * m)) & 0xfu;
                 if (q < ngroups) {
-                    uint32_t e[4];
-                    if constexpr (ES == 2) {
-                        e[0] = w[2 * q] & 0xffffu; e[1] = w[2 * q] >> 16;
-                        e[2] = w[2 * q + 1] & 0xffffu; e[3] = w[2 * q + 1] >> 16;
-                    } else {
-                        e[0] = w[q] & 0xffu; e[1] = (w[q] >> 8) & 0xffu;
-                        e[2] = (w[q] >> 16) & 0xffu; e[3] = w[q] >> 24;
-                    }
-                    const uint32_t m = nonzero<DT>(e[0]) | nonzero<DT>(e[1]) << 1 | nonzero<DT>(e[2]) << 2 |
-                                       nonzero<DT>(e[3]) << 3;
-                    uint32_t viol;
-                    const uint32_t nib = pick_pair(m, &viol);
-                    bad += viol;
-                    bits |= nib << (4 * q);
-                    const uint32_t v0 = e[nib & 3u], v1 = e[nib >> 2];
-                    if constexpr (ES == 2) out[q] = v0 | (v1 << 16);
-                    else out[q / 2] |= (v0 | (v1 << 8)) << (16 * (q % 2));
+                    bad += (kViolations >> m) & 1u;
+                    bits |= nib[q] << (4 * q);
+                }
+            }
+            if constexpr (ES == 2) {
+                // group q -> one word: [half p0, half p1] picked from the 8 bytes (w[2q+1]:w[2q])
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const uint32_t a = 2 * (nib[q] & 3u), b = 2 * (nib[q] >> 2);
+                    out[q] = __builtin_amdgcn_perm(w[2 * q + 1], w[2 * q], a | ((a + 1) << 8) | (b << 16) | ((b + 1) << 24));
+                }
+            } else {
+                // groups 2h, 2h+1 -> one word: [g0.p0, g0.p1, g1.p0, g1.p1] picked from (w[2h+1]:w[2h])
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t n0 = nib[2 * h], n1 = nib[2 * h + 1];
+                    const uint32_t sel = (n0 & 3u) | ((n0 >> 2) << 8) | ((4u + (n1 & 3u)) << 16) | ((4u + (n1 >> 2)) << 24);
+                    out[h] = __builtin_amdgcn_perm(w[2 * h + 1], w[2 * h], sel);
                 }
             }
             if (ngroups == GROUPS) {
                 *reinterpret_cast<i32x2 *>(dst) = i32x2{(int)out[0], (int)out[1]};
+            } else if constexpr (ES == 2) {
+                for (int q = 0; q < ngroups; ++q) reinterpret_cast<uint32_t *>(dst)[q] = out[q];
             } else {
-                // ngroups * 2 elements of ES bytes: a whole number of 2-byte (1-byte types) or
-                // 4-byte (2-byte types) pieces
-                if constexpr (ES == 2) {
-                    for (int q = 0; q < ngroups; ++q) reinterpret_cast<uint32_t *>(dst)[q] = out[q];
-                } else {
-                    for (int q = 0; q < ngroups; ++q)
-                        reinterpret_cast<uint16_t *>(dst)[q] = (uint16_t)(out[q / 2] >> (16 * (q % 2)));
-                }
+                for (int q = 0; q < ngroups; ++q)
+                    reinterpret_cast<uint16_t *>(dst)[q] = (uint16_t)(out[q / 2] >> (16 * (q % 2)));
             }
         }
-        // gather the index bits of the LPW chunks of one word (whole wave takes part)
+        // gather the index bits of the LPW chunks of one word (the whole wave takes part)
         uint32_t word = bits << (4 * GROUPS * (ch % LPW));
         word |= __shfl_xor(word, 1);
         if constexpr (LPW == 4) word |= __shfl_xor(word, 2);
-        if (t < total && (ch % LPW) == 0 && ch / LPW < words)
-            p.idx[row * p.idx_pitch + ch / LPW] = word;
+        if ((ch % LPW) == 0 && ch / LPW < words) p.idx[(int64_t)row * p.idx_pitch + ch / LPW] = word;
     }
     if (p.bad) {
         // one atomic per wave that saw a violation
@@ -123,20 +132,14 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressParams p, int cpr
 
 hipError_t launch_compress(int dt, CompressParams p, hipStream_t s) {
     const int es = (dt == DT_F16 || dt == DT_BF16) ? 2 : 1;
-    const int lpw = es == 2 ? 4 : 2;
-    const int cpr = (int)(((int64_t)p.K * es + 15) / 16);
-    const int cpr_pad = (cpr + lpw - 1) / lpw * lpw;
-    const int64_t total = (int64_t)p.M * cpr_pad;
-    const int64_t max_blocks = 256 * 64;          // enough waves to cover the chip many times over
-    const int64_t blocks = std::min<int64_t>((total + 255) / 256, max_blocks);
-    const int64_t iters = (total + blocks * 256 - 1) / (blocks * 256);
-    const dim3 grid((unsigned)blocks), block(256);
+    const int cpr = (int)(((int64_t)p.K * es + 15) / 16);      // 16-byte chunks per row
+    const dim3 grid((unsigned)((cpr + 255) / 256), (unsigned)std::min(p.M, 65535)), block(256);
     switch (dt) {
-    case DT_F16: hipLaunchKernelGGL(compress_kernel<DT_F16>, grid, block, 0, s, p, cpr, cpr_pad, total, iters); break;
-    case DT_BF16: hipLaunchKernelGGL(compress_kernel<DT_BF16>, grid, block, 0, s, p, cpr, cpr_pad, total, iters); break;
-    case DT_I8: hipLaunchKernelGGL(compress_kernel<DT_I8>, grid, block, 0, s, p, cpr, cpr_pad, total, iters); break;
-    case DT_E4M3: hipLaunchKernelGGL(compress_kernel<DT_E4M3>, grid, block, 0, s, p, cpr, cpr_pad, total, iters); break;
-    case DT_E5M2: hipLaunchKernelGGL(compress_kernel<DT_E5M2>, grid, block, 0, s, p, cpr, cpr_pad, total, iters); break;
+    case DT_F16: hipLaunchKernelGGL(compress_kernel<DT_F16>, grid, block, 0, s, p, cpr); break;
+    case DT_BF16: hipLaunchKernelGGL(compress_kernel<DT_BF16>, grid, block, 0, s, p, cpr); break;
+    case DT_I8: hipLaunchKernelGGL(compress_kernel<DT_I8>, grid, block, 0, s, p, cpr); break;
+    case DT_E4M3: hipLaunchKernelGGL(compress_kernel<DT_E4M3>, grid, block, 0, s, p, cpr); break;
+    case DT_E5M2: hipLaunchKernelGGL(compress_kernel<DT_E5M2>, grid, block, 0, s, p, cpr); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
