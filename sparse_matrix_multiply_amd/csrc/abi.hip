@@ -30,8 +30,7 @@ bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 
 bool integral_i32(double v) { return std::isfinite(v) && v == std::floor(v) && v >= -2147483648.0 && v <= 2147483647.0; }
 
-// Optional overrides for tuning: MMAC_TILE=256|128|64|16 (16 = skinny, M <= 32), MMAC_WAVES=4|8 (waves of
-// a 256 x 256 tile), MMAC_GROUP_M=<n>.
+// Optional overrides for tuning: MMAC_TILE=256|128|64|16 (16 = skinny, M <= 32), MMAC_GROUP_M=<n>.
 int env_int(const char *name, int dflt) {
     const char *s = std::getenv(name);
     if (!s || !*s) return dflt;
@@ -40,7 +39,7 @@ int env_int(const char *name, int dflt) {
 
 TileShape pick_shape(int64_t M, int64_t N, bool sparse = false) {
     const int forced = env_int("MMAC_TILE", 0);
-    if (forced == 256) return env_int("MMAC_WAVES", 8) == 4 ? TILE_256 : TILE_256_W8;
+    if (forced == 256) return TILE_256;
     if (forced == 128) return TILE_128;
     if (forced == 64) return TILE_64;
     if (forced == 16 && !sparse && M <= 32) return TILE_SKINNY;
@@ -48,7 +47,7 @@ TileShape pick_shape(int64_t M, int64_t N, bool sparse = false) {
     if (!sparse && M <= 32) return TILE_SKINNY;
     // Largest tile that still gives about one tile per compute unit (256 CUs).
     auto tiles = [&](int t) { return ((M + t - 1) / t) * ((N + t - 1) / t); };
-    if (tiles(256) >= 192) return env_int("MMAC_WAVES", 8) == 4 ? TILE_256 : TILE_256_W8;
+    if (tiles(256) >= 192) return TILE_256;
     if (tiles(128) >= 192) return TILE_128;
     return TILE_64;
 }
@@ -95,6 +94,14 @@ GemmParams make_params(int a, int64_t M, int64_t N, int64_t K, double alpha, con
     p.ialpha = a == MMAC_I8 ? (int)alpha : 0;
     p.ibeta = a == MMAC_I8 ? (int)beta : 0;
     p.use_c = beta != 0.0 ? 1 : 0;
+    if (p.use_c) {
+        if (a == MMAC_I8) {
+            p.fold_c = alpha == 1.0;
+        } else if (alpha != 0.0) {
+            p.fold_c = 1;
+            p.c_scale = alpha == beta ? 1.0f : (float)(beta / alpha);
+        }
+    }
     const int t = tile_rows(shape);
     p.tiles_m = (int)((M + t - 1) / t);
     p.tiles_n = (int)((N + t - 1) / t);

@@ -342,12 +342,40 @@ struct TiledGemm {
         const int rows = min(BM, p.M - row0);
         const rsrc_t rd = make_rsrc(reinterpret_cast<out_t *>(p.D) + (int64_t)row0 * p.ldd,
                                     (uint32_t)(rows * p.ldd * sizeof(out_t)));
-        if (p.use_c) {
+        if (p.use_c && !p.fold_c) {
             const rsrc_t rc = make_rsrc(reinterpret_cast<const out_t *>(p.C) + (int64_t)row0 * p.ldc,
                                         (uint32_t)(rows * p.ldc * sizeof(out_t)));
             store_tiles<true>(rd, rc);
         } else {
             store_tiles<false>(rd, rd);
+        }
+    }
+
+    // Folded beta * C: the accumulator starts as c_scale * C, read with the same
+    // branch-free buffer accesses as the epilogue.  Called right after the first
+    // copies are issued, so the two latencies overlap.
+    __device__ __forceinline__ void load_c_into_acc() {
+        const int rows = min(BM, p.M - row0);
+        const rsrc_t rc = make_rsrc(reinterpret_cast<const out_t *>(p.C) + (int64_t)row0 * p.ldc,
+                                    (uint32_t)(rows * p.ldc * sizeof(out_t)));
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int col = col0 + wn * WTN + j * 32 + l32;
+#pragma unroll
+                for (int G = 0; G < 16; ++G) {
+                    const int r = wm * WTM + i * 32 + 8 * (G / 4) + 4 * g + (G % 4);
+                    const bool in = (row0 + r < p.M) && (col < p.N);
+                    const uint32_t oc = in ? (uint32_t)((r * p.ldc + col) * sizeof(out_t)) : kOutOfRange;
+                    const uint32_t c = __builtin_amdgcn_raw_buffer_load_b32(rc, oc, 0, 0);
+                    if constexpr (std::is_same<out_t, float>::value)
+                        acc[i][j][G] = p.c_scale * __builtin_bit_cast(float, c);
+                    else
+                        acc[i][j][G] = (int32_t)((uint32_t)p.ibeta * c);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);   // at most one row of instruction tiles of C in flight
         }
     }
 
@@ -408,7 +436,7 @@ void gemm_tiled_kernel(GemmParams p) {
     const int nk = p.K / Op::kBK;                        // whole k-tiles
     const int nkt = nk + (p.K > nk * Op::kBK ? 1 : 0);   // plus a ragged one
 
-    // prologue: start k-tiles 0 .. STAGES-2
+    // prologue: start k-tiles 0 .. STAGES-2 (and the folded C, whose loads overlap them)
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s) {
         if (s < nkt) {
@@ -416,6 +444,7 @@ void gemm_tiled_kernel(GemmParams p) {
             else t.fill_masked(smem + s * T::STAGE, s);
         }
     }
+    if (p.fold_c) t.load_c_into_acc();
     // Copies are counted per wave in issue order.  Before using k-tile kt + 1 the
     // copies of the later k-tiles may stay in flight, provided they are all
     // whole k-tiles (the ragged one issues fewer copy instructions); otherwise

@@ -23,6 +23,11 @@ struct GemmParams {
     float alpha, beta;
     int ialpha, ibeta;
     int use_c;       // beta != 0
+    // fold_c: the accumulator starts as c_scale * C and the epilogue only
+    // scales by alpha (float: c_scale = beta / alpha, alpha != 0; int32:
+    // alpha == 1 and c_scale = beta, exact modulo 2^32).
+    int fold_c;
+    float c_scale;
     int tiles_m, tiles_n, group_m;
 };
 
@@ -38,7 +43,8 @@ struct CompressParams {
 };
 
 // Tile shapes the host can pick from.
-enum TileShape : int { TILE_256 = 0, TILE_128 = 1, TILE_64 = 2, TILE_SKINNY = 3, TILE_256_W8 = 4 };
+// 256 x 256 tiles run 8 waves (2 per SIMD, 128 x 64 each); 128 and 64 run 4 waves.
+enum TileShape : int { TILE_256 = 0, TILE_128 = 1, TILE_64 = 2, TILE_SKINNY = 3 };
 
 // Launchers (defined in the kernel files).  `dt_a`/`dt_b` use the public
 // mmac_dtype_t codes.  They return hipSuccess or the launch error.
@@ -48,8 +54,6 @@ hipError_t launch_gemm_skinny(int dt_a, int dt_b, GemmParams p, hipStream_t s);
 hipError_t launch_compress(int dt, CompressParams p, hipStream_t s);
 
 // Geometry of a tile shape.
-inline int tile_rows(TileShape t) {
-    return (t == TILE_256 || t == TILE_256_W8) ? 256 : t == TILE_128 ? 128 : t == TILE_64 ? 64 : 32;
-}
+inline int tile_rows(TileShape t) { return t == TILE_256 ? 256 : t == TILE_128 ? 128 : t == TILE_64 ? 64 : 32; }
 
 }  // namespace mmac

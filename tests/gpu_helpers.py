@@ -81,9 +81,9 @@ def env(**kv):
                 os.environ[k] = v
 
 
-def tile_shape(t, waves=4):
-    """Force the library's tile shape (MMAC_TILE) and, for 256 x 256 tiles, its wave count."""
-    return env(MMAC_TILE=t, MMAC_WAVES=waves)
+def tile_shape(t):
+    """Force the library's tile shape (MMAC_TILE) for the calls inside the block."""
+    return env(MMAC_TILE=t)
 
 
 def assert_close(D_gpu, D_ref, S, t, K, alpha, beta, C=None, what=""):

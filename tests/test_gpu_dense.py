@@ -35,12 +35,12 @@ def inputs(ta, tb, M, N, K, seed):
     return A, B, C, 1.5, -0.75
 
 
-@pytest.mark.parametrize("tile,waves", [(256, 4), (256, 8), (128, 4), (64, 4)])
+@pytest.mark.parametrize("tile", [256, 128, 64])
 @pytest.mark.parametrize("ta,tb", PAIRS)
 @pytest.mark.parametrize("M,N,K", SHAPES)
-def test_dense_matches_oracle(ta, tb, M, N, K, tile, waves):
+def test_dense_matches_oracle(ta, tb, M, N, K, tile):
     A, B, C, alpha, beta = inputs(ta, tb, M, N, K, M * 7 + N * 3 + K + ta * 11 + tb)
-    with tile_shape(tile, waves):
+    with tile_shape(tile):
         D = run_dense(ta, tb, A, B, alpha, beta, C)
     Dref, aux = oracle.gemm_dense(ta, tb, A, B, alpha, beta, C)
     if ta == I8:
@@ -151,3 +151,21 @@ def test_skinny_path_matches_oracle(ta, tb, M, N, K):
         assert_close(D, Dref, aux, ta, K, alpha, beta, C, f"skinny {ta},{tb} {M}x{N}x{K}")
     D2 = run_dense(ta, tb, A, B, alpha, beta, C)        # default choice, same kernel: same bits
     assert np.array_equal(D, D2)
+
+
+@pytest.mark.parametrize("ta,alpha,beta", [(BF16, 1.0, 1.0), (BF16, 2.0, 0.5), (BF16, 0.0, 2.0), (E4M3, -1.0, 3.0),
+                                            (I8, 1, 5), (I8, 1, -1), (I8, 0, 7), (I8, -2, 3)])
+@pytest.mark.parametrize("tile", [256, 64])
+def test_alpha_beta_combinations(ta, alpha, beta, tile):
+    """beta * C is folded into the accumulator when alpha != 0 (floating) or alpha == 1 (int8),
+    and applied in the epilogue otherwise; both must agree with the oracle."""
+    tb = E5M2 if ta == E4M3 else ta
+    M, N, K = 300, 270, 160
+    A, B, C, _, _ = inputs(ta, tb, M, N, K, 31)
+    with tile_shape(tile):
+        D = run_dense(ta, tb, A, B, alpha, beta, C)
+    Dref, aux = oracle.gemm_dense(ta, tb, A, B, alpha, beta, C)
+    if ta == I8:
+        assert np.array_equal(D, Dref)
+    else:
+        assert_close(D, Dref, aux, ta, K, alpha, beta, C, f"alpha {alpha} beta {beta}")
