@@ -105,7 +105,7 @@ GemmParams make_params(int a, int64_t M, int64_t N, int64_t K, double alpha, con
     const int t = tile_rows(shape);
     p.tiles_m = (int)((M + t - 1) / t);
     p.tiles_n = (int)((N + t - 1) / t);
-    p.group_m = std::max(1, env_int("MMAC_GROUP_M", 4));
+    p.group_m = std::max(1, env_int("MMAC_GROUP_M", 8));
     return p;
 }
 

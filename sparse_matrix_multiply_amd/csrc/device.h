@@ -141,7 +141,7 @@ template <int FA, int FB> struct MmaDenseF8 {
 template <int DT> struct MmaSparse16 {
     static constexpr bool kSparse = true;
     static constexpr int kEsize = 2, kAFrag = 16, kBFrag = 32, kKStep = 32;
-    static constexpr int kBK = 32;
+    static constexpr int kBK = 64;                 // 64-byte compressed A rows, 128-byte B rows
     static constexpr int kARowBytes = kBK / 2 * kEsize, kBRowBytes = kBK * kEsize;
     static constexpr int kIdxWordsPerTile = kBK / 32;
     typedef f32x16 acc_t;
@@ -166,7 +166,7 @@ template <int DT> struct MmaSparse16 {
 template <int DT_A, int DT_B> struct MmaSparse8 {
     static constexpr bool kSparse = true;
     static constexpr int kEsize = 1, kAFrag = 16, kBFrag = 32, kKStep = 64;
-    static constexpr int kBK = 64;
+    static constexpr int kBK = 128;                // 64-byte compressed A rows, 128-byte B rows
     static constexpr int kARowBytes = kBK / 2, kBRowBytes = kBK;
     static constexpr int kIdxWordsPerTile = kBK / 32;
     static constexpr bool kInt = (DT_A == DT_I8);
