@@ -81,6 +81,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="rows of the oracle slice (0 = calibrate)")
+    ap.add_argument("--suite", action="store_true",
+                    help="instead of the step, time every workload once (one JSON line with a 'suite' object)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain elementwise copy of this many MiB (fp32) three times: the known-size "
                          "kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters")
@@ -102,6 +104,9 @@ def main():
     args = parse()
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
+        return
+    if args.suite:
+        suite()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -235,6 +240,116 @@ def main():
         "parts": report, "roofline": roof, "cpu_baseline": cpu, "check": check,
     }
     print(json.dumps(line), flush=True)
+
+
+def suite():
+    """Time each workload on its own: median of repeated launches timed with HIP events on the
+    launch stream.  HBM-bound cases rotate through enough copies of their inputs to exceed the
+    256 MB Infinity Cache, so they measure HBM, not the cache."""
+    import numpy as np
+    import torch
+
+    import sparse_matrix_multiply_amd as mm
+    import workloads as W
+
+    mm.lib()
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+
+    def to_dev(bits, t):
+        if t == W.I8:
+            return torch.from_numpy(np.ascontiguousarray(bits)).to(dev)
+        host = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16 if bits.dtype == np.uint16 else np.int8))
+        return host.to(dev).view({W.BF16: torch.bfloat16, W.F16: torch.float16, W.E4M3: torch.float8_e4m3fn,
+                                  W.E5M2: torch.float8_e5m2}[t])
+
+    def median_ms(fns, reps):
+        """fns: list of callables used round-robin (buffer rotation).  Returns the mean time of one
+        launch in a back-to-back batch (throughput; launch overheads overlap) and the median of
+        single launches each bracketed by events (latency)."""
+        for f in fns[:2]:
+            f()
+        torch.cuda.synchronize()
+        times = []
+        for r in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fns[r % len(fns)]()
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for r in range(reps):
+            fns[r % len(fns)]()
+        e1.record(stream)
+        e1.synchronize()
+        batch.append(sorted(times)[len(times) // 2])
+        return e0.elapsed_time(e1) / reps
+
+    batch = []
+
+    out = {}
+
+    def dense_case(name, key, reps=20, rotate=1):
+        w = W.workload(name)
+        A, B = to_dev(w["A"], w["ta"]), to_dev(w["B"], w["tb"])
+        C = torch.from_numpy(w["C"]).to(dev) if w["beta"] != 0 else None
+        integer = w["ta"] == W.I8
+        Ds = [torch.empty((w["M"], w["N"]), dtype=torch.int32 if integer else torch.float32, device=dev)
+              for _ in range(rotate)]
+        Bs = [B] + [B.clone() for _ in range(rotate - 1)]
+        fns = [lambda i=i: mm.gemm_dense(A, Bs[i], Ds[i], w["alpha"], w["beta"], C, a_type=w["ta"], b_type=w["tb"],
+                                         stream=stream) for i in range(rotate)]
+        ms = median_ms(fns, reps)
+        f = gemm_flops(w["M"], w["N"], w["K"])
+        es = 2 if w["ta"] in (W.BF16, W.F16) else 1
+        byt = (w["M"] + w["N"]) * w["K"] * es + w["M"] * w["N"] * 4 * (2 if w["beta"] != 0 else 1)
+        out[key] = {"us": round(ms * 1e3, 1), "single_launch_us": round(batch[-1] * 1e3, 1),
+                    ("TOP/s" if integer else "TFLOP/s"): round(f / ms / 1e9, 1),
+                    "GB/s": round(byt / ms / 1e6, 1), "shape": [w["M"], w["N"], w["K"]], "alpha": w["alpha"],
+                    "beta": w["beta"]}
+        del A, B, Bs, C, Ds
+        torch.cuda.empty_cache()
+
+    # reference: a plain device copy of the skinny GEMM's bytes, rotated the same way
+    n = (16 * 4096 * 2 + 4096 * 4096 * 2 + 2 * 16 * 4096 * 4) // 8
+    srcs = [torch.ones(n, dtype=torch.float32, device=dev) for _ in range(16)]
+    dsts = [torch.empty_like(x) for x in srcs]
+    cms = median_ms([lambda i=i: dsts[i].copy_(srcs[i]) for i in range(16)], 200)
+    out["reference_copy_32.6MiB"] = {"us": round(cms * 1e3, 1), "GB/s": round(2 * n * 4 / cms / 1e6, 1)}
+    del srcs, dsts
+
+    dense_case("bf16_256", "bf16_256^3", reps=200)
+    dense_case("i8_1024", "int8_1024^3", reps=200)
+    dense_case("bf16_4096", "bf16_4096^3_beta1")
+    dense_case("bf16_skinny", "bf16_16x4096x4096_beta1", reps=200, rotate=16)
+    dense_case("bf16_8192", "bf16_8192^3_beta1")
+    dense_case("fp8_8192", "fp8e4m3xbf8e5m2_8192^3")
+
+    for name, key, rot in (("f16_sparse", "f16_4:2_4096x4096x8192", 8), ("fp8_8192_sparse", "fp8_4:2_8192^3", 8)):
+        w = W.workload(name)
+        ta, tb, M, N, K = w["ta"], w["tb"], w["M"], w["N"], w["K"]
+        As = [to_dev(w["A"], ta)]
+        As += [As[0].clone() for _ in range(rot - 1)]
+        tdt = As[0].dtype
+        Acs = [torch.empty((M, K // 2), dtype=tdt, device=dev) for _ in range(rot)]
+        idxs = [torch.empty((M, K // 32), dtype=torch.int32, device=dev) for _ in range(rot)]
+        cms = median_ms([lambda i=i: mm.sparse24_compress(As[i], Acs[i], idxs[i], a_type=ta, stream=stream)
+                         for i in range(rot)], 40)
+        es = 2 if ta in (W.BF16, W.F16) else 1
+        cbytes = M * K * es + M * (K // 2) * es + M * (K // 32) * 4
+        B = to_dev(w["B"], tb)
+        D = torch.empty((M, N), dtype=torch.float32, device=dev)
+        gms = median_ms([lambda: mm.gemm_sparse24(Acs[0], idxs[0], B, D, K=K, a_type=ta, b_type=tb, stream=stream)], 20)
+        f = gemm_flops(M, N, K)
+        out[key] = {"compress_us": round(cms * 1e3, 1), "compress_GB/s": round(cbytes / cms / 1e6, 1),
+                    "gemm_us": round(gms * 1e3, 1), "TFLOP/s_dense_equivalent": round(f / gms / 1e9, 1),
+                    "TFLOP/s_effective": round(f / 2 / gms / 1e9, 1), "shape": [M, N, K]}
+        del As, Acs, idxs, B, D
+        torch.cuda.empty_cache()
+    print(json.dumps({"suite": out, "note": "median of repeated single launches (HIP events); skinny GEMM and "
+                      "compressors rotate through copies larger than the 256 MB Infinity Cache"}), flush=True)
 
 
 def spot_check(wb, w8, ws, Db, D8, Ds, Ac, idx, dev):

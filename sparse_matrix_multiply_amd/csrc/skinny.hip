@@ -104,6 +104,25 @@ __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(GemmParams p) {
     const rsrc_t ra = make_rsrc(p.A, (uint32_t)(p.M * p.a_pitch));
     const rsrc_t rb = make_rsrc(p.B + (int64_t)col0 * p.b_pitch, (uint32_t)(bcols * p.b_pitch));
 
+    // The output this thread writes after the reduction; its C element is
+    // loaded now so that the load overlaps the streaming of B.  Buffer accesses
+    // over D's / C's first M rows: elements outside M x N get an offset past the
+    // end, where loads return zero and stores are dropped.
+    constexpr int OUTS = MB * CB * 4 * 64;
+    static_assert(OUTS <= WK * 64, "one output per thread");
+    const int o = threadIdx.x;
+    const int oln = o & 63, orr = (o >> 6) & 3, oc = (o >> 8) % CB, om = (o >> 8) / CB;
+    const int orow = om * 16 + 4 * (oln >> 4) + orr, ocol = col0 + oc * 16 + (oln & 15);
+    const bool oin = o < OUTS && orow < p.M && ocol < p.N;
+    const rsrc_t rd = make_rsrc(p.D, (uint32_t)(p.M * p.ldd * sizeof(out_t)));
+    const uint32_t od = oin ? (uint32_t)((orow * p.ldd + ocol) * sizeof(out_t)) : kOutOfRange;
+    uint32_t cpre = 0;
+    if (p.use_c) {
+        const rsrc_t rcc = make_rsrc(p.C, (uint32_t)(p.M * p.ldc * sizeof(out_t)));
+        cpre = __builtin_amdgcn_raw_buffer_load_b32(rcc, oin ? (uint32_t)((orow * p.ldc + ocol) * sizeof(out_t)) : kOutOfRange,
+                                                   0, 0);
+    }
+
     // contiguous range of K steps for this wave
     const int nsteps = (p.K + KS - 1) / KS;
     const int per_wave = (nsteps + WK - 1) / WK;
@@ -139,7 +158,7 @@ __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(GemmParams p) {
                 for (int c = 0; c < CB; ++c) acc[m][c] = Op::mma(a[u][m], b[u][c], acc[m][c]);
     }
 
-    // combine the WK partial tiles in LDS, in wave order
+    // combine the WK partial tiles in LDS, in wave order; each thread then owns one output
     __shared__ out_t red[WK][MB][CB][4][64];
 #pragma unroll
     for (int m = 0; m < MB; ++m)
@@ -148,36 +167,30 @@ __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(GemmParams p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) red[wave][m][c][r][lane] = acc[m][c][r];
     __syncthreads();
-    constexpr int OUTS = MB * CB * 4 * 64;
-    for (int o = threadIdx.x; o < OUTS; o += WK * 64) {
-        const int ln = o & 63, r = (o >> 6) & 3, c = (o >> 8) % CB, m = (o >> 8) / CB;
-        out_t v = red[0][m][c][r][ln];
+    if (o < OUTS) {
+        out_t v = red[0][om][oc][orr][oln];
         for (int w = 1; w < WK; ++w) {
-            if constexpr (std::is_same<out_t, float>::value) v += red[w][m][c][r][ln];
-            else v = (out_t)((uint32_t)v + (uint32_t)red[w][m][c][r][ln]);
+            if constexpr (std::is_same<out_t, float>::value) v += red[w][om][oc][orr][oln];
+            else v = (out_t)((uint32_t)v + (uint32_t)red[w][om][oc][orr][oln]);
         }
-        const int row = m * 16 + 4 * (ln >> 4) + r;
-        const int col = col0 + c * 16 + (ln & 15);
-        if (row < p.M && col < p.N) {
-            out_t *d = reinterpret_cast<out_t *>(p.D) + (int64_t)row * p.ldd + col;
-            if constexpr (std::is_same<out_t, float>::value) {
-                float x = p.alpha * v;
-                if (p.use_c) x = fmaf(p.beta, reinterpret_cast<const float *>(p.C)[(int64_t)row * p.ldc + col], x);
-                *d = x;
-            } else {
-                uint32_t x = (uint32_t)p.ialpha * (uint32_t)v;
-                if (p.use_c)
-                    x += (uint32_t)p.ibeta * (uint32_t)reinterpret_cast<const int32_t *>(p.C)[(int64_t)row * p.ldc + col];
-                *d = (int32_t)x;
-            }
+        uint32_t bits;
+        if constexpr (std::is_same<out_t, float>::value) {
+            float x = p.alpha * v;
+            if (p.use_c) x = fmaf(p.beta, __builtin_bit_cast(float, cpre), x);
+            bits = __builtin_bit_cast(uint32_t, x);
+        } else {
+            uint32_t x = (uint32_t)p.ialpha * (uint32_t)v;
+            if (p.use_c) x += (uint32_t)p.ibeta * cpre;
+            bits = x;
         }
+        __builtin_amdgcn_raw_buffer_store_b32(bits, rd, od, 0, 0);
     }
 }
 
 template <int DA, int DB>
 static hipError_t launch_types(const GemmParams &p, hipStream_t s) {
     typedef Mma16<DA, DB> Op;
-    constexpr int CB = 1, WK = 4, U = 4;
+    constexpr int CB = 1, WK = 8, U = 8;   // 8 waves x 8 steps of loads in flight per workgroup
     const dim3 grid((p.N + 16 * CB - 1) / (16 * CB)), block(WK * 64);
     if (p.M <= 16) hipLaunchKernelGGL((gemm_skinny_kernel<Op, 1, CB, WK, U>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((gemm_skinny_kernel<Op, 2, CB, WK, U>), grid, block, 0, s, p);
