@@ -54,8 +54,13 @@
  *     next synchronisation.
  *   - Errors: no exception crosses this interface.  Argument errors are
  *     detected before any GPU work is enqueued; nothing is written then.
- *   - Thread safety: calls are re-entrant; the library keeps no mutable state
- *     besides a per-device cache of device properties, filled once.
+ *   - Thread safety: calls are re-entrant; the library keeps no state between
+ *     calls.
+ *   - Tuning: two environment variables, read on every call, override the
+ *     tile choice: MMAC_TILE (256, 128 or 64 forces that output tile; 16
+ *     forces the one-wave-column path for M <= 32) and MMAC_GROUP_M (tile rows
+ *     visited together by the scheduler, default 8).  Results do not depend
+ *     on them beyond floating-point rounding.
  */
 #ifndef MMAC_H
 #define MMAC_H
