@@ -120,12 +120,14 @@ struct TiledGemm {
     typedef typename Op::acc_t acc_t;
     typedef typename Op::out_t out_t;
     static constexpr int NW = WM * WN, NT = NW * 64, STAGES = STAGES_;
+    static constexpr int STEPS = Op::kBK / Op::kKStep;
     static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 tiles");
     static constexpr int AW = Op::kARowBytes / 16, BW = Op::kBRowBytes / 16;  // 16-byte units per LDS row
     static_assert(AW == 2 || AW == 4 || AW == 8, "A LDS rows of 32, 64 or 128 bytes");
     static_assert(BW == 4 || BW == 8, "B LDS rows of 64 or 128 bytes");
     static constexpr int IW = Op::kSparse ? Op::kBK / 32 : 0;                  // index words per row
+    static_assert(!Op::kSparse || (STEPS == 2 && IW % 2 == 0), "one 8-byte index read per row and k-tile");
     // copy units per wave: 16-byte units of A and B, 4-byte words of the index
     static constexpr int AUPW = BM * AW / NW, BUPW = BN * BW / NW, IUPW = BM * IW / NW;
     static_assert(AUPW * NW == BM * AW && BUPW * NW == BN * BW && IUPW * NW == BM * IW, "uneven copy split");
@@ -133,7 +135,6 @@ struct TiledGemm {
     static constexpr int LPT = AP + BP + IP;        // copy instructions per wave per k-tile
     static constexpr int A_BYTES = BM * AW * 16, B_BYTES = BN * BW * 16, I_BYTES = BM * IW * 4;
     static constexpr int STAGE = A_BYTES + B_BYTES + I_BYTES;
-    static constexpr int STEPS = Op::kBK / Op::kKStep;
     static constexpr int LDS_BYTES = STAGES * STAGE;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 workgroup");
 
@@ -145,7 +146,7 @@ struct TiledGemm {
     __device__ __forceinline__ TiledGemm(const GemmParams &p_) : p(p_) {
         const int tid = threadIdx.x;
         lane = tid & 63;
-        wave = tid >> 6;
+        wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases go straight to M0
         g = lane >> 5;
         l32 = lane & 31;
         wm = wave / WN;
@@ -173,9 +174,11 @@ struct TiledGemm {
         return (L / W) * (uint32_t)pitch + (uint32_t)(kt * W * 16) + (L % W) * 16;
     }
 
-    // Byte offset of word d (= row * IW + w) of the index tile at k-tile kt.
+    // Byte offset of the source of LDS index word d (= row * IW + slot) at
+    // k-tile kt; the op decides which word of the row each slot holds.
     __device__ __forceinline__ uint32_t idx_off(uint32_t d, int kt) const {
-        return ((d / IW) * (uint32_t)p.idx_pitch + kt * IW + d % IW) * 4;
+        const uint32_t r = d / IW;
+        return (r * (uint32_t)p.idx_pitch + kt * IW + Op::idx_src_word(d % IW, r)) * 4;
     }
 
     __device__ __forceinline__ void copy_index(uint8_t *st, int kt) const {
@@ -241,8 +244,9 @@ struct TiledGemm {
     typedef Frag<Op::kAFrag> FragA;
     typedef Frag<Op::kBFrag> FragB;
 
-    // Fragments (and index bits) of step s of the k-tile held in LDS stage `st`.
-    __device__ __forceinline__ void load_frags(FragA (&a)[TM], FragB (&b)[TN], uint32_t (&ix)[TM], const uint8_t *st,
+    // Fragments of step s of the k-tile held in LDS stage `st`, and with step 0
+    // the index words of every step of that k-tile (sparse A).
+    __device__ __forceinline__ void load_frags(FragA (&a)[TM], FragB (&b)[TN], i32x2 (&ix)[TM], const uint8_t *st,
                                                int s) const {
         const uint8_t *sa = st, *sb = st + A_BYTES;
         const uint32_t *sx = reinterpret_cast<const uint32_t *>(st + A_BYTES + B_BYTES);
@@ -250,8 +254,13 @@ struct TiledGemm {
         for (int i = 0; i < TM; ++i) {
             const uint32_t r = wm * WTM + i * 32 + l32;
             lds_frag<AW>(a[i], sa, r * AW + Op::a_unit(s, g, 0), r * AW + Op::a_unit(s, g, 1));
-            if constexpr (Op::kSparse) ix[i] = Op::lane_idx(sx + r * IW, s, g);
-            else ix[i] = 0;
+            if constexpr (Op::kSparse) {
+                if (s == 0)
+                    ix[i] = *reinterpret_cast<const i32x2 *>(reinterpret_cast<const uint8_t *>(sx + r * IW) +
+                                                             Op::idx_pair_offset(r, g));
+            } else {
+                ix[i] = i32x2{0, 0};
+            }
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
@@ -264,16 +273,22 @@ struct TiledGemm {
     static constexpr int NMMA = TM * TN;
     static constexpr int NREAD = TM * (Op::kAFrag / 16) + TN * (Op::kBFrag / 16) + (Op::kSparse ? TM : 0);
 
+    // Index operand of the matrix instruction of step s.
+    __device__ __forceinline__ uint32_t step_idx(const i32x2 &x, int s) const {
+        if constexpr (Op::kSparse) return Op::lane_idx(x, s, g);
+        else return 0;
+    }
+
     // The TM x TN matrix instructions of one step, interleaved by the scheduler
     // with the LDS reads (next step's fragments) and copy instructions issued
     // before them in the same region: one matrix instruction, then one read,
     // then one copy, so the reads and copies go out while the matrix unit works.
-    __device__ __forceinline__ void mma_step(const FragA (&a)[TM], const FragB (&b)[TN], const uint32_t (&ix)[TM],
+    __device__ __forceinline__ void mma_step(const FragA (&a)[TM], const FragB (&b)[TN], const i32x2 (&ix)[TM], int s,
                                              int ncopies) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] = Op::mma(a[i], b[j], acc[i][j], ix[i]);
+            for (int j = 0; j < TN; ++j) acc[i][j] = Op::mma(a[i], b[j], acc[i][j], step_idx(ix[i], s));
 #pragma unroll
         for (int k = 0; k < NMMA; ++k) {
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
@@ -285,7 +300,7 @@ struct TiledGemm {
     // Fragment double buffer: a0/b0/x0 feed the current step, a1/b1/x1 receive the next.
     FragA a0[TM], a1[TM];
     FragB b0[TN], b1[TN];
-    uint32_t x0[TM], x1[TM];
+    i32x2 x0[TM], x1[TM];
 
     // One k-tile: start the copy of k-tile kt + STAGES - 1 into the stage that
     // k-tile kt - 1 freed, then the STEPS steps of k-tile kt (in stage `cur`).
@@ -319,11 +334,11 @@ struct TiledGemm {
                 block_barrier();
                 load_frags(a1, b1, x1, sn, 0);   // past the last k-tile this reads a stale stage, unused
             }
-            mma_step(a0, b0, x0, (STEADY && s == 0) ? LPT : 0);
+            mma_step(a0, b0, x0, s, (STEADY && s == 0) ? LPT : 0);
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 a0[i] = a1[i];
-                x0[i] = x1[i];
+                if (s + 1 == STEPS) x0[i] = x1[i];   // index words change once per k-tile
             }
 #pragma unroll
             for (int j = 0; j < TN; ++j) b0[j] = b1[j];
