@@ -291,8 +291,14 @@ def suite():
 
     out = {}
 
-    def dense_case(name, key, reps=20, rotate=1):
-        w = W.workload(name)
+    def dense_case(name, key, reps=20, rotate=1, n_share=None):
+        """n_share: keep only the first n_share columns of B, C and D (one GPU's share when N is
+        split across GPUs)."""
+        w = dict(W.workload(name))
+        if n_share:
+            w["B"], w["N"] = w["B"][:n_share], n_share
+            if w["C"] is not None:
+                w["C"] = np.ascontiguousarray(w["C"][:, :n_share])
         A, B = to_dev(w["A"], w["ta"]), to_dev(w["B"], w["tb"])
         C = torch.from_numpy(w["C"]).to(dev) if w["beta"] != 0 else None
         integer = w["ta"] == W.I8
@@ -326,9 +332,16 @@ def suite():
     dense_case("bf16_skinny", "bf16_16x4096x4096_beta1", reps=200, rotate=16)
     dense_case("bf16_8192", "bf16_8192^3_beta1")
     dense_case("fp8_8192", "fp8e4m3xbf8e5m2_8192^3")
+    # one GPU's share of the 8192^3 GEMMs split 8 ways along N
+    dense_case("bf16_8192", "share_bf16_8192x1024x8192_beta1", n_share=1024)
+    dense_case("fp8_8192", "share_fp8e4m3xbf8e5m2_8192x1024x8192", n_share=1024)
 
-    for name, key, rot in (("f16_sparse", "f16_4:2_4096x4096x8192", 8), ("fp8_8192_sparse", "fp8_4:2_8192^3", 8)):
-        w = W.workload(name)
+    for name, key, rot, n_share in (("f16_sparse", "f16_4:2_4096x4096x8192", 8, None),
+                                    ("fp8_8192_sparse", "fp8_4:2_8192^3", 8, None),
+                                    ("fp8_8192_sparse", "share_fp8_4:2_8192x1024x8192", 8, 1024)):
+        w = dict(W.workload(name))
+        if n_share:
+            w["B"], w["N"] = w["B"][:n_share], n_share
         ta, tb, M, N, K = w["ta"], w["tb"], w["M"], w["N"], w["K"]
         As = [to_dev(w["A"], ta)]
         As += [As[0].clone() for _ in range(rot - 1)]

@@ -77,3 +77,37 @@ def test_sparse_workloads(name):
     fn = lambda ii, jj: oracle.gemm_sparse24_entries(ta, tb, Ac_ref, idx_ref, w["B"], ii, jj, w["alpha"],
                                                      w["beta"], w["C"])
     check_sampled(D, w, fn, 8)
+
+
+def share_of(name, n_share=1024):
+    """One GPU's share of an 8192^3 workload split 8 ways along N: all of A, the first
+    n_share columns of B (and C)."""
+    w = dict(W.workload(name))
+    w["B"], w["N"] = np.ascontiguousarray(w["B"][:n_share]), n_share
+    if w["C"] is not None:
+        w["C"] = np.ascontiguousarray(w["C"][:, :n_share])
+    return w
+
+
+@pytest.mark.parametrize("name", ["bf16_8192", "fp8_8192"])
+def test_share_shape_dense_sampled(name):
+    w = share_of(name)
+    D = dense_on_gpu(w)
+    fn = lambda ii, jj: oracle.gemm_dense_entries(w["ta"], w["tb"], w["A"], w["B"], ii, jj, w["alpha"],
+                                                  w["beta"], w["C"])
+    check_sampled(D, w, fn, 9)
+
+
+def test_share_shape_sparse_sampled():
+    w = share_of("fp8_8192_sparse")
+    ta, tb, M, N, K = w["ta"], w["tb"], w["M"], w["N"], w["K"]
+    Ac_ref, idx_ref, _ = oracle.compress24(ta, w["A"])
+    Acd = to_dev_bits(Ac_ref, ta)
+    idxd = torch.from_numpy(idx_ref.view(np.int32)).to(dev())
+    D = out_tensor(M, N, False)
+    mm.gemm_sparse24(Acd, idxd, to_dev_bits(w["B"], tb), D, K=K, alpha=w["alpha"], beta=w["beta"],
+                     a_type=ta, b_type=tb)
+    torch.cuda.synchronize()
+    fn = lambda ii, jj: oracle.gemm_sparse24_entries(ta, tb, Ac_ref, idx_ref, w["B"], ii, jj, w["alpha"],
+                                                     w["beta"], w["C"])
+    check_sampled(D, w, fn, 10)
