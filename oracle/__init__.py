@@ -44,6 +44,7 @@ def lib():
                                            i64, i64, vp, i64, vp]
         L.oracle_compress24.argtypes = [ip, i64, i64, vp, i64, vp, i64, vp, i64, vp]
         L.oracle_decompress24.argtypes = [ip, i64, i64, vp, i64, vp, i64, vp, i64]
+        L.oracle_prune_compress24.argtypes = [ip, i64, i64, vp, i64, vp, i64, vp, i64, vp]
         L.oracle_gemm_sparse24_f64.argtypes = [ip, ip, i64, i64, i64, dbl, vp, i64, vp, i64, vp, i64,
                                                dbl, vp, i64, i64, i64, vp, i64, vp, i64]
         L.oracle_gemm_sparse24_f64_entries.argtypes = [ip, ip, i64, i64, i64, dbl, vp, i64, vp, i64, vp,
@@ -138,6 +139,21 @@ def compress24(t, A):
     bad = ctypes.c_int64(0)
     _check(lib().oracle_compress24(t, M, K, _p(A), K, _p(Ac), K // 2, _p(idx), W, ctypes.byref(bad)),
            "compress24")
+    return Ac, idx, int(bad.value)
+
+
+def prune_compress24(t, A):
+    """Magnitude pruning of a dense A to 4:2 (two largest |a| per group of four, NaN
+    largest, ties to the lower position), then compression.  Returns
+    (Ac, idx, groups_with_more_than_two_nonzeros)."""
+    A = _c2(A, BITS_DTYPE[t])
+    M, K = A.shape
+    Ac = np.zeros((M, K // 2), BITS_DTYPE[t])
+    W = (K + 31) // 32
+    idx = np.zeros((M, W), np.uint32)
+    bad = ctypes.c_int64(0)
+    _check(lib().oracle_prune_compress24(t, M, K, _p(A), K, _p(Ac), K // 2, _p(idx), W, ctypes.byref(bad)),
+           "prune_compress24")
     return Ac, idx, int(bad.value)
 
 

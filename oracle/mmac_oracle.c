@@ -5,6 +5,7 @@
  * computes:
  *   - dense   D = alpha * A*B + beta * C       (fp64 or int64 accumulation)
  *   - 4:2 compression of a structured-sparse A into non-zeros + index nibbles
+ *   - magnitude pruning of a dense A to 4:2 followed by that compression
  *   - sparse  D = alpha * A*B + beta * C with A given in compressed form
  *
  * Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
@@ -275,6 +276,59 @@ int oracle_compress24(int t, int64_t M, int64_t K, const void *A, int64_t lda,
             store_bits(t, Ac, i * ldac + 2 * g + 1, load_bits(t, A, i * lda + 4 * g + pos[1]));
             uint32_t nib = (uint32_t)pos[0] | ((uint32_t)pos[1] << 2);
             idx[i * ldidx + g / 8] |= nib << (4 * (g % 8));
+        }
+    }
+    if (bad_groups) *bad_groups = bad;
+    return 0;
+}
+
+/*
+ * Magnitude pruning to the 4:2 pattern, then compression.  The pages give the
+ * pattern and the compressed form ("CDNA3 sparse MFMA builtins", "Structured
+ * sparsity (4:2 pattern)") but not how a dense A is brought to it; this
+ * follows the usual magnitude rule:
+ *   - in every group of four along K keep the two elements of largest |a|
+ *     (decoded value; int8 -128 has magnitude 128);
+ *   - a NaN is larger than every number, infinities included; all NaNs tie;
+ *   - ties go to the lower position;
+ *   - the two kept elements are then stored exactly as the compressor above
+ *     stores them (ascending positions, bits copied, nibble p0 | (p1 << 2)).
+ * *bad_groups counts the groups that held more than two non-zeros (the ones
+ * pruning changed), with the compressor's notion of non-zero.
+ */
+static int mag_greater(double x, double y) {   /* |x| > |y| with NaN above everything */
+    int nx = isnan(x), ny = isnan(y);
+    if (nx || ny) return nx && !ny;
+    return fabs(x) > fabs(y);
+}
+
+int oracle_prune_compress24(int t, int64_t M, int64_t K, const void *A, int64_t lda,
+                            void *Ac, int64_t ldac, uint32_t *idx, int64_t ldidx, int64_t *bad_groups) {
+    if (t < OR_F16 || t > OR_E5M2 || M < 0 || K < 0 || (K % 4) != 0) return -1;
+    const int64_t G = K / 4, words = (K + 31) / 32;
+    int64_t bad = 0;
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t w = 0; w < words; ++w) idx[i * ldidx + w] = 0u;
+        for (int64_t g = 0; g < G; ++g) {
+            double v[4];
+            int order[4], nz = 0;
+            for (int p = 0; p < 4; ++p) {
+                uint32_t b = load_bits(t, A, i * lda + 4 * g + p);
+                v[p] = oracle_decode_one(t, b);
+                nz += !elem_is_zero(t, b);
+                order[p] = p;
+            }
+            if (nz > 2) ++bad;
+            /* stable insertion sort of the positions by decreasing magnitude */
+            for (int a = 1; a < 4; ++a)
+                for (int b = a; b > 0 && mag_greater(v[order[b]], v[order[b - 1]]); --b) {
+                    int tmp = order[b]; order[b] = order[b - 1]; order[b - 1] = tmp;
+                }
+            int p0 = order[0], p1 = order[1];
+            if (p0 > p1) { int tmp = p0; p0 = p1; p1 = tmp; }
+            store_bits(t, Ac, i * ldac + 2 * g, load_bits(t, A, i * lda + 4 * g + p0));
+            store_bits(t, Ac, i * ldac + 2 * g + 1, load_bits(t, A, i * lda + 4 * g + p1));
+            idx[i * ldidx + g / 8] |= ((uint32_t)p0 | ((uint32_t)p1 << 2)) << (4 * (g % 8));
         }
     }
     if (bad_groups) *bad_groups = bad;

@@ -294,6 +294,103 @@ def test_compress_matches_generator_pattern_and_round_trips(t):
     assert np.array_equal(oracle.decompress24(t, Ac, idx, K), A)
 
 
+# ------------------------------------------------- magnitude prune + compress --
+# Magnitude pruning is not on the pages (they give the 4:2 pattern and the
+# compressed form only): keep the two largest |a| of each group of four, a NaN
+# above every number, ties to the lower position.  Pinned by a rank-count
+# brute force over torch-decoded values (a different algorithm from the
+# oracle's sort), by hand-worked groups, and by agreement with the plain
+# compressor wherever the input already has the 4:2 pattern.
+
+def _mag_greater(x, y):
+    if np.isnan(x) or np.isnan(y):
+        return bool(np.isnan(x) and not np.isnan(y))
+    return abs(x) > abs(y)
+
+
+def _kept_by_rank(v):
+    """Positions whose rank (elements ahead of them by magnitude, earlier position on ties) is < 2."""
+    kept = []
+    for p in range(4):
+        ahead = sum(1 for q in range(4) if q != p and (_mag_greater(v[q], v[p]) or
+                                                      (q < p and not _mag_greater(v[p], v[q]))))
+        if ahead < 2:
+            kept.append(p)
+    return tuple(kept)
+
+
+PRUNE_ALPHABET = {
+    F16: [0x0000, 0x8000, 0x3C00, 0xBC00, 0x4000, 0xC000, 0x7C00, 0xFC00, 0x7E00, 0x0001],
+    BF16: [0x0000, 0x8000, 0x3F80, 0xBF80, 0x4000, 0xC000, 0x7F80, 0xFF80, 0x7FC0, 0x0001],
+    E4M3: [0x00, 0x80, 0x38, 0xB8, 0x40, 0xC0, 0x7E, 0xFE, 0x7F, 0x01],
+    E5M2: [0x00, 0x80, 0x3C, 0xBC, 0x40, 0xC0, 0x7C, 0xFC, 0x7E, 0x01],
+    I8: [0, 1, -1, 2, -2, 127, -127, -128, 64, -64],
+}
+
+
+@pytest.mark.parametrize("t", [F16, BF16, E4M3, E5M2, I8])
+def test_prune_compress_vs_rank_brute_force(t):
+    """Random groups over an alphabet with equal magnitudes, signed zeros, extremes, infinities
+    and NaN (where the format has them), ragged K."""
+    g = np.random.default_rng(31 + t)
+    alpha = np.array(PRUNE_ALPHABET[t], oracle.BITS_DTYPE[t])
+    M, K = 37, 4 * 75
+    A = alpha[g.integers(0, len(alpha), size=(M, K))]
+    Ac, idx, bad = oracle.prune_compress24(t, A)
+    v = torch_decode(A, t)
+    n_bad = 0
+    for i in range(M):
+        for gr in range(K // 4):
+            grp = v[i, 4 * gr:4 * gr + 4]
+            p0, p1 = _kept_by_rank(grp)
+            nib = (int(idx[i, gr // 8]) >> (4 * (gr % 8))) & 0xF
+            assert nib == NIBBLE[(p0, p1)], (i, gr, grp)
+            assert Ac[i, 2 * gr] == A[i, 4 * gr + p0] and Ac[i, 2 * gr + 1] == A[i, 4 * gr + p1]
+            n_bad += sum(1 for x in grp if x != 0 or np.isnan(x)) > 2
+    assert bad == n_bad
+    assert (int(idx[0, -1]) >> (4 * ((K // 4) % 8))) == 0    # bits past the last group stay clear
+
+
+def test_prune_compress_hand_worked_groups():
+    cases = [  # (type, group values, kept positions)
+        (F16, [1.0, -3.0, 2.0, 0.5], (1, 2)),
+        (F16, [1.0, 1.0, 1.0, 1.0], (0, 1)),
+        (F16, [-1.0, 1.0, 2.0, -2.0], (2, 3)),
+        (BF16, [0.25, -8.0, 0.0, 8.0], (1, 3)),
+        (E4M3, [0.0, 0.0, -0.5, 0.0], (0, 2)),
+        (E5M2, [float("nan"), 5.0, float("inf"), 1.0], (0, 2)),
+        (E5M2, [1.0, float("-inf"), 2.0, 3.0], (1, 3)),
+    ]
+    for t, vals, (p0, p1) in cases:
+        A = W.to_bits(np.array(vals), t).reshape(1, 4) if not any(np.isnan(vals)) else \
+            np.array([[0x7E, 0x45, 0x7C, 0x3C]], np.uint8)          # E5M2 NaN, 5, inf, 1
+        Ac, idx, bad = oracle.prune_compress24(t, A)
+        assert int(idx[0, 0]) == NIBBLE[(p0, p1)], (t, vals)
+        assert list(Ac[0]) == [A[0, p0], A[0, p1]]
+    # signed zeros are copied bit for bit; -128 has the largest int8 magnitude
+    A = np.array([[0x8000, 0x0000, 0x0000, 0x8000]], np.uint16)
+    Ac, idx, _ = oracle.prune_compress24(F16, A)
+    assert int(idx[0, 0]) == NIBBLE[(0, 1)] and list(Ac[0]) == [0x8000, 0x0000]
+    A = np.array([[127, -128, 0, -127]], np.int8)
+    Ac, idx, bad = oracle.prune_compress24(I8, A)
+    assert int(idx[0, 0]) == NIBBLE[(0, 1)] and list(Ac[0]) == [127, -128] and bad == 1
+
+
+@pytest.mark.parametrize("t", [F16, BF16, E4M3, E5M2, I8])
+def test_prune_compress_equals_compress_on_4_2_input(t):
+    """Where every group already has at most two non-zeros, pruning changes nothing."""
+    M, K = 11, 4 * 41
+    pats = np.random.default_rng(12).integers(0, 6, size=(M, K // 4))
+    keep = W.prune_mask(M, K, 0, patterns=pats) & (np.random.default_rng(13).random((M, K)) > 0.15)
+    if t == I8:
+        dense = np.random.default_rng(14).integers(-128, 128, size=(M, K)).astype(np.int8)
+        A = np.where(keep, dense, np.int8(0))
+    else:
+        A = np.where(keep, W.to_bits(np.random.default_rng(14).standard_normal((M, K)), t), W.zero_bits(t))
+    got, want = oracle.prune_compress24(t, A), oracle.compress24(t, A)
+    assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1]) and got[2] == want[2] == 0
+
+
 # ------------------------------------------------------------ sparse GEMM --
 
 @pytest.mark.parametrize("ta,tb", [(F16, F16), (BF16, BF16), (E4M3, E5M2), (E5M2, E5M2)])
