@@ -350,6 +350,8 @@ def suite():
         idxs = [torch.empty((M, K // 32), dtype=torch.int32, device=dev) for _ in range(rot)]
         cms = median_ms([lambda i=i: mm.sparse24_compress(As[i], Acs[i], idxs[i], a_type=ta, stream=stream)
                          for i in range(rot)], 40)
+        pms = median_ms([lambda i=i: mm.sparse24_prune_compress(As[i], Acs[i], idxs[i], a_type=ta, stream=stream)
+                         for i in range(rot)], 40)
         es = 2 if ta in (W.BF16, W.F16) else 1
         cbytes = M * K * es + M * (K // 2) * es + M * (K // 32) * 4
         B = to_dev(w["B"], tb)
@@ -357,6 +359,7 @@ def suite():
         gms = median_ms([lambda: mm.gemm_sparse24(Acs[0], idxs[0], B, D, K=K, a_type=ta, b_type=tb, stream=stream)], 20)
         f = gemm_flops(M, N, K)
         out[key] = {"compress_us": round(cms * 1e3, 1), "compress_GB/s": round(cbytes / cms / 1e6, 1),
+                    "prune_compress_us": round(pms * 1e3, 1), "prune_compress_GB/s": round(cbytes / pms / 1e6, 1),
                     "gemm_us": round(gms * 1e3, 1), "TFLOP/s_dense_equivalent": round(f / gms / 1e9, 1),
                     "TFLOP/s_effective": round(f / 2 / gms / 1e9, 1), "shape": [M, N, K]}
         del As, Acs, idxs, B, D

@@ -123,6 +123,28 @@ mmac_status_t mmac_sparse24_compress(mmac_dtype_t a_type, int64_t M, int64_t K,
                                      uint32_t *bad_groups, void *stream);
 
 /*
+ * Magnitude pruning to the 4:2 pattern fused with the compression above, in
+ * one pass over A.  The pages give the pattern and the compressed form
+ * ("CDNA3 sparse MFMA builtins", "Structured sparsity (4:2 pattern)") but not
+ * how a dense A is brought to it; this keeps, in every group of four along K,
+ * the two elements of largest magnitude:
+ *   - |a| of the decoded value; int8 -128 has magnitude 128;
+ *   - a NaN is larger than every number (infinities included), all NaNs tie;
+ *   - ties go to the lower position.
+ * The kept pair is stored as the compressor stores it (ascending positions,
+ * bits copied, same index layout).  Arguments, alignment, error behaviour and
+ * bad_groups (groups that held more than two non-zeros, i.e. the groups that
+ * pruning changed) are those of mmac_sparse24_compress.  Output is bit-exact
+ * and deterministic; on an A that already has the 4:2 pattern it equals the
+ * plain compressor's.
+ */
+mmac_status_t mmac_sparse24_prune_compress(mmac_dtype_t a_type, int64_t M, int64_t K,
+                                           const void *A, int64_t lda,
+                                           void *Ac, int64_t ldac,
+                                           uint32_t *idx, int64_t ldidx,
+                                           uint32_t *bad_groups, void *stream);
+
+/*
  * Sparse GEMM with a compressed 4:2 A: D = alpha * A*B + beta * C, where A is
  * the dense M x K matrix described by (Ac, idx) and B, C, D are as in
  * mmac_gemm_dense.  K is the dense K and must be a multiple of 4.  Supported

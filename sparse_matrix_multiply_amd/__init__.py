@@ -1,6 +1,6 @@
 """Python binding of libmmac: tiled dense and 4:2-sparse GEMM for MI355X (gfx950).
 
-Thin ctypes layer over the C ABI in include/mmac.h, with the same three entry
+Thin ctypes layer over the C ABI in include/mmac.h, with the same entry
 points.  It only marshals arguments: torch tensors provide device memory and
 the current HIP stream; every step of the computation runs in the library's
 HIP kernels.  If libmmac.so is missing, importing the binding succeeds but the
@@ -48,6 +48,8 @@ def lib():
         L.mmac_gemm_dense.argtypes = [i32, i32, i64, i64, i64, dbl, vp, i64, vp, i64, dbl, vp, i64, vp, i64, vp]
         L.mmac_sparse24_compress.restype = i32
         L.mmac_sparse24_compress.argtypes = [i32, i64, i64, vp, i64, vp, i64, vp, i64, vp, vp]
+        L.mmac_sparse24_prune_compress.restype = i32
+        L.mmac_sparse24_prune_compress.argtypes = [i32, i64, i64, vp, i64, vp, i64, vp, i64, vp, vp]
         L.mmac_gemm_sparse24.restype = i32
         L.mmac_gemm_sparse24.argtypes = [i32, i32, i64, i64, i64, dbl, vp, i64, vp, i64, vp, i64, dbl, vp, i64,
                                          vp, i64, vp]
@@ -105,6 +107,17 @@ def sparse24_compress(A, Ac, idx, bad_groups=None, a_type=None, stream=None):
     st = lib().mmac_sparse24_compress(ta, M, K, _ptr(A), _ld(A), _ptr(Ac), _ld(Ac), _ptr(idx), _ld(idx),
                                       _ptr(bad_groups), _stream(stream))
     _check(st, "mmac_sparse24_compress")
+    return Ac, idx
+
+
+def sparse24_prune_compress(A, Ac, idx, bad_groups=None, a_type=None, stream=None):
+    """Prune a dense A (M x K) to 4:2 by magnitude (two largest |a| per group of four) and
+    compress it into Ac (M x K/2) and idx (M x ceil(K/32) words), in one pass."""
+    M, K = A.shape
+    ta = _dtype(A, a_type)
+    st = lib().mmac_sparse24_prune_compress(ta, M, K, _ptr(A), _ld(A), _ptr(Ac), _ld(Ac), _ptr(idx), _ld(idx),
+                                            _ptr(bad_groups), _stream(stream))
+    _check(st, "mmac_sparse24_prune_compress")
     return Ac, idx
 
 

@@ -111,6 +111,32 @@ GemmParams make_params(int a, int64_t M, int64_t N, int64_t K, double alpha, con
 
 mmac_status_t launched(hipError_t e) { return e == hipSuccess ? MMAC_OK : MMAC_ERR_HIP; }
 
+// Shared by the plain and the pruning compressor.
+mmac_status_t compress_call(mmac_dtype_t a_type, int64_t M, int64_t K, const void *A, int64_t lda, void *Ac,
+                            int64_t ldac, uint32_t *idx, int64_t ldidx, uint32_t *bad_groups, bool prune,
+                            void *stream) {
+    if (!valid_type(a_type)) return MMAC_ERR_UNSUPPORTED;
+    if (M < 0 || K < 0 || M > kMaxDim || K > kMaxDim || (K % 4) != 0) return MMAC_ERR_INVALID_ARG;
+    if (!A || !Ac || !idx) return MMAC_ERR_INVALID_ARG;
+    const int64_t words = (K + 31) / 32;
+    if (lda < K || ldac < K / 2 || ldidx < words || lda < 1 || ldac < 1 || ldidx < 1) return MMAC_ERR_INVALID_ARG;
+    const int es = elem_size(a_type);
+    if (!aligned16(A) || !aligned16(Ac) || (lda * es) % 16 || (ldac * es) % 16) return MMAC_ERR_MISALIGNED;
+    if (!aligned4(idx) || (bad_groups && !aligned4(bad_groups))) return MMAC_ERR_MISALIGNED;
+    if (M == 0 || K == 0) return MMAC_OK;
+    CompressParams p{};
+    p.A = static_cast<const uint8_t *>(A);
+    p.a_pitch = lda * es;
+    p.Ac = static_cast<uint8_t *>(Ac);
+    p.ac_pitch = ldac * es;
+    p.idx = idx;
+    p.idx_pitch = ldidx;
+    p.bad = bad_groups;
+    p.M = (int)M;
+    p.K = (int)K;
+    return launched(launch_compress(a_type, p, prune, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -131,26 +157,13 @@ mmac_status_t mmac_gemm_dense(mmac_dtype_t a_type, mmac_dtype_t b_type, int64_t 
 mmac_status_t mmac_sparse24_compress(mmac_dtype_t a_type, int64_t M, int64_t K, const void *A, int64_t lda,
                                      void *Ac, int64_t ldac, uint32_t *idx, int64_t ldidx, uint32_t *bad_groups,
                                      void *stream) {
-    if (!valid_type(a_type)) return MMAC_ERR_UNSUPPORTED;
-    if (M < 0 || K < 0 || M > kMaxDim || K > kMaxDim || (K % 4) != 0) return MMAC_ERR_INVALID_ARG;
-    if (!A || !Ac || !idx) return MMAC_ERR_INVALID_ARG;
-    const int64_t words = (K + 31) / 32;
-    if (lda < K || ldac < K / 2 || ldidx < words || lda < 1 || ldac < 1 || ldidx < 1) return MMAC_ERR_INVALID_ARG;
-    const int es = elem_size(a_type);
-    if (!aligned16(A) || !aligned16(Ac) || (lda * es) % 16 || (ldac * es) % 16) return MMAC_ERR_MISALIGNED;
-    if (!aligned4(idx) || (bad_groups && !aligned4(bad_groups))) return MMAC_ERR_MISALIGNED;
-    if (M == 0 || K == 0) return MMAC_OK;
-    CompressParams p{};
-    p.A = static_cast<const uint8_t *>(A);
-    p.a_pitch = lda * es;
-    p.Ac = static_cast<uint8_t *>(Ac);
-    p.ac_pitch = ldac * es;
-    p.idx = idx;
-    p.idx_pitch = ldidx;
-    p.bad = bad_groups;
-    p.M = (int)M;
-    p.K = (int)K;
-    return launched(launch_compress(a_type, p, static_cast<hipStream_t>(stream)));
+    return compress_call(a_type, M, K, A, lda, Ac, ldac, idx, ldidx, bad_groups, false, stream);
+}
+
+mmac_status_t mmac_sparse24_prune_compress(mmac_dtype_t a_type, int64_t M, int64_t K, const void *A, int64_t lda,
+                                           void *Ac, int64_t ldac, uint32_t *idx, int64_t ldidx,
+                                           uint32_t *bad_groups, void *stream) {
+    return compress_call(a_type, M, K, A, lda, Ac, ldac, idx, ldidx, bad_groups, true, stream);
 }
 
 mmac_status_t mmac_gemm_sparse24(mmac_dtype_t a_type, mmac_dtype_t b_type, int64_t M, int64_t N, int64_t K,

@@ -1,4 +1,5 @@
-// 4:2 compressor: dense A (M x K) -> compressed A (M x K/2) + index words.
+// 4:2 compressor: dense A (M x K) -> compressed A (M x K/2) + index words,
+// optionally after magnitude pruning to the 4:2 pattern.
 //
 // "CDNA3 sparse MFMA builtins", section "Structured sparsity (4:2 pattern)":
 // walk each row along K in groups of four, find the two non-zero positions and
@@ -17,6 +18,10 @@
 // contiguous.  The index bits of the 4 (two-byte types) or 2 (one-byte types)
 // chunks that share a 32-bit word are gathered with lane shuffles and written
 // by the first of those lanes.
+//
+// With pruning, the kept pair of a group is the two largest magnitudes
+// (ties to the lower position) instead of the non-zeros; everything else is
+// the same pass, so a dense A goes to the compressed form in one read.
 #include <algorithm>
 
 #include "device.h"
@@ -58,7 +63,50 @@ __device__ __forceinline__ uint32_t group_mask16(uint32_t w0, uint32_t w1) {
     return ((n0 >> 15) & 1u) | ((n0 >> 30) & 2u) | ((n1 >> 13) & 4u) | ((n1 >> 28) & 8u);
 }
 
+// Magnitude pruning: sort key of element p of a group (raw bits e).  The
+// magnitude bits of these sign-magnitude formats order like the magnitudes;
+// every NaN maps to one value just above infinity (so all NaNs tie and beat
+// every number), int8 takes |v| (-128 -> 128).  The low two bits make the keys
+// distinct, the lower position winning a tie.
 template <int DT>
+__device__ __forceinline__ uint32_t mag_key(uint32_t e, int p) {
+    uint32_t m;
+    if constexpr (DT == DT_F16) m = min(e & 0x7fffu, 0x7c01u);
+    else if constexpr (DT == DT_BF16) m = min(e & 0x7fffu, 0x7f81u);
+    else if constexpr (DT == DT_E5M2) m = min(e & 0x7fu, 0x7du);
+    else if constexpr (DT == DT_E4M3) m = e & 0x7fu;      // its only NaN is already the largest code
+    else {
+        const int v = (int)(int8_t)(e & 0xffu);
+        m = (uint32_t)(v < 0 ? -v : v);
+    }
+    return (m << 2) | (uint32_t)(3 - p);
+}
+
+// Mask of the two largest of four distinct keys: element p is kept when fewer
+// than two keys exceed its own.
+__device__ __forceinline__ uint32_t top2_mask(uint32_t k0, uint32_t k1, uint32_t k2, uint32_t k3) {
+    const uint32_t a = k1 > k0, b = k2 > k0, c = k3 > k0, d = k2 > k1, e = k3 > k1, f = k3 > k2;
+    const uint32_t r0 = a + b + c, r1 = 1 - a + d + e, r2 = 2 - b - d + f, r3 = 3 - c - e - f;
+    return (uint32_t)(r0 < 2) | ((uint32_t)(r1 < 2) << 1) | ((uint32_t)(r2 < 2) << 2) | ((uint32_t)(r3 < 2) << 3);
+}
+
+// Kept-position mask of group q of the chunk w: the non-zeros (plain
+// compression) or the two largest magnitudes (PRUNE).
+template <int DT, bool PRUNE>
+__device__ __forceinline__ uint32_t keep_mask(const uint32_t (&w)[4], int q, uint32_t nonzero) {
+    if constexpr (!PRUNE) {
+        return nonzero;
+    } else if constexpr (DT == DT_F16 || DT == DT_BF16) {
+        const uint32_t lo = w[2 * q], hi = w[2 * q + 1];
+        return top2_mask(mag_key<DT>(lo & 0xffffu, 0), mag_key<DT>(lo >> 16, 1), mag_key<DT>(hi & 0xffffu, 2),
+                         mag_key<DT>(hi >> 16, 3));
+    } else {
+        const uint32_t x = w[q];
+        return top2_mask(mag_key<DT>(x, 0), mag_key<DT>(x >> 8, 1), mag_key<DT>(x >> 16, 2), mag_key<DT>(x >> 24, 3));
+    }
+}
+
+template <int DT, bool PRUNE>
 __global__ __launch_bounds__(256) void compress_kernel(CompressParams p, int cpr) {
     constexpr int ES = (DT == DT_F16 || DT == DT_BF16) ? 2 : 1;
     constexpr int PER = 16 / ES;         // elements per chunk
@@ -86,7 +134,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressParams p, int cpr
 #pragma unroll
             for (int q = 0; q < GROUPS; ++q) {
                 const uint32_t m = (ES == 2) ? group_mask16(w[2 * q], w[2 * q + 1]) : group_mask8<DT>(w[q]);
-                nib[q] = (uint32_t)(kPairTable >> (4 * m)) & 0xfu;
+                nib[q] = (uint32_t)(kPairTable >> (4 * keep_mask<DT, PRUNE>(w, q, m))) & 0xfu;
                 if (q < ngroups) {
                     bad += (kViolations >> m) & 1u;
                     bits |= nib[q] << (4 * q);
@@ -130,19 +178,24 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressParams p, int cpr
     }
 }
 
-hipError_t launch_compress(int dt, CompressParams p, hipStream_t s) {
+template <bool PRUNE>
+static hipError_t launch_mode(int dt, const CompressParams &p, hipStream_t s) {
     const int es = (dt == DT_F16 || dt == DT_BF16) ? 2 : 1;
     const int cpr = (int)(((int64_t)p.K * es + 15) / 16);      // 16-byte chunks per row
     const dim3 grid((unsigned)((cpr + 255) / 256), (unsigned)std::min(p.M, 65535)), block(256);
     switch (dt) {
-    case DT_F16: hipLaunchKernelGGL(compress_kernel<DT_F16>, grid, block, 0, s, p, cpr); break;
-    case DT_BF16: hipLaunchKernelGGL(compress_kernel<DT_BF16>, grid, block, 0, s, p, cpr); break;
-    case DT_I8: hipLaunchKernelGGL(compress_kernel<DT_I8>, grid, block, 0, s, p, cpr); break;
-    case DT_E4M3: hipLaunchKernelGGL(compress_kernel<DT_E4M3>, grid, block, 0, s, p, cpr); break;
-    case DT_E5M2: hipLaunchKernelGGL(compress_kernel<DT_E5M2>, grid, block, 0, s, p, cpr); break;
+    case DT_F16: hipLaunchKernelGGL((compress_kernel<DT_F16, PRUNE>), grid, block, 0, s, p, cpr); break;
+    case DT_BF16: hipLaunchKernelGGL((compress_kernel<DT_BF16, PRUNE>), grid, block, 0, s, p, cpr); break;
+    case DT_I8: hipLaunchKernelGGL((compress_kernel<DT_I8, PRUNE>), grid, block, 0, s, p, cpr); break;
+    case DT_E4M3: hipLaunchKernelGGL((compress_kernel<DT_E4M3, PRUNE>), grid, block, 0, s, p, cpr); break;
+    case DT_E5M2: hipLaunchKernelGGL((compress_kernel<DT_E5M2, PRUNE>), grid, block, 0, s, p, cpr); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_compress(int dt, CompressParams p, bool prune, hipStream_t s) {
+    return prune ? launch_mode<true>(dt, p, s) : launch_mode<false>(dt, p, s);
 }
 
 }  // namespace mmac

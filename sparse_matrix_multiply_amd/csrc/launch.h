@@ -51,7 +51,7 @@ enum TileShape : int { TILE_256 = 0, TILE_128 = 1, TILE_64 = 2, TILE_SKINNY = 3 
 hipError_t launch_gemm_dense(int dt_a, int dt_b, TileShape shape, GemmParams p, hipStream_t s);
 hipError_t launch_gemm_sparse(int dt_a, int dt_b, TileShape shape, GemmParams p, hipStream_t s);
 hipError_t launch_gemm_skinny(int dt_a, int dt_b, GemmParams p, hipStream_t s);
-hipError_t launch_compress(int dt, CompressParams p, hipStream_t s);
+hipError_t launch_compress(int dt, CompressParams p, bool prune, hipStream_t s);
 
 // Geometry of a tile shape.
 inline int tile_rows(TileShape t) { return t == TILE_256 ? 256 : t == TILE_128 ? 128 : t == TILE_64 ? 64 : 32; }

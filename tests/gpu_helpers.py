@@ -108,13 +108,14 @@ def run_dense(ta, tb, A, B, alpha, beta, C, ldd=None, C_dev=None):
     return D.cpu().numpy()
 
 
-def compress_dev(t, Ad, M, K):
-    """Run mmac_sparse24_compress on a device A; returns (Ac, idx, bad) device tensors."""
+def compress_dev(t, Ad, M, K, prune=False):
+    """Run mmac_sparse24_compress (or, with prune, mmac_sparse24_prune_compress) on a device A;
+    returns (Ac, idx, bad) device tensors."""
     Ac = to_dev_bits(np.zeros((M, K // 2), oracle.BITS_DTYPE[t]), t)
     W = (K + 31) // 32
     idx = torch.full((M, W), -1, dtype=torch.int32, device=dev())
     bad = torch.zeros(1, dtype=torch.int32, device=dev())
-    mm.sparse24_compress(Ad, Ac, idx, bad, a_type=t)
+    (mm.sparse24_prune_compress if prune else mm.sparse24_compress)(Ad, Ac, idx, bad, a_type=t)
     return Ac, idx, bad
 
 

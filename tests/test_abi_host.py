@@ -33,7 +33,7 @@ def L():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["mmac_gemm_dense", "mmac_gemm_sparse24", "mmac_sparse24_compress",
-                                    "mmac_status_string"]
+                                    "mmac_sparse24_prune_compress", "mmac_status_string"]
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -68,11 +68,11 @@ def sparse(L, **kw):
                                 a["ldd"], a["stream"])
 
 
-def compress(L, **kw):
+def compress(L, entry="mmac_sparse24_compress", **kw):
     a = dict(a=mm.F16, M=64, K=64, A=P, lda=64, Ac=P, ldac=32, idx=P, ldidx=2, bad=None, stream=None)
     a.update(kw)
-    return L.mmac_sparse24_compress(a["a"], a["M"], a["K"], a["A"], a["lda"], a["Ac"], a["ldac"], a["idx"],
-                                    a["ldidx"], a["bad"], a["stream"])
+    return getattr(L, entry)(a["a"], a["M"], a["K"], a["A"], a["lda"], a["Ac"], a["ldac"], a["idx"],
+                             a["ldidx"], a["bad"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -138,10 +138,12 @@ def test_sparse_empty_is_a_no_op(L):
     (dict(ldac=36), mm.ERR_MISALIGNED),
     (dict(bad=P + 1), mm.ERR_MISALIGNED),
 ])
-def test_compress_argument_errors(L, kw, code):
-    assert compress(L, **kw) == code
+@pytest.mark.parametrize("entry", ["mmac_sparse24_compress", "mmac_sparse24_prune_compress"])
+def test_compress_argument_errors(L, kw, code, entry):
+    assert compress(L, entry, **kw) == code
 
 
-def test_compress_empty_is_a_no_op(L):
-    assert compress(L, M=0) == mm.OK
-    assert compress(L, K=0, ldidx=1, lda=8, ldac=8) == mm.OK
+@pytest.mark.parametrize("entry", ["mmac_sparse24_compress", "mmac_sparse24_prune_compress"])
+def test_compress_empty_is_a_no_op(L, entry):
+    assert compress(L, entry, M=0) == mm.OK
+    assert compress(L, entry, K=0, ldidx=1, lda=8, ldac=8) == mm.OK

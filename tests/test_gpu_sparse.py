@@ -142,3 +142,83 @@ def test_gpu_compress_feeds_gpu_sparse_gemm(ta, tb):
     torch.cuda.synchronize()
     Ddense, S = oracle.gemm_dense(ta, tb, A, B, alpha, beta, C)
     assert_close(D.cpu().numpy(), Ddense, S, ta, K, alpha, beta, C)
+
+
+# ---------------------------------------------------- magnitude prune + compress --
+
+PRUNE_ALPHABET = {
+    F16: [0x0000, 0x8000, 0x3C00, 0xBC00, 0x4000, 0xC000, 0x7C00, 0xFC00, 0x7E00, 0x7C01, 0x0001],
+    BF16: [0x0000, 0x8000, 0x3F80, 0xBF80, 0x4000, 0xC000, 0x7F80, 0xFF80, 0x7FC0, 0xFF81, 0x0001],
+    E4M3: [0x00, 0x80, 0x38, 0xB8, 0x40, 0xC0, 0x7E, 0xFE, 0x7F, 0xFF, 0x01],
+    E5M2: [0x00, 0x80, 0x3C, 0xBC, 0x40, 0xC0, 0x7C, 0xFC, 0x7E, 0x7D, 0x01],
+    I8: [0, 1, -1, 2, -2, 127, -127, -128, 64, -64, 3],
+}
+
+
+def dense_a(t, M, K, seed):
+    """Dense A (no pattern): normal values with some exact zeros and repeated magnitudes."""
+    g = np.random.default_rng(seed)
+    if t == I8:
+        A = g.integers(-128, 128, size=(M, K)).astype(np.int8)
+    else:
+        A = W.to_bits(np.round(g.standard_normal((M, K)) * 8) / 8, t)   # many equal magnitudes
+    zero = np.int8(0) if t == I8 else W.zero_bits(t)
+    return np.ascontiguousarray(np.where(g.random((M, K)) < 0.1, zero, A))
+
+
+@pytest.mark.parametrize("t", TYPES)
+@pytest.mark.parametrize("M,K", [(1, 4), (3, 12), (64, 64), (77, 200), (130, 1028), (9, 4100)])
+def test_prune_compress_bit_exact(t, M, K):
+    A = dense_a(t, M, K, 3 * M + K + t)
+    Ac_ref, idx_ref, bad_ref = oracle.prune_compress24(t, A)
+    Ac, idx, bad = compress_dev(t, to_dev_bits(A, t), M, K, prune=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(dev_bits_to_host(Ac, t), Ac_ref)
+    assert np.array_equal(idx.cpu().numpy().view(np.uint32), idx_ref)
+    assert int(bad.item()) == bad_ref
+
+
+@pytest.mark.parametrize("t", TYPES)
+def test_prune_compress_special_values(t):
+    """Ties, signed zeros, infinities, every NaN payload, int8 -128."""
+    M, K = 16, 4 * 96
+    alpha = np.array(PRUNE_ALPHABET[t], oracle.BITS_DTYPE[t])
+    A = alpha[np.random.default_rng(t).integers(0, len(alpha), size=(M, K))]
+    Ac_ref, idx_ref, bad_ref = oracle.prune_compress24(t, A)
+    Ac, idx, bad = compress_dev(t, to_dev_bits(A, t), M, K, prune=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(dev_bits_to_host(Ac, t), Ac_ref)
+    assert np.array_equal(idx.cpu().numpy().view(np.uint32), idx_ref)
+    assert int(bad.item()) == bad_ref
+
+
+@pytest.mark.parametrize("t", [F16, E4M3])
+def test_prune_compress_equals_compress_on_4_2_input(t):
+    M, K = 100, 520
+    A = sparse_a(t, M, K, 21, zero_kept=0.1)
+    got = compress_dev(t, to_dev_bits(A, t), M, K, prune=True)
+    want = compress_dev(t, to_dev_bits(A, t), M, K, prune=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(dev_bits_to_host(got[0], t), dev_bits_to_host(want[0], t))
+    assert torch.equal(got[1].cpu(), want[1].cpu()) and int(got[2].item()) == int(want[2].item()) == 0
+
+
+@pytest.mark.parametrize("ta,tb", [(F16, F16), (BF16, BF16), (E4M3, E5M2), (I8, I8)])
+def test_gpu_prune_compress_feeds_gpu_sparse_gemm(ta, tb):
+    """Dense A -> GPU prune+compress -> GPU sparse GEMM, against the oracle's dense GEMM of the
+    pruned matrix (the oracle's pruning, decompressed)."""
+    M, N, K = 200, 136, 640
+    A = dense_a(ta, M, K, 5)
+    B, C, alpha, beta = b_and_c(tb, N, M, K, 6)
+    Acd, idxd, _ = compress_dev(ta, to_dev_bits(A, ta), M, K, prune=True)
+    D = out_tensor(M, N, ta == I8)
+    Cd = torch.from_numpy(C).to(dev())
+    mm.gemm_sparse24(Acd, idxd, to_dev_bits(B, tb), D, K=K, alpha=alpha, beta=beta, C=Cd, a_type=ta, b_type=tb)
+    torch.cuda.synchronize()
+    Ac_ref, idx_ref, _ = oracle.prune_compress24(ta, A)
+    Apruned = oracle.decompress24(ta, Ac_ref, idx_ref, K)
+    Dref, aux = oracle.gemm_dense(ta, tb, Apruned, B, alpha, beta, C)
+    if ta == I8:
+        assert np.array_equal(D.cpu().numpy(), Dref)
+    else:
+        assert_close(D.cpu().numpy(), Dref, aux, ta, K, alpha, beta, C, f"pruned {ta},{tb}")
