@@ -57,8 +57,9 @@
  *   - Thread safety: calls are re-entrant; the library keeps no state between
  *     calls.
  *   - Tuning: two environment variables, read on every call, override the
- *     tile choice: MMAC_TILE (256, 128 or 64 forces that output tile; 16
- *     forces the one-wave-column path for M <= 32) and MMAC_GROUP_M (tile rows
+ *     tile choice: MMAC_TILE (256, 128 or 64 forces that square output tile,
+ *     2561 forces 256 x 128 and 1282 forces 128 x 256; 16 forces the
+ *     one-wave-column path for M <= 32) and MMAC_GROUP_M (tile rows
  *     visited together by the scheduler, default 8).  Results do not depend
  *     on them beyond floating-point rounding.
  */

@@ -30,7 +30,8 @@ bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 
 bool integral_i32(double v) { return std::isfinite(v) && v == std::floor(v) && v >= -2147483648.0 && v <= 2147483647.0; }
 
-// Optional overrides for tuning: MMAC_TILE=256|128|64|16 (16 = skinny, M <= 32), MMAC_GROUP_M=<n>.
+// Optional overrides for tuning: MMAC_TILE=256|2561|1282|128|64|16 (2561 = 256 x 128, 1282 = 128 x 256,
+// 16 = skinny, M <= 32), MMAC_GROUP_M=<n>.
 int env_int(const char *name, int dflt) {
     const char *s = std::getenv(name);
     if (!s || !*s) return dflt;
@@ -40,15 +41,23 @@ int env_int(const char *name, int dflt) {
 TileShape pick_shape(int64_t M, int64_t N, bool sparse = false) {
     const int forced = env_int("MMAC_TILE", 0);
     if (forced == 256) return TILE_256;
+    if (forced == 2561) return TILE_256x128;
+    if (forced == 1282) return TILE_128x256;
     if (forced == 128) return TILE_128;
     if (forced == 64) return TILE_64;
     if (forced == 16 && !sparse && M <= 32) return TILE_SKINNY;
     // At most 32 rows: stream B once with the skinny kernel (dense A only).
     if (!sparse && M <= 32) return TILE_SKINNY;
     // Largest tile that still gives about one tile per compute unit (256 CUs).
-    auto tiles = [&](int t) { return ((M + t - 1) / t) * ((N + t - 1) / t); };
-    if (tiles(256) >= 192) return TILE_256;
-    if (tiles(128) >= 192) return TILE_128;
+    // Between 256 x 256 and 128 x 128 come the two 128 x 256 halves: 128 x 256
+    // measured at least as fast on both 8192 x 1024 and 1024 x 8192 (K 8192),
+    // so it wins unless 256 x 128 pads less (N below 256, say).
+    auto tiles = [&](int tm, int tn) { return ((M + tm - 1) / tm) * ((N + tn - 1) / tn); };
+    if (tiles(256, 256) >= 192) return TILE_256;
+    const bool wide = tiles(128, 256) >= 192, tall = tiles(256, 128) >= 192;
+    if (wide && (!tall || tiles(128, 256) <= tiles(256, 128))) return TILE_128x256;
+    if (tall) return TILE_256x128;
+    if (tiles(128, 128) >= 192) return TILE_128;
     return TILE_64;
 }
 
@@ -102,9 +111,9 @@ GemmParams make_params(int a, int64_t M, int64_t N, int64_t K, double alpha, con
             p.c_scale = alpha == beta ? 1.0f : (float)(beta / alpha);
         }
     }
-    const int t = tile_rows(shape);
-    p.tiles_m = (int)((M + t - 1) / t);
-    p.tiles_n = (int)((N + t - 1) / t);
+    const int tm = tile_rows(shape), tn = tile_cols(shape);
+    p.tiles_m = (int)((M + tm - 1) / tm);
+    p.tiles_n = (int)((N + tn - 1) / tn);
     p.group_m = std::max(1, env_int("MMAC_GROUP_M", 8));
     return p;
 }

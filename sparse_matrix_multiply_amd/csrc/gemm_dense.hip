@@ -8,6 +8,8 @@ static hipError_t launch_shape(TileShape shape, const GemmParams &p, hipStream_t
     const dim3 grid(p.tiles_m * p.tiles_n), block(256);
     switch (shape) {
     case TILE_256: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 256, 256, 2, 4, 4>), grid, dim3(512), 0, s, p); break;
+    case TILE_256x128: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 256, 128, 2, 2, 4>), grid, block, 0, s, p); break;
+    case TILE_128x256: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 128, 256, 2, 2, 4>), grid, block, 0, s, p); break;
     case TILE_128: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 128, 128, 2, 2, 4>), grid, block, 0, s, p); break;
     case TILE_64: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 64, 64, 2, 2, 4>), grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;

@@ -43,8 +43,10 @@ struct CompressParams {
 };
 
 // Tile shapes the host can pick from.
-// 256 x 256 tiles run 8 waves (2 per SIMD, 128 x 64 each); 128 and 64 run 4 waves.
-enum TileShape : int { TILE_256 = 0, TILE_128 = 1, TILE_64 = 2, TILE_SKINNY = 3 };
+// 256 x 256 tiles run 8 waves (2 per SIMD, 128 x 64 each); 256 x 128 and
+// 128 x 256 tiles run 4 waves of 128 x 64 or 64 x 128 (one per SIMD); 128 and
+// 64 run 4 waves.
+enum TileShape : int { TILE_256 = 0, TILE_128 = 1, TILE_64 = 2, TILE_SKINNY = 3, TILE_256x128 = 4, TILE_128x256 = 5 };
 
 // Launchers (defined in the kernel files).  `dt_a`/`dt_b` use the public
 // mmac_dtype_t codes.  They return hipSuccess or the launch error.
@@ -54,6 +56,11 @@ hipError_t launch_gemm_skinny(int dt_a, int dt_b, GemmParams p, hipStream_t s);
 hipError_t launch_compress(int dt, CompressParams p, bool prune, hipStream_t s);
 
 // Geometry of a tile shape.
-inline int tile_rows(TileShape t) { return t == TILE_256 ? 256 : t == TILE_128 ? 128 : t == TILE_64 ? 64 : 32; }
+inline int tile_rows(TileShape t) {
+    return t == TILE_256 || t == TILE_256x128 ? 256 : t == TILE_128 || t == TILE_128x256 ? 128 : t == TILE_64 ? 64 : 32;
+}
+inline int tile_cols(TileShape t) {
+    return t == TILE_256x128 ? 128 : t == TILE_128x256 ? 256 : tile_rows(t);
+}
 
 }  // namespace mmac

@@ -35,7 +35,7 @@ def inputs(ta, tb, M, N, K, seed):
     return A, B, C, 1.5, -0.75
 
 
-@pytest.mark.parametrize("tile", [256, 128, 64])
+@pytest.mark.parametrize("tile", [256, 2561, 1282, 128, 64])
 @pytest.mark.parametrize("ta,tb", PAIRS)
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_dense_matches_oracle(ta, tb, M, N, K, tile):

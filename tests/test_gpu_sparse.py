@@ -92,7 +92,7 @@ def b_and_c(tb, N, M, K, seed):
     return W.to_bits(g.standard_normal((N, K)), tb), g.standard_normal((M, N)).astype(np.float32), 1.25, 0.5
 
 
-@pytest.mark.parametrize("tile", [256, 128, 64])
+@pytest.mark.parametrize("tile", [256, 2561, 1282, 128, 64])
 @pytest.mark.parametrize("ta,tb", PAIRS)
 @pytest.mark.parametrize("M,N,K", [(64, 64, 64), (100, 77, 200), (257, 130, 332), (40, 300, 1028)])
 def test_sparse_matches_oracle(ta, tb, M, N, K, tile):
