@@ -148,14 +148,17 @@ template <int DT> struct MmaSparse16 {
     typedef float out_t;
     __device__ __forceinline__ static constexpr int a_unit(int s, int g, int) { return 2 * s + g; }
     __device__ __forceinline__ static constexpr int b_unit(int s, int g, int h) { return 4 * s + g + 2 * h; }
-    // Index words in LDS: slot q of a row holds word q; each lane reads its
-    // row's two words (one per step) with one 8-byte read, both lane halves
-    // the same address, so the 32 rows of a read fill the 64 banks once.
-    __device__ __forceinline__ static constexpr uint32_t idx_src_word(uint32_t q, uint32_t) { return q; }
-    __device__ __forceinline__ static constexpr uint32_t idx_pair_offset(uint32_t, int) { return 0; }
-    // index bits of lane half g for step s, from the lane's pair of words
-    __device__ __forceinline__ static uint32_t lane_idx(i32x2 pair, int s, int g) {
-        return (uint32_t)pair[s] >> (16 * g);
+    // Index words in LDS: the k-tile's two words of each row (one per step),
+    // copied 4 bytes per lane, read by each lane with one 8-byte read (both
+    // lane halves the same address, so the 32 rows of a read fill the 64 banks
+    // once); lane half g takes bits [16g, 16g + 16) of the step's word.
+    static constexpr int kIdxCopyBytes = 4;
+    typedef i32x2 idx_t;
+    __device__ __forceinline__ static idx_t load_idx(const uint8_t *row, int) {
+        return *reinterpret_cast<const i32x2 *>(row);
+    }
+    __device__ __forceinline__ static uint32_t lane_idx(const idx_t &w, int s, int g) {
+        return (uint32_t)w[s] >> (16 * g);
     }
     __device__ __forceinline__ static acc_t mma(const Frag<16> &a, const Frag<32> &b, acc_t c, uint32_t idx) {
         if constexpr (DT == DT_BF16)
@@ -181,17 +184,18 @@ template <int DT_A, int DT_B> struct MmaSparse8 {
     typedef typename std::conditional<kInt, int32_t, float>::type out_t;
     __device__ __forceinline__ static constexpr int a_unit(int s, int g, int) { return 2 * s + g; }
     __device__ __forceinline__ static constexpr int b_unit(int s, int g, int h) { return 4 * s + g + 2 * h; }
-    // Index words in LDS: lane half g needs words g (step 0) and 2 + g (step 1)
-    // of its row, kept side by side as 8-byte pair g ^ (bit 4 of the row), so
-    // the 32 rows one lane half reads with one 8-byte read fill the 64 banks
-    // once.  Slot q of a row: pair q / 2, step q % 2.
-    __device__ __forceinline__ static constexpr uint32_t idx_src_word(uint32_t q, uint32_t r) {
-        return ((q >> 1) ^ ((r >> 4) & 1u)) + 2 * (q & 1u);
+    // Index words in LDS: the k-tile's four words of each row (16 bytes, one
+    // copy lane per row), read by each lane with one 16-byte read, so 16
+    // consecutive rows fill the 64 banks once; lane half g takes word g for
+    // step 0 and word 2 + g for step 1.
+    static constexpr int kIdxCopyBytes = 16;
+    typedef i32x4 idx_t;
+    __device__ __forceinline__ static idx_t load_idx(const uint8_t *row, int) {
+        return *reinterpret_cast<const i32x4 *>(row);
     }
-    __device__ __forceinline__ static constexpr uint32_t idx_pair_offset(uint32_t r, int g) {
-        return 8 * ((uint32_t)g ^ ((r >> 4) & 1u));
+    __device__ __forceinline__ static uint32_t lane_idx(const idx_t &w, int s, int g) {
+        return (uint32_t)(g ? w[2 * s + 1] : w[2 * s]);
     }
-    __device__ __forceinline__ static uint32_t lane_idx(i32x2 pair, int s, int) { return (uint32_t)pair[s]; }
     __device__ __forceinline__ static acc_t mma(const Frag<16> &a, const Frag<32> &b, acc_t c, uint32_t idx) {
         if constexpr (kInt)
             return __builtin_amdgcn_smfmac_i32_32x32x64_i8(a.v, join(b), c, (int)idx, 0, 0);

@@ -115,6 +115,13 @@ __device__ __forceinline__ void wait_copies(int n) {
     }
 }
 
+// Bytes of index words one copy lane moves (sparse A only).
+template <class O>
+constexpr int idx_copy_bytes() {
+    if constexpr (O::kSparse) return O::kIdxCopyBytes;
+    else return 4;
+}
+
 template <class Op, int BM, int BN, int WM, int WN, int STAGES_>
 struct TiledGemm {
     typedef typename Op::acc_t acc_t;
@@ -127,10 +134,12 @@ struct TiledGemm {
     static_assert(AW == 2 || AW == 4 || AW == 8, "A LDS rows of 32, 64 or 128 bytes");
     static_assert(BW == 4 || BW == 8, "B LDS rows of 64 or 128 bytes");
     static constexpr int IW = Op::kSparse ? Op::kBK / 32 : 0;                  // index words per row
-    static_assert(!Op::kSparse || (STEPS == 2 && IW % 2 == 0), "one 8-byte index read per row and k-tile");
+    static_assert(!Op::kSparse || STEPS == 2, "index words of a k-tile read once, for two steps");
     // copy units per wave: 16-byte units of A and B, 4-byte words of the index
-    static constexpr int AUPW = BM * AW / NW, BUPW = BN * BW / NW, IUPW = BM * IW / NW;
-    static_assert(AUPW * NW == BM * AW && BUPW * NW == BN * BW && IUPW * NW == BM * IW, "uneven copy split");
+    static constexpr int IES = idx_copy_bytes<Op>();                           // index bytes per copy lane
+    static constexpr int AUPW = BM * AW / NW, BUPW = BN * BW / NW, IUPW = BM * IW * 4 / IES / NW;
+    static_assert(AUPW * NW == BM * AW && BUPW * NW == BN * BW && IUPW * NW * IES == BM * IW * 4,
+                  "uneven copy split");
     static constexpr int AP = (AUPW + 63) / 64, BP = (BUPW + 63) / 64, IP = (IUPW + 63) / 64;  // passes
     static constexpr int LPT = AP + BP + IP;        // copy instructions per wave per k-tile
     static constexpr int A_BYTES = BM * AW * 16, B_BYTES = BN * BW * 16, I_BYTES = BM * IW * 4;
@@ -174,44 +183,39 @@ struct TiledGemm {
         return (L / W) * (uint32_t)pitch + (uint32_t)(kt * W * 16) + (L % W) * 16;
     }
 
-    // Byte offset of the source of LDS index word d (= row * IW + slot) at
-    // k-tile kt; the op decides which word of the row each slot holds.
+    // Byte offset of the source of index copy lane d (LDS bytes [d*IES,
+    // (d+1)*IES) of the row-major tile of IW words per row) at k-tile kt.
     __device__ __forceinline__ uint32_t idx_off(uint32_t d, int kt) const {
-        const uint32_t r = d / IW;
-        return (r * (uint32_t)p.idx_pitch + kt * IW + Op::idx_src_word(d % IW, r)) * 4;
+        const uint32_t byte = d * IES, r = byte / (IW * 4);
+        return (r * (uint32_t)p.idx_pitch + kt * IW) * 4 + byte % (IW * 4);
     }
 
-    __device__ __forceinline__ void copy_index(uint8_t *st, int kt) const {
-        if constexpr (Op::kSparse) {
-#pragma unroll
-            for (int q = 0; q < IP; ++q) {
-                const int u = q * 64 + lane;
-                if (IUPW % 64 == 0 || u < IUPW)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        rx, (lds_void *)(st + A_BYTES + B_BYTES + (wave * IUPW + q * 64) * 4), 4,
-                        idx_off(wave * IUPW + u, kt), 0, 0, 0);
-            }
-        }
-    }
-
-    // Start the copy of k-tile kt into LDS stage `st` (every wave issues LPT
-    // instructions; each writes one contiguous run of LDS).
-    __device__ __forceinline__ void dma(uint8_t *st, int kt) const {
-#pragma unroll
-        for (int q = 0; q < AP; ++q) {
-            const int u = q * 64 + lane;
+    // Copy instruction j (0 <= j < LPT: the A passes, then B, then the index)
+    // of k-tile kt into LDS stage `st`; each writes one contiguous run of LDS.
+    __device__ __forceinline__ void dma_pass(uint8_t *st, int kt, int j) const {
+        if (j < AP) {
+            const int u = j * 64 + lane;
             if (AUPW % 64 == 0 || u < AUPW)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(st + (wave * AUPW + q * 64) * 16), 16,
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(st + (wave * AUPW + j * 64) * 16), 16,
                                                          src_off<AW>(wave * AUPW + u, p.a_pitch, kt), 0, 0, 0);
-        }
-#pragma unroll
-        for (int q = 0; q < BP; ++q) {
-            const int u = q * 64 + lane;
+        } else if (j < AP + BP) {
+            const int q = j - AP, u = q * 64 + lane;
             if (BUPW % 64 == 0 || u < BUPW)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(st + A_BYTES + (wave * BUPW + q * 64) * 16),
                                                          16, src_off<BW>(wave * BUPW + u, p.b_pitch, kt), 0, 0, 0);
+        } else if constexpr (Op::kSparse) {
+            const int q = j - AP - BP, u = q * 64 + lane;
+            if (IUPW % 64 == 0 || u < IUPW)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rx, (lds_void *)(st + A_BYTES + B_BYTES + (wave * IUPW + q * 64) * IES), IES,
+                    idx_off(wave * IUPW + u, kt), 0, 0, 0);
         }
-        copy_index(st, kt);
+    }
+
+    // Start the whole copy of k-tile kt into LDS stage `st` (LPT instructions per wave).
+    __device__ __forceinline__ void dma(uint8_t *st, int kt) const {
+#pragma unroll
+        for (int j = 0; j < LPT; ++j) dma_pass(st, kt, j);
     }
 
     // The ragged last k-tile: A and B through registers with elements past K set
@@ -238,15 +242,19 @@ struct TiledGemm {
                     masked_unit<Op::kEsize>(rb, src_off<BW>(P, p.b_pitch, kt), e0, p.K);
             }
         }
-        copy_index(st, kt);
+#pragma unroll
+        for (int j = AP + BP; j < LPT; ++j) dma_pass(st, kt, j);   // the index words, by copy
     }
 
     typedef Frag<Op::kAFrag> FragA;
     typedef Frag<Op::kBFrag> FragB;
+    template <class O, bool S = O::kSparse> struct IdxOf { typedef i32x2 type; };
+    template <class O> struct IdxOf<O, true> { typedef typename O::idx_t type; };
+    typedef typename IdxOf<Op>::type IdxT;      // index words a lane holds for one k-tile
 
     // Fragments of step s of the k-tile held in LDS stage `st`, and with step 0
     // the index words of every step of that k-tile (sparse A).
-    __device__ __forceinline__ void load_frags(FragA (&a)[TM], FragB (&b)[TN], i32x2 (&ix)[TM], const uint8_t *st,
+    __device__ __forceinline__ void load_frags(FragA (&a)[TM], FragB (&b)[TN], IdxT (&ix)[TM], const uint8_t *st,
                                                int s) const {
         const uint8_t *sa = st, *sb = st + A_BYTES;
         const uint32_t *sx = reinterpret_cast<const uint32_t *>(st + A_BYTES + B_BYTES);
@@ -255,11 +263,9 @@ struct TiledGemm {
             const uint32_t r = wm * WTM + i * 32 + l32;
             lds_frag<AW>(a[i], sa, r * AW + Op::a_unit(s, g, 0), r * AW + Op::a_unit(s, g, 1));
             if constexpr (Op::kSparse) {
-                if (s == 0)
-                    ix[i] = *reinterpret_cast<const i32x2 *>(reinterpret_cast<const uint8_t *>(sx + r * IW) +
-                                                             Op::idx_pair_offset(r, g));
+                if (s == 0) ix[i] = Op::load_idx(reinterpret_cast<const uint8_t *>(sx + r * IW), g);
             } else {
-                ix[i] = i32x2{0, 0};
+                ix[i] = IdxT{};
             }
         }
 #pragma unroll
@@ -274,7 +280,7 @@ struct TiledGemm {
     static constexpr int NREAD = TM * (Op::kAFrag / 16) + TN * (Op::kBFrag / 16) + (Op::kSparse ? TM : 0);
 
     // Index operand of the matrix instruction of step s.
-    __device__ __forceinline__ uint32_t step_idx(const i32x2 &x, int s) const {
+    __device__ __forceinline__ uint32_t step_idx(const IdxT &x, int s) const {
         if constexpr (Op::kSparse) return Op::lane_idx(x, s, g);
         else return 0;
     }
@@ -283,7 +289,7 @@ struct TiledGemm {
     // with the LDS reads (next step's fragments) and copy instructions issued
     // before them in the same region: one matrix instruction, then one read,
     // then one copy, so the reads and copies go out while the matrix unit works.
-    __device__ __forceinline__ void mma_step(const FragA (&a)[TM], const FragB (&b)[TN], const i32x2 (&ix)[TM], int s,
+    __device__ __forceinline__ void mma_step(const FragA (&a)[TM], const FragB (&b)[TN], const IdxT (&ix)[TM], int s,
                                              int ncopies) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -300,7 +306,7 @@ struct TiledGemm {
     // Fragment double buffer: a0/b0/x0 feed the current step, a1/b1/x1 receive the next.
     FragA a0[TM], a1[TM];
     FragB b0[TN], b1[TN];
-    i32x2 x0[TM], x1[TM];
+    IdxT x0[TM], x1[TM];
 
     // One k-tile: start the copy of k-tile kt + STAGES - 1 into the stage that
     // k-tile kt - 1 freed, then the STEPS steps of k-tile kt (in stage `cur`).
@@ -308,12 +314,21 @@ struct TiledGemm {
     // the first fragments of k-tile kt + 1 are read while that step runs; every
     // read of a stage completes before the barrier that precedes the copy into
     // it.  STEADY: every k-tile up to kt + STAGES - 1 is whole (no branches).
+    // Steady k-tiles issue their copies in two halves: P0 instructions with the
+    // first step, the rest right after the barrier, with the last step, so the
+    // texture-address queue sees a steadier stream than all waves issuing every
+    // copy at once after the barrier.  Loads complete in issue order, so the
+    // wait before the barrier may leave this k-tile's first P0 copies and the
+    // STAGES - 3 whole k-tiles before them in flight.
+    static constexpr int P0 = LPT - LPT / 2;
+
     template <bool STEADY>
     __device__ __forceinline__ void iteration(uint8_t *smem, int kt, int cur, int nk, int nkt) {
         const int pre = kt + STAGES - 1;
         uint8_t *st_pre = smem + (cur == 0 ? STAGES - 1 : cur - 1) * STAGE;
         if constexpr (STEADY) {
-            dma(st_pre, pre);
+#pragma unroll
+            for (int j = 0; j < P0; ++j) dma_pass(st_pre, pre, j);
         } else if (pre < nkt) {
             if (pre < nk) dma(st_pre, pre);
             else fill_masked(st_pre, pre);
@@ -326,15 +341,21 @@ struct TiledGemm {
                 load_frags(a1, b1, x1, sc, s + 1);
             } else {
                 if constexpr (STEADY) {
-                    wait_vm_lgkm0<(STAGES - 2) * LPT>();
+                    static_assert(STAGES >= 3, "split copies need three stages");
+                    wait_vm_lgkm0<(STAGES - 3) * LPT + P0>();
                 } else {
                     const int after = min(STAGES - 2, nkt - 2 - kt);
                     wait_copies<LPT, STAGES - 2>(after <= 0 || kt + 1 + after >= nk ? 0 : after);
                 }
                 block_barrier();
+                if constexpr (STEADY) {
+#pragma unroll
+                    for (int j = P0; j < LPT; ++j) dma_pass(st_pre, pre, j);
+                }
                 load_frags(a1, b1, x1, sn, 0);   // past the last k-tile this reads a stale stage, unused
             }
-            mma_step(a0, b0, x0, s, (STEADY && s == 0) ? LPT : 0);
+            const int ncopies = !STEADY ? 0 : (s + 1 == STEPS ? LPT - P0 : (s == 0 ? P0 : 0));
+            mma_step(a0, b0, x0, s, ncopies);
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 a0[i] = a1[i];
