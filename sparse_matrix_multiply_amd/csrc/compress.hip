@@ -63,22 +63,16 @@ __device__ __forceinline__ uint32_t group_mask16(uint32_t w0, uint32_t w1) {
     return ((n0 >> 15) & 1u) | ((n0 >> 30) & 2u) | ((n1 >> 13) & 4u) | ((n1 >> 28) & 8u);
 }
 
-// Magnitude pruning: sort key of element p of a group (raw bits e).  The
-// magnitude bits of these sign-magnitude formats order like the magnitudes;
-// every NaN maps to one value just above infinity (so all NaNs tie and beat
-// every number), int8 takes |v| (-128 -> 128).  The low two bits make the keys
-// distinct, the lower position winning a tie.
+// Magnitude pruning: sort key of element p of a group of two-byte elements
+// (raw bits e).  The magnitude bits of these sign-magnitude formats order like
+// the magnitudes; every NaN maps to one value just above infinity (so all NaNs
+// tie and beat every number).  The low two bits make the keys distinct, the
+// lower position winning a tie.  (The one-byte types use top2_nibbles8 below;
+// there E4M3's only NaN code is already the largest magnitude.)
 template <int DT>
 __device__ __forceinline__ uint32_t mag_key(uint32_t e, int p) {
-    uint32_t m;
-    if constexpr (DT == DT_F16) m = min(e & 0x7fffu, 0x7c01u);
-    else if constexpr (DT == DT_BF16) m = min(e & 0x7fffu, 0x7f81u);
-    else if constexpr (DT == DT_E5M2) m = min(e & 0x7fu, 0x7du);
-    else if constexpr (DT == DT_E4M3) m = e & 0x7fu;      // its only NaN is already the largest code
-    else {
-        const int v = (int)(int8_t)(e & 0xffu);
-        m = (uint32_t)(v < 0 ? -v : v);
-    }
+    static_assert(DT == DT_F16 || DT == DT_BF16, "two-byte types");
+    const uint32_t m = min(e & 0x7fffu, DT == DT_F16 ? 0x7c01u : 0x7f81u);
     return (m << 2) | (uint32_t)(3 - p);
 }
 
@@ -101,9 +95,55 @@ __device__ __forceinline__ uint32_t keep_mask(const uint32_t (&w)[4], int q, uin
         return top2_mask(mag_key<DT>(lo & 0xffffu, 0), mag_key<DT>(lo >> 16, 1), mag_key<DT>(hi & 0xffffu, 2),
                          mag_key<DT>(hi >> 16, 3));
     } else {
-        const uint32_t x = w[q];
-        return top2_mask(mag_key<DT>(x, 0), mag_key<DT>(x >> 8, 1), mag_key<DT>(x >> 16, 2), mag_key<DT>(x >> 24, 3));
+        static_assert(DT == DT_F16 || DT == DT_BF16, "one-byte types prune with top2_nibbles8");
+        return 0;
     }
+}
+
+// Packed form of the pruning rank for the one-byte types: two groups at once,
+// one per 16-bit half of each register, with v_pk_max/min_u16.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_max(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
+}
+__device__ __forceinline__ uint32_t pk_min(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
+}
+
+// Magnitudes of the four one-byte elements of a word, byte for byte: fp8
+// drops the sign; int8 takes |v| (one's complement plus one where negative; no
+// byte carries, -128 -> 0x80).
+template <int DT>
+__device__ __forceinline__ uint32_t mag_bytes(uint32_t w) {
+    if constexpr (DT == DT_I8) {
+        const uint32_t s = (w >> 7) & 0x01010101u;
+        return (w ^ (s * 0xffu)) + s;
+    } else {
+        return w & 0x7f7f7f7fu;
+    }
+}
+
+// Kept-pair nibbles of two groups of four one-byte elements (words wa, wb):
+// nib(wa) | nib(wb) << 16.  Key of element p = magnitude << 2 | (3 - p) in a
+// 16-bit half (E5M2 NaNs first folded to one code above infinity); the two
+// largest of four keys are the larger pair winner and the larger of the other
+// winner and both losers.
+template <int DT>
+__device__ __forceinline__ uint32_t top2_nibbles8(uint32_t wa, uint32_t wb) {
+    const uint32_t ma = mag_bytes<DT>(wa), mb = mag_bytes<DT>(wb);
+    uint32_t k[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        // [ma byte e, 0, mb byte e, 0]
+        uint32_t m = __builtin_amdgcn_perm(mb, ma, (uint32_t)e | (0x0cu << 8) | ((4u + e) << 16) | (0x0cu << 24));
+        if constexpr (DT == DT_E5M2) m = pk_min(m, 0x007d007du);
+        k[e] = (m << 2) | ((3u - e) * 0x00010001u);
+    }
+    const uint32_t m1 = pk_max(k[0], k[1]), n1 = pk_min(k[0], k[1]);
+    const uint32_t m2 = pk_max(k[2], k[3]), n2 = pk_min(k[2], k[3]);
+    const uint32_t first = pk_max(m1, m2), second = pk_max(pk_min(m1, m2), pk_max(n1, n2));
+    const uint32_t pf = 0x00030003u - (first & 0x00030003u), ps = 0x00030003u - (second & 0x00030003u);
+    return pk_min(pf, ps) | (pk_max(pf, ps) << 2);
 }
 
 template <int DT, bool PRUNE>
@@ -131,10 +171,19 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressParams p, int cpr
             }
             uint32_t out[2] = {0, 0};     // 8 compressed bytes
             uint32_t nib[4];
+            if constexpr (PRUNE && ES == 1) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t nn = top2_nibbles8<DT>(w[2 * h], w[2 * h + 1]);
+                    nib[2 * h] = nn & 0xfu;
+                    nib[2 * h + 1] = nn >> 16;
+                }
+            }
 #pragma unroll
             for (int q = 0; q < GROUPS; ++q) {
                 const uint32_t m = (ES == 2) ? group_mask16(w[2 * q], w[2 * q + 1]) : group_mask8<DT>(w[q]);
-                nib[q] = (uint32_t)(kPairTable >> (4 * keep_mask<DT, PRUNE>(w, q, m))) & 0xfu;
+                if constexpr (!(PRUNE && ES == 1))
+                    nib[q] = (uint32_t)(kPairTable >> (4 * keep_mask<DT, PRUNE>(w, q, m))) & 0xfu;
                 if (q < ngroups) {
                     bad += (kViolations >> m) & 1u;
                     bits |= nib[q] << (4 * q);
