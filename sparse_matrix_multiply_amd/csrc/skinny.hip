@@ -146,9 +146,14 @@ __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(GemmParams p) {
         for (int u = 0; u < U; ++u) {
             const int k0 = (s + u < s1) ? (s + u) * KS : p.K;   // past this wave's range: all zero
 #pragma unroll
-            for (int m = 0; m < MB; ++m) load_frag16<Op>(a[u][m], ra, aoff[m], k0, p.K, q);
-#pragma unroll
             for (int c = 0; c < CB; ++c) load_frag16<Op>(b[u][c], rb, boff[c], k0, p.K, q);
+        }
+        // A after B: B streams from HBM (long latency), A comes from L2
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k0 = (s + u < s1) ? (s + u) * KS : p.K;
+#pragma unroll
+            for (int m = 0; m < MB; ++m) load_frag16<Op>(a[u][m], ra, aoff[m], k0, p.K, q);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
