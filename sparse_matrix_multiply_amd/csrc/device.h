@@ -73,11 +73,16 @@ __device__ __forceinline__ i32x8 join(const Frag<32> &f) {
     return i32x8{f.lo[0], f.lo[1], f.lo[2], f.lo[3], f.hi[0], f.hi[1], f.hi[2], f.hi[3]};
 }
 
+// Every op's LDS k-tile rows are 128 bytes: a copy instruction then covers
+// whole 128-byte lines (8 lanes per row), and the vector L1 handles half as
+// many line requests per byte as with 64-byte rows; that request rate, not
+// the bytes, is what limits the copies.
+
 // Dense bf16 / fp16: v_mfma_f32_32x32x16_{bf16,f16}, 8 elements (16 B) per lane.
 template <int DT> struct MmaDense16 {
     static constexpr bool kSparse = false;
     static constexpr int kEsize = 2, kAFrag = 16, kBFrag = 16, kKStep = 16;
-    static constexpr int kBK = 32;                 // dense K per LDS k-tile (64-byte rows)
+    static constexpr int kBK = 64;                 // dense K per LDS k-tile
     static constexpr int kARowBytes = kBK * kEsize, kBRowBytes = kBK * kEsize;
     typedef f32x16 acc_t;
     typedef float out_t;
@@ -98,7 +103,7 @@ template <int DT> struct MmaDense16 {
 struct MmaDenseI8 {
     static constexpr bool kSparse = false;
     static constexpr int kEsize = 1, kAFrag = 16, kBFrag = 16, kKStep = 32;
-    static constexpr int kBK = 64;
+    static constexpr int kBK = 128;
     static constexpr int kARowBytes = kBK, kBRowBytes = kBK;
     typedef i32x16 acc_t;
     typedef int32_t out_t;
@@ -114,7 +119,7 @@ struct MmaDenseI8 {
 template <int FA, int FB> struct MmaDenseF8 {
     static constexpr bool kSparse = false;
     static constexpr int kEsize = 1, kAFrag = 32, kBFrag = 32, kKStep = 64;
-    static constexpr int kBK = 64;
+    static constexpr int kBK = 128;
     static constexpr int kARowBytes = kBK, kBRowBytes = kBK;
     typedef f32x16 acc_t;
     typedef float out_t;

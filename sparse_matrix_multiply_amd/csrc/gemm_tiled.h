@@ -320,16 +320,24 @@ struct TiledGemm {
     // copy at once after the barrier.  Loads complete in issue order, so the
     // wait before the barrier may leave this k-tile's first P0 copies and the
     // STAGES - 3 whole k-tiles before them in flight.
-    static constexpr int P0 = LPT - LPT / 2;
+    //
+    // With two stages the stage of k-tile kt is free right after the barrier
+    // of k-tile kt (its last step already holds its fragments in registers), so
+    // the copy of k-tile kt + 2 goes out there, into that stage, and has STEPS
+    // steps to land before the barrier of k-tile kt + 1 drains it.
+    static constexpr bool TWO = STAGES == 2;
+    static constexpr int AHEAD = TWO ? 2 : STAGES - 1;          // k-tile copied during k-tile kt: kt + AHEAD
+    static constexpr int P0 = TWO ? 0 : LPT - LPT / 2;
+    static constexpr int STEADY_WAIT = TWO ? 0 : (STAGES - 3) * LPT + P0;
 
     template <bool STEADY>
     __device__ __forceinline__ void iteration(uint8_t *smem, int kt, int cur, int nk, int nkt) {
-        const int pre = kt + STAGES - 1;
-        uint8_t *st_pre = smem + (cur == 0 ? STAGES - 1 : cur - 1) * STAGE;
+        const int pre = kt + AHEAD;
+        uint8_t *st_pre = smem + (TWO ? cur : (cur == 0 ? STAGES - 1 : cur - 1)) * STAGE;
         if constexpr (STEADY) {
 #pragma unroll
             for (int j = 0; j < P0; ++j) dma_pass(st_pre, pre, j);
-        } else if (pre < nkt) {
+        } else if (!TWO && pre < nkt) {
             if (pre < nk) dma(st_pre, pre);
             else fill_masked(st_pre, pre);
         }
@@ -341,8 +349,9 @@ struct TiledGemm {
                 load_frags(a1, b1, x1, sc, s + 1);
             } else {
                 if constexpr (STEADY) {
-                    static_assert(STAGES >= 3, "split copies need three stages");
-                    wait_vm_lgkm0<(STAGES - 3) * LPT + P0>();
+                    wait_vm_lgkm0<STEADY_WAIT>();
+                } else if constexpr (TWO) {
+                    wait_vm_lgkm0<0>();
                 } else {
                     const int after = min(STAGES - 2, nkt - 2 - kt);
                     wait_copies<LPT, STAGES - 2>(after <= 0 || kt + 1 + after >= nk ? 0 : after);
@@ -351,6 +360,9 @@ struct TiledGemm {
                 if constexpr (STEADY) {
 #pragma unroll
                     for (int j = P0; j < LPT; ++j) dma_pass(st_pre, pre, j);
+                } else if (TWO && pre < nkt) {
+                    if (pre < nk) dma(st_pre, pre);
+                    else fill_masked(st_pre, pre);
                 }
                 load_frags(a1, b1, x1, sn, 0);   // past the last k-tile this reads a stale stage, unused
             }
@@ -472,9 +484,9 @@ void gemm_tiled_kernel(GemmParams p) {
     const int nk = p.K / Op::kBK;                        // whole k-tiles
     const int nkt = nk + (p.K > nk * Op::kBK ? 1 : 0);   // plus a ragged one
 
-    // prologue: start k-tiles 0 .. STAGES-2 (and the folded C, whose loads overlap them)
+    // prologue: start k-tiles 0 .. AHEAD-1 (and the folded C, whose loads overlap them)
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) {
+    for (int s = 0; s < T::AHEAD; ++s) {
         if (s < nkt) {
             if (s < nk) t.dma(smem + s * T::STAGE, s);
             else t.fill_masked(smem + s * T::STAGE, s);
@@ -486,13 +498,13 @@ void gemm_tiled_kernel(GemmParams p) {
     // whole k-tiles (the ragged one issues fewer copy instructions); otherwise
     // wait for everything.
     {
-        const int after = min(STAGES - 2, nkt - 1);
-        wait_copies<T::LPT, STAGES - 2>(after <= 0 || after >= nk ? 0 : after);
+        const int after = min(T::AHEAD - 1, nkt - 1);
+        wait_copies<T::LPT, T::AHEAD - 1>(after <= 0 || after >= nk ? 0 : after);
         block_barrier();
     }
     if (nkt > 0) t.load_frags(t.a0, t.b0, t.x0, smem, 0);
     int kt = 0, cur = 0;
-    for (; kt + STAGES - 1 < nk; ++kt) {
+    for (; kt + T::AHEAD < nk; ++kt) {
         t.template iteration<true>(smem, kt, cur, nk, nkt);
         cur = (cur + 1 == STAGES) ? 0 : cur + 1;
     }
