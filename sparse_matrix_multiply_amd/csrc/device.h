@@ -38,6 +38,11 @@ constexpr int kBufferWord3 = 0x00020000;
 // A byte offset that is never inside any buffer this library builds: loads
 // from it return zero.
 constexpr uint32_t kOutOfRange = 0x80000000u;
+// Cache-policy operand of buffer loads/stores: non-temporal (the nt bit), for
+// data touched once -- C read at a tile's start and D written at its end -- so
+// it streams past the caches instead of evicting the A and B panels that
+// other tiles still reuse.
+constexpr int kNonTemporal = 2;
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef __attribute__((address_space(3))) void lds_void;

@@ -416,7 +416,7 @@ struct TiledGemm {
                     const int r = wm * WTM + i * 32 + 8 * (G / 4) + 4 * g + (G % 4);
                     const bool in = (row0 + r < p.M) && (col < p.N);
                     const uint32_t oc = in ? (uint32_t)((r * p.ldc + col) * sizeof(out_t)) : kOutOfRange;
-                    const uint32_t c = __builtin_amdgcn_raw_buffer_load_b32(rc, oc, 0, 0);
+                    const uint32_t c = __builtin_amdgcn_raw_buffer_load_b32(rc, oc, 0, kNonTemporal);
                     if constexpr (std::is_same<out_t, float>::value)
                         acc[i][j][G] = p.c_scale * __builtin_bit_cast(float, c);
                     else
@@ -446,7 +446,7 @@ struct TiledGemm {
                         od[jj][G] = in ? (uint32_t)((r * p.ldd + col) * sizeof(out_t)) : kOutOfRange;
                         if constexpr (USE_C) {
                             const uint32_t oc = in ? (uint32_t)((r * p.ldc + col) * sizeof(out_t)) : kOutOfRange;
-                            c[jj][G] = __builtin_amdgcn_raw_buffer_load_b32(rc, oc, 0, 0);
+                            c[jj][G] = __builtin_amdgcn_raw_buffer_load_b32(rc, oc, 0, kNonTemporal);
                         }
                     }
                 }
@@ -464,7 +464,7 @@ struct TiledGemm {
                             if constexpr (USE_C) v += (uint32_t)p.ibeta * c[jj][G];
                             bits = v;
                         }
-                        __builtin_amdgcn_raw_buffer_store_b32(bits, rd, od[jj][G], 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b32(bits, rd, od[jj][G], 0, kNonTemporal);
                     }
                 }
             }
