@@ -111,6 +111,7 @@ GemmParams make_params(int a, int64_t M, int64_t N, int64_t K, double alpha, con
             p.c_scale = alpha == beta ? 1.0f : (float)(beta / alpha);
         }
     }
+    p.vec_d = aligned16(D) && ldd % 4 == 0;
     const int tm = tile_rows(shape), tn = tile_cols(shape);
     p.tiles_m = (int)((M + tm - 1) / tm);
     p.tiles_n = (int)((N + tn - 1) / tn);

@@ -386,7 +386,7 @@ struct TiledGemm {
     // past the end of the buffer, where loads return zero and stores are
     // dropped, so there are no branches and all loads of a row of instruction
     // tiles are in flight together.
-    __device__ __forceinline__ void epilogue() {
+    __device__ __forceinline__ void epilogue(uint8_t *smem) {
         const int rows = min(BM, p.M - row0);
         const rsrc_t rd = make_rsrc(reinterpret_cast<out_t *>(p.D) + (int64_t)row0 * p.ldd,
                                     (uint32_t)(rows * p.ldd * sizeof(out_t)));
@@ -394,8 +394,78 @@ struct TiledGemm {
             const rsrc_t rc = make_rsrc(reinterpret_cast<const out_t *>(p.C) + (int64_t)row0 * p.ldc,
                                         (uint32_t)(rows * p.ldc * sizeof(out_t)));
             store_tiles<true>(rd, rc);
+        } else if (p.vec_d) {
+            store_tiles_lds(rd, smem);
         } else {
             store_tiles<false>(rd, rd);
+        }
+    }
+
+    // The epilogue through LDS (free once the last k-tile is done: no copy is
+    // in flight and no remaining read matters), so that D goes out with
+    // 16-byte stores, each instruction writing 8 whole 128-byte row segments
+    // instead of 2.  Each wave stages up to EPI_TILES of its 32 x 32 instruction
+    // tiles at a time in its own 4 KiB-per-tile region (no other wave touches
+    // it, so no barrier): lanes write their 16 registers in the accumulator
+    // layout, then read back row-contiguous 16-byte chunks (lane L: row
+    // 8q + L / 8 of the tile, chunk L mod 8).  Row r of a tile sits at row
+    // slot r ^ ((r >> 2) & 1): rows r and r + 4, written by the two lane halves
+    // together, then fall in opposite halves of the 64 banks, and so do the two
+    // rows of each 16-lane read.
+    static constexpr int epi_tiles() {   // most instruction tiles per pass: fits and divides TM * TN
+        int t = TM * TN;
+        while (t > 1 && (t * 4096 * NW > LDS_BYTES || (TM * TN) % t != 0)) --t;
+        return t;
+    }
+    static constexpr int EPI_TILES = epi_tiles();
+    static_assert(EPI_TILES * 4096 * NW <= LDS_BYTES, "epilogue staging space");
+
+    __device__ __forceinline__ void store_tiles_lds(rsrc_t rd, uint8_t *smem) {
+        uint8_t *region = smem + wave * EPI_TILES * 4096;
+#pragma unroll
+        for (int t0 = 0; t0 < TM * TN; t0 += EPI_TILES) {
+#pragma unroll
+            for (int t = 0; t < EPI_TILES; ++t) {
+                const int i = (t0 + t) / TN, j = (t0 + t) % TN;
+                uint8_t *base = region + t * 4096;
+#pragma unroll
+                for (int G = 0; G < 16; ++G) {
+                    const int r = 8 * (G / 4) + 4 * g + (G % 4);
+                    const int slot = r ^ ((r >> 2) & 1);
+                    uint32_t bits;
+                    if constexpr (std::is_same<out_t, float>::value) bits = __builtin_bit_cast(uint32_t, p.alpha * acc[i][j][G]);
+                    else bits = (uint32_t)p.ialpha * (uint32_t)acc[i][j][G];
+                    *reinterpret_cast<uint32_t *>(base + slot * 128 + l32 * 4) = bits;
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's staging writes are done
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < EPI_TILES; ++t) {
+                const int i = (t0 + t) / TN, j = (t0 + t) % TN;
+                const uint8_t *base = region + t * 4096;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = 8 * q + lane / 8, c = lane % 8;
+                    const int slot = r ^ ((r >> 2) & 1);
+                    const i32x4 v = *reinterpret_cast<const i32x4 *>(base + slot * 128 + c * 16);
+                    const int tr = wm * WTM + i * 32 + r;                    // row within the block tile
+                    const int col = col0 + wn * WTN + j * 32 + 4 * c;       // first of the 4 columns
+                    const bool rin = row0 + tr < p.M;
+                    const uint32_t o = (uint32_t)((tr * p.ldd + col) * sizeof(out_t));
+                    if (col + 3 < p.N) {
+                        __builtin_amdgcn_raw_buffer_store_b128(v, rd, rin ? o : kOutOfRange, 0, kNonTemporal);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            __builtin_amdgcn_raw_buffer_store_b32((uint32_t)v[e], rd,
+                                                                  rin && col + e < p.N ? o + 4 * e : kOutOfRange, 0,
+                                                                  kNonTemporal);
+                    }
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // the reads are done before the region is written again
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
@@ -512,7 +582,7 @@ void gemm_tiled_kernel(GemmParams p) {
         t.template iteration<false>(smem, kt, cur, nk, nkt);
         cur = (cur + 1 == STAGES) ? 0 : cur + 1;
     }
-    t.epilogue();
+    t.epilogue(smem);
 }
 
 }  // namespace mmac

@@ -28,6 +28,10 @@ struct GemmParams {
     // alpha == 1 and c_scale = beta, exact modulo 2^32).
     int fold_c;
     float c_scale;
+    // vec_d: D starts on a 16-byte boundary and its row pitch is a multiple of
+    // 4 elements, so the epilogue may store 4 consecutive elements of a row
+    // with one 16-byte access.
+    int vec_d;
     int tiles_m, tiles_n, group_m;
 };
 
