@@ -114,18 +114,25 @@ def test_k_zero_gives_beta_c():
     assert np.array_equal(D.cpu().numpy(), (np.float32(0.5) * C))
 
 
-def test_output_pitch_and_untouched_padding():
+@pytest.mark.parametrize("tile", [256, 64])
+@pytest.mark.parametrize("ldd,first", [(50, 0), (36, 0), (64, 0), (64, 1)])
+@pytest.mark.parametrize("beta", [0.0, 0.5])
+def test_output_pitch_and_untouched_padding(ldd, first, beta, tile):
+    """D inside a padded buffer: pitches that do (36, 64) and do not (50) allow 16-byte
+    row chunks, a D that starts off a 16-byte boundary (first column 1), and an N
+    whose last chunk is partial; the padding must stay untouched."""
     M, N, K = 65, 33, 100
-    A, B, C, alpha, beta = inputs(F16, F16, M, N, K, 9)
-    ldd = 50
+    A, B, C, alpha, _ = inputs(F16, F16, M, N, K, 9)
     Ad, Bd = to_dev_bits(A, F16), to_dev_bits(B, F16)
     buf = torch.full((M, ldd), 123.0, dtype=torch.float32, device=dev())
-    mm.gemm_dense(Ad, Bd, buf[:, :N], alpha, beta, torch.from_numpy(C).to(dev()), a_type=F16, b_type=F16)
+    Cd = torch.from_numpy(C).to(dev()) if beta != 0 else None
+    with tile_shape(tile):
+        mm.gemm_dense(Ad, Bd, buf[:, first:first + N], alpha, beta, Cd, a_type=F16, b_type=F16)
     torch.cuda.synchronize()
     out = buf.cpu().numpy()
-    assert (out[:, N:] == 123.0).all()
+    assert (out[:, :first] == 123.0).all() and (out[:, first + N:] == 123.0).all()
     Dref, S = oracle.gemm_dense(F16, F16, A, B, alpha, beta, C)
-    assert_close(out[:, :N], Dref, S, F16, K, alpha, beta, C)
+    assert_close(out[:, first:first + N], Dref, S, F16, K, alpha, beta, C)
 
 
 @pytest.mark.parametrize("ta,tb", [(BF16, BF16), (E4M3, E5M2)])
