@@ -45,6 +45,8 @@ def lib():
         L.oracle_compress24.argtypes = [ip, i64, i64, vp, i64, vp, i64, vp, i64, vp]
         L.oracle_decompress24.argtypes = [ip, i64, i64, vp, i64, vp, i64, vp, i64]
         L.oracle_prune_compress24.argtypes = [ip, i64, i64, vp, i64, vp, i64, vp, i64, vp]
+        L.oracle_epilogue.argtypes = [i64, i64, vp, i64, vp, ip, ip, vp, i64, vp]
+        L.oracle_round.argtypes = [ip, i64, vp, vp]
         L.oracle_gemm_sparse24_f64.argtypes = [ip, ip, i64, i64, i64, dbl, vp, i64, vp, i64, vp, i64,
                                                dbl, vp, i64, i64, i64, vp, i64, vp, i64]
         L.oracle_gemm_sparse24_f64_entries.argtypes = [ip, ip, i64, i64, i64, dbl, vp, i64, vp, i64, vp,
@@ -155,6 +157,32 @@ def prune_compress24(t, A):
     _check(lib().oracle_prune_compress24(t, M, K, _p(A), K, _p(Ac), K // 2, _p(idx), W, ctypes.byref(bad)),
            "prune_compress24")
     return Ac, idx, int(bad.value)
+
+
+OUT_F32, OUT_BF16, OUT_F16 = 0, 1, 2
+ACT_NONE, ACT_RELU = 0, 1
+
+
+def epilogue(Y, bias=None, act=ACT_NONE, out_type=OUT_F32):
+    """Epilogue variants on the exact GEMM value Y (float64 M x N): + bias[j] (float32),
+    activation, rounding to the output format.  Returns (bits or float32 array, the
+    float64 value before rounding)."""
+    Y = _c2(Y, np.float64)
+    M, N = Y.shape
+    out = np.zeros((M, N), np.uint16 if out_type else np.float32)
+    Yout = np.zeros((M, N), np.float64)
+    b = None if bias is None else np.ascontiguousarray(bias, np.float32)
+    _check(lib().oracle_epilogue(M, N, _p(Y), N, _p(b) if b is not None else None, act, out_type, _p(out), N,
+                                 _p(Yout)), "epilogue")
+    return out, Yout
+
+
+def round_to(out_type, x):
+    """Round float64 values to bfloat16 (OUT_BF16) or binary16 (OUT_F16) bits, saturating."""
+    x = np.ascontiguousarray(x, np.float64)
+    bits = np.zeros(x.shape, np.uint16)
+    _check(lib().oracle_round(out_type, x.size, _p(x), _p(bits)), "round")
+    return bits
 
 
 def decompress24(t, Ac, idx, K):

@@ -6,6 +6,8 @@
  *   - dense   D = alpha * A*B + beta * C       (fp64 or int64 accumulation)
  *   - 4:2 compression of a structured-sparse A into non-zeros + index nibbles
  *   - magnitude pruning of a dense A to 4:2 followed by that compression
+ *   - the output epilogue variants: per-column bias, ReLU, rounding to
+ *     bfloat16 / binary16 with saturation
  *   - sparse  D = alpha * A*B + beta * C with A given in compressed form
  *
  * Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
@@ -279,6 +281,73 @@ int oracle_compress24(int t, int64_t M, int64_t K, const void *A, int64_t lda,
         }
     }
     if (bad_groups) *bad_groups = bad;
+    return 0;
+}
+
+/*
+ * Output epilogue variants (beyond the pages, which accumulate in fp32/int32
+ * and return that): from the exact value y = alpha*A*B + beta*C of the plain
+ * GEMM, add a per-column bias, apply an activation, then round to the output
+ * format.
+ *   activation 0: none; 1: ReLU, max(y, 0) (a NaN stays NaN);
+ *   output 1: bfloat16, 2: IEEE binary16; rounding to nearest, ties to even
+ *   (from the exact value), saturating: a finite value beyond the largest
+ *   finite magnitude becomes that magnitude with its sign; infinities stay
+ *   infinities, a NaN becomes the format's quiet NaN with the same sign.
+ */
+static uint32_t round_to_format(double y, int mant_bits, int exp_bits) {
+    const int bias = (1 << (exp_bits - 1)) - 1, emax = bias, emin = 1 - bias;
+    const uint32_t sign = signbit(y) ? 1u : 0u;
+    const uint32_t exp_all = (1u << exp_bits) - 1u, total = 1u + (uint32_t)exp_bits + (uint32_t)mant_bits;
+    const uint32_t sbit = sign << (total - 1);
+    if (isnan(y)) return sbit | (exp_all << mant_bits) | (1u << (mant_bits - 1));
+    if (isinf(y)) return sbit | (exp_all << mant_bits);
+    double a = fabs(y);
+    const double max_finite = ldexp(2.0 - ldexp(1.0, -mant_bits), emax);
+    /* quantum of the binade holding a (subnormal quantum below 2^emin) */
+    int e = (a > 0.0) ? ilogb(a) : emin;
+    if (e < emin) e = emin;
+    const double q = ldexp(1.0, e - mant_bits);
+    double n = a / q;                         /* exact: a is a double, q a power of two */
+    double r = floor(n);
+    const double frac = n - r;
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+    double v = r * q;                         /* rounded magnitude (may reach the next binade) */
+    if (v > max_finite) v = max_finite;       /* saturate */
+    if (v == 0.0) return sbit;
+    int ev = ilogb(v);
+    uint32_t field, mant;
+    if (ev < emin) {                          /* subnormal */
+        field = 0u;
+        mant = (uint32_t)(v / ldexp(1.0, emin - mant_bits));
+    } else {
+        field = (uint32_t)(ev + bias);
+        mant = (uint32_t)((v / ldexp(1.0, ev) - 1.0) * ldexp(1.0, mant_bits));
+    }
+    return sbit | (field << mant_bits) | mant;
+}
+
+int oracle_epilogue(int64_t M, int64_t N, const double *Y, int64_t ldy, const float *bias, int act, int out_type,
+                    void *out, int64_t ldo, double *Yout) {
+    if (M < 0 || N < 0 || act < 0 || act > 1 || out_type < 0 || out_type > 2) return -1;
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j) {
+            double y = Y[i * ldy + j];
+            if (bias) y += (double)bias[j];
+            if (act == 1 && y < 0.0) y = 0.0;
+            if (Yout) Yout[i * ldo + j] = y;
+            if (out_type == 1) ((uint16_t *)out)[i * ldo + j] = (uint16_t)round_to_format(y, 7, 8);
+            else if (out_type == 2) ((uint16_t *)out)[i * ldo + j] = (uint16_t)round_to_format(y, 10, 5);
+            else ((float *)out)[i * ldo + j] = (float)y;
+        }
+    return 0;
+}
+
+/* Round n doubles to bfloat16 (out_type 1) or binary16 (2) bits, as above (for the pins). */
+int oracle_round(int out_type, int64_t n, const double *x, uint16_t *bits) {
+    if (out_type != 1 && out_type != 2) return -1;
+    for (int64_t q = 0; q < n; ++q)
+        bits[q] = (uint16_t)(out_type == 1 ? round_to_format(x[q], 7, 8) : round_to_format(x[q], 10, 5));
     return 0;
 }
 

@@ -435,3 +435,56 @@ def test_sparse_rejects_invalid_nibble():
 def test_normwise_error_metric():
     D = np.array([[1.0, 2.0]]); S = np.array([[3.0, 4.0]])
     assert oracle.normwise_error(D + np.array([[0.0, 0.5]]), D, S, 1.0, 0.0) == pytest.approx(0.1)
+
+
+# -------------------------------------------------------- output epilogue --
+# Rounding to bfloat16 / binary16 (nearest, ties to even, saturating) and the
+# bias + ReLU step are not on the pages; they are pinned by round trips over
+# every code, by torch's own float64 casts, and by hand-worked ties.
+
+@pytest.mark.parametrize("out_type,t", [(oracle.OUT_BF16, BF16), (oracle.OUT_F16, F16)])
+def test_round_trips_every_code(out_type, t):
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = torch_decode(codes, t)
+    back = oracle.round_to(out_type, vals)
+    finite_or_inf = ~np.isnan(vals)
+    assert np.array_equal(back[finite_or_inf], codes[finite_or_inf])
+    nan_code = 0x7FC0 if t == BF16 else 0x7E00
+    assert np.all((back[~finite_or_inf] & 0x7FFF) == nan_code)
+
+
+@pytest.mark.parametrize("out_type,tdt,maxf", [(oracle.OUT_BF16, torch.bfloat16, 3.3895313892515355e38),
+                                               (oracle.OUT_F16, torch.float16, 65504.0)])
+def test_rounding_matches_torch_in_range_and_saturates(out_type, tdt, maxf):
+    g = np.random.default_rng(17)
+    x = np.concatenate([g.standard_normal(20000) * np.exp(g.uniform(-40, 40, 20000)),
+                        g.uniform(-1e-7, 1e-7, 2000), g.uniform(-maxf, maxf, 2000)])
+    # values exact in float32: torch converts float64 through float32 (a second rounding)
+    x = x.astype(np.float32).astype(np.float64)
+    ours = oracle.round_to(out_type, x)
+    theirs = torch.from_numpy(x).to(tdt).view(torch.int16).numpy().astype(np.uint16)
+    over = np.isinf(torch.from_numpy(x).to(tdt).float().numpy())
+    assert np.array_equal(ours[~over], theirs[~over])
+    # beyond the largest finite value: saturated, sign kept
+    sat = oracle.round_to(out_type, np.array([maxf * 2, -maxf * 2, np.inf, -np.inf]))
+    top = 0x7F7F if out_type == oracle.OUT_BF16 else 0x7BFF
+    inf = 0x7F80 if out_type == oracle.OUT_BF16 else 0x7C00
+    assert list(sat) == [top, top | 0x8000, inf, inf | 0x8000]
+
+
+def test_rounding_ties_to_even():
+    f16 = oracle.round_to(oracle.OUT_F16, np.array([1 + 2 ** -11, 1 + 3 * 2 ** -11, -(1 + 2 ** -11), 2 ** -25,
+                                                    3 * 2 ** -25]))
+    assert list(f16) == [0x3C00, 0x3C02, 0xBC00, 0x0000, 0x0002]
+    bf16 = oracle.round_to(oracle.OUT_BF16, np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 2 ** -134, 3 * 2 ** -134]))
+    assert list(bf16) == [0x3F80, 0x3F82, 0x0000, 0x0002]
+
+
+def test_epilogue_bias_and_relu():
+    Y = np.array([[1.5, -2.0, 0.0], [np.nan, -0.25, 3.0]])
+    bias = np.array([0.25, 1.0, -4.0], np.float32)
+    out, y = oracle.epilogue(Y, bias, oracle.ACT_RELU, oracle.OUT_F32)
+    assert np.array_equal(out[0], np.array([1.75, 0.0, 0.0], np.float32))
+    assert np.isnan(out[1, 0]) and out[1, 1] == 0.75 and out[1, 2] == 0.0
+    out, _ = oracle.epilogue(Y, None, oracle.ACT_NONE, oracle.OUT_BF16)
+    assert list(out[0]) == [0x3FC0, 0xC000, 0x0000]
