@@ -294,30 +294,36 @@ def suite():
 
     out = {}
 
-    def dense_case(name, key, reps=20, rotate=1, n_share=None):
+    def dense_case(name, key, reps=20, rotate=1, n_share=None, bf16_out=False):
         """n_share: keep only the first n_share columns of B, C and D (one GPU's share when N is
-        split across GPUs)."""
+        split across GPUs).  bf16_out: the epilogue variant with bfloat16 C and D, a per-column
+        bias and ReLU."""
         w = dict(W.workload(name))
         if n_share:
             w["B"], w["N"] = w["B"][:n_share], n_share
             if w["C"] is not None:
                 w["C"] = np.ascontiguousarray(w["C"][:, :n_share])
         A, B = to_dev(w["A"], w["ta"]), to_dev(w["B"], w["tb"])
-        C = torch.from_numpy(w["C"]).to(dev) if w["beta"] != 0 else None
         integer = w["ta"] == W.I8
-        Ds = [torch.empty((w["M"], w["N"]), dtype=torch.int32 if integer else torch.float32, device=dev)
-              for _ in range(rotate)]
+        odt = torch.bfloat16 if bf16_out else torch.int32 if integer else torch.float32
+        C = torch.from_numpy(w["C"]).to(dev).to(odt) if w["beta"] != 0 else None
+        bias = torch.linspace(-1, 1, w["N"], device=dev) if bf16_out else None
+        act = mm.ACT_RELU if bf16_out else mm.ACT_NONE
+        Ds = [torch.empty((w["M"], w["N"]), dtype=odt, device=dev) for _ in range(rotate)]
         Bs = [B] + [B.clone() for _ in range(rotate - 1)]
         fns = [lambda i=i: mm.gemm_dense(A, Bs[i], Ds[i], w["alpha"], w["beta"], C, a_type=w["ta"], b_type=w["tb"],
-                                         stream=stream) for i in range(rotate)]
+                                         stream=stream, bias=bias, act=act) for i in range(rotate)]
         ms = median_ms(fns, reps)
         f = gemm_flops(w["M"], w["N"], w["K"])
         es = 2 if w["ta"] in (W.BF16, W.F16) else 1
-        byt = (w["M"] + w["N"]) * w["K"] * es + w["M"] * w["N"] * 4 * (2 if w["beta"] != 0 else 1)
+        oes = 2 if bf16_out else 4
+        byt = (w["M"] + w["N"]) * w["K"] * es + w["M"] * w["N"] * oes * (2 if w["beta"] != 0 else 1)
         out[key] = {"us": round(ms * 1e3, 1), "single_launch_us": round(batch[-1] * 1e3, 1),
                     ("TOP/s" if integer else "TFLOP/s"): round(f / ms / 1e9, 1),
                     "GB/s": round(byt / ms / 1e6, 1), "shape": [w["M"], w["N"], w["K"]], "alpha": w["alpha"],
                     "beta": w["beta"]}
+        if bf16_out:
+            out[key]["epilogue"] = "bf16 C/D, bias, ReLU"
         del A, B, Bs, C, Ds
         torch.cuda.empty_cache()
 
@@ -338,6 +344,10 @@ def suite():
     # one GPU's share of the 8192^3 GEMMs split 8 ways along N
     dense_case("bf16_8192", "share_bf16_8192x1024x8192_beta1", n_share=1024)
     dense_case("fp8_8192", "share_fp8e4m3xbf8e5m2_8192x1024x8192", n_share=1024)
+    # epilogue variant: bfloat16 C and D with bias and ReLU (half the output bytes)
+    dense_case("bf16_8192", "bf16_8192^3_beta1_bf16out_bias_relu", bf16_out=True)
+    dense_case("fp8_8192", "fp8e4m3xbf8e5m2_8192^3_bf16out_bias_relu", bf16_out=True)
+    dense_case("bf16_skinny", "bf16_16x4096x4096_beta1_bf16out_bias_relu", reps=200, rotate=16, bf16_out=True)
 
     for name, key, rot, n_share in (("f16_sparse", "f16_4:2_4096x4096x8192", 8, None),
                                     ("fp8_8192_sparse", "fp8_4:2_8192^3", 8, None),

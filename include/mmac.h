@@ -162,6 +162,64 @@ mmac_status_t mmac_gemm_sparse24(mmac_dtype_t a_type, mmac_dtype_t b_type,
                                  double beta, const void *C, int64_t ldc,
                                  void *D, int64_t ldd, void *stream);
 
+/*
+ * Epilogue variants ("Epilogue variants" below): the type of C and D, a
+ * per-column bias and an activation, applied after alpha * A*B + beta * C.
+ */
+typedef enum {
+    MMAC_OUT_ACC = 0,  /* fp32 (int32 for int8 inputs): the plain calls' output */
+    MMAC_OUT_BF16 = 1, /* bfloat16 */
+    MMAC_OUT_F16 = 2   /* IEEE binary16 */
+} mmac_out_type_t;
+
+typedef enum {
+    MMAC_ACT_NONE = 0,
+    MMAC_ACT_RELU = 1 /* max(v, 0): negative values become +0; NaN and -0 pass unchanged */
+} mmac_act_t;
+
+typedef struct mmac_epilogue {
+    int32_t d_type;     /* mmac_out_type_t: element type of D and of C */
+    int32_t act;        /* mmac_act_t */
+    const float *bias;  /* NULL, or device memory holding N fp32 values (4-byte aligned) */
+} mmac_epilogue_t;
+
+/*
+ * Epilogue variants of the two GEMMs.  Arguments are those of mmac_gemm_dense
+ * and mmac_gemm_sparse24 plus `ep` (host pointer, read during the call only;
+ * NULL means { MMAC_OUT_ACC, MMAC_ACT_NONE, NULL }, i.e. the plain call).
+ * Every element of D is
+ *     D[i][j] = round( act( alpha * acc[i][j] + beta * C[i][j] + bias[j] ) )
+ * where acc is A*B accumulated in fp32, the sum is formed in fp32 (bias is
+ * added only when given), and round converts to d_type: to nearest, ties to
+ * even, saturating -- a finite value beyond the type's largest finite value
+ * (bfloat16 0x7f7f, binary16 65504) becomes that value with its sign;
+ * infinities stay infinite; NaN becomes the type's quiet NaN (0x7fc0 /
+ * 0x7e00) with its sign.  C has d_type and row pitch ldc; D has d_type and
+ * row pitch ldd.  For bfloat16 / binary16 C and D need 2-byte alignment, and
+ * the row pitch limit of 8 MiB applies to ldc / ldd times 2.
+ * int8 inputs accept only { MMAC_OUT_ACC, MMAC_ACT_NONE, NULL }
+ * (MMAC_ERR_UNSUPPORTED otherwise).  An unknown d_type or act gives
+ * MMAC_ERR_INVALID_ARG; a bias not 4-byte aligned gives MMAC_ERR_MISALIGNED.
+ * The pages define the product and the beta * C term only; the other steps
+ * are the usual fused output stage of a GEMM library.
+ */
+mmac_status_t mmac_gemm_dense_ep(mmac_dtype_t a_type, mmac_dtype_t b_type,
+                                 int64_t M, int64_t N, int64_t K, double alpha,
+                                 const void *A, int64_t lda,
+                                 const void *B, int64_t ldb,
+                                 double beta, const void *C, int64_t ldc,
+                                 void *D, int64_t ldd,
+                                 const mmac_epilogue_t *ep, void *stream);
+
+mmac_status_t mmac_gemm_sparse24_ep(mmac_dtype_t a_type, mmac_dtype_t b_type,
+                                    int64_t M, int64_t N, int64_t K, double alpha,
+                                    const void *Ac, int64_t ldac,
+                                    const uint32_t *idx, int64_t ldidx,
+                                    const void *B, int64_t ldb,
+                                    double beta, const void *C, int64_t ldc,
+                                    void *D, int64_t ldd,
+                                    const mmac_epilogue_t *ep, void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *mmac_status_string(mmac_status_t s);
 

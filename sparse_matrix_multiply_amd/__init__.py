@@ -9,7 +9,10 @@ first call raises -- there is no fallback path.
 Tensor conventions (element strides; the last dimension must be contiguous):
     A   M x K  row-major             (torch dtype gives the element type)
     B   N x K  (the K x N matrix B stored column-major)
-    C,D M x N  float32 (int32 for int8 inputs)
+    C,D M x N  float32 (int32 for int8 inputs); with floating inputs also
+               bfloat16 or float16 (the epilogue variants: D's dtype picks the
+               output type, C has D's dtype), plus an optional fp32 bias of N
+               values and ReLU
     Ac  M x K/2, idx M x ceil(K/32) int32/uint32 words
 """
 import ctypes
@@ -23,11 +26,20 @@ LIB_PATH = os.path.join(_HERE, "libmmac.so")
 F16, BF16, I8, FP8_E4M3, BF8_E5M2 = 1, 2, 3, 4, 5
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_HIP = 0, 1, 2, 3, 4
 
+OUT_ACC, OUT_BF16, OUT_F16 = 0, 1, 2
+ACT_NONE, ACT_RELU = 0, 1
+OUT_OF = {torch.float32: OUT_ACC, torch.int32: OUT_ACC, torch.bfloat16: OUT_BF16, torch.float16: OUT_F16}
+
 DTYPE_OF = {torch.float16: F16, torch.bfloat16: BF16, torch.int8: I8,
             torch.float8_e4m3fn: FP8_E4M3, torch.float8_e5m2: BF8_E5M2}
 TORCH_OF = {v: k for k, v in DTYPE_OF.items()}
 
 _lib = None
+
+
+class Epilogue(ctypes.Structure):
+    """mmac_epilogue_t."""
+    _fields_ = [("d_type", ctypes.c_int32), ("act", ctypes.c_int32), ("bias", ctypes.c_void_p)]
 
 
 class MmacError(RuntimeError):
@@ -53,6 +65,12 @@ def lib():
         L.mmac_gemm_sparse24.restype = i32
         L.mmac_gemm_sparse24.argtypes = [i32, i32, i64, i64, i64, dbl, vp, i64, vp, i64, vp, i64, dbl, vp, i64,
                                          vp, i64, vp]
+        ep = ctypes.POINTER(Epilogue)
+        L.mmac_gemm_dense_ep.restype = i32
+        L.mmac_gemm_dense_ep.argtypes = [i32, i32, i64, i64, i64, dbl, vp, i64, vp, i64, dbl, vp, i64, vp, i64, ep, vp]
+        L.mmac_gemm_sparse24_ep.restype = i32
+        L.mmac_gemm_sparse24_ep.argtypes = [i32, i32, i64, i64, i64, dbl, vp, i64, vp, i64, vp, i64, dbl, vp, i64,
+                                            vp, i64, ep, vp]
         L.mmac_status_string.restype = ctypes.c_char_p
         L.mmac_status_string.argtypes = [i32]
         _lib = L
@@ -89,14 +107,29 @@ def _check(status, what):
         raise MmacError(status, what)
 
 
-def gemm_dense(A, B, D, alpha=1.0, beta=0.0, C=None, a_type=None, b_type=None, stream=None):
-    """D = alpha * A @ B + beta * C with A M x K (row-major) and B given as its N x K transpose."""
+def _epilogue(D, bias, act, d_type):
+    """The mmac_epilogue_t of a call, or None for the plain call."""
+    d_type = OUT_OF.get(D.dtype, OUT_ACC) if d_type is None else d_type
+    if d_type == OUT_ACC and bias is None and act == ACT_NONE:
+        return None
+    return Epilogue(d_type, act, None if bias is None else bias.data_ptr())
+
+
+def gemm_dense(A, B, D, alpha=1.0, beta=0.0, C=None, a_type=None, b_type=None, stream=None, bias=None,
+               act=ACT_NONE, d_type=None):
+    """D = alpha * A @ B + beta * C with A M x K (row-major) and B given as its N x K transpose.
+    With bias (N fp32 values), act or a bfloat16 / float16 D (d_type overrides what D's dtype
+    says) this is mmac_gemm_dense_ep: D = round(act(alpha * A @ B + beta * C + bias))."""
     M, K = A.shape
     N = B.shape[0]
     ta, tb = _dtype(A, a_type), _dtype(B, b_type)
-    st = lib().mmac_gemm_dense(ta, tb, M, N, K, float(alpha), _ptr(A), _ld(A), _ptr(B), _ld(B), float(beta),
-                               _ptr(C), _ld(C) if C is not None else 0, _ptr(D), _ld(D), _stream(stream))
-    _check(st, "mmac_gemm_dense")
+    args = (ta, tb, M, N, K, float(alpha), _ptr(A), _ld(A), _ptr(B), _ld(B), float(beta),
+            _ptr(C), _ld(C) if C is not None else 0, _ptr(D), _ld(D))
+    ep = _epilogue(D, bias, act, d_type)
+    if ep is None:
+        _check(lib().mmac_gemm_dense(*args, _stream(stream)), "mmac_gemm_dense")
+    else:
+        _check(lib().mmac_gemm_dense_ep(*args, ctypes.byref(ep), _stream(stream)), "mmac_gemm_dense_ep")
     return D
 
 
@@ -121,16 +154,21 @@ def sparse24_prune_compress(A, Ac, idx, bad_groups=None, a_type=None, stream=Non
     return Ac, idx
 
 
-def gemm_sparse24(Ac, idx, B, D, K=None, alpha=1.0, beta=0.0, C=None, a_type=None, b_type=None, stream=None):
-    """D = alpha * A @ B + beta * C with A given compressed (Ac, idx); K is the dense K."""
+def gemm_sparse24(Ac, idx, B, D, K=None, alpha=1.0, beta=0.0, C=None, a_type=None, b_type=None, stream=None,
+                  bias=None, act=ACT_NONE, d_type=None):
+    """D = alpha * A @ B + beta * C with A given compressed (Ac, idx); K is the dense K.
+    bias / act / a 16-bit D select mmac_gemm_sparse24_ep, as in gemm_dense."""
     M = Ac.shape[0]
     N, KB = B.shape
     K = KB if K is None else K
     ta, tb = _dtype(Ac, a_type), _dtype(B, b_type)
-    st = lib().mmac_gemm_sparse24(ta, tb, M, N, K, float(alpha), _ptr(Ac), _ld(Ac), _ptr(idx), _ld(idx),
-                                  _ptr(B), _ld(B), float(beta), _ptr(C), _ld(C) if C is not None else 0,
-                                  _ptr(D), _ld(D), _stream(stream))
-    _check(st, "mmac_gemm_sparse24")
+    args = (ta, tb, M, N, K, float(alpha), _ptr(Ac), _ld(Ac), _ptr(idx), _ld(idx), _ptr(B), _ld(B), float(beta),
+            _ptr(C), _ld(C) if C is not None else 0, _ptr(D), _ld(D))
+    ep = _epilogue(D, bias, act, d_type)
+    if ep is None:
+        _check(lib().mmac_gemm_sparse24(*args, _stream(stream)), "mmac_gemm_sparse24")
+    else:
+        _check(lib().mmac_gemm_sparse24_ep(*args, ctypes.byref(ep), _stream(stream)), "mmac_gemm_sparse24_ep")
     return D
 
 

@@ -1,6 +1,7 @@
 """Build libmmac.so (the HIP kernels and the C ABI) for gfx950, in-tree.
 
-Every HIP source is compiled with hipcc for --offload-arch=gfx950 into
+Every HIP source (csrc/*.hip and the per-type-pair kernel instantiations in
+csrc/inst/*.hip) is compiled with hipcc for --offload-arch=gfx950 into
 sparse_matrix_multiply_amd/_build/, in parallel, then linked into
 sparse_matrix_multiply_amd/libmmac.so.  Usage: python -m sparse_matrix_multiply_amd.build
 """
@@ -26,11 +27,16 @@ FLAGS = [
 
 
 def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    """Every .hip file under csrc/ and csrc/inst/ (one kernel set per file)."""
+    out = []
+    for d in (CSRC, os.path.join(CSRC, "inst")):
+        out += [os.path.join(d, f) for f in os.listdir(d) if f.endswith(".hip")]
+    return sorted(out)
 
 
 def _compile(src, verbose):
-    obj = os.path.join(OUT, os.path.basename(src)[:-4] + ".o")
+    rel = os.path.relpath(src, CSRC)[:-4].replace(os.sep, "_")   # inst/dense_bf16 -> inst_dense_bf16
+    obj = os.path.join(OUT, rel + ".o")
     cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)

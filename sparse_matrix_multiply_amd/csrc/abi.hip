@@ -61,11 +61,25 @@ TileShape pick_shape(int64_t M, int64_t N, bool sparse = false) {
     return TILE_64;
 }
 
+// The epilogue variant a call asks for (NULL: the plain call).
+mmac_epilogue_t epilogue_of(const mmac_epilogue_t *ep) {
+    return ep ? *ep : mmac_epilogue_t{MMAC_OUT_ACC, MMAC_ACT_NONE, nullptr};
+}
+
+// Bytes of one C / D element.
+int out_size(const mmac_epilogue_t &ep) { return ep.d_type == MMAC_OUT_ACC ? 4 : 2; }
+
+bool aligned_to(const void *p, int n) { return reinterpret_cast<uintptr_t>(p) % n == 0; }
+
 // Common checks of the GEMM calls.  Returns MMAC_OK or the error.
 mmac_status_t check_gemm(int a, int b, int64_t M, int64_t N, int64_t K, double alpha, const void *A,
                          int64_t lda, int64_t a_cols, const void *B, int64_t ldb, double beta, const void *C,
-                         int64_t ldc, const void *D, int64_t ldd) {
+                         int64_t ldc, const void *D, int64_t ldd, const mmac_epilogue_t &ep) {
     if (!supported_pair(a, b)) return MMAC_ERR_UNSUPPORTED;
+    if (ep.d_type < MMAC_OUT_ACC || ep.d_type > MMAC_OUT_F16 || ep.act < MMAC_ACT_NONE || ep.act > MMAC_ACT_RELU)
+        return MMAC_ERR_INVALID_ARG;
+    if (a == MMAC_I8 && (ep.d_type != MMAC_OUT_ACC || ep.act != MMAC_ACT_NONE || ep.bias))
+        return MMAC_ERR_UNSUPPORTED;
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return MMAC_ERR_INVALID_ARG;
     if ((K > 0 && (!A || !B)) || !D) return MMAC_ERR_INVALID_ARG;
     if (beta != 0.0 && !C) return MMAC_ERR_INVALID_ARG;
@@ -76,15 +90,17 @@ mmac_status_t check_gemm(int a, int b, int64_t M, int64_t N, int64_t K, double a
     if (C == D && beta != 0.0 && ldc != ldd) return MMAC_ERR_INVALID_ARG;
     const int es = elem_size(a);
     if (lda * es > kMaxPitchBytes || ldb * es > kMaxPitchBytes) return MMAC_ERR_UNSUPPORTED;
-    if (ldd * 4 > kMaxPitchBytes || (C && beta != 0.0 && ldc * 4 > kMaxPitchBytes)) return MMAC_ERR_UNSUPPORTED;
+    const int oes = out_size(ep);
+    if (ldd * oes > kMaxPitchBytes || (C && beta != 0.0 && ldc * oes > kMaxPitchBytes)) return MMAC_ERR_UNSUPPORTED;
     if (!aligned16(A) || !aligned16(B) || (lda * es) % 16 || (ldb * es) % 16) return MMAC_ERR_MISALIGNED;
-    if (!aligned4(D) || (C && beta != 0.0 && !aligned4(C))) return MMAC_ERR_MISALIGNED;
+    if (!aligned_to(D, oes) || (C && beta != 0.0 && !aligned_to(C, oes))) return MMAC_ERR_MISALIGNED;
+    if (ep.bias && !aligned4(ep.bias)) return MMAC_ERR_MISALIGNED;
     return MMAC_OK;
 }
 
 GemmParams make_params(int a, int64_t M, int64_t N, int64_t K, double alpha, const void *A, int64_t lda,
                        const void *B, int64_t ldb, double beta, const void *C, int64_t ldc, void *D, int64_t ldd,
-                       TileShape shape) {
+                       const mmac_epilogue_t &ep, TileShape shape) {
     GemmParams p{};
     const int es = elem_size(a);
     p.A = static_cast<const uint8_t *>(A);
@@ -111,7 +127,10 @@ GemmParams make_params(int a, int64_t M, int64_t N, int64_t K, double alpha, con
             p.c_scale = alpha == beta ? 1.0f : (float)(beta / alpha);
         }
     }
-    p.vec_d = aligned16(D) && ldd % 4 == 0;
+    p.vec_d = aligned16(D) && (ldd * out_size(ep)) % 16 == 0;
+    p.d_type = ep.d_type;
+    p.act = ep.act;
+    p.bias = ep.bias;
     const int tm = tile_rows(shape), tn = tile_cols(shape);
     p.tiles_m = (int)((M + tm - 1) / tm);
     p.tiles_n = (int)((N + tn - 1) / tn);
@@ -151,17 +170,25 @@ mmac_status_t compress_call(mmac_dtype_t a_type, int64_t M, int64_t K, const voi
 
 extern "C" {
 
-mmac_status_t mmac_gemm_dense(mmac_dtype_t a_type, mmac_dtype_t b_type, int64_t M, int64_t N, int64_t K,
-                              double alpha, const void *A, int64_t lda, const void *B, int64_t ldb, double beta,
-                              const void *C, int64_t ldc, void *D, int64_t ldd, void *stream) {
-    const mmac_status_t st = check_gemm(a_type, b_type, M, N, K, alpha, A, lda, K, B, ldb, beta, C, ldc, D, ldd);
+mmac_status_t mmac_gemm_dense_ep(mmac_dtype_t a_type, mmac_dtype_t b_type, int64_t M, int64_t N, int64_t K,
+                                 double alpha, const void *A, int64_t lda, const void *B, int64_t ldb, double beta,
+                                 const void *C, int64_t ldc, void *D, int64_t ldd, const mmac_epilogue_t *ep_in,
+                                 void *stream) {
+    const mmac_epilogue_t ep = epilogue_of(ep_in);
+    const mmac_status_t st = check_gemm(a_type, b_type, M, N, K, alpha, A, lda, K, B, ldb, beta, C, ldc, D, ldd, ep);
     if (st != MMAC_OK) return st;
     if (M == 0 || N == 0) return MMAC_OK;
     const TileShape shape = pick_shape(M, N);
-    const GemmParams p = make_params(a_type, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd, shape);
+    const GemmParams p = make_params(a_type, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd, ep, shape);
     if (shape == TILE_SKINNY)
         return launched(launch_gemm_skinny(a_type, b_type, p, static_cast<hipStream_t>(stream)));
     return launched(launch_gemm_dense(a_type, b_type, shape, p, static_cast<hipStream_t>(stream)));
+}
+
+mmac_status_t mmac_gemm_dense(mmac_dtype_t a_type, mmac_dtype_t b_type, int64_t M, int64_t N, int64_t K,
+                              double alpha, const void *A, int64_t lda, const void *B, int64_t ldb, double beta,
+                              const void *C, int64_t ldc, void *D, int64_t ldd, void *stream) {
+    return mmac_gemm_dense_ep(a_type, b_type, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd, nullptr, stream);
 }
 
 mmac_status_t mmac_sparse24_compress(mmac_dtype_t a_type, int64_t M, int64_t K, const void *A, int64_t lda,
@@ -176,22 +203,32 @@ mmac_status_t mmac_sparse24_prune_compress(mmac_dtype_t a_type, int64_t M, int64
     return compress_call(a_type, M, K, A, lda, Ac, ldac, idx, ldidx, bad_groups, true, stream);
 }
 
-mmac_status_t mmac_gemm_sparse24(mmac_dtype_t a_type, mmac_dtype_t b_type, int64_t M, int64_t N, int64_t K,
-                                 double alpha, const void *Ac, int64_t ldac, const uint32_t *idx, int64_t ldidx,
-                                 const void *B, int64_t ldb, double beta, const void *C, int64_t ldc, void *D,
-                                 int64_t ldd, void *stream) {
+mmac_status_t mmac_gemm_sparse24_ep(mmac_dtype_t a_type, mmac_dtype_t b_type, int64_t M, int64_t N, int64_t K,
+                                    double alpha, const void *Ac, int64_t ldac, const uint32_t *idx, int64_t ldidx,
+                                    const void *B, int64_t ldb, double beta, const void *C, int64_t ldc, void *D,
+                                    int64_t ldd, const mmac_epilogue_t *ep_in, void *stream) {
+    const mmac_epilogue_t ep = epilogue_of(ep_in);
     if (K >= 0 && (K % 4) != 0) return MMAC_ERR_INVALID_ARG;
-    const mmac_status_t st = check_gemm(a_type, b_type, M, N, K, alpha, Ac, ldac, K / 2, B, ldb, beta, C, ldc, D, ldd);
+    const mmac_status_t st =
+        check_gemm(a_type, b_type, M, N, K, alpha, Ac, ldac, K / 2, B, ldb, beta, C, ldc, D, ldd, ep);
     if (st != MMAC_OK) return st;
     if ((K > 0 && !idx) || ldidx < (K + 31) / 32 || ldidx < 1) return MMAC_ERR_INVALID_ARG;
     if (ldidx * 4 * 256 > ((int64_t)1 << 31)) return MMAC_ERR_UNSUPPORTED;
     if (!aligned4(idx)) return MMAC_ERR_MISALIGNED;
     if (M == 0 || N == 0) return MMAC_OK;
     const TileShape shape = pick_shape(M, N, true);
-    GemmParams p = make_params(a_type, M, N, K, alpha, Ac, ldac, B, ldb, beta, C, ldc, D, ldd, shape);
+    GemmParams p = make_params(a_type, M, N, K, alpha, Ac, ldac, B, ldb, beta, C, ldc, D, ldd, ep, shape);
     p.idx = idx;
     p.idx_pitch = ldidx;
     return launched(launch_gemm_sparse(a_type, b_type, shape, p, static_cast<hipStream_t>(stream)));
+}
+
+mmac_status_t mmac_gemm_sparse24(mmac_dtype_t a_type, mmac_dtype_t b_type, int64_t M, int64_t N, int64_t K,
+                                 double alpha, const void *Ac, int64_t ldac, const uint32_t *idx, int64_t ldidx,
+                                 const void *B, int64_t ldb, double beta, const void *C, int64_t ldc, void *D,
+                                 int64_t ldd, void *stream) {
+    return mmac_gemm_sparse24_ep(a_type, b_type, M, N, K, alpha, Ac, ldac, idx, ldidx, B, ldb, beta, C, ldc, D, ldd,
+                                 nullptr, stream);
 }
 
 const char *mmac_status_string(mmac_status_t s) {

@@ -51,6 +51,62 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufferWord3);
 }
 
+// ---- output conversions --------------------------------------------------
+// Element types of C and D besides the accumulator type (float / int32).
+enum : int { OUT_ACC = 0, OUT_BF16 = 1, OUT_F16 = 2 };
+
+// fp32 -> bfloat16 bits: round to nearest, ties to even; a finite value whose
+// rounding would leave the finite range gives the largest finite value of its
+// sign (saturation); infinities stay infinite; NaN gives the quiet NaN 0x7fc0
+// with the sign kept.  bfloat16 is the top half of an fp32, so rounding the
+// low 16 bits away (with the carry into the exponent) is the whole conversion,
+// subnormals included.
+__device__ __forceinline__ uint32_t to_bf16_sat(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v), s = (u >> 16) & 0x8000u, a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return s | 0x7fc0u;
+    if (a == 0x7f800000u) return s | 0x7f80u;
+    const uint32_t h = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    return (h & 0x7fffu) == 0x7f80u ? (s | 0x7f7fu) : h;
+}
+
+// fp32 -> IEEE binary16 bits with the same rules (largest finite 65504; the
+// quiet NaN is 0x7e00).  Normal results: move the exponent from bias 127 to
+// bias 15 and round the 13 dropped significand bits to nearest even (a carry
+// moves into the exponent, as it should).  Subnormal results (|v| < 2^-14):
+// the quantum is 2^-24, so |v| * 2^24 (exact) rounded to the nearest integer,
+// ties to even, is the significand field; 1024 there is the smallest normal.
+__device__ __forceinline__ uint32_t to_f16_sat(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v), s = (u >> 16) & 0x8000u, a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return s | 0x7e00u;
+    if (a == 0x7f800000u) return s | 0x7c00u;
+    if (a >= 0x477ff000u) return s | 0x7bffu;          // |v| >= 65520 rounds past 65504
+    if (a >= 0x38800000u) {                              // |v| >= 2^-14
+        const uint32_t m = a - 0x38000000u;
+        return s | ((m + 0xfffu + ((m >> 13) & 1u)) >> 13);
+    }
+    return s | (uint32_t)__builtin_rintf(__builtin_bit_cast(float, a) * 16777216.0f);
+}
+
+// Stored C element (bits) -> fp32, exact for both 16-bit types.
+template <int OT>
+__device__ __forceinline__ float from_out_bits(uint32_t h) {
+    if constexpr (OT == OUT_BF16) return __builtin_bit_cast(float, h << 16);
+    else if constexpr (OT == OUT_F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+    else return __builtin_bit_cast(float, h);
+}
+
+// The end of every floating epilogue: v = alpha * acc + beta * C already
+// formed in fp32; add the column's bias (when there is one), apply ReLU (when
+// asked: negative values become +0, NaN and -0 pass), and round to D's type.
+template <int OT>
+__device__ __forceinline__ uint32_t finish(float v, float bias, bool has_bias, bool relu) {
+    if (has_bias) v += bias;
+    if (relu) v = v < 0.0f ? 0.0f : v;
+    if constexpr (OT == OUT_BF16) return to_bf16_sat(v);
+    else if constexpr (OT == OUT_F16) return to_f16_sat(v);
+    else return __builtin_bit_cast(uint32_t, v);
+}
+
 // LDS tiles are stored in 16-byte units, W units per row (row-major).  The
 // LDS of gfx950 serves 16 lanes' 16-byte reads per cycle from 64 banks (256
 // bytes); the fragment reads of the kernels have 16 consecutive lanes read

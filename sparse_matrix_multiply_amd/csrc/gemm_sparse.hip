@@ -1,33 +1,21 @@
-// Sparse (4:2 A) GEMM instantiations: fp16, bf16, int8 and the four fp8/bf8 pairs.
-// Three LDS stages of 128-byte B rows: the sparse kernel moves 1.5x the bytes per
-// unit of matrix work of the dense one, and whole 128-byte rows per copy
-// request measured faster than more, narrower stages.
-#include "gemm_tiled.h"
+// Sparse GEMM: dispatch on the element-type pair to the instantiations under inst/.
+#include "device.h"
+#include "launch.h"
 
 namespace mmac {
 
+// Defined in tiles_sparse.h, instantiated once per type pair under inst/.
 template <class Op>
-static hipError_t launch_shape(TileShape shape, const GemmParams &p, hipStream_t s) {
-    const dim3 grid(p.tiles_m * p.tiles_n), block(256);
-    switch (shape) {
-    case TILE_256: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 256, 256, 2, 4, 3>), grid, dim3(512), 0, s, p); break;
-    case TILE_256x128: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 256, 128, 2, 2, 4>), grid, block, 0, s, p); break;
-    case TILE_128x256: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 128, 256, 2, 2, 3>), grid, block, 0, s, p); break;
-    case TILE_128: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 128, 128, 2, 2, 3>), grid, block, 0, s, p); break;
-    case TILE_64: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 64, 64, 2, 2, 3>), grid, block, 0, s, p); break;
-    default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
+hipError_t launch_sparse_op(TileShape shape, const GemmParams &p, hipStream_t s);
 
 hipError_t launch_gemm_sparse(int a, int b, TileShape shape, GemmParams p, hipStream_t s) {
-    if (a == DT_F16 && b == DT_F16) return launch_shape<MmaSparse16<DT_F16>>(shape, p, s);
-    if (a == DT_BF16 && b == DT_BF16) return launch_shape<MmaSparse16<DT_BF16>>(shape, p, s);
-    if (a == DT_I8 && b == DT_I8) return launch_shape<MmaSparse8<DT_I8, DT_I8>>(shape, p, s);
-    if (a == DT_E4M3 && b == DT_E4M3) return launch_shape<MmaSparse8<DT_E4M3, DT_E4M3>>(shape, p, s);
-    if (a == DT_E4M3 && b == DT_E5M2) return launch_shape<MmaSparse8<DT_E4M3, DT_E5M2>>(shape, p, s);
-    if (a == DT_E5M2 && b == DT_E4M3) return launch_shape<MmaSparse8<DT_E5M2, DT_E4M3>>(shape, p, s);
-    if (a == DT_E5M2 && b == DT_E5M2) return launch_shape<MmaSparse8<DT_E5M2, DT_E5M2>>(shape, p, s);
+    if (a == DT_F16 && b == DT_F16) return launch_sparse_op<MmaSparse16<DT_F16>>(shape, p, s);
+    if (a == DT_BF16 && b == DT_BF16) return launch_sparse_op<MmaSparse16<DT_BF16>>(shape, p, s);
+    if (a == DT_I8 && b == DT_I8) return launch_sparse_op<MmaSparse8<DT_I8, DT_I8>>(shape, p, s);
+    if (a == DT_E4M3 && b == DT_E4M3) return launch_sparse_op<MmaSparse8<DT_E4M3, DT_E4M3>>(shape, p, s);
+    if (a == DT_E4M3 && b == DT_E5M2) return launch_sparse_op<MmaSparse8<DT_E4M3, DT_E5M2>>(shape, p, s);
+    if (a == DT_E5M2 && b == DT_E4M3) return launch_sparse_op<MmaSparse8<DT_E5M2, DT_E4M3>>(shape, p, s);
+    if (a == DT_E5M2 && b == DT_E5M2) return launch_sparse_op<MmaSparse8<DT_E5M2, DT_E5M2>>(shape, p, s);
     return hipErrorInvalidValue;
 }
 

@@ -378,7 +378,8 @@ struct TiledGemm {
         }
     }
 
-    // D = alpha * acc + beta * C.  Element (i, j) of a 32 x 32 instruction tile
+    // D = alpha * acc + beta * C, then (floating inputs) the column bias, ReLU
+    // and rounding to D's type.  Element (i, j) of a 32 x 32 instruction tile
     // is register G of lane L with i = 8*floor(G/4) + 4*floor(L/32) + (G mod 4),
     // j = L mod 32, so for each register lanes 0-31 and 32-63 each cover 32
     // consecutive elements of a row.  C and D are accessed with buffer
@@ -387,31 +388,78 @@ struct TiledGemm {
     // dropped, so there are no branches and all loads of a row of instruction
     // tiles are in flight together.
     __device__ __forceinline__ void epilogue(uint8_t *smem) {
+        if constexpr (std::is_same<out_t, float>::value) {
+            if (p.d_type == OUT_BF16) return epilogue_as<OUT_BF16>(smem);
+            if (p.d_type == OUT_F16) return epilogue_as<OUT_F16>(smem);
+        }
+        epilogue_as<OUT_ACC>(smem);
+    }
+
+    template <int OT>
+    __device__ __forceinline__ void epilogue_as(uint8_t *smem) {
+        constexpr int ES = OT == OUT_ACC ? 4 : 2;
         const int rows = min(BM, p.M - row0);
-        const rsrc_t rd = make_rsrc(reinterpret_cast<out_t *>(p.D) + (int64_t)row0 * p.ldd,
-                                    (uint32_t)(rows * p.ldd * sizeof(out_t)));
+        const rsrc_t rd = make_rsrc(static_cast<uint8_t *>(p.D) + (int64_t)row0 * p.ldd * ES,
+                                    (uint32_t)(rows * p.ldd * ES));
+        float bias[TN];   // this lane's column of each instruction-tile column
+        const bool has_bias = std::is_same<out_t, float>::value && p.bias != nullptr;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bias[j] = 0.0f;
+        if (has_bias) {
+            const rsrc_t rb = make_rsrc(p.bias + col0, (uint32_t)(min(BN, p.N - col0) * 4));
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int c = wn * WTN + j * 32 + l32;   // column within the block tile
+                bias[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                        rb, col0 + c < p.N ? (uint32_t)c * 4 : kOutOfRange, 0, 0));
+            }
+        }
         if (p.use_c && !p.fold_c) {
-            const rsrc_t rc = make_rsrc(reinterpret_cast<const out_t *>(p.C) + (int64_t)row0 * p.ldc,
-                                        (uint32_t)(rows * p.ldc * sizeof(out_t)));
-            store_tiles<true>(rd, rc);
+            const rsrc_t rc = make_rsrc(static_cast<const uint8_t *>(p.C) + (int64_t)row0 * p.ldc * ES,
+                                        (uint32_t)(rows * p.ldc * ES));
+            store_tiles<true, OT>(rd, rc, bias, has_bias);
         } else if (p.vec_d) {
-            store_tiles_lds(rd, smem);
+            store_tiles_lds<OT>(rd, smem, bias, has_bias);
         } else {
-            store_tiles<false>(rd, rd);
+            store_tiles<false, OT>(rd, rd, bias, has_bias);
+        }
+    }
+
+    // One output element's bits from its accumulator value and (USE_C) the
+    // stored bits of its C element.
+    template <bool USE_C, int OT, class A>
+    __device__ __forceinline__ uint32_t out_bits(A a, uint32_t c, float bias, bool has_bias) const {
+        if constexpr (std::is_same<out_t, float>::value) {
+            float v = p.alpha * a;
+            if constexpr (USE_C) v = fmaf(p.beta, from_out_bits<OT>(c), v);
+            return finish<OT>(v, bias, has_bias, p.act != 0);
+        } else {
+            uint32_t v = (uint32_t)p.ialpha * (uint32_t)a;
+            if constexpr (USE_C) v += (uint32_t)p.ibeta * c;
+            return v;
         }
     }
 
     // The epilogue through LDS (free once the last k-tile is done: no copy is
     // in flight and no remaining read matters), so that D goes out with
-    // 16-byte stores, each instruction writing 8 whole 128-byte row segments
-    // instead of 2.  Each wave stages up to EPI_TILES of its 32 x 32 instruction
-    // tiles at a time in its own 4 KiB-per-tile region (no other wave touches
-    // it, so no barrier): lanes write their 16 registers in the accumulator
-    // layout, then read back row-contiguous 16-byte chunks (lane L: row
-    // 8q + L / 8 of the tile, chunk L mod 8).  Row r of a tile sits at row
-    // slot r ^ ((r >> 2) & 1): rows r and r + 4, written by the two lane halves
-    // together, then fall in opposite halves of the 64 banks, and so do the two
-    // rows of each 16-lane read.
+    // 16-byte stores, each instruction writing whole row segments of 128 bytes
+    // (fp32 / int32 D: 8 per instruction) or 64 bytes (16-bit D: 16) instead
+    // of 2 segments of 32 elements.  Each wave stages up to EPI_TILES of its
+    // 32 x 32 instruction tiles at a time in its own 4 KiB-per-tile region (no
+    // other wave touches it, so no barrier): lanes write their 16 registers in
+    // the accumulator layout, then read back row-contiguous 16-byte chunks.
+    //   32-bit D: 128-byte rows; lane L reads row 8q + L / 8 of the tile,
+    //   chunk L mod 8.  Row r sits at row slot r ^ ((r >> 2) & 1): rows r and
+    //   r + 4, written by the two lane halves together, then fall in opposite
+    //   halves of the 64 banks, and so do the two rows of each 16-lane read.
+    //   16-bit D: 64-byte rows.  For each pair of registers (rows r, r + 1 of
+    //   the lane's column) neighbouring lanes swap one value (DPP quad_perm
+    //   1,0,3,2): the even lane then writes the word of columns (L, L + 1) of
+    //   row r, the odd lane that of row r + 1, so the writes are whole words.
+    //   Row r sits at slot r ^ (2 * ((r >> 2) & 1)), which keeps the 64 lanes'
+    //   words (rows r, r+1 from one lane half, r+4, r+5 from the other) and each
+    //   16-lane read (four rows) on distinct banks; lane L reads row
+    //   16q + L / 4, chunk L mod 4.
     static constexpr int epi_tiles() {   // most instruction tiles per pass: fits and divides TM * TN
         int t = TM * TN;
         while (t > 1 && (t * 4096 * NW > LDS_BYTES || (TM * TN) % t != 0)) --t;
@@ -420,22 +468,40 @@ struct TiledGemm {
     static constexpr int EPI_TILES = epi_tiles();
     static_assert(EPI_TILES * 4096 * NW <= LDS_BYTES, "epilogue staging space");
 
-    __device__ __forceinline__ void store_tiles_lds(rsrc_t rd, uint8_t *smem) {
+    template <int OT>
+    __device__ __forceinline__ void store_tiles_lds(rsrc_t rd, uint8_t *smem, const float *bias, bool has_bias) {
+        constexpr int ES = OT == OUT_ACC ? 4 : 2;
+        constexpr int RB = 32 * ES;            // bytes of a staged row
+        constexpr int CPR = RB / 16;           // 16-byte chunks per row
+        constexpr int RPR = 64 / CPR;          // rows per read instruction
         uint8_t *region = smem + wave * EPI_TILES * 4096;
+        const bool odd = lane & 1;
 #pragma unroll
         for (int t0 = 0; t0 < TM * TN; t0 += EPI_TILES) {
 #pragma unroll
             for (int t = 0; t < EPI_TILES; ++t) {
                 const int i = (t0 + t) / TN, j = (t0 + t) % TN;
                 uint8_t *base = region + t * 4096;
+                if constexpr (ES == 4) {
 #pragma unroll
-                for (int G = 0; G < 16; ++G) {
-                    const int r = 8 * (G / 4) + 4 * g + (G % 4);
-                    const int slot = r ^ ((r >> 2) & 1);
-                    uint32_t bits;
-                    if constexpr (std::is_same<out_t, float>::value) bits = __builtin_bit_cast(uint32_t, p.alpha * acc[i][j][G]);
-                    else bits = (uint32_t)p.ialpha * (uint32_t)acc[i][j][G];
-                    *reinterpret_cast<uint32_t *>(base + slot * 128 + l32 * 4) = bits;
+                    for (int G = 0; G < 16; ++G) {
+                        const int r = 8 * (G / 4) + 4 * g + (G % 4);
+                        const int slot = r ^ ((r >> 2) & 1);
+                        *reinterpret_cast<uint32_t *>(base + slot * RB + l32 * 4) =
+                            out_bits<false, OT>(acc[i][j][G], 0u, bias[j], has_bias);
+                    }
+                } else {
+#pragma unroll
+                    for (int G = 0; G < 16; G += 2) {
+                        const uint32_t h0 = out_bits<false, OT>(acc[i][j][G], 0u, bias[j], has_bias);
+                        const uint32_t h1 = out_bits<false, OT>(acc[i][j][G + 1], 0u, bias[j], has_bias);
+                        const uint32_t recv =
+                            (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(odd ? h0 : h1), 0xB1, 0xF, 0xF, false);
+                        const uint32_t word = odd ? (recv | (h1 << 16)) : (h0 | (recv << 16));
+                        const int r = 8 * (G / 4) + 4 * g + (G % 4) + (odd ? 1 : 0);
+                        const int slot = r ^ (((r >> 2) & 1) << 1);
+                        *reinterpret_cast<uint32_t *>(base + slot * RB + (l32 >> 1) * 4) = word;
+                    }
                 }
             }
             __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's staging writes are done
@@ -445,22 +511,27 @@ struct TiledGemm {
                 const int i = (t0 + t) / TN, j = (t0 + t) % TN;
                 const uint8_t *base = region + t * 4096;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int r = 8 * q + lane / 8, c = lane % 8;
-                    const int slot = r ^ ((r >> 2) & 1);
-                    const i32x4 v = *reinterpret_cast<const i32x4 *>(base + slot * 128 + c * 16);
-                    const int tr = wm * WTM + i * 32 + r;                    // row within the block tile
-                    const int col = col0 + wn * WTN + j * 32 + 4 * c;       // first of the 4 columns
+                for (int q = 0; q < 32 / RPR; ++q) {
+                    const int r = RPR * q + lane / CPR, c = lane % CPR;
+                    const int slot = ES == 4 ? r ^ ((r >> 2) & 1) : r ^ (((r >> 2) & 1) << 1);
+                    const i32x4 v = *reinterpret_cast<const i32x4 *>(base + slot * RB + c * 16);
+                    constexpr int PER = 16 / ES;                                  // elements per chunk
+                    const int tr = wm * WTM + i * 32 + r;                         // row within the block tile
+                    const int col = col0 + wn * WTN + j * 32 + PER * c;          // first of the chunk's columns
                     const bool rin = row0 + tr < p.M;
-                    const uint32_t o = (uint32_t)((tr * p.ldd + col) * sizeof(out_t));
-                    if (col + 3 < p.N) {
+                    const uint32_t o = (uint32_t)((tr * p.ldd + col) * ES);
+                    if (col + PER - 1 < p.N) {
                         __builtin_amdgcn_raw_buffer_store_b128(v, rd, rin ? o : kOutOfRange, 0, kNonTemporal);
                     } else {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            __builtin_amdgcn_raw_buffer_store_b32((uint32_t)v[e], rd,
-                                                                  rin && col + e < p.N ? o + 4 * e : kOutOfRange, 0,
-                                                                  kNonTemporal);
+                        for (int e = 0; e < PER; ++e) {
+                            const uint32_t oe = rin && col + e < p.N ? o + ES * e : kOutOfRange;
+                            if constexpr (ES == 4)
+                                __builtin_amdgcn_raw_buffer_store_b32((uint32_t)v[e], rd, oe, 0, kNonTemporal);
+                            else
+                                __builtin_amdgcn_raw_buffer_store_b16(
+                                    (unsigned short)((uint32_t)v[e / 2] >> (16 * (e % 2))), rd, oe, 0, kNonTemporal);
+                        }
                     }
                 }
             }
@@ -473,9 +544,19 @@ struct TiledGemm {
     // branch-free buffer accesses as the epilogue.  Called right after the first
     // copies are issued, so the two latencies overlap.
     __device__ __forceinline__ void load_c_into_acc() {
+        if constexpr (std::is_same<out_t, float>::value) {
+            if (p.d_type == OUT_BF16) return load_c_as<OUT_BF16>();
+            if (p.d_type == OUT_F16) return load_c_as<OUT_F16>();
+        }
+        load_c_as<OUT_ACC>();
+    }
+
+    template <int OT>
+    __device__ __forceinline__ void load_c_as() {
+        constexpr int ES = OT == OUT_ACC ? 4 : 2;
         const int rows = min(BM, p.M - row0);
-        const rsrc_t rc = make_rsrc(reinterpret_cast<const out_t *>(p.C) + (int64_t)row0 * p.ldc,
-                                    (uint32_t)(rows * p.ldc * sizeof(out_t)));
+        const rsrc_t rc = make_rsrc(static_cast<const uint8_t *>(p.C) + (int64_t)row0 * p.ldc * ES,
+                                    (uint32_t)(rows * p.ldc * ES));
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -485,10 +566,11 @@ struct TiledGemm {
                 for (int G = 0; G < 16; ++G) {
                     const int r = wm * WTM + i * 32 + 8 * (G / 4) + 4 * g + (G % 4);
                     const bool in = (row0 + r < p.M) && (col < p.N);
-                    const uint32_t oc = in ? (uint32_t)((r * p.ldc + col) * sizeof(out_t)) : kOutOfRange;
-                    const uint32_t c = __builtin_amdgcn_raw_buffer_load_b32(rc, oc, 0, kNonTemporal);
+                    const uint32_t oc = in ? (uint32_t)((r * p.ldc + col) * ES) : kOutOfRange;
+                    const uint32_t c = ES == 4 ? __builtin_amdgcn_raw_buffer_load_b32(rc, oc, 0, kNonTemporal)
+                                               : __builtin_amdgcn_raw_buffer_load_b16(rc, oc, 0, kNonTemporal);
                     if constexpr (std::is_same<out_t, float>::value)
-                        acc[i][j][G] = p.c_scale * __builtin_bit_cast(float, c);
+                        acc[i][j][G] = p.c_scale * from_out_bits<OT>(c);
                     else
                         acc[i][j][G] = (int32_t)((uint32_t)p.ibeta * c);
                 }
@@ -497,8 +579,9 @@ struct TiledGemm {
         }
     }
 
-    template <bool USE_C>
-    __device__ __forceinline__ void store_tiles(rsrc_t rd, rsrc_t rc) {
+    template <bool USE_C, int OT>
+    __device__ __forceinline__ void store_tiles(rsrc_t rd, rsrc_t rc, const float *bias, bool has_bias) {
+        constexpr int ES = OT == OUT_ACC ? 4 : 2;
         constexpr int JB = TN < 2 ? TN : 2;             // instruction tiles per batch of loads
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
@@ -513,10 +596,12 @@ struct TiledGemm {
                     for (int G = 0; G < 16; ++G) {
                         const int r = wm * WTM + i * 32 + 8 * (G / 4) + 4 * g + (G % 4);   // row within the tile
                         const bool in = (row0 + r < p.M) && (col < p.N);
-                        od[jj][G] = in ? (uint32_t)((r * p.ldd + col) * sizeof(out_t)) : kOutOfRange;
+                        od[jj][G] = in ? (uint32_t)((r * p.ldd + col) * ES) : kOutOfRange;
+                        c[jj][G] = 0;
                         if constexpr (USE_C) {
-                            const uint32_t oc = in ? (uint32_t)((r * p.ldc + col) * sizeof(out_t)) : kOutOfRange;
-                            c[jj][G] = __builtin_amdgcn_raw_buffer_load_b32(rc, oc, 0, kNonTemporal);
+                            const uint32_t oc = in ? (uint32_t)((r * p.ldc + col) * ES) : kOutOfRange;
+                            c[jj][G] = ES == 4 ? __builtin_amdgcn_raw_buffer_load_b32(rc, oc, 0, kNonTemporal)
+                                               : __builtin_amdgcn_raw_buffer_load_b16(rc, oc, 0, kNonTemporal);
                         }
                     }
                 }
@@ -524,17 +609,11 @@ struct TiledGemm {
                 for (int jj = 0; jj < JB; ++jj) {
 #pragma unroll
                     for (int G = 0; G < 16; ++G) {
-                        uint32_t bits;
-                        if constexpr (std::is_same<out_t, float>::value) {
-                            float v = p.alpha * acc[i][j0 + jj][G];
-                            if constexpr (USE_C) v = fmaf(p.beta, __builtin_bit_cast(float, c[jj][G]), v);
-                            bits = __builtin_bit_cast(uint32_t, v);
-                        } else {
-                            uint32_t v = (uint32_t)p.ialpha * (uint32_t)acc[i][j0 + jj][G];
-                            if constexpr (USE_C) v += (uint32_t)p.ibeta * c[jj][G];
-                            bits = v;
-                        }
-                        __builtin_amdgcn_raw_buffer_store_b32(bits, rd, od[jj][G], 0, kNonTemporal);
+                        const uint32_t bits = out_bits<USE_C, OT>(acc[i][j0 + jj][G], c[jj][G], bias[j0 + jj], has_bias);
+                        if constexpr (ES == 4)
+                            __builtin_amdgcn_raw_buffer_store_b32(bits, rd, od[jj][G], 0, kNonTemporal);
+                        else
+                            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bits, rd, od[jj][G], 0, kNonTemporal);
                     }
                 }
             }

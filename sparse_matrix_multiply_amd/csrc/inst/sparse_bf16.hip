@@ -1,0 +1,6 @@
+// Sparse GEMM kernels (every tile shape) for A x B = bfloat16 x bfloat16.
+#include "../tiles_sparse.h"
+
+namespace mmac {
+template hipError_t launch_sparse_op<MmaSparse16<DT_BF16>>(TileShape, const GemmParams &, hipStream_t);
+}  // namespace mmac

@@ -29,9 +29,15 @@ struct GemmParams {
     int fold_c;
     float c_scale;
     // vec_d: D starts on a 16-byte boundary and its row pitch is a multiple of
-    // 4 elements, so the epilogue may store 4 consecutive elements of a row
-    // with one 16-byte access.
+    // 16 bytes, so the epilogue may store 16 consecutive bytes of a row with
+    // one access.
     int vec_d;
+    // Epilogue variant (floating inputs only): d_type is OUT_ACC (C and D are
+    // fp32), OUT_BF16 or OUT_F16 (C and D are of that type); bias is NULL or
+    // N fp32 values added per column; act 1 applies ReLU.
+    int d_type;
+    int act;
+    const float *bias;
     int tiles_m, tiles_n, group_m;
 };
 

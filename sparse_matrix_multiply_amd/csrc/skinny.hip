@@ -114,14 +114,23 @@ __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(GemmParams p) {
     const int oln = o & 63, orr = (o >> 6) & 3, oc = (o >> 8) % CB, om = (o >> 8) / CB;
     const int orow = om * 16 + 4 * (oln >> 4) + orr, ocol = col0 + oc * 16 + (oln & 15);
     const bool oin = o < OUTS && orow < p.M && ocol < p.N;
-    const rsrc_t rd = make_rsrc(p.D, (uint32_t)(p.M * p.ldd * sizeof(out_t)));
-    const uint32_t od = oin ? (uint32_t)((orow * p.ldd + ocol) * sizeof(out_t)) : kOutOfRange;
+    constexpr bool kFloat = std::is_same<out_t, float>::value;
+    const int es = kFloat && p.d_type != OUT_ACC ? 2 : 4;   // bytes of a C / D element
+    const rsrc_t rd = make_rsrc(p.D, (uint32_t)(p.M * p.ldd * es));
+    const uint32_t od = oin ? (uint32_t)((orow * p.ldd + ocol) * es) : kOutOfRange;
     uint32_t cpre = 0;
     if (p.use_c) {
-        const rsrc_t rcc = make_rsrc(p.C, (uint32_t)(p.M * p.ldc * sizeof(out_t)));
-        cpre = __builtin_amdgcn_raw_buffer_load_b32(rcc, oin ? (uint32_t)((orow * p.ldc + ocol) * sizeof(out_t)) : kOutOfRange,
-                                                   0, 0);
+        const rsrc_t rcc = make_rsrc(p.C, (uint32_t)(p.M * p.ldc * es));
+        const uint32_t oc = oin ? (uint32_t)((orow * p.ldc + ocol) * es) : kOutOfRange;
+        cpre = es == 4 ? __builtin_amdgcn_raw_buffer_load_b32(rcc, oc, 0, 0)
+                       : __builtin_amdgcn_raw_buffer_load_b16(rcc, oc, 0, 0);
     }
+    const bool has_bias = kFloat && p.bias != nullptr;
+    float bias = 0.0f;
+    if (has_bias)
+        bias = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             make_rsrc(p.bias + col0, (uint32_t)(bcols * 4)),
+                                             oin ? (uint32_t)(ocol - col0) * 4 : kOutOfRange, 0, 0));
 
     // contiguous range of K steps for this wave
     const int nsteps = (p.K + KS - 1) / KS;
@@ -178,17 +187,27 @@ __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(GemmParams p) {
             if constexpr (std::is_same<out_t, float>::value) v += red[w][om][oc][orr][oln];
             else v = (out_t)((uint32_t)v + (uint32_t)red[w][om][oc][orr][oln]);
         }
-        uint32_t bits;
-        if constexpr (std::is_same<out_t, float>::value) {
+        if constexpr (kFloat) {
+            // alpha * acc + beta * C, then bias, ReLU and rounding to D's type
+            const bool relu = p.act != 0;
             float x = p.alpha * v;
-            if (p.use_c) x = fmaf(p.beta, __builtin_bit_cast(float, cpre), x);
-            bits = __builtin_bit_cast(uint32_t, x);
+            if (p.d_type == OUT_BF16) {
+                if (p.use_c) x = fmaf(p.beta, from_out_bits<OUT_BF16>(cpre), x);
+                __builtin_amdgcn_raw_buffer_store_b16((unsigned short)finish<OUT_BF16>(x, bias, has_bias, relu), rd,
+                                                      od, 0, 0);
+            } else if (p.d_type == OUT_F16) {
+                if (p.use_c) x = fmaf(p.beta, from_out_bits<OUT_F16>(cpre), x);
+                __builtin_amdgcn_raw_buffer_store_b16((unsigned short)finish<OUT_F16>(x, bias, has_bias, relu), rd,
+                                                      od, 0, 0);
+            } else {
+                if (p.use_c) x = fmaf(p.beta, __builtin_bit_cast(float, cpre), x);
+                __builtin_amdgcn_raw_buffer_store_b32(finish<OUT_ACC>(x, bias, has_bias, relu), rd, od, 0, 0);
+            }
         } else {
             uint32_t x = (uint32_t)p.ialpha * (uint32_t)v;
             if (p.use_c) x += (uint32_t)p.ibeta * cpre;
-            bits = x;
+            __builtin_amdgcn_raw_buffer_store_b32(x, rd, od, 0, 0);
         }
-        __builtin_amdgcn_raw_buffer_store_b32(bits, rd, od, 0, 0);
     }
 }
 

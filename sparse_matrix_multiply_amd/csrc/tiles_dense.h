@@ -1,0 +1,28 @@
+// Dense GEMM instantiations: bf16, fp16, int8 and the four OCP fp8/bf8 pairs.
+// LDS stages of 128-byte rows: two for 256 x 256 tiles (64 KiB each; the next
+// copy goes out right after the barrier that frees a stage), three for the
+// 256 x 128 halves, four for the smaller tiles.
+#pragma once
+
+#include "gemm_tiled.h"
+
+namespace mmac {
+
+// Kernels of one instruction class Op for every tile shape; each element-type
+// pair is instantiated in a source file of its own under inst/, so that the
+// build compiles them in parallel.
+template <class Op>
+hipError_t launch_dense_op(TileShape shape, const GemmParams &p, hipStream_t s) {
+    const dim3 grid(p.tiles_m * p.tiles_n), block(256);
+    switch (shape) {
+    case TILE_256: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 256, 256, 2, 4, 2>), grid, dim3(512), 0, s, p); break;
+    case TILE_256x128: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 256, 128, 2, 2, 3>), grid, block, 0, s, p); break;
+    case TILE_128x256: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 128, 256, 2, 2, 3>), grid, block, 0, s, p); break;
+    case TILE_128: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 128, 128, 2, 2, 4>), grid, block, 0, s, p); break;
+    case TILE_64: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 64, 64, 2, 2, 4>), grid, block, 0, s, p); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace mmac

@@ -32,7 +32,8 @@ def L():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["mmac_gemm_dense", "mmac_gemm_sparse24", "mmac_sparse24_compress",
+    assert declared_functions() == ["mmac_gemm_dense", "mmac_gemm_dense_ep", "mmac_gemm_sparse24",
+                                    "mmac_gemm_sparse24_ep", "mmac_sparse24_compress",
                                     "mmac_sparse24_prune_compress", "mmac_status_string"]
 
 
@@ -147,3 +148,54 @@ def test_compress_argument_errors(L, kw, code, entry):
 def test_compress_empty_is_a_no_op(L, entry):
     assert compress(L, entry, M=0) == mm.OK
     assert compress(L, entry, K=0, ldidx=1, lda=8, ldac=8) == mm.OK
+
+
+def dense_ep(L, ep, **kw):
+    a = dict(a=mm.BF16, b=mm.BF16, M=64, N=64, K=64, alpha=1.0, A=P, lda=64, B=P, ldb=64, beta=0.0,
+             C=None, ldc=64, D=P, ldd=64, stream=None)
+    a.update(kw)
+    return L.mmac_gemm_dense_ep(a["a"], a["b"], a["M"], a["N"], a["K"], a["alpha"], a["A"], a["lda"], a["B"],
+                                a["ldb"], a["beta"], a["C"], a["ldc"], a["D"], a["ldd"],
+                                None if ep is None else ctypes.byref(ep), a["stream"])
+
+
+def sparse_ep(L, ep, **kw):
+    a = dict(a=mm.F16, b=mm.F16, M=64, N=64, K=64, alpha=1.0, Ac=P, ldac=32, idx=P, ldidx=2, B=P, ldb=64,
+             beta=0.0, C=None, ldc=64, D=P, ldd=64, stream=None)
+    a.update(kw)
+    return L.mmac_gemm_sparse24_ep(a["a"], a["b"], a["M"], a["N"], a["K"], a["alpha"], a["Ac"], a["ldac"],
+                                   a["idx"], a["ldidx"], a["B"], a["ldb"], a["beta"], a["C"], a["ldc"], a["D"],
+                                   a["ldd"], None if ep is None else ctypes.byref(ep), a["stream"])
+
+
+EP_ERRORS = [
+    (dict(d_type=3), {}, mm.ERR_INVALID_ARG),
+    (dict(d_type=-1), {}, mm.ERR_INVALID_ARG),
+    (dict(act=2), {}, mm.ERR_INVALID_ARG),
+    (dict(bias=P + 2), {}, mm.ERR_MISALIGNED),
+    (dict(d_type=mm.OUT_BF16), dict(D=P + 1), mm.ERR_MISALIGNED),                 # 2-byte D, odd address
+    (dict(d_type=mm.OUT_F16), dict(beta=1.0, C=P + 4097), mm.ERR_MISALIGNED),
+    (dict(d_type=mm.OUT_F16), dict(ldd=(1 << 22) + 1, N=64), mm.ERR_UNSUPPORTED),  # > 8 MiB of binary16
+    (dict(d_type=mm.OUT_BF16), dict(a=mm.I8, b=mm.I8), mm.ERR_UNSUPPORTED),       # int8: plain output only
+    (dict(act=mm.ACT_RELU), dict(a=mm.I8, b=mm.I8), mm.ERR_UNSUPPORTED),
+    (dict(bias=P), dict(a=mm.I8, b=mm.I8), mm.ERR_UNSUPPORTED),
+    (dict(), dict(ldd=63), mm.ERR_INVALID_ARG),                                   # plain checks still apply
+]
+
+
+@pytest.mark.parametrize("epkw,kw,code", EP_ERRORS)
+def test_epilogue_argument_errors(L, epkw, kw, code):
+    ep = mm.Epilogue(epkw.get("d_type", mm.OUT_ACC), epkw.get("act", mm.ACT_NONE), epkw.get("bias"))
+    assert dense_ep(L, ep, **kw) == code
+    if kw.get("a") != mm.I8:
+        assert sparse_ep(L, ep, **kw) == code
+
+
+def test_epilogue_null_and_empty(L):
+    # NULL epilogue = the plain call (same checks); empty outputs are a no-op for every variant
+    assert dense_ep(L, None, ldd=63) == mm.ERR_INVALID_ARG
+    assert sparse_ep(L, None, K=66) == mm.ERR_INVALID_ARG
+    for d in (mm.OUT_ACC, mm.OUT_BF16, mm.OUT_F16):
+        ep = mm.Epilogue(d, mm.ACT_RELU, P)
+        assert dense_ep(L, ep, M=0) == mm.OK
+        assert sparse_ep(L, ep, N=0) == mm.OK

@@ -1,0 +1,274 @@
+"""GPU parity of the epilogue variants (mmac_gemm_dense_ep, mmac_gemm_sparse24_ep) against
+the oracle's epilogue: bfloat16 / binary16 C and D, a per-column fp32 bias, ReLU, and the
+saturating round-to-nearest-even conversion.
+
+Three kinds of check:
+  - conversion, bit for bit: with A*B = 0 the value before rounding is the bias itself, so
+    D must equal the oracle's rounding of every bias value; the bias runs over a million
+    random fp32 bit patterns plus ties, binade edges, subnormals, the saturation window,
+    infinities and NaN;
+  - whole products, bit for bit: small-integer inputs make every fp32 partial sum exact,
+    and power-of-two alpha / beta move the results across rounding ties, into binary16
+    subnormals and past the largest finite values, so the GPU and the oracle round the
+    same exact value;
+  - general inputs: the GPU forms alpha*acc + beta*C + bias in fp32, within the parity
+    tolerance of the exact value y; ReLU and rounding are monotone, so each output must
+    lie between the oracle's epilogue of y - delta and of y + delta.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_matrix_multiply_amd as mm
+import workloads as W
+from gpu_helpers import compress_dev, dev, tile_shape, to_dev_bits, tolerance
+from oracle import BF16, E4M3, E5M2, F16, I8
+
+pytestmark = pytest.mark.gpu
+
+FLOAT_PAIRS = [(BF16, BF16), (F16, F16), (E4M3, E4M3), (E4M3, E5M2), (E5M2, E4M3), (E5M2, E5M2)]
+OUTS = [(mm.OUT_BF16, torch.bfloat16, oracle.OUT_BF16), (mm.OUT_F16, torch.float16, oracle.OUT_F16)]
+
+
+def decode_out(bits, out):
+    """bfloat16 / binary16 bits -> float64 (exact)."""
+    b = np.ascontiguousarray(bits).view(np.uint16)
+    if out == oracle.OUT_BF16:
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return b.view(np.float16).astype(np.float64)
+
+
+def out_bits(D):
+    return D.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def c_tensor(C32, torch_dtype, ld=None):
+    """fp32 host C -> device tensor of D's type (values must be representable)."""
+    M, N = C32.shape
+    ld = N if ld is None else ld
+    buf = torch.zeros((M, ld), dtype=torch_dtype, device=dev())
+    buf[:, :N] = torch.from_numpy(C32).to(dev()).to(torch_dtype)
+    return buf[:, :N]
+
+
+def special_bias_values():
+    """fp32 values at the edges of both 16-bit formats (as float32)."""
+    v = []
+    # bfloat16: every tie and near-tie around a few binades, the saturation window, subnormals
+    for e in (-140, -133, -127, -126, -1, 0, 1, 7, 100, 126, 127):
+        for m in (0x0000, 0x0001, 0x7fff, 0x8000, 0x8001, 0xffff, 0x18000, 0x17fff):
+            v.append(np.uint32(((e + 127) & 0xff) << 23 if e > -127 else 0) | np.uint32(m & 0x7fffff))
+    v = list(np.array(v, np.uint32).view(np.float32))
+    f32max = np.float32(np.finfo(np.float32).max)
+    bfmax = np.float32(3.3895313892515355e38)
+    v += [bfmax, np.nextafter(bfmax, f32max), np.float32(3.3961775292304e38), np.float32(3.3961778e38), f32max]
+    # binary16: 65504, the tie at 65520 and its neighbours, the subnormal range and its ties
+    for x in (65504.0, 65519.0, 65519.99, 65520.0, 65521.0, 70000.0, 2.0 ** -14, 2.0 ** -15, 2.0 ** -24,
+              2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -26, 1.5 * 2.0 ** -24, 2.5 * 2.0 ** -24, 1023.5 * 2.0 ** -24,
+              1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 2049.0, 2051.0, 1.0e-8, 0.0):
+        v += [np.float32(x), np.float32(-x)]
+    v += [np.float32(np.inf), np.float32(-np.inf), np.float32(-0.0)]
+    return np.array(v, np.float32)
+
+
+def bias_values(n, seed):
+    g = np.random.default_rng(seed)
+    rnd = g.integers(0, 2 ** 32, size=n, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    rnd = rnd[np.isfinite(rnd)]
+    # values near 1: many land on or next to rounding ties of both formats
+    near = (np.float32(1.0) + g.integers(0, 2 ** 14, size=4096).astype(np.float32) * np.float32(2.0 ** -14))
+    b = np.concatenate([special_bias_values(), rnd, near, -near, np.array([np.nan], np.float32)])
+    return np.ascontiguousarray(b, np.float32)
+
+
+# skinny kernel; tiled kernel with 16-byte stores through LDS (padded pitch) and with
+# element stores (odd pitch)
+@pytest.mark.parametrize("M,pad", [(1, False), (40, True), (41, False)])
+@pytest.mark.parametrize("d_type,tdt,oout", OUTS)
+@pytest.mark.parametrize("act", [mm.ACT_NONE, mm.ACT_RELU])
+def test_conversion_of_every_bias_value(M, pad, d_type, tdt, oout, act):
+    """A = B = 0, beta = 0: D[i, j] = round(act(0 + bias[j])) for every row."""
+    b = bias_values(1 << 20, 11 + d_type)
+    N, K = b.size, 16
+    if not pad and N % 2 == 0:
+        b, N = b[:-1], N - 1
+    ld = (N + 7) // 8 * 8 if pad else N
+    A = torch.zeros((M, K), dtype=torch.bfloat16, device=dev())
+    B = torch.zeros((N, K), dtype=torch.bfloat16, device=dev())
+    D = torch.empty((M, ld), dtype=tdt, device=dev())[:, :N]
+    bias = torch.from_numpy(b).to(dev())
+    mm.gemm_dense(A, B, D, 1.0, 0.0, None, bias=bias, act=act)
+    torch.cuda.synchronize()
+    got = out_bits(D)
+    ref, _ = oracle.epilogue(np.zeros((1, N)), b, act, oout)
+    ref = ref[0]
+    nan_ref = np.isnan(decode_out(ref, oout))
+    for i in sorted({0, M - 1}):
+        row = got[i]
+        assert np.isnan(decode_out(row, oout))[nan_ref].all()
+        bad = np.flatnonzero((row != ref) & ~nan_ref)
+        assert bad.size == 0, (f"row {i}: {bad.size} mismatches, first bias values "
+                               f"{b[bad[:4]]!r} -> {row[bad[:4]]} vs {ref[bad[:4]]}")
+    assert (got == got[0]).all()
+
+
+def integer_problem(ta, tb, M, N, K, seed):
+    """|a|, |b| <= 4 and |K| <= 600: every partial sum is an integer below 2^24 (exact in fp32)."""
+    g = np.random.default_rng(seed)
+    A = W.to_bits(g.integers(-4, 5, size=(M, K)).astype(np.float64), ta)
+    B = W.to_bits(g.integers(-4, 5, size=(N, K)).astype(np.float64), tb)
+    C = g.integers(-64, 65, size=(M, N)).astype(np.float32)          # exact in both 16-bit formats
+    bias = g.integers(-300, 301, size=N).astype(np.float32)
+    return A, B, C, bias
+
+
+# (alpha, beta): power-of-two scalings keep every value exact in fp32; they move the results
+# across ties, into binary16 subnormals (2^-30), past 65504 (2^4) and to the top binades of
+# bfloat16 (2^113).  The bias is used only where value + bias stays exact in fp32.
+SCALES = [(1.0, 0.0), (1.0, 1.0), (0.5, -2.0), (2.0 ** -30, 2.0 ** -30), (16.0, 16.0), (2.0 ** 113, 2.0 ** 113)]
+
+
+def run_ep(sparse, ta, tb, A, B, Cdev, alpha, beta, bias_dev, act, tdt, ldd=None, D=None):
+    M, N, K = A.shape[0], B.shape[0], A.shape[1]
+    if D is None:
+        ld = N if ldd is None else ldd
+        D = torch.full((M, ld), float("nan"), dtype=tdt, device=dev())[:, :N]
+    Bd = to_dev_bits(B, tb)
+    if sparse:
+        Acd, idxd, _ = compress_dev(ta, to_dev_bits(A, ta), M, K, prune=True)
+        mm.gemm_sparse24(Acd, idxd, Bd, D, K=K, alpha=alpha, beta=beta, C=Cdev, a_type=ta, b_type=tb,
+                         bias=bias_dev, act=act)
+    else:
+        mm.gemm_dense(to_dev_bits(A, ta), Bd, D, alpha, beta, Cdev, a_type=ta, b_type=tb, bias=bias_dev, act=act)
+    torch.cuda.synchronize()
+    return D
+
+
+def oracle_y(sparse, ta, tb, A, B, alpha, beta, C):
+    """Exact alpha * A*B + beta * C (sparse: A pruned to 4:2 first) and the error scale S."""
+    if sparse:
+        Ac, idx, _ = oracle.prune_compress24(ta, A)
+        return oracle.gemm_sparse24(ta, tb, Ac, idx, B, alpha, beta, C)
+    return oracle.gemm_dense(ta, tb, A, B, alpha, beta, C)
+
+
+@pytest.mark.parametrize("sparse", [False, True])
+@pytest.mark.parametrize("ta,tb", FLOAT_PAIRS)
+@pytest.mark.parametrize("d_type,tdt,oout", OUTS)
+def test_integer_products_bit_exact(sparse, ta, tb, d_type, tdt, oout):
+    M, N, K = 200, 136, 520
+    A, B, C, bias = integer_problem(ta, tb, M, N, K, 3 * ta + tb + 17 * d_type + 101 * sparse)
+    bias_dev = torch.from_numpy(bias).to(dev())
+    Cdev = c_tensor(C, tdt)
+    for k, (alpha, beta) in enumerate(SCALES):
+        Y, _ = oracle_y(sparse, ta, tb, A, B, alpha, beta, C if beta else None)
+        for act in (mm.ACT_NONE, mm.ACT_RELU):
+            bias_k = None if k % 2 else bias_dev
+            tiles = (256, 64) if k == 0 else (256,)
+            for tile in tiles:
+                with tile_shape(tile):
+                    D = run_ep(sparse, ta, tb, A, B, Cdev if beta else None, alpha, beta, bias_k, act, tdt)
+                ref, _ = oracle.epilogue(Y, None if bias_k is None else bias, act, oout)
+                got = out_bits(D)
+                bad = np.argwhere(got != ref)
+                assert bad.size == 0, (f"alpha {alpha} beta {beta} act {act} bias {bias_k is not None} "
+                                       f"tile {tile}: {len(bad)} mismatches, first {bad[:3].tolist()}: "
+                                       f"{got[tuple(bad[0])]:#06x} vs {ref[tuple(bad[0])]:#06x}")
+
+
+def assert_bracketed(got_bits, Y, S, C, beta, alpha, bias, act, oout, t, K, what):
+    """Every output between the oracle's epilogue of y - delta and y + delta."""
+    delta = 4 * tolerance(t, K) * (abs(alpha) * S + (abs(beta) * np.abs(C) if C is not None else 0.0))
+    if bias is not None:
+        delta = delta + 2.0 ** -22 * np.abs(bias)[None, :]
+    lo, _ = oracle.epilogue(Y - delta, bias, act, oout)
+    hi, _ = oracle.epilogue(Y + delta, bias, act, oout)
+    g, l, h = decode_out(got_bits, oout), decode_out(lo, oout), decode_out(hi, oout)
+    ok = (l <= g) & (g <= h)
+    assert ok.all(), f"{what}: {np.count_nonzero(~ok)} outputs outside the bracket, first {np.argwhere(~ok)[:3]}"
+    # and most of them round exactly as the oracle does
+    ref, _ = oracle.epilogue(Y, bias, act, oout)
+    assert np.count_nonzero(got_bits == ref) >= 0.5 * got_bits.size, what
+
+
+SHAPES = [(64, 64, 64), (257, 130, 333), (33, 300, 1000), (300, 260, 128), (1, 1, 4), (20, 77, 256)]
+
+
+@pytest.mark.parametrize("sparse", [False, True])
+@pytest.mark.parametrize("ta,tb", [(BF16, BF16), (F16, F16), (E4M3, E5M2)])
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_general_inputs_bracketed(sparse, ta, tb, M, N, K):
+    if sparse and K % 4:
+        pytest.skip("sparse K is a multiple of 4")
+    g = np.random.default_rng(M * 5 + N + K + ta)
+    A = W.to_bits(g.standard_normal((M, K)), ta)
+    B = W.to_bits(g.standard_normal((N, K)), tb)
+    bias = g.standard_normal(N).astype(np.float32)
+    for d_type, tdt, oout in OUTS:
+        C = c_tensor(g.standard_normal((M, N)).astype(np.float32), tdt)
+        C32 = C.float().cpu().numpy()
+        for alpha, beta, act, with_bias in ((1.5, -0.75, mm.ACT_RELU, True), (1.0, 0.0, mm.ACT_NONE, False),
+                                            (0.0, 2.0, mm.ACT_RELU, True)):
+            Y, S = oracle_y(sparse, ta, tb, A, B, alpha, beta, C32 if beta else None)
+            D = run_ep(sparse, ta, tb, A, B, C if beta else None, alpha, beta,
+                       torch.from_numpy(bias).to(dev()) if with_bias else None, act, tdt)
+            assert_bracketed(out_bits(D), Y, S, C32 if beta else None, beta, alpha, bias if with_bias else None,
+                             act, oout, ta, K, f"{'sparse' if sparse else 'dense'} {M}x{N}x{K} out {d_type} "
+                             f"alpha {alpha} beta {beta}")
+
+
+@pytest.mark.parametrize("d_type,tdt,oout", OUTS)
+@pytest.mark.parametrize("ldd,first", [(136, 0), (130, 1), (141, 3), (136, 8)])
+@pytest.mark.parametrize("M", [20, 100])
+def test_pitch_offset_and_padding(d_type, tdt, oout, ldd, first, M):
+    """16-bit D with a padded pitch, starting at an element that is (or is not) 16-byte
+    aligned; the padding columns and the rows' other elements stay untouched."""
+    ta = tb = BF16
+    N, K = 129, 96
+    A, B, C, bias = integer_problem(ta, tb, M, N, K, 9 + ldd + first)
+    buf = torch.full((M, ldd + first), -7.0, dtype=tdt, device=dev())
+    D = buf[:, first:first + N]
+    Cdev = c_tensor(C, tdt, ld=ldd)
+    run_ep(False, ta, tb, A, B, Cdev, 1.0, 1.0, torch.from_numpy(bias).to(dev()), mm.ACT_RELU, tdt, D=D)
+    Y, _ = oracle.gemm_dense(ta, tb, A, B, 1.0, 1.0, C)
+    ref, _ = oracle.epilogue(Y, bias, mm.ACT_RELU, oout)
+    assert np.array_equal(out_bits(D), ref)
+    rest = buf.float().cpu().numpy()
+    rest[:, first:first + N] = -7.0
+    assert (rest == -7.0).all()
+
+
+@pytest.mark.parametrize("d_type,tdt,oout", OUTS)
+def test_in_place_c_equals_d_16bit(d_type, tdt, oout):
+    ta = tb = F16
+    M, N, K = 300, 200, 160
+    A, B, C, bias = integer_problem(ta, tb, M, N, K, 21)
+    D = c_tensor(C, tdt)
+    run_ep(False, ta, tb, A, B, D, 2.0, -1.0, torch.from_numpy(bias).to(dev()), mm.ACT_NONE, tdt, D=D)
+    Y, _ = oracle.gemm_dense(ta, tb, A, B, 2.0, -1.0, C)
+    ref, _ = oracle.epilogue(Y, bias, mm.ACT_NONE, oout)
+    assert np.array_equal(out_bits(D), ref)
+
+
+def test_fp32_output_with_bias_and_relu():
+    """The epilogue on fp32 D (MMAC_OUT_ACC): bias and ReLU on exact integer results."""
+    ta = tb = E4M3
+    M, N, K = 260, 300, 200
+    A, B, C, bias = integer_problem(ta, tb, M, N, K, 5)
+    for tile in (256, 128):
+        with tile_shape(tile):
+            D = run_ep(False, ta, tb, A, B, torch.from_numpy(C).to(dev()), 0.5, 2.0,
+                       torch.from_numpy(bias).to(dev()), mm.ACT_RELU, torch.float32)
+        Y, _ = oracle.gemm_dense(ta, tb, A, B, 0.5, 2.0, C)
+        ref, _ = oracle.epilogue(Y, bias, mm.ACT_RELU, oracle.OUT_F32)
+        assert np.array_equal(D.cpu().numpy(), ref)
+
+
+def test_int8_rejects_variants():
+    A = torch.zeros((64, 64), dtype=torch.int8, device=dev())
+    B = torch.zeros((64, 64), dtype=torch.int8, device=dev())
+    D = torch.zeros((64, 64), dtype=torch.int32, device=dev())
+    with pytest.raises(mm.MmacError):
+        mm.gemm_dense(A, B, D, act=mm.ACT_RELU)
+    assert I8 == mm.I8
