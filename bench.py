@@ -294,10 +294,10 @@ def suite():
 
     out = {}
 
-    def dense_case(name, key, reps=20, rotate=1, n_share=None, bf16_out=False):
+    def dense_case(name, key, reps=20, rotate=1, n_share=None, bf16_out=False, split=False):
         """n_share: keep only the first n_share columns of B, C and D (one GPU's share when N is
         split across GPUs).  bf16_out: the epilogue variant with bfloat16 C and D, a per-column
-        bias and ReLU."""
+        bias and ReLU.  split: the split-K call with the workspace the library asks for."""
         w = dict(W.workload(name))
         if n_share:
             w["B"], w["N"] = w["B"][:n_share], n_share
@@ -311,8 +311,9 @@ def suite():
         act = mm.ACT_RELU if bf16_out else mm.ACT_NONE
         Ds = [torch.empty((w["M"], w["N"]), dtype=odt, device=dev) for _ in range(rotate)]
         Bs = [B] + [B.clone() for _ in range(rotate - 1)]
+        ws = mm.workspace(w["ta"], w["M"], w["N"], w["K"], device=dev) if split else None
         fns = [lambda i=i: mm.gemm_dense(A, Bs[i], Ds[i], w["alpha"], w["beta"], C, a_type=w["ta"], b_type=w["tb"],
-                                         stream=stream, bias=bias, act=act) for i in range(rotate)]
+                                         stream=stream, bias=bias, act=act, workspace=ws) for i in range(rotate)]
         ms = median_ms(fns, reps)
         f = gemm_flops(w["M"], w["N"], w["K"])
         es = 2 if w["ta"] in (W.BF16, W.F16) else 1
@@ -324,6 +325,8 @@ def suite():
                     "beta": w["beta"]}
         if bf16_out:
             out[key]["epilogue"] = "bf16 C/D, bias, ReLU"
+        if split:
+            out[key]["workspace_MiB"] = round((0 if ws is None else ws.numel()) / 2 ** 20, 1)
         del A, B, Bs, C, Ds
         torch.cuda.empty_cache()
 
@@ -344,6 +347,8 @@ def suite():
     # one GPU's share of the 8192^3 GEMMs split 8 ways along N
     dense_case("bf16_8192", "share_bf16_8192x1024x8192_beta1", n_share=1024)
     dense_case("fp8_8192", "share_fp8e4m3xbf8e5m2_8192x1024x8192", n_share=1024)
+    dense_case("bf16_8192", "share_bf16_8192x1024x8192_beta1_splitk", n_share=1024, split=True)
+    dense_case("fp8_8192", "share_fp8e4m3xbf8e5m2_8192x1024x8192_splitk", n_share=1024, split=True)
     # epilogue variant: bfloat16 C and D with bias and ReLU (half the output bytes)
     dense_case("bf16_8192", "bf16_8192^3_beta1_bf16out_bias_relu", bf16_out=True)
     dense_case("fp8_8192", "fp8e4m3xbf8e5m2_8192^3_bf16out_bias_relu", bf16_out=True)
@@ -371,11 +376,18 @@ def suite():
         D = torch.empty((M, N), dtype=torch.float32, device=dev)
         gms = median_ms([lambda: mm.gemm_sparse24(Acs[0], idxs[0], B, D, K=K, a_type=ta, b_type=tb, stream=stream)], 20)
         f = gemm_flops(M, N, K)
+        ws = mm.workspace(ta, M, N, K, sparse=True, device=dev)
+        if ws is not None:
+            sms = median_ms([lambda: mm.gemm_sparse24(Acs[0], idxs[0], B, D, K=K, a_type=ta, b_type=tb, stream=stream,
+                                                      workspace=ws)], 20)
         out[key] = {"compress_us": round(cms * 1e3, 1), "compress_GB/s": round(cbytes / cms / 1e6, 1),
                     "prune_compress_us": round(pms * 1e3, 1), "prune_compress_GB/s": round(cbytes / pms / 1e6, 1),
                     "gemm_us": round(gms * 1e3, 1), "TFLOP/s_dense_equivalent": round(f / gms / 1e9, 1),
                     "TFLOP/s_effective": round(f / 2 / gms / 1e9, 1), "shape": [M, N, K]}
-        del As, Acs, idxs, B, D
+        if ws is not None:
+            out[key]["splitk_gemm_us"] = round(sms * 1e3, 1)
+            out[key]["splitk_TFLOP/s_dense_equivalent"] = round(f / sms / 1e9, 1)
+        del As, Acs, idxs, B, D, ws
         torch.cuda.empty_cache()
     print(json.dumps({"suite": out, "note": "median of repeated single launches (HIP events); skinny GEMM and "
                       "compressors rotate through copies larger than the 256 MB Infinity Cache"}), flush=True)

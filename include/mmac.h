@@ -220,6 +220,54 @@ mmac_status_t mmac_gemm_sparse24_ep(mmac_dtype_t a_type, mmac_dtype_t b_type,
                                     void *D, int64_t ldd,
                                     const mmac_epilogue_t *ep, void *stream);
 
+/*
+ * Split-K variants: the calls above, plus a caller-provided workspace that lets
+ * the library cut K into up to four ranges when the output has too few
+ * 256 x 256 tiles to occupy the GPU's 256 compute units (for example one
+ * GPU's 8192 x 1024 share of an 8192^3 product).  Each (tile, K range) is one
+ * workgroup; the range that finishes a tile last sums the fp32 (int32)
+ * partial tiles in range order 0, 1, 2, ... and applies the epilogue, so
+ * results are deterministic and independent of timing.
+ *   workspace        device memory, 16-byte aligned, or NULL.  Its first
+ *                    bytes hold one counter per output tile: they must be
+ *                    zero before the first call that uses the workspace, and
+ *                    every call leaves them zero again (zero it once after
+ *                    allocating it, e.g. with hipMemset).
+ *   workspace_bytes  its size.  If it is smaller than
+ *                    mmac_gemm_workspace_bytes(...) for the call (or
+ *                    workspace is NULL) the call runs unsplit, exactly as
+ *                    the _ep call.  A negative size is MMAC_ERR_INVALID_ARG;
+ *                    a misaligned workspace MMAC_ERR_MISALIGNED.
+ * Calls that share a workspace must not run concurrently (different streams)
+ * on the same device; calls in one stream may share it.  Results of a split
+ * call differ from the unsplit call only by floating-point summation order
+ * (int8: not at all).  MMAC_SPLITK=<S> in the environment forces S ranges
+ * (if the workspace holds them).
+ */
+mmac_status_t mmac_gemm_dense_ws(mmac_dtype_t a_type, mmac_dtype_t b_type,
+                                 int64_t M, int64_t N, int64_t K, double alpha,
+                                 const void *A, int64_t lda,
+                                 const void *B, int64_t ldb,
+                                 double beta, const void *C, int64_t ldc,
+                                 void *D, int64_t ldd, const mmac_epilogue_t *ep,
+                                 void *workspace, int64_t workspace_bytes, void *stream);
+
+mmac_status_t mmac_gemm_sparse24_ws(mmac_dtype_t a_type, mmac_dtype_t b_type,
+                                    int64_t M, int64_t N, int64_t K, double alpha,
+                                    const void *Ac, int64_t ldac,
+                                    const uint32_t *idx, int64_t ldidx,
+                                    const void *B, int64_t ldb,
+                                    double beta, const void *C, int64_t ldc,
+                                    void *D, int64_t ldd, const mmac_epilogue_t *ep,
+                                    void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * Workspace bytes the _ws calls use for an M x N x K product with A of type
+ * a_type (sparse != 0: mmac_gemm_sparse24_ws), under the current environment;
+ * 0 when they would not split.  Host-only, no GPU work.
+ */
+int64_t mmac_gemm_workspace_bytes(mmac_dtype_t a_type, int64_t M, int64_t N, int64_t K, int sparse);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *mmac_status_string(mmac_status_t s);
 

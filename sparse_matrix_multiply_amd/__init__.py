@@ -71,6 +71,14 @@ def lib():
         L.mmac_gemm_sparse24_ep.restype = i32
         L.mmac_gemm_sparse24_ep.argtypes = [i32, i32, i64, i64, i64, dbl, vp, i64, vp, i64, vp, i64, dbl, vp, i64,
                                             vp, i64, ep, vp]
+        L.mmac_gemm_dense_ws.restype = i32
+        L.mmac_gemm_dense_ws.argtypes = [i32, i32, i64, i64, i64, dbl, vp, i64, vp, i64, dbl, vp, i64, vp, i64, ep,
+                                         vp, i64, vp]
+        L.mmac_gemm_sparse24_ws.restype = i32
+        L.mmac_gemm_sparse24_ws.argtypes = [i32, i32, i64, i64, i64, dbl, vp, i64, vp, i64, vp, i64, dbl, vp, i64,
+                                            vp, i64, ep, vp, i64, vp]
+        L.mmac_gemm_workspace_bytes.restype = i64
+        L.mmac_gemm_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
         L.mmac_status_string.restype = ctypes.c_char_p
         L.mmac_status_string.argtypes = [i32]
         _lib = L
@@ -115,18 +123,36 @@ def _epilogue(D, bias, act, d_type):
     return Epilogue(d_type, act, None if bias is None else bias.data_ptr())
 
 
+def workspace_bytes(a_type, M, N, K, sparse=False):
+    """Bytes of workspace the split-K calls use for this product (0: they would not split)."""
+    return int(lib().mmac_gemm_workspace_bytes(int(a_type), M, N, K, 1 if sparse else 0))
+
+
+def workspace(a_type, M, N, K, sparse=False, device=None):
+    """A zeroed workspace tensor for the split-K calls (None if they would not split)."""
+    n = workspace_bytes(a_type, M, N, K, sparse)
+    if n == 0:
+        return None
+    return torch.zeros(n, dtype=torch.uint8, device=device if device is not None else torch.device("cuda"))
+
+
 def gemm_dense(A, B, D, alpha=1.0, beta=0.0, C=None, a_type=None, b_type=None, stream=None, bias=None,
-               act=ACT_NONE, d_type=None):
+               act=ACT_NONE, d_type=None, workspace=None):
     """D = alpha * A @ B + beta * C with A M x K (row-major) and B given as its N x K transpose.
     With bias (N fp32 values), act or a bfloat16 / float16 D (d_type overrides what D's dtype
-    says) this is mmac_gemm_dense_ep: D = round(act(alpha * A @ B + beta * C + bias))."""
+    says) this is mmac_gemm_dense_ep: D = round(act(alpha * A @ B + beta * C + bias)); with a
+    workspace tensor (see workspace()) it is mmac_gemm_dense_ws, which may split K."""
     M, K = A.shape
     N = B.shape[0]
     ta, tb = _dtype(A, a_type), _dtype(B, b_type)
     args = (ta, tb, M, N, K, float(alpha), _ptr(A), _ld(A), _ptr(B), _ld(B), float(beta),
             _ptr(C), _ld(C) if C is not None else 0, _ptr(D), _ld(D))
     ep = _epilogue(D, bias, act, d_type)
-    if ep is None:
+    if workspace is not None:
+        _check(lib().mmac_gemm_dense_ws(*args, None if ep is None else ctypes.byref(ep), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(stream)),
+               "mmac_gemm_dense_ws")
+    elif ep is None:
         _check(lib().mmac_gemm_dense(*args, _stream(stream)), "mmac_gemm_dense")
     else:
         _check(lib().mmac_gemm_dense_ep(*args, ctypes.byref(ep), _stream(stream)), "mmac_gemm_dense_ep")
@@ -155,9 +181,10 @@ def sparse24_prune_compress(A, Ac, idx, bad_groups=None, a_type=None, stream=Non
 
 
 def gemm_sparse24(Ac, idx, B, D, K=None, alpha=1.0, beta=0.0, C=None, a_type=None, b_type=None, stream=None,
-                  bias=None, act=ACT_NONE, d_type=None):
+                  bias=None, act=ACT_NONE, d_type=None, workspace=None):
     """D = alpha * A @ B + beta * C with A given compressed (Ac, idx); K is the dense K.
-    bias / act / a 16-bit D select mmac_gemm_sparse24_ep, as in gemm_dense."""
+    bias / act / a 16-bit D select mmac_gemm_sparse24_ep and a workspace mmac_gemm_sparse24_ws,
+    as in gemm_dense."""
     M = Ac.shape[0]
     N, KB = B.shape
     K = KB if K is None else K
@@ -165,7 +192,11 @@ def gemm_sparse24(Ac, idx, B, D, K=None, alpha=1.0, beta=0.0, C=None, a_type=Non
     args = (ta, tb, M, N, K, float(alpha), _ptr(Ac), _ld(Ac), _ptr(idx), _ld(idx), _ptr(B), _ld(B), float(beta),
             _ptr(C), _ld(C) if C is not None else 0, _ptr(D), _ld(D))
     ep = _epilogue(D, bias, act, d_type)
-    if ep is None:
+    if workspace is not None:
+        _check(lib().mmac_gemm_sparse24_ws(*args, None if ep is None else ctypes.byref(ep), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), _stream(stream)),
+               "mmac_gemm_sparse24_ws")
+    elif ep is None:
         _check(lib().mmac_gemm_sparse24(*args, _stream(stream)), "mmac_gemm_sparse24")
     else:
         _check(lib().mmac_gemm_sparse24_ep(*args, ctypes.byref(ep), _stream(stream)), "mmac_gemm_sparse24_ep")

@@ -135,7 +135,60 @@ GemmParams make_params(int a, int64_t M, int64_t N, int64_t K, double alpha, con
     p.tiles_m = (int)((M + tm - 1) / tm);
     p.tiles_n = (int)((N + tn - 1) / tn);
     p.group_m = std::max(1, env_int("MMAC_GROUP_M", 8));
+    p.splits = 1;
+    p.kt_per_split = 0x7fffffff;
     return p;
+}
+
+// ---- split-K -------------------------------------------------------------
+// K elements per k-tile of the tiled kernels (16-bit elements: 64; 8-bit: 128).
+int64_t k_tile(int a) { return elem_size(a) == 2 ? 64 : 128; }
+
+struct SplitPlan {
+    TileShape shape;
+    int splits;
+    int64_t kt_per_split;
+    int64_t counter_bytes, bytes;   // workspace: counters, then the partial tiles
+};
+
+// Split-K when even the tile shape picked above leaves most of the 256
+// compute units idle (at most 128 tiles) and K is long: S = 256 / tiles
+// ranges (at most 8, each at least 8 k-tiles) of that shape.  Measured on
+// MI355X: 512 x 512 x 32768 bf16 runs 2.1x faster with 4 ranges of 64 x 64
+// tiles, 256 x 256 x 65536 3.3x with 4, 1024 x 512 x 8192 1.4x with 2; with
+// about one tile per compute unit already (an 8192 x 1024 output in 128 x 256
+// tiles) splitting only adds the partial-tile traffic.  MMAC_SPLITK=<S>
+// forces S ranges.
+SplitPlan plan_split(int a, int64_t M, int64_t N, int64_t K, bool sparse) {
+    SplitPlan sp{pick_shape(M, N, sparse), 1, 0, 0, 0};
+    if (sp.shape == TILE_SKINNY || M == 0 || N == 0 || K == 0) return sp;
+    const int64_t nkt = (K + k_tile(a) - 1) / k_tile(a);
+    const int64_t tm = tile_rows(sp.shape), tn = tile_cols(sp.shape);
+    const int64_t tiles = ((M + tm - 1) / tm) * ((N + tn - 1) / tn);
+    int64_t S = env_int("MMAC_SPLITK", 0);
+    if (S <= 0) S = tiles <= 128 ? std::min<int64_t>({8, 256 / tiles, nkt / 8}) : 1;
+    S = std::max<int64_t>(1, std::min<int64_t>(S, nkt));
+    if (S < 2) return sp;
+    sp.kt_per_split = (nkt + S - 1) / S;
+    sp.splits = (int)((nkt + sp.kt_per_split - 1) / sp.kt_per_split);   // no empty range
+    if (sp.splits < 2) return SplitPlan{sp.shape, 1, 0, 0, 0};
+    sp.counter_bytes = (tiles * 4 + 255) / 256 * 256;
+    sp.bytes = sp.counter_bytes + tiles * sp.splits * tm * tn * 4;
+    return sp;
+}
+
+// Applies a split plan when the workspace holds it; otherwise the unsplit shape.
+TileShape apply_split(GemmParams &p, const SplitPlan &sp, int64_t M, int64_t N, bool sparse, void *ws,
+                      int64_t ws_bytes) {
+    if (sp.splits < 2 || !ws || ws_bytes < sp.bytes) return pick_shape(M, N, sparse);
+    p.splits = sp.splits;
+    p.kt_per_split = (int)sp.kt_per_split;
+    p.counters = static_cast<uint32_t *>(ws);
+    p.partials = static_cast<uint8_t *>(ws) + sp.counter_bytes;
+    const int tm = tile_rows(sp.shape), tn = tile_cols(sp.shape);
+    p.tiles_m = (int)((M + tm - 1) / tm);
+    p.tiles_n = (int)((N + tn - 1) / tn);
+    return sp.shape;
 }
 
 mmac_status_t launched(hipError_t e) { return e == hipSuccess ? MMAC_OK : MMAC_ERR_HIP; }
@@ -170,19 +223,30 @@ mmac_status_t compress_call(mmac_dtype_t a_type, int64_t M, int64_t K, const voi
 
 extern "C" {
 
-mmac_status_t mmac_gemm_dense_ep(mmac_dtype_t a_type, mmac_dtype_t b_type, int64_t M, int64_t N, int64_t K,
+mmac_status_t mmac_gemm_dense_ws(mmac_dtype_t a_type, mmac_dtype_t b_type, int64_t M, int64_t N, int64_t K,
                                  double alpha, const void *A, int64_t lda, const void *B, int64_t ldb, double beta,
                                  const void *C, int64_t ldc, void *D, int64_t ldd, const mmac_epilogue_t *ep_in,
-                                 void *stream) {
+                                 void *workspace, int64_t workspace_bytes, void *stream) {
     const mmac_epilogue_t ep = epilogue_of(ep_in);
     const mmac_status_t st = check_gemm(a_type, b_type, M, N, K, alpha, A, lda, K, B, ldb, beta, C, ldc, D, ldd, ep);
     if (st != MMAC_OK) return st;
+    if (workspace_bytes < 0) return MMAC_ERR_INVALID_ARG;
+    if (workspace && !aligned16(workspace)) return MMAC_ERR_MISALIGNED;
     if (M == 0 || N == 0) return MMAC_OK;
-    const TileShape shape = pick_shape(M, N);
-    const GemmParams p = make_params(a_type, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd, ep, shape);
+    TileShape shape = pick_shape(M, N);
+    GemmParams p = make_params(a_type, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd, ep, shape);
     if (shape == TILE_SKINNY)
         return launched(launch_gemm_skinny(a_type, b_type, p, static_cast<hipStream_t>(stream)));
+    shape = apply_split(p, plan_split(a_type, M, N, K, false), M, N, false, workspace, workspace_bytes);
     return launched(launch_gemm_dense(a_type, b_type, shape, p, static_cast<hipStream_t>(stream)));
+}
+
+mmac_status_t mmac_gemm_dense_ep(mmac_dtype_t a_type, mmac_dtype_t b_type, int64_t M, int64_t N, int64_t K,
+                                 double alpha, const void *A, int64_t lda, const void *B, int64_t ldb, double beta,
+                                 const void *C, int64_t ldc, void *D, int64_t ldd, const mmac_epilogue_t *ep,
+                                 void *stream) {
+    return mmac_gemm_dense_ws(a_type, b_type, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd, ep, nullptr, 0,
+                              stream);
 }
 
 mmac_status_t mmac_gemm_dense(mmac_dtype_t a_type, mmac_dtype_t b_type, int64_t M, int64_t N, int64_t K,
@@ -203,10 +267,11 @@ mmac_status_t mmac_sparse24_prune_compress(mmac_dtype_t a_type, int64_t M, int64
     return compress_call(a_type, M, K, A, lda, Ac, ldac, idx, ldidx, bad_groups, true, stream);
 }
 
-mmac_status_t mmac_gemm_sparse24_ep(mmac_dtype_t a_type, mmac_dtype_t b_type, int64_t M, int64_t N, int64_t K,
+mmac_status_t mmac_gemm_sparse24_ws(mmac_dtype_t a_type, mmac_dtype_t b_type, int64_t M, int64_t N, int64_t K,
                                     double alpha, const void *Ac, int64_t ldac, const uint32_t *idx, int64_t ldidx,
                                     const void *B, int64_t ldb, double beta, const void *C, int64_t ldc, void *D,
-                                    int64_t ldd, const mmac_epilogue_t *ep_in, void *stream) {
+                                    int64_t ldd, const mmac_epilogue_t *ep_in, void *workspace,
+                                    int64_t workspace_bytes, void *stream) {
     const mmac_epilogue_t ep = epilogue_of(ep_in);
     if (K >= 0 && (K % 4) != 0) return MMAC_ERR_INVALID_ARG;
     const mmac_status_t st =
@@ -215,12 +280,29 @@ mmac_status_t mmac_gemm_sparse24_ep(mmac_dtype_t a_type, mmac_dtype_t b_type, in
     if ((K > 0 && !idx) || ldidx < (K + 31) / 32 || ldidx < 1) return MMAC_ERR_INVALID_ARG;
     if (ldidx * 4 * 256 > ((int64_t)1 << 31)) return MMAC_ERR_UNSUPPORTED;
     if (!aligned4(idx)) return MMAC_ERR_MISALIGNED;
+    if (workspace_bytes < 0) return MMAC_ERR_INVALID_ARG;
+    if (workspace && !aligned16(workspace)) return MMAC_ERR_MISALIGNED;
     if (M == 0 || N == 0) return MMAC_OK;
-    const TileShape shape = pick_shape(M, N, true);
-    GemmParams p = make_params(a_type, M, N, K, alpha, Ac, ldac, B, ldb, beta, C, ldc, D, ldd, ep, shape);
+    GemmParams p = make_params(a_type, M, N, K, alpha, Ac, ldac, B, ldb, beta, C, ldc, D, ldd, ep,
+                               pick_shape(M, N, true));
     p.idx = idx;
     p.idx_pitch = ldidx;
+    const TileShape shape =
+        apply_split(p, plan_split(a_type, M, N, K, true), M, N, true, workspace, workspace_bytes);
     return launched(launch_gemm_sparse(a_type, b_type, shape, p, static_cast<hipStream_t>(stream)));
+}
+
+mmac_status_t mmac_gemm_sparse24_ep(mmac_dtype_t a_type, mmac_dtype_t b_type, int64_t M, int64_t N, int64_t K,
+                                    double alpha, const void *Ac, int64_t ldac, const uint32_t *idx, int64_t ldidx,
+                                    const void *B, int64_t ldb, double beta, const void *C, int64_t ldc, void *D,
+                                    int64_t ldd, const mmac_epilogue_t *ep, void *stream) {
+    return mmac_gemm_sparse24_ws(a_type, b_type, M, N, K, alpha, Ac, ldac, idx, ldidx, B, ldb, beta, C, ldc, D, ldd,
+                                 ep, nullptr, 0, stream);
+}
+
+int64_t mmac_gemm_workspace_bytes(mmac_dtype_t a_type, int64_t M, int64_t N, int64_t K, int sparse) {
+    if (!valid_type(a_type) || M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
+    return plan_split(a_type, M, N, K, sparse != 0).bytes;
 }
 
 mmac_status_t mmac_gemm_sparse24(mmac_dtype_t a_type, mmac_dtype_t b_type, int64_t M, int64_t N, int64_t K,

@@ -43,6 +43,11 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 // it streams past the caches instead of evicting the A and B panels that
 // other tiles still reuse.
 constexpr int kNonTemporal = 2;
+// Cache-policy operand for device-scope (agent-scope) accesses: the SC1 bit.
+// Such a store is written through to the memory side of the L2 caches, and
+// such a load is served from there, so data one XCD writes is seen by
+// another without cache-wide write-back or invalidation.
+constexpr int kDeviceScope = 16;
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef __attribute__((address_space(3))) void lds_void;

@@ -29,15 +29,18 @@
 
 namespace mmac {
 
-// Workgroup -> output tile.  Workgroups are dealt to the 8 XCDs round-robin
-// (workgroup w runs on XCD w mod 8), so first give each XCD a contiguous run of
-// tile numbers, then walk tile numbers in groups of `group_m` tile rows,
-// column by column, so the tiles an XCD runs at the same time share A row
-// panels and B column panels in that XCD's L2.
-__device__ __forceinline__ void tile_coords(int wg, const GemmParams &p, int &tm, int &tn) {
-    const int T = p.tiles_m * p.tiles_n;
-    const int x = wg & 7, local = wg >> 3, q = T >> 3, r = T & 7;
-    const int t = x * q + (x < r ? x : r) + local;
+// Workgroup -> (output tile, K range).  Workgroups are dealt to the 8 XCDs
+// round-robin (workgroup w runs on XCD w mod 8), so first give each XCD a
+// contiguous run of unit numbers (the K ranges of one tile are consecutive
+// units, so they normally share an XCD and its L2), then walk tile numbers in
+// groups of `group_m` tile rows, column by column, so the tiles an XCD runs at
+// the same time share A row panels and B column panels in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int wg, const GemmParams &p, int &tm, int &tn, int &split) {
+    const int U = p.tiles_m * p.tiles_n * p.splits;
+    const int x = wg & 7, local = wg >> 3, q = U >> 3, r = U & 7;
+    const int u = x * q + (x < r ? x : r) + local;
+    const int t = u / p.splits;
+    split = u - t * p.splits;
     const int per_group = p.group_m * p.tiles_n;
     const int grp = t / per_group;
     const int first = grp * p.group_m;
@@ -149,6 +152,7 @@ struct TiledGemm {
 
     const GemmParams &p;
     int wave, lane, g, l32, wm, wn, row0, col0;
+    int tile, split, kt0;   // output tile number, K range, its first k-tile
     rsrc_t ra, rb, rx;
     acc_t acc[TM][TN];
 
@@ -161,7 +165,9 @@ struct TiledGemm {
         wm = wave / WN;
         wn = wave % WN;
         int tm, tn;
-        tile_coords(blockIdx.x, p, tm, tn);
+        tile_coords(blockIdx.x, p, tm, tn, split);
+        tile = tm * p.tiles_n + tn;
+        kt0 = split * p.kt_per_split;
         row0 = tm * BM;
         col0 = tn * BN;
         const int arows = min(BM, p.M - row0), bcols = min(BN, p.N - col0);
@@ -180,14 +186,14 @@ struct TiledGemm {
     template <int W>
     __device__ __forceinline__ uint32_t src_off(uint32_t P, int64_t pitch, int kt) const {
         const uint32_t L = swz<W>(P);
-        return (L / W) * (uint32_t)pitch + (uint32_t)(kt * W * 16) + (L % W) * 16;
+        return (L / W) * (uint32_t)pitch + (uint32_t)((kt + kt0) * W * 16) + (L % W) * 16;
     }
 
     // Byte offset of the source of index copy lane d (LDS bytes [d*IES,
     // (d+1)*IES) of the row-major tile of IW words per row) at k-tile kt.
     __device__ __forceinline__ uint32_t idx_off(uint32_t d, int kt) const {
         const uint32_t byte = d * IES, r = byte / (IW * 4);
-        return (r * (uint32_t)p.idx_pitch + kt * IW) * 4 + byte % (IW * 4);
+        return (r * (uint32_t)p.idx_pitch + (kt + kt0) * IW) * 4 + byte % (IW * 4);
     }
 
     // Copy instruction j (0 <= j < LPT: the A passes, then B, then the index)
@@ -227,7 +233,7 @@ struct TiledGemm {
             const int u = q * 64 + lane;
             const uint32_t P = wave * AUPW + u;
             if (AUPW % 64 == 0 || u < AUPW) {
-                const int e0 = (kt * AW * 16 + (int)(swz<AW>(P) % AW) * 16) / Op::kEsize;
+                const int e0 = ((kt + kt0) * AW * 16 + (int)(swz<AW>(P) % AW) * 16) / Op::kEsize;
                 *reinterpret_cast<i32x4 *>(st + P * 16) =
                     masked_unit<Op::kEsize>(ra, src_off<AW>(P, p.a_pitch, kt), e0, climit);
             }
@@ -237,7 +243,7 @@ struct TiledGemm {
             const int u = q * 64 + lane;
             const uint32_t P = wave * BUPW + u;
             if (BUPW % 64 == 0 || u < BUPW) {
-                const int e0 = (kt * BW * 16 + (int)(swz<BW>(P) % BW) * 16) / Op::kEsize;
+                const int e0 = ((kt + kt0) * BW * 16 + (int)(swz<BW>(P) % BW) * 16) / Op::kEsize;
                 *reinterpret_cast<i32x4 *>(st + A_BYTES + P * 16) =
                     masked_unit<Op::kEsize>(rb, src_off<BW>(P, p.b_pitch, kt), e0, p.K);
             }
@@ -376,6 +382,96 @@ struct TiledGemm {
 #pragma unroll
             for (int j = 0; j < TN; ++j) b0[j] = b1[j];
         }
+    }
+
+    // Split-K fix-up, after this workgroup's K range.  Every range writes its
+    // partial tile (in the accumulator's register order: per instruction tile
+    // and group of 4 registers, 16 bytes per thread, so each store
+    // instruction covers 1 KiB) with device-scope stores, waits until they
+    // have completed, and then counts itself in with one atomic add on the
+    // tile's counter.  The range that arrives last resets the counter to
+    // zero and sums the partials, read with device-scope loads, in range
+    // order 0, 1, ..., splits - 1 (its own from registers), so the result does
+    // not depend on which range finished last; it alone goes on to the
+    // epilogue.  No workgroup waits for another.  Device scope on the partial
+    // accesses themselves (the SC1 cache-policy bit: the data goes to and
+    // comes from the memory side of the XCDs' L2 caches, which are not
+    // coherent with each other) replaces whole-L2 write-back and invalidate
+    // fences, which stall every workgroup of the XCD.  Returns true in the
+    // last workgroup.  The arrival rank reaches the other threads through the
+    // first LDS word (the k-tile stages are no longer read by then); a second
+    // LDS array for it would make the compiler wait for every outstanding
+    // copy before LDS reads in the main loop.
+    static constexpr int SLOT_BYTES = BM * BN * 4;
+    __device__ __forceinline__ bool fixup(uint32_t *arrived) {
+        const int S = p.splits;
+        uint8_t *tile_ws = p.partials + (int64_t)tile * S * SLOT_BYTES;
+        const int tid = threadIdx.x;
+        {
+            const rsrc_t rw = make_rsrc(tile_ws + (int64_t)split * SLOT_BYTES, SLOT_BYTES);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int G4 = 0; G4 < 4; ++G4) {
+                        // elements copied to scalars first: a bit cast of a vector
+                        // element expression reads the vector's first element
+                        const out_t e0 = acc[i][j][4 * G4], e1 = acc[i][j][4 * G4 + 1],
+                                    e2 = acc[i][j][4 * G4 + 2], e3 = acc[i][j][4 * G4 + 3];
+                        const i32x4 v = {__builtin_bit_cast(int, e0), __builtin_bit_cast(int, e1),
+                                         __builtin_bit_cast(int, e2), __builtin_bit_cast(int, e3)};
+                        const uint32_t o = (uint32_t)((((i * TN + j) * 4 + G4) * NT + tid) * 16);
+                        __builtin_amdgcn_raw_buffer_store_b128(v, rw, o, 0, kDeviceScope);
+                    }
+        }
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this thread's partial has reached device scope
+        __syncthreads();
+        if (tid == 0) {
+            const uint32_t before = __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
+            if (before == (uint32_t)S - 1)
+                __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *arrived = before;
+        }
+        __syncthreads();
+        const bool last = *arrived == (uint32_t)S - 1;
+        __syncthreads();   // read by every wave before the epilogue reuses the LDS
+        if (!last) return false;
+        // acc = p_0 + p_1 + ... in range order
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int G4 = 0; G4 < 4; ++G4) {
+                    const uint32_t o = (uint32_t)((((i * TN + j) * 4 + G4) * NT + tid) * 16);
+                    out_t sum[4];
+                    for (int s = 0; s < S; ++s) {
+                        out_t x[4];
+                        if (s == split) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) x[e] = acc[i][j][4 * G4 + e];
+                        } else {
+                            const rsrc_t rr = make_rsrc(tile_ws + (int64_t)s * SLOT_BYTES, SLOT_BYTES);
+                            const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rr, o, 0, kDeviceScope);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const int w = v[e];
+                                x[e] = __builtin_bit_cast(out_t, w);
+                            }
+                        }
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if (s == 0) sum[e] = x[e];
+                            else if constexpr (std::is_same<out_t, float>::value) sum[e] = sum[e] + x[e];
+                            else sum[e] = (int32_t)((uint32_t)sum[e] + (uint32_t)x[e]);
+                        }
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[i][j][4 * G4 + e] = sum[e];
+                }
+        return true;
     }
 
     // D = alpha * acc + beta * C, then (floating inputs) the column bias, ReLU
@@ -630,8 +726,13 @@ void gemm_tiled_kernel(GemmParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[T::LDS_BYTES];
     T t(p);
 
-    const int nk = p.K / Op::kBK;                        // whole k-tiles
-    const int nkt = nk + (p.K > nk * Op::kBK ? 1 : 0);   // plus a ragged one
+    // this workgroup's K range: k-tiles [kt0, kt0 + nkt) of the matrix, the
+    // first nk of them whole (a ragged k-tile can only be the matrix's last)
+    const int nk_all = p.K / Op::kBK;
+    const int nkt_all = nk_all + (p.K > nk_all * Op::kBK ? 1 : 0);
+    const int kt_end = min(t.kt0 + p.kt_per_split, nkt_all);
+    const int nkt = kt_end - t.kt0;
+    const int nk = min(kt_end, nk_all) - t.kt0;
 
     // prologue: start k-tiles 0 .. AHEAD-1 (and the folded C, whose loads overlap them)
 #pragma unroll
@@ -641,7 +742,7 @@ void gemm_tiled_kernel(GemmParams p) {
             else t.fill_masked(smem + s * T::STAGE, s);
         }
     }
-    if (p.fold_c) t.load_c_into_acc();
+    if (p.fold_c && t.split == 0) t.load_c_into_acc();
     // Copies are counted per wave in issue order.  Before using k-tile kt + 1 the
     // copies of the later k-tiles may stay in flight, provided they are all
     // whole k-tiles (the ragged one issues fewer copy instructions); otherwise
@@ -661,6 +762,7 @@ void gemm_tiled_kernel(GemmParams p) {
         t.template iteration<false>(smem, kt, cur, nk, nkt);
         cur = (cur + 1 == STAGES) ? 0 : cur + 1;
     }
+    if (p.splits > 1 && !t.fixup(reinterpret_cast<uint32_t *>(smem))) return;
     t.epilogue(smem);
 }
 

@@ -39,6 +39,14 @@ struct GemmParams {
     int act;
     const float *bias;
     int tiles_m, tiles_n, group_m;
+    // Split-K: K is cut into `splits` ranges of kt_per_split k-tiles (the last
+    // range may be shorter) and each (output tile, range) pair is one
+    // workgroup.  counters: one word per output tile, zero before and after
+    // every call; partials: splits fp32 / int32 tiles of BM x BN per output
+    // tile.  splits == 1: one range, counters and partials unused.
+    int splits, kt_per_split;
+    uint32_t *counters;
+    uint8_t *partials;
 };
 
 struct CompressParams {

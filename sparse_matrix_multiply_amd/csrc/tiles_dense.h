@@ -13,7 +13,7 @@ namespace mmac {
 // build compiles them in parallel.
 template <class Op>
 hipError_t launch_dense_op(TileShape shape, const GemmParams &p, hipStream_t s) {
-    const dim3 grid(p.tiles_m * p.tiles_n), block(256);
+    const dim3 grid(p.tiles_m * p.tiles_n * p.splits), block(256);   // one workgroup per tile and K range
     switch (shape) {
     case TILE_256: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 256, 256, 2, 4, 2>), grid, dim3(512), 0, s, p); break;
     case TILE_256x128: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 256, 128, 2, 2, 3>), grid, block, 0, s, p); break;

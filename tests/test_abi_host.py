@@ -32,8 +32,9 @@ def L():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["mmac_gemm_dense", "mmac_gemm_dense_ep", "mmac_gemm_sparse24",
-                                    "mmac_gemm_sparse24_ep", "mmac_sparse24_compress",
+    assert declared_functions() == ["mmac_gemm_dense", "mmac_gemm_dense_ep", "mmac_gemm_dense_ws",
+                                    "mmac_gemm_sparse24", "mmac_gemm_sparse24_ep", "mmac_gemm_sparse24_ws",
+                                    "mmac_gemm_workspace_bytes", "mmac_sparse24_compress",
                                     "mmac_sparse24_prune_compress", "mmac_status_string"]
 
 
@@ -199,3 +200,47 @@ def test_epilogue_null_and_empty(L):
         ep = mm.Epilogue(d, mm.ACT_RELU, P)
         assert dense_ep(L, ep, M=0) == mm.OK
         assert sparse_ep(L, ep, N=0) == mm.OK
+
+
+def dense_ws(L, ws, ws_bytes, **kw):
+    a = dict(a=mm.BF16, b=mm.BF16, M=8192, N=1024, K=8192, alpha=1.0, A=P, lda=8192, B=P, ldb=8192, beta=0.0,
+             C=None, ldc=1024, D=P, ldd=1024, stream=None)
+    a.update(kw)
+    return L.mmac_gemm_dense_ws(a["a"], a["b"], a["M"], a["N"], a["K"], a["alpha"], a["A"], a["lda"], a["B"],
+                                a["ldb"], a["beta"], a["C"], a["ldc"], a["D"], a["ldd"], None, ws, ws_bytes,
+                                a["stream"])
+
+
+def test_workspace_bytes_plan(L, monkeypatch):
+    monkeypatch.delenv("MMAC_SPLITK", raising=False)
+    monkeypatch.delenv("MMAC_TILE", raising=False)
+    T64 = 64 * 64 * 4                                    # bytes of one fp32 64 x 64 partial tile
+    # 512 x 512 in 64 x 64 tiles: 64 tiles, so four K ranges (counters padded to 256 bytes)
+    assert mm.workspace_bytes(mm.BF16, 512, 512, 32768) == 256 + 4 * 64 * T64
+    # 256 x 256: 16 tiles, at most eight ranges; 1024 x 512: 128 tiles (512 counter bytes), two ranges
+    assert mm.workspace_bytes(mm.BF16, 256, 256, 65536) == 256 + 8 * 16 * T64
+    assert mm.workspace_bytes(mm.FP8_E4M3, 1024, 512, 8192) == 512 + 2 * 128 * T64
+    assert mm.workspace_bytes(mm.FP8_E4M3, 1024, 512, 8192, sparse=True) == 512 + 2 * 128 * T64
+    # about one tile per compute unit already, the skinny path, too little K, empty: no split
+    assert mm.workspace_bytes(mm.BF16, 8192, 1024, 8192) == 0
+    assert mm.workspace_bytes(mm.BF16, 8192, 8192, 8192) == 0
+    assert mm.workspace_bytes(mm.BF16, 16, 4096, 4096) == 0
+    assert mm.workspace_bytes(mm.BF16, 512, 512, 256) == 0
+    assert mm.workspace_bytes(mm.BF16, 0, 1024, 8192) == 0
+    # forced: three ranges of the 256 x 256 tiles of an 8192^3 product
+    monkeypatch.setenv("MMAC_SPLITK", "3")
+    assert mm.workspace_bytes(mm.BF16, 8192, 8192, 8192) == 4096 + 3 * 1024 * 256 * 256 * 4
+
+
+@pytest.mark.parametrize("ws,nbytes,code", [
+    (P + 8, 1 << 30, mm.ERR_MISALIGNED),
+    (P, -1, mm.ERR_INVALID_ARG),
+])
+def test_workspace_argument_errors(L, ws, nbytes, code):
+    assert dense_ws(L, ws, nbytes) == code
+    assert dense_ws(L, ws, nbytes, M=0) == code        # checked before the empty-output shortcut
+
+
+def test_workspace_calls_validate_like_the_plain_ones(L):
+    assert dense_ws(L, None, 0, ldd=1000) == mm.ERR_INVALID_ARG
+    assert dense_ws(L, None, 0, M=0) == mm.OK
