@@ -33,11 +33,12 @@ PEAK_HBM_GBS = 8000.0
 # applies only while their hash is the one recorded there.
 _KSRC = {
     "dense": ["include/mmac.h", "sparse_matrix_multiply_amd/csrc/device.h", "sparse_matrix_multiply_amd/csrc/gemm_tiled.h",
-              "sparse_matrix_multiply_amd/csrc/launch.h", "sparse_matrix_multiply_amd/csrc/gemm_dense.hip",
-              "sparse_matrix_multiply_amd/csrc/abi.hip"],
+              "sparse_matrix_multiply_amd/csrc/launch.h", "sparse_matrix_multiply_amd/csrc/tiles_dense.h",
+              "sparse_matrix_multiply_amd/csrc/inst/dense_bf16.hip",
+              "sparse_matrix_multiply_amd/csrc/inst/dense_e4m3_e5m2.hip", "sparse_matrix_multiply_amd/csrc/abi.hip"],
     "sparse": ["include/mmac.h", "sparse_matrix_multiply_amd/csrc/device.h", "sparse_matrix_multiply_amd/csrc/gemm_tiled.h",
-               "sparse_matrix_multiply_amd/csrc/launch.h", "sparse_matrix_multiply_amd/csrc/gemm_sparse.hip",
-               "sparse_matrix_multiply_amd/csrc/abi.hip"],
+               "sparse_matrix_multiply_amd/csrc/launch.h", "sparse_matrix_multiply_amd/csrc/tiles_sparse.h",
+               "sparse_matrix_multiply_amd/csrc/inst/sparse_e4m3_e5m2.hip", "sparse_matrix_multiply_amd/csrc/abi.hip"],
     "compress": ["include/mmac.h", "sparse_matrix_multiply_amd/csrc/device.h", "sparse_matrix_multiply_amd/csrc/launch.h",
                  "sparse_matrix_multiply_amd/csrc/compress.hip", "sparse_matrix_multiply_amd/csrc/abi.hip"],
 }
@@ -294,10 +295,10 @@ def suite():
 
     out = {}
 
-    def dense_case(name, key, reps=20, rotate=1, n_share=None, bf16_out=False, split=False):
+    def dense_case(name, key, reps=20, rotate=1, n_share=None, bf16_out=False):
         """n_share: keep only the first n_share columns of B, C and D (one GPU's share when N is
         split across GPUs).  bf16_out: the epilogue variant with bfloat16 C and D, a per-column
-        bias and ReLU.  split: the split-K call with the workspace the library asks for."""
+        bias and ReLU."""
         w = dict(W.workload(name))
         if n_share:
             w["B"], w["N"] = w["B"][:n_share], n_share
@@ -311,9 +312,8 @@ def suite():
         act = mm.ACT_RELU if bf16_out else mm.ACT_NONE
         Ds = [torch.empty((w["M"], w["N"]), dtype=odt, device=dev) for _ in range(rotate)]
         Bs = [B] + [B.clone() for _ in range(rotate - 1)]
-        ws = mm.workspace(w["ta"], w["M"], w["N"], w["K"], device=dev) if split else None
         fns = [lambda i=i: mm.gemm_dense(A, Bs[i], Ds[i], w["alpha"], w["beta"], C, a_type=w["ta"], b_type=w["tb"],
-                                         stream=stream, bias=bias, act=act, workspace=ws) for i in range(rotate)]
+                                         stream=stream, bias=bias, act=act) for i in range(rotate)]
         ms = median_ms(fns, reps)
         f = gemm_flops(w["M"], w["N"], w["K"])
         es = 2 if w["ta"] in (W.BF16, W.F16) else 1
@@ -325,8 +325,6 @@ def suite():
                     "beta": w["beta"]}
         if bf16_out:
             out[key]["epilogue"] = "bf16 C/D, bias, ReLU"
-        if split:
-            out[key]["workspace_MiB"] = round((0 if ws is None else ws.numel()) / 2 ** 20, 1)
         del A, B, Bs, C, Ds
         torch.cuda.empty_cache()
 
@@ -347,8 +345,25 @@ def suite():
     # one GPU's share of the 8192^3 GEMMs split 8 ways along N
     dense_case("bf16_8192", "share_bf16_8192x1024x8192_beta1", n_share=1024)
     dense_case("fp8_8192", "share_fp8e4m3xbf8e5m2_8192x1024x8192", n_share=1024)
-    dense_case("bf16_8192", "share_bf16_8192x1024x8192_beta1_splitk", n_share=1024, split=True)
-    dense_case("fp8_8192", "share_fp8e4m3xbf8e5m2_8192x1024x8192_splitk", n_share=1024, split=True)
+
+    def split_case(M, N, K, t, key):
+        """Small output, long K: unsplit vs the library's split-K plan (synthetic N(0,1) operands)."""
+        tdt = {W.BF16: torch.bfloat16, W.E4M3: torch.float8_e4m3fn}[t]
+        A = torch.randn(M, K, device=dev).to(tdt)
+        B = torch.randn(N, K, device=dev).to(tdt)
+        D = torch.empty((M, N), dtype=torch.float32, device=dev)
+        ws = mm.workspace(t, M, N, K, device=dev)
+        u = median_ms([lambda: mm.gemm_dense(A, B, D, stream=stream)], 50)
+        sp = median_ms([lambda: mm.gemm_dense(A, B, D, stream=stream, workspace=ws)], 50)
+        f = gemm_flops(M, N, K)
+        out[key] = {"unsplit_us": round(u * 1e3, 1), "splitk_us": round(sp * 1e3, 1),
+                    "splitk_TFLOP/s": round(f / sp / 1e9, 1), "shape": [M, N, K],
+                    "workspace_MiB": round((0 if ws is None else ws.numel()) / 2 ** 20, 1)}
+        del A, B, D, ws
+
+    split_case(512, 512, 32768, W.BF16, "splitk_bf16_512x512x32768")
+    split_case(256, 256, 65536, W.BF16, "splitk_bf16_256x256x65536")
+    split_case(1024, 512, 8192, W.E4M3, "splitk_fp8e4m3_1024x512x8192")
     # epilogue variant: bfloat16 C and D with bias and ReLU (half the output bytes)
     dense_case("bf16_8192", "bf16_8192^3_beta1_bf16out_bias_relu", bf16_out=True)
     dense_case("fp8_8192", "fp8e4m3xbf8e5m2_8192^3_bf16out_bias_relu", bf16_out=True)
@@ -376,18 +391,13 @@ def suite():
         D = torch.empty((M, N), dtype=torch.float32, device=dev)
         gms = median_ms([lambda: mm.gemm_sparse24(Acs[0], idxs[0], B, D, K=K, a_type=ta, b_type=tb, stream=stream)], 20)
         f = gemm_flops(M, N, K)
-        ws = mm.workspace(ta, M, N, K, sparse=True, device=dev)
-        if ws is not None:
-            sms = median_ms([lambda: mm.gemm_sparse24(Acs[0], idxs[0], B, D, K=K, a_type=ta, b_type=tb, stream=stream,
-                                                      workspace=ws)], 20)
+
         out[key] = {"compress_us": round(cms * 1e3, 1), "compress_GB/s": round(cbytes / cms / 1e6, 1),
                     "prune_compress_us": round(pms * 1e3, 1), "prune_compress_GB/s": round(cbytes / pms / 1e6, 1),
                     "gemm_us": round(gms * 1e3, 1), "TFLOP/s_dense_equivalent": round(f / gms / 1e9, 1),
                     "TFLOP/s_effective": round(f / 2 / gms / 1e9, 1), "shape": [M, N, K]}
-        if ws is not None:
-            out[key]["splitk_gemm_us"] = round(sms * 1e3, 1)
-            out[key]["splitk_TFLOP/s_dense_equivalent"] = round(f / sms / 1e9, 1)
-        del As, Acs, idxs, B, D, ws
+
+        del As, Acs, idxs, B, D
         torch.cuda.empty_cache()
     print(json.dumps({"suite": out, "note": "median of repeated single launches (HIP events); skinny GEMM and "
                       "compressors rotate through copies larger than the 256 MB Infinity Cache"}), flush=True)
