@@ -159,17 +159,18 @@ def prune_compress24(t, A):
     return Ac, idx, int(bad.value)
 
 
-OUT_F32, OUT_BF16, OUT_F16 = 0, 1, 2
+OUT_F32, OUT_BF16, OUT_F16, OUT_E4M3, OUT_E5M2 = 0, 1, 2, 3, 4
 ACT_NONE, ACT_RELU = 0, 1
 
 
 def epilogue(Y, bias=None, act=ACT_NONE, out_type=OUT_F32):
     """Epilogue variants on the exact GEMM value Y (float64 M x N): + bias[j] (float32),
-    activation, rounding to the output format.  Returns (bits or float32 array, the
-    float64 value before rounding)."""
+    activation, rounding to the output format.  Returns (bits -- uint16 for bfloat16 /
+    binary16, uint8 for E4M3 / E5M2 -- or a float32 array, the float64 value before rounding)."""
     Y = _c2(Y, np.float64)
     M, N = Y.shape
-    out = np.zeros((M, N), np.uint16 if out_type else np.float32)
+    dt = np.float32 if out_type == OUT_F32 else np.uint16 if out_type in (OUT_BF16, OUT_F16) else np.uint8
+    out = np.zeros((M, N), dt)
     Yout = np.zeros((M, N), np.float64)
     b = None if bias is None else np.ascontiguousarray(bias, np.float32)
     _check(lib().oracle_epilogue(M, N, _p(Y), N, _p(b) if b is not None else None, act, out_type, _p(out), N,
@@ -178,11 +179,12 @@ def epilogue(Y, bias=None, act=ACT_NONE, out_type=OUT_F32):
 
 
 def round_to(out_type, x):
-    """Round float64 values to bfloat16 (OUT_BF16) or binary16 (OUT_F16) bits, saturating."""
+    """Round float64 values to bfloat16 (OUT_BF16), binary16 (OUT_F16) bits (uint16), or OCP
+    E4M3 / E5M2 bits (uint8), saturating."""
     x = np.ascontiguousarray(x, np.float64)
     bits = np.zeros(x.shape, np.uint16)
     _check(lib().oracle_round(out_type, x.size, _p(x), _p(bits)), "round")
-    return bits
+    return bits if out_type in (OUT_BF16, OUT_F16) else bits.astype(np.uint8)
 
 
 def decompress24(t, Ac, idx, K):

@@ -290,10 +290,11 @@ int oracle_compress24(int t, int64_t M, int64_t K, const void *A, int64_t lda,
  * GEMM, add a per-column bias, apply an activation, then round to the output
  * format.
  *   activation 0: none; 1: ReLU, max(y, 0) (a NaN stays NaN);
- *   output 1: bfloat16, 2: IEEE binary16; rounding to nearest, ties to even
- *   (from the exact value), saturating: a finite value beyond the largest
- *   finite magnitude becomes that magnitude with its sign; infinities stay
- *   infinities, a NaN becomes the format's quiet NaN with the same sign.
+ *   output 1: bfloat16, 2: IEEE binary16 (3, 4: OCP fp8, below); rounding to
+ *   nearest, ties to even (from the exact value), saturating: a finite value
+ *   beyond the largest finite magnitude becomes that magnitude with its
+ *   sign; infinities stay infinities, a NaN becomes the format's quiet NaN
+ *   with the same sign.
  */
 static uint32_t round_to_format(double y, int mant_bits, int exp_bits) {
     const int bias = (1 << (exp_bits - 1)) - 1, emax = bias, emin = 1 - bias;
@@ -327,27 +328,75 @@ static uint32_t round_to_format(double y, int mant_bits, int exp_bits) {
     return sbit | (field << mant_bits) | mant;
 }
 
+/*
+ * Rounding to the OCP 8-bit floats (the fp8 encodings gfx950 uses: "CDNA3
+ * sparse MFMA builtins", note under the FP8 sparse kernel; OCP 8-bit floating
+ * point formats):
+ *   E4M3 (out_type 3): exponent bias 7, 3 fraction bits, subnormal quantum
+ *     2^-9, largest finite 448 = 1.75 * 2^8 (code 0x7E: the all-ones exponent
+ *     still holds normal numbers except fraction 111, which is NaN), no
+ *     infinities;
+ *   E5M2 (out_type 4): bias 15, 2 fraction bits, subnormal quantum 2^-16,
+ *     largest finite 57344 = 1.75 * 2^15, infinities 0x7C, NaNs above.
+ * To nearest, ties to even, from the exact value, saturating as above; an
+ * infinity stays infinite in E5M2 and becomes the largest finite value in
+ * E4M3 (which has none); NaN becomes 0x7F (E4M3) / 0x7E (E5M2), sign kept.
+ */
+static uint32_t round_to_fp8(double y, int e4m3) {
+    const int mant_bits = e4m3 ? 3 : 2, bias = e4m3 ? 7 : 15;
+    const double max_finite = e4m3 ? 448.0 : 57344.0;
+    const uint32_t sbit = signbit(y) ? 0x80u : 0u;
+    if (isnan(y)) return sbit | (e4m3 ? 0x7Fu : 0x7Eu);
+    if (isinf(y)) return sbit | (e4m3 ? 0x7Eu : 0x7Cu);
+    const double a = fabs(y);
+    const int emin = 1 - bias;
+    int e = (a > 0.0) ? ilogb(a) : emin;
+    if (e < emin) e = emin;
+    const double q = ldexp(1.0, e - mant_bits);       /* quantum of a's binade */
+    const double n = a / q;                           /* exact */
+    double r = floor(n);
+    const double frac = n - r;
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+    double v = r * q;
+    if (v > max_finite) v = max_finite;               /* saturate */
+    if (v == 0.0) return sbit;
+    const int ev = ilogb(v);
+    if (ev < emin) return sbit | (uint32_t)(v / ldexp(1.0, emin - mant_bits));        /* subnormal */
+    const uint32_t mant = (uint32_t)((v / ldexp(1.0, ev) - 1.0) * ldexp(1.0, mant_bits));
+    return sbit | ((uint32_t)(ev + bias) << mant_bits) | mant;
+}
+
+/* One output element of the given type: bits (1 bfloat16, 2 binary16, 3 E4M3, 4 E5M2). */
+static uint32_t round_out(int out_type, double y) {
+    switch (out_type) {
+    case 1: return round_to_format(y, 7, 8);
+    case 2: return round_to_format(y, 10, 5);
+    case 3: return round_to_fp8(y, 1);
+    default: return round_to_fp8(y, 0);
+    }
+}
+
 int oracle_epilogue(int64_t M, int64_t N, const double *Y, int64_t ldy, const float *bias, int act, int out_type,
                     void *out, int64_t ldo, double *Yout) {
-    if (M < 0 || N < 0 || act < 0 || act > 1 || out_type < 0 || out_type > 2) return -1;
+    if (M < 0 || N < 0 || act < 0 || act > 1 || out_type < 0 || out_type > 4) return -1;
     for (int64_t i = 0; i < M; ++i)
         for (int64_t j = 0; j < N; ++j) {
             double y = Y[i * ldy + j];
             if (bias) y += (double)bias[j];
             if (act == 1 && y < 0.0) y = 0.0;
             if (Yout) Yout[i * ldo + j] = y;
-            if (out_type == 1) ((uint16_t *)out)[i * ldo + j] = (uint16_t)round_to_format(y, 7, 8);
-            else if (out_type == 2) ((uint16_t *)out)[i * ldo + j] = (uint16_t)round_to_format(y, 10, 5);
+            if (out_type == 1 || out_type == 2) ((uint16_t *)out)[i * ldo + j] = (uint16_t)round_out(out_type, y);
+            else if (out_type >= 3) ((uint8_t *)out)[i * ldo + j] = (uint8_t)round_out(out_type, y);
             else ((float *)out)[i * ldo + j] = (float)y;
         }
     return 0;
 }
 
-/* Round n doubles to bfloat16 (out_type 1) or binary16 (2) bits, as above (for the pins). */
+/* Round n doubles to bfloat16 (out_type 1), binary16 (2), E4M3 (3) or E5M2 (4) bits, as above
+ * (for the pins; 8-bit results are returned in the low byte of each 16-bit word). */
 int oracle_round(int out_type, int64_t n, const double *x, uint16_t *bits) {
-    if (out_type != 1 && out_type != 2) return -1;
-    for (int64_t q = 0; q < n; ++q)
-        bits[q] = (uint16_t)(out_type == 1 ? round_to_format(x[q], 7, 8) : round_to_format(x[q], 10, 5));
+    if (out_type < 1 || out_type > 4) return -1;
+    for (int64_t q = 0; q < n; ++q) bits[q] = (uint16_t)round_out(out_type, x[q]);
     return 0;
 }
 

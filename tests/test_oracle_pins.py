@@ -488,3 +488,39 @@ def test_epilogue_bias_and_relu():
     assert np.isnan(out[1, 0]) and out[1, 1] == 0.75 and out[1, 2] == 0.0
     out, _ = oracle.epilogue(Y, None, oracle.ACT_NONE, oracle.OUT_BF16)
     assert list(out[0]) == [0x3FC0, 0xC000, 0x0000]
+
+
+# OCP fp8 output (E4M3 / E5M2): every code round-trips, torch's casts agree in range,
+# hand-worked ties and the saturation rules (E4M3 has no infinity: it saturates too).
+@pytest.mark.parametrize("out_type,t", [(oracle.OUT_E4M3, E4M3), (oracle.OUT_E5M2, E5M2)])
+def test_fp8_round_trips_every_code(out_type, t):
+    codes = np.arange(256, dtype=np.uint8)
+    vals = torch_decode(codes, t)
+    back = oracle.round_to(out_type, vals)
+    nan = np.isnan(vals)
+    assert np.array_equal(back[~nan], codes[~nan])
+    assert np.all((back[nan] & 0x7F) == (0x7F if t == E4M3 else 0x7E))
+
+
+@pytest.mark.parametrize("out_type,tdt,maxf", [(oracle.OUT_E4M3, torch.float8_e4m3fn, 448.0),
+                                               (oracle.OUT_E5M2, torch.float8_e5m2, 57344.0)])
+def test_fp8_rounding_matches_torch_in_range(out_type, tdt, maxf):
+    g = np.random.default_rng(23)
+    x = np.concatenate([g.uniform(-maxf, maxf, 20000), g.standard_normal(20000) * np.exp(g.uniform(-20, 5, 20000))])
+    x = x.astype(np.float32).astype(np.float64)          # one rounding on both sides
+    x = x[np.abs(x) <= maxf]
+    ours = oracle.round_to(out_type, x)
+    theirs = torch.from_numpy(x.astype(np.float32)).to(tdt).view(torch.uint8).numpy()
+    assert np.array_equal(ours, theirs)
+
+
+def test_fp8_ties_and_saturation():
+    e4 = oracle.round_to(oracle.OUT_E4M3, np.array([1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10, 464.0, 465.0, 1e30,
+                                                    np.inf, -np.inf, np.nan, -0.0]))
+    assert list(e4) == [0x38, 0x3A, 0x00, 0x02, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0x7F, 0x80]
+    e5 = oracle.round_to(oracle.OUT_E5M2, np.array([1.125, 1.375, 2.0 ** -17, 3 * 2.0 ** -17, 61440.0, 1e30,
+                                                    np.inf, -np.inf, np.nan]))
+    assert list(e5) == [0x3C, 0x3E, 0x00, 0x02, 0x7B, 0x7B, 0x7C, 0xFC, 0x7E]
+    out, _ = oracle.epilogue(np.array([[3.0, -500.0]]), np.array([0.25, 0.0], np.float32), oracle.ACT_NONE,
+                             oracle.OUT_E4M3)
+    assert out.dtype == np.uint8 and list(out[0]) == [0x45, 0xFE]      # 3.25 -> 3.25 (0x45), -500 -> -448
