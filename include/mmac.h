@@ -169,7 +169,9 @@ mmac_status_t mmac_gemm_sparse24(mmac_dtype_t a_type, mmac_dtype_t b_type,
 typedef enum {
     MMAC_OUT_ACC = 0,  /* fp32 (int32 for int8 inputs): the plain calls' output */
     MMAC_OUT_BF16 = 1, /* bfloat16 */
-    MMAC_OUT_F16 = 2   /* IEEE binary16 */
+    MMAC_OUT_F16 = 2,  /* IEEE binary16 */
+    MMAC_OUT_FP8_E4M3 = 3, /* OCP FP8 E4M3: largest finite 448, no infinities */
+    MMAC_OUT_BF8_E5M2 = 4  /* OCP BF8 E5M2: largest finite 57344 */
 } mmac_out_type_t;
 
 typedef enum {
@@ -192,11 +194,14 @@ typedef struct mmac_epilogue {
  * where acc is A*B accumulated in fp32, the sum is formed in fp32 (bias is
  * added only when given), and round converts to d_type: to nearest, ties to
  * even, saturating -- a finite value beyond the type's largest finite value
- * (bfloat16 0x7f7f, binary16 65504) becomes that value with its sign;
- * infinities stay infinite; NaN becomes the type's quiet NaN (0x7fc0 /
- * 0x7e00) with its sign.  C has d_type and row pitch ldc; D has d_type and
- * row pitch ldd.  For bfloat16 / binary16 C and D need 2-byte alignment, and
- * the row pitch limit of 8 MiB applies to ldc / ldd times 2.
+ * (bfloat16 0x7f7f, binary16 65504, E4M3 448, E5M2 57344) becomes that value
+ * with its sign; infinities stay infinite (E4M3 has none: they saturate too);
+ * NaN becomes the type's quiet NaN (0x7fc0, 0x7e00, 0x7f, 0x7e) with its
+ * sign.  The fp8 encodings are the OCP ones gfx950 uses ("CDNA3 sparse MFMA
+ * builtins", note under "FP8 16x16 sparse kernel").  C has d_type and row
+ * pitch ldc; D has d_type and row pitch ldd.  16-bit C and D need 2-byte
+ * alignment (8-bit: none), and the row pitch limit of 8 MiB applies to
+ * ldc / ldd times the element size.
  * int8 inputs accept only { MMAC_OUT_ACC, MMAC_ACT_NONE, NULL }
  * (MMAC_ERR_UNSUPPORTED otherwise).  An unknown d_type or act gives
  * MMAC_ERR_INVALID_ARG; a bias not 4-byte aligned gives MMAC_ERR_MISALIGNED.

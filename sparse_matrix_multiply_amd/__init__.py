@@ -10,9 +10,9 @@ Tensor conventions (element strides; the last dimension must be contiguous):
     A   M x K  row-major             (torch dtype gives the element type)
     B   N x K  (the K x N matrix B stored column-major)
     C,D M x N  float32 (int32 for int8 inputs); with floating inputs also
-               bfloat16 or float16 (the epilogue variants: D's dtype picks the
-               output type, C has D's dtype), plus an optional fp32 bias of N
-               values and ReLU
+               bfloat16, float16, float8_e4m3fn or float8_e5m2 (the epilogue
+               variants: D's dtype picks the output type, C has D's dtype),
+               plus an optional fp32 bias of N values and ReLU
     Ac  M x K/2, idx M x ceil(K/32) int32/uint32 words
 """
 import ctypes
@@ -26,9 +26,10 @@ LIB_PATH = os.path.join(_HERE, "libmmac.so")
 F16, BF16, I8, FP8_E4M3, BF8_E5M2 = 1, 2, 3, 4, 5
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_HIP = 0, 1, 2, 3, 4
 
-OUT_ACC, OUT_BF16, OUT_F16 = 0, 1, 2
+OUT_ACC, OUT_BF16, OUT_F16, OUT_FP8_E4M3, OUT_BF8_E5M2 = 0, 1, 2, 3, 4
 ACT_NONE, ACT_RELU = 0, 1
-OUT_OF = {torch.float32: OUT_ACC, torch.int32: OUT_ACC, torch.bfloat16: OUT_BF16, torch.float16: OUT_F16}
+OUT_OF = {torch.float32: OUT_ACC, torch.int32: OUT_ACC, torch.bfloat16: OUT_BF16, torch.float16: OUT_F16,
+          torch.float8_e4m3fn: OUT_FP8_E4M3, torch.float8_e5m2: OUT_BF8_E5M2}
 
 DTYPE_OF = {torch.float16: F16, torch.bfloat16: BF16, torch.int8: I8,
             torch.float8_e4m3fn: FP8_E4M3, torch.float8_e5m2: BF8_E5M2}

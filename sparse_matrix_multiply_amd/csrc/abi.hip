@@ -67,7 +67,9 @@ mmac_epilogue_t epilogue_of(const mmac_epilogue_t *ep) {
 }
 
 // Bytes of one C / D element.
-int out_size(const mmac_epilogue_t &ep) { return ep.d_type == MMAC_OUT_ACC ? 4 : 2; }
+int out_size(const mmac_epilogue_t &ep) {
+    return ep.d_type == MMAC_OUT_ACC ? 4 : ep.d_type <= MMAC_OUT_F16 ? 2 : 1;
+}
 
 bool aligned_to(const void *p, int n) { return reinterpret_cast<uintptr_t>(p) % n == 0; }
 
@@ -76,7 +78,7 @@ mmac_status_t check_gemm(int a, int b, int64_t M, int64_t N, int64_t K, double a
                          int64_t lda, int64_t a_cols, const void *B, int64_t ldb, double beta, const void *C,
                          int64_t ldc, const void *D, int64_t ldd, const mmac_epilogue_t &ep) {
     if (!supported_pair(a, b)) return MMAC_ERR_UNSUPPORTED;
-    if (ep.d_type < MMAC_OUT_ACC || ep.d_type > MMAC_OUT_F16 || ep.act < MMAC_ACT_NONE || ep.act > MMAC_ACT_RELU)
+    if (ep.d_type < MMAC_OUT_ACC || ep.d_type > MMAC_OUT_BF8_E5M2 || ep.act < MMAC_ACT_NONE || ep.act > MMAC_ACT_RELU)
         return MMAC_ERR_INVALID_ARG;
     if (a == MMAC_I8 && (ep.d_type != MMAC_OUT_ACC || ep.act != MMAC_ACT_NONE || ep.bias))
         return MMAC_ERR_UNSUPPORTED;

@@ -58,7 +58,10 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 
 // ---- output conversions --------------------------------------------------
 // Element types of C and D besides the accumulator type (float / int32).
-enum : int { OUT_ACC = 0, OUT_BF16 = 1, OUT_F16 = 2 };
+enum : int { OUT_ACC = 0, OUT_BF16 = 1, OUT_F16 = 2, OUT_E4M3 = 3, OUT_E5M2 = 4 };
+
+// Bytes of one C / D element of output type OT.
+template <int OT> constexpr int out_esize() { return OT == OUT_ACC ? 4 : OT <= OUT_F16 ? 2 : 1; }
 
 // fp32 -> bfloat16 bits: round to nearest, ties to even; a finite value whose
 // rounding would leave the finite range gives the largest finite value of its
@@ -92,12 +95,58 @@ __device__ __forceinline__ uint32_t to_f16_sat(float v) {
     return s | (uint32_t)__builtin_rintf(__builtin_bit_cast(float, a) * 16777216.0f);
 }
 
-// Stored C element (bits) -> fp32, exact for both 16-bit types.
+// fp32 -> OCP fp8 bits with the same rules.  E4M3 (bias 7, 3 fraction
+// bits): largest finite 448 (0x7E), no infinities, so infinities saturate
+// too, NaN 0x7F; E5M2 (bias 15, 2 fraction bits): largest finite 57344
+// (0x7B), infinity 0x7C, quiet NaN 0x7E.  Any magnitude at or above the
+// largest finite value rounds (or saturates) to it, so that test comes
+// first; then normal results rebias the exponent and round the dropped
+// significand bits to nearest even, and subnormal ones (quantum 2^-9 /
+// 2^-16) scale exactly and round with rint, as for binary16.
+__device__ __forceinline__ uint32_t to_e4m3_sat(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v), s = (u >> 24) & 0x80u, a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return s | 0x7fu;
+    if (a >= 0x43e00000u) return s | 0x7eu;             // |v| >= 448, infinities included
+    if (a >= 0x3c800000u) {                              // |v| >= 2^-6
+        const uint32_t m = a - 0x3c000000u;              // exponent rebias 127 -> 7
+        return s | ((m + 0x7ffffu + ((m >> 20) & 1u)) >> 20);
+    }
+    return s | (uint32_t)__builtin_rintf(__builtin_bit_cast(float, a) * 512.0f);
+}
+
+__device__ __forceinline__ uint32_t to_e5m2_sat(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v), s = (u >> 24) & 0x80u, a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return s | 0x7eu;
+    if (a == 0x7f800000u) return s | 0x7cu;
+    if (a >= 0x47600000u) return s | 0x7bu;             // |v| >= 57344
+    if (a >= 0x38800000u) {                              // |v| >= 2^-14
+        const uint32_t m = a - 0x38000000u;              // exponent rebias 127 -> 15
+        return s | ((m + 0xfffffu + ((m >> 21) & 1u)) >> 21);
+    }
+    return s | (uint32_t)__builtin_rintf(__builtin_bit_cast(float, a) * 65536.0f);
+}
+
+// Stored C element (bits) -> fp32, exact for every output type.  E5M2 is the
+// top byte of a binary16 with the same exponent bias.
 template <int OT>
 __device__ __forceinline__ float from_out_bits(uint32_t h) {
-    if constexpr (OT == OUT_BF16) return __builtin_bit_cast(float, h << 16);
-    else if constexpr (OT == OUT_F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-    else return __builtin_bit_cast(float, h);
+    if constexpr (OT == OUT_BF16) {
+        return __builtin_bit_cast(float, h << 16);
+    } else if constexpr (OT == OUT_F16) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+    } else if constexpr (OT == OUT_E5M2) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(h << 8));
+    } else if constexpr (OT == OUT_E4M3) {
+        const uint32_t s = (h & 0x80u) << 24, e = (h >> 3) & 15u, m = h & 7u;
+        if (e == 15u && m == 7u) return __builtin_bit_cast(float, s | 0x7fc00000u);
+        if (e == 0u) {
+            const float x = (float)m * 0.001953125f;     // m * 2^-9, exact
+            return s ? -x : x;
+        }
+        return __builtin_bit_cast(float, s | ((e + 120u) << 23) | (m << 20));
+    } else {
+        return __builtin_bit_cast(float, h);
+    }
 }
 
 // The end of every floating epilogue: v = alpha * acc + beta * C already
@@ -109,6 +158,8 @@ __device__ __forceinline__ uint32_t finish(float v, float bias, bool has_bias, b
     if (relu) v = v < 0.0f ? 0.0f : v;
     if constexpr (OT == OUT_BF16) return to_bf16_sat(v);
     else if constexpr (OT == OUT_F16) return to_f16_sat(v);
+    else if constexpr (OT == OUT_E4M3) return to_e4m3_sat(v);
+    else if constexpr (OT == OUT_E5M2) return to_e5m2_sat(v);
     else return __builtin_bit_cast(uint32_t, v);
 }
 

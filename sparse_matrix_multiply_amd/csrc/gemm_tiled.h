@@ -487,13 +487,15 @@ struct TiledGemm {
         if constexpr (std::is_same<out_t, float>::value) {
             if (p.d_type == OUT_BF16) return epilogue_as<OUT_BF16>(smem);
             if (p.d_type == OUT_F16) return epilogue_as<OUT_F16>(smem);
+            if (p.d_type == OUT_E4M3) return epilogue_as<OUT_E4M3>(smem);
+            if (p.d_type == OUT_E5M2) return epilogue_as<OUT_E5M2>(smem);
         }
         epilogue_as<OUT_ACC>(smem);
     }
 
     template <int OT>
     __device__ __forceinline__ void epilogue_as(uint8_t *smem) {
-        constexpr int ES = OT == OUT_ACC ? 4 : 2;
+        constexpr int ES = out_esize<OT>();
         const int rows = min(BM, p.M - row0);
         const rsrc_t rd = make_rsrc(static_cast<uint8_t *>(p.D) + (int64_t)row0 * p.ldd * ES,
                                     (uint32_t)(rows * p.ldd * ES));
@@ -514,7 +516,7 @@ struct TiledGemm {
             const rsrc_t rc = make_rsrc(static_cast<const uint8_t *>(p.C) + (int64_t)row0 * p.ldc * ES,
                                         (uint32_t)(rows * p.ldc * ES));
             store_tiles<true, OT>(rd, rc, bias, has_bias);
-        } else if (p.vec_d) {
+        } else if (ES >= 2 && p.vec_d) {   // one-byte D: element stores
             store_tiles_lds<OT>(rd, smem, bias, has_bias);
         } else {
             store_tiles<false, OT>(rd, rd, bias, has_bias);
@@ -566,7 +568,7 @@ struct TiledGemm {
 
     template <int OT>
     __device__ __forceinline__ void store_tiles_lds(rsrc_t rd, uint8_t *smem, const float *bias, bool has_bias) {
-        constexpr int ES = OT == OUT_ACC ? 4 : 2;
+        constexpr int ES = out_esize<OT>() < 2 ? 2 : out_esize<OT>();   // never called for one-byte D
         constexpr int RB = 32 * ES;            // bytes of a staged row
         constexpr int CPR = RB / 16;           // 16-byte chunks per row
         constexpr int RPR = 64 / CPR;          // rows per read instruction
@@ -643,13 +645,15 @@ struct TiledGemm {
         if constexpr (std::is_same<out_t, float>::value) {
             if (p.d_type == OUT_BF16) return load_c_as<OUT_BF16>();
             if (p.d_type == OUT_F16) return load_c_as<OUT_F16>();
+            if (p.d_type == OUT_E4M3) return load_c_as<OUT_E4M3>();
+            if (p.d_type == OUT_E5M2) return load_c_as<OUT_E5M2>();
         }
         load_c_as<OUT_ACC>();
     }
 
     template <int OT>
     __device__ __forceinline__ void load_c_as() {
-        constexpr int ES = OT == OUT_ACC ? 4 : 2;
+        constexpr int ES = out_esize<OT>();
         const int rows = min(BM, p.M - row0);
         const rsrc_t rc = make_rsrc(static_cast<const uint8_t *>(p.C) + (int64_t)row0 * p.ldc * ES,
                                     (uint32_t)(rows * p.ldc * ES));
@@ -663,8 +667,7 @@ struct TiledGemm {
                     const int r = wm * WTM + i * 32 + 8 * (G / 4) + 4 * g + (G % 4);
                     const bool in = (row0 + r < p.M) && (col < p.N);
                     const uint32_t oc = in ? (uint32_t)((r * p.ldc + col) * ES) : kOutOfRange;
-                    const uint32_t c = ES == 4 ? __builtin_amdgcn_raw_buffer_load_b32(rc, oc, 0, kNonTemporal)
-                                               : __builtin_amdgcn_raw_buffer_load_b16(rc, oc, 0, kNonTemporal);
+                    const uint32_t c = load_elem<ES>(rc, oc);
                     if constexpr (std::is_same<out_t, float>::value)
                         acc[i][j][G] = p.c_scale * from_out_bits<OT>(c);
                     else
@@ -675,9 +678,23 @@ struct TiledGemm {
         }
     }
 
+    // One C element (ES bytes) / one D element, non-temporal.
+    template <int ES>
+    __device__ __forceinline__ static uint32_t load_elem(rsrc_t r, uint32_t off) {
+        if constexpr (ES == 4) return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kNonTemporal);
+        else if constexpr (ES == 2) return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kNonTemporal);
+        else return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, kNonTemporal);
+    }
+    template <int ES>
+    __device__ __forceinline__ static void store_elem(uint32_t v, rsrc_t r, uint32_t off) {
+        if constexpr (ES == 4) __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kNonTemporal);
+        else if constexpr (ES == 2) __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, off, 0, kNonTemporal);
+        else __builtin_amdgcn_raw_buffer_store_b8((unsigned char)v, r, off, 0, kNonTemporal);
+    }
+
     template <bool USE_C, int OT>
     __device__ __forceinline__ void store_tiles(rsrc_t rd, rsrc_t rc, const float *bias, bool has_bias) {
-        constexpr int ES = OT == OUT_ACC ? 4 : 2;
+        constexpr int ES = out_esize<OT>();
         constexpr int JB = TN < 2 ? TN : 2;             // instruction tiles per batch of loads
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
@@ -696,8 +713,7 @@ struct TiledGemm {
                         c[jj][G] = 0;
                         if constexpr (USE_C) {
                             const uint32_t oc = in ? (uint32_t)((r * p.ldc + col) * ES) : kOutOfRange;
-                            c[jj][G] = ES == 4 ? __builtin_amdgcn_raw_buffer_load_b32(rc, oc, 0, kNonTemporal)
-                                               : __builtin_amdgcn_raw_buffer_load_b16(rc, oc, 0, kNonTemporal);
+                            c[jj][G] = load_elem<ES>(rc, oc);
                         }
                     }
                 }
@@ -706,10 +722,7 @@ struct TiledGemm {
 #pragma unroll
                     for (int G = 0; G < 16; ++G) {
                         const uint32_t bits = out_bits<USE_C, OT>(acc[i][j0 + jj][G], c[jj][G], bias[j0 + jj], has_bias);
-                        if constexpr (ES == 4)
-                            __builtin_amdgcn_raw_buffer_store_b32(bits, rd, od[jj][G], 0, kNonTemporal);
-                        else
-                            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bits, rd, od[jj][G], 0, kNonTemporal);
+                        store_elem<ES>(bits, rd, od[jj][G]);
                     }
                 }
             }

@@ -115,15 +115,16 @@ __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(GemmParams p) {
     const int orow = om * 16 + 4 * (oln >> 4) + orr, ocol = col0 + oc * 16 + (oln & 15);
     const bool oin = o < OUTS && orow < p.M && ocol < p.N;
     constexpr bool kFloat = std::is_same<out_t, float>::value;
-    const int es = kFloat && p.d_type != OUT_ACC ? 2 : 4;   // bytes of a C / D element
+    const int es = !kFloat || p.d_type == OUT_ACC ? 4 : p.d_type <= OUT_F16 ? 2 : 1;   // bytes of a C / D element
     const rsrc_t rd = make_rsrc(p.D, (uint32_t)(p.M * p.ldd * es));
     const uint32_t od = oin ? (uint32_t)((orow * p.ldd + ocol) * es) : kOutOfRange;
     uint32_t cpre = 0;
     if (p.use_c) {
         const rsrc_t rcc = make_rsrc(p.C, (uint32_t)(p.M * p.ldc * es));
         const uint32_t oc = oin ? (uint32_t)((orow * p.ldc + ocol) * es) : kOutOfRange;
-        cpre = es == 4 ? __builtin_amdgcn_raw_buffer_load_b32(rcc, oc, 0, 0)
-                       : __builtin_amdgcn_raw_buffer_load_b16(rcc, oc, 0, 0);
+        cpre = es == 4   ? __builtin_amdgcn_raw_buffer_load_b32(rcc, oc, 0, 0)
+               : es == 2 ? __builtin_amdgcn_raw_buffer_load_b16(rcc, oc, 0, 0)
+                         : __builtin_amdgcn_raw_buffer_load_b8(rcc, oc, 0, 0);
     }
     const bool has_bias = kFloat && p.bias != nullptr;
     float bias = 0.0f;
@@ -199,6 +200,14 @@ __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(GemmParams p) {
                 if (p.use_c) x = fmaf(p.beta, from_out_bits<OUT_F16>(cpre), x);
                 __builtin_amdgcn_raw_buffer_store_b16((unsigned short)finish<OUT_F16>(x, bias, has_bias, relu), rd,
                                                       od, 0, 0);
+            } else if (p.d_type == OUT_E4M3) {
+                if (p.use_c) x = fmaf(p.beta, from_out_bits<OUT_E4M3>(cpre), x);
+                __builtin_amdgcn_raw_buffer_store_b8((unsigned char)finish<OUT_E4M3>(x, bias, has_bias, relu), rd,
+                                                     od, 0, 0);
+            } else if (p.d_type == OUT_E5M2) {
+                if (p.use_c) x = fmaf(p.beta, from_out_bits<OUT_E5M2>(cpre), x);
+                __builtin_amdgcn_raw_buffer_store_b8((unsigned char)finish<OUT_E5M2>(x, bias, has_bias, relu), rd,
+                                                     od, 0, 0);
             } else {
                 if (p.use_c) x = fmaf(p.beta, __builtin_bit_cast(float, cpre), x);
                 __builtin_amdgcn_raw_buffer_store_b32(finish<OUT_ACC>(x, bias, has_bias, relu), rd, od, 0, 0);

@@ -170,13 +170,15 @@ def sparse_ep(L, ep, **kw):
 
 
 EP_ERRORS = [
-    (dict(d_type=3), {}, mm.ERR_INVALID_ARG),
+    (dict(d_type=5), {}, mm.ERR_INVALID_ARG),
     (dict(d_type=-1), {}, mm.ERR_INVALID_ARG),
     (dict(act=2), {}, mm.ERR_INVALID_ARG),
     (dict(bias=P + 2), {}, mm.ERR_MISALIGNED),
     (dict(d_type=mm.OUT_BF16), dict(D=P + 1), mm.ERR_MISALIGNED),                 # 2-byte D, odd address
     (dict(d_type=mm.OUT_F16), dict(beta=1.0, C=P + 4097), mm.ERR_MISALIGNED),
     (dict(d_type=mm.OUT_F16), dict(ldd=(1 << 22) + 1, N=64), mm.ERR_UNSUPPORTED),  # > 8 MiB of binary16
+    (dict(d_type=mm.OUT_BF8_E5M2), dict(ldd=(1 << 23) + 1, N=64), mm.ERR_UNSUPPORTED),  # > 8 MiB of bytes
+    (dict(d_type=mm.OUT_FP8_E4M3), dict(a=mm.I8, b=mm.I8), mm.ERR_UNSUPPORTED),
     (dict(d_type=mm.OUT_BF16), dict(a=mm.I8, b=mm.I8), mm.ERR_UNSUPPORTED),       # int8: plain output only
     (dict(act=mm.ACT_RELU), dict(a=mm.I8, b=mm.I8), mm.ERR_UNSUPPORTED),
     (dict(bias=P), dict(a=mm.I8, b=mm.I8), mm.ERR_UNSUPPORTED),
@@ -196,7 +198,7 @@ def test_epilogue_null_and_empty(L):
     # NULL epilogue = the plain call (same checks); empty outputs are a no-op for every variant
     assert dense_ep(L, None, ldd=63) == mm.ERR_INVALID_ARG
     assert sparse_ep(L, None, K=66) == mm.ERR_INVALID_ARG
-    for d in (mm.OUT_ACC, mm.OUT_BF16, mm.OUT_F16):
+    for d in (mm.OUT_ACC, mm.OUT_BF16, mm.OUT_F16, mm.OUT_FP8_E4M3, mm.OUT_BF8_E5M2):
         ep = mm.Epilogue(d, mm.ACT_RELU, P)
         assert dense_ep(L, ep, M=0) == mm.OK
         assert sparse_ep(L, ep, N=0) == mm.OK

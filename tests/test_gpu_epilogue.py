@@ -1,6 +1,6 @@
 """GPU parity of the epilogue variants (mmac_gemm_dense_ep, mmac_gemm_sparse24_ep) against
-the oracle's epilogue: bfloat16 / binary16 C and D, a per-column fp32 bias, ReLU, and the
-saturating round-to-nearest-even conversion.
+the oracle's epilogue: bfloat16 / binary16 / OCP fp8 E4M3 and E5M2 C and D, a per-column fp32
+bias, ReLU, and the saturating round-to-nearest-even conversion.
 
 Three kinds of check:
   - conversion, bit for bit: with A*B = 0 the value before rounding is the bias itself, so
@@ -13,7 +13,8 @@ Three kinds of check:
     same exact value;
   - general inputs: the GPU forms alpha*acc + beta*C + bias in fp32, within the parity
     tolerance of the exact value y; ReLU and rounding are monotone, so each output must
-    lie between the oracle's epilogue of y - delta and of y + delta.
+    lie between the oracle's epilogue of y - delta and of y + delta;
+  - C's decoder: with A*B = 0 and beta = 1 every finite code of the type comes back.
 """
 import numpy as np
 import pytest
@@ -28,18 +29,26 @@ from oracle import BF16, E4M3, E5M2, F16, I8
 pytestmark = pytest.mark.gpu
 
 FLOAT_PAIRS = [(BF16, BF16), (F16, F16), (E4M3, E4M3), (E4M3, E5M2), (E5M2, E4M3), (E5M2, E5M2)]
-OUTS = [(mm.OUT_BF16, torch.bfloat16, oracle.OUT_BF16), (mm.OUT_F16, torch.float16, oracle.OUT_F16)]
+OUTS = [(mm.OUT_BF16, torch.bfloat16, oracle.OUT_BF16), (mm.OUT_F16, torch.float16, oracle.OUT_F16),
+        (mm.OUT_FP8_E4M3, torch.float8_e4m3fn, oracle.OUT_E4M3), (mm.OUT_BF8_E5M2, torch.float8_e5m2, oracle.OUT_E5M2)]
+ONE_BYTE = (oracle.OUT_E4M3, oracle.OUT_E5M2)
 
 
 def decode_out(bits, out):
-    """bfloat16 / binary16 bits -> float64 (exact)."""
+    """bfloat16 / binary16 / E4M3 / E5M2 bits -> float64 (exact), with torch's own decoders."""
+    if out in ONE_BYTE:
+        b = torch.from_numpy(np.ascontiguousarray(bits).astype(np.uint8))
+        return b.view(torch.float8_e4m3fn if out == oracle.OUT_E4M3 else torch.float8_e5m2).double().numpy()
     b = np.ascontiguousarray(bits).view(np.uint16)
     if out == oracle.OUT_BF16:
-        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        with np.errstate(invalid="ignore"):          # signalling-NaN codes
+            return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     return b.view(np.float16).astype(np.float64)
 
 
 def out_bits(D):
+    if D.element_size() == 1:
+        return D.contiguous().view(torch.uint8).cpu().numpy()
     return D.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
@@ -68,6 +77,10 @@ def special_bias_values():
               2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -26, 1.5 * 2.0 ** -24, 2.5 * 2.0 ** -24, 1023.5 * 2.0 ** -24,
               1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 2049.0, 2051.0, 1.0e-8, 0.0):
         v += [np.float32(x), np.float32(-x)]
+    # E4M3 and E5M2: largest finite values, the ties beyond them, subnormal quanta and their ties
+    for x in (448.0, 464.0, 465.0, 479.0, 480.0, 57344.0, 61439.0, 61440.0, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -10,
+              2.0 ** -6, 2.0 ** -16, 2.0 ** -17, 3 * 2.0 ** -17, 1.0625, 1.1875, 1.125, 1.375):
+        v += [np.float32(x), np.float32(-x)]
     v += [np.float32(np.inf), np.float32(-np.inf), np.float32(-0.0)]
     return np.array(v, np.float32)
 
@@ -93,7 +106,7 @@ def test_conversion_of_every_bias_value(M, pad, d_type, tdt, oout, act):
     N, K = b.size, 16
     if not pad and N % 2 == 0:
         b, N = b[:-1], N - 1
-    ld = (N + 7) // 8 * 8 if pad else N
+    ld = (N + 15) // 16 * 16 if pad else N
     A = torch.zeros((M, K), dtype=torch.bfloat16, device=dev())
     B = torch.zeros((N, K), dtype=torch.bfloat16, device=dev())
     D = torch.empty((M, ld), dtype=tdt, device=dev())[:, :N]
@@ -161,6 +174,7 @@ def test_integer_products_bit_exact(sparse, ta, tb, d_type, tdt, oout):
     A, B, C, bias = integer_problem(ta, tb, M, N, K, 3 * ta + tb + 17 * d_type + 101 * sparse)
     bias_dev = torch.from_numpy(bias).to(dev())
     Cdev = c_tensor(C, tdt)
+    C = Cdev.float().cpu().numpy()                        # the values the device holds
     for k, (alpha, beta) in enumerate(SCALES):
         Y, _ = oracle_y(sparse, ta, tb, A, B, alpha, beta, C if beta else None)
         for act in (mm.ACT_NONE, mm.ACT_RELU):
@@ -230,6 +244,7 @@ def test_pitch_offset_and_padding(d_type, tdt, oout, ldd, first, M):
     buf = torch.full((M, ldd + first), -7.0, dtype=tdt, device=dev())
     D = buf[:, first:first + N]
     Cdev = c_tensor(C, tdt, ld=ldd)
+    C = Cdev.float().cpu().numpy()
     run_ep(False, ta, tb, A, B, Cdev, 1.0, 1.0, torch.from_numpy(bias).to(dev()), mm.ACT_RELU, tdt, D=D)
     Y, _ = oracle.gemm_dense(ta, tb, A, B, 1.0, 1.0, C)
     ref, _ = oracle.epilogue(Y, bias, mm.ACT_RELU, oout)
@@ -245,6 +260,7 @@ def test_in_place_c_equals_d_16bit(d_type, tdt, oout):
     M, N, K = 300, 200, 160
     A, B, C, bias = integer_problem(ta, tb, M, N, K, 21)
     D = c_tensor(C, tdt)
+    C = D.float().cpu().numpy()
     run_ep(False, ta, tb, A, B, D, 2.0, -1.0, torch.from_numpy(bias).to(dev()), mm.ACT_NONE, tdt, D=D)
     Y, _ = oracle.gemm_dense(ta, tb, A, B, 2.0, -1.0, C)
     ref, _ = oracle.epilogue(Y, bias, mm.ACT_NONE, oout)
@@ -272,3 +288,29 @@ def test_int8_rejects_variants():
     with pytest.raises(mm.MmacError):
         mm.gemm_dense(A, B, D, act=mm.ACT_RELU)
     assert I8 == mm.I8
+
+
+@pytest.mark.parametrize("d_type,tdt,oout", OUTS)
+@pytest.mark.parametrize("M", [8, 64])
+def test_c_decoder_every_code(d_type, tdt, oout, M):
+    """A*B = 0, beta = 1: D = round(C) = C for every finite code of the output type (C's
+    decoder and the conversion agree on every value the type holds)."""
+    nbits = 8 if oout in ONE_BYTE else 16
+    codes = np.arange(2 ** nbits, dtype=np.uint32).astype(np.uint8 if nbits == 8 else np.uint16)
+    vals = decode_out(codes, oout)
+    codes = codes[np.isfinite(vals)]
+    N = codes.size
+    K = 16
+    C = torch.from_numpy(codes.view(np.uint8 if nbits == 8 else np.int16))
+    C = C.to(dev()).view(tdt).reshape(1, N).expand(M, N).contiguous()
+    D = torch.zeros((M, N), dtype=tdt, device=dev())
+    A = torch.zeros((M, K), dtype=torch.bfloat16, device=dev())
+    B = torch.zeros((N, K), dtype=torch.bfloat16, device=dev())
+    mm.gemm_dense(A, B, D, 1.0, 1.0, C, d_type=d_type)
+    torch.cuda.synchronize()
+    got = out_bits(D)
+    want = codes.astype(got.dtype)
+    # -0 * ... : 0 + 1 * (-0) = +0 in fp32, so the negative-zero code comes back as +0
+    neg_zero = 0x80 if nbits == 8 else 0x8000
+    want = np.where(want == neg_zero, 0, want).astype(got.dtype)
+    assert np.array_equal(got, np.broadcast_to(want, got.shape))
