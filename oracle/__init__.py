@@ -53,6 +53,10 @@ def lib():
                                                        i64, dbl, vp, i64, i64, vp, vp, vp, vp]
         L.oracle_gemm_sparse24_i8.argtypes = [i64, i64, i64, i64, vp, i64, vp, i64, vp, i64, i64, vp, i64,
                                               i64, i64, vp, i64, vp]
+        L.oracle_gemm_mx_f64.argtypes = [ip, ip, i64, i64, i64, dbl, vp, i64, vp, i64, vp, i64, vp, i64, dbl, vp,
+                                         i64, i64, i64, vp, i64, vp, i64]
+        L.oracle_gemm_mx_f64_entries.argtypes = [ip, ip, i64, i64, i64, dbl, vp, i64, vp, i64, vp, i64, vp, i64,
+                                                 dbl, vp, i64, i64, vp, vp, vp, vp]
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -128,6 +132,40 @@ def gemm_dense_entries(ta, tb, A, B, ii, jj, alpha=1.0, beta=0.0, C=None):
     _check(lib().oracle_gemm_dense_f64_entries(ta, tb, M, N, K, float(alpha), _p(A), K, _p(B), K,
                                                float(beta), _p(Cc), N, ii.size, _p(ii), _p(jj),
                                                _p(out), _p(S)), "gemm_dense_f64_entries")
+    return out, S
+
+
+def gemm_mx(ta, tb, A, SA, B, SB, alpha=1.0, beta=0.0, C=None, rows=None):
+    """Block-scaled (MX) GEMM: A M x K, B N x K (fp8 bits), SA M x K/32 and SB N x K/32 E8M0
+    scale bytes; returns (D fp64, S fp64) for output rows [r0, r1)."""
+    M, K = A.shape
+    N = B.shape[0]
+    r0, r1 = (0, M) if rows is None else rows
+    A, B = _c2(A, BITS_DTYPE[ta]), _c2(B, BITS_DTYPE[tb])
+    SA, SB = _c2(SA, np.uint8), _c2(SB, np.uint8)
+    assert SA.shape == (M, K // 32) and SB.shape == (N, K // 32)
+    Cc = None if beta == 0 else _c2(C, np.float32)
+    D = np.empty((r1 - r0, N), np.float64)
+    S = np.empty((r1 - r0, N), np.float64)
+    _check(lib().oracle_gemm_mx_f64(ta, tb, M, N, K, float(alpha), _p(A), K, _p(SA), K // 32, _p(B), K, _p(SB),
+                                    K // 32, float(beta), _p(Cc), N, r0, r1, _p(D), N, _p(S), N), "gemm_mx_f64")
+    return D, S
+
+
+def gemm_mx_entries(ta, tb, A, SA, B, SB, ii, jj, alpha=1.0, beta=0.0, C=None):
+    """Block-scaled GEMM at output positions (ii[q], jj[q]); returns (D, S) 1-D fp64."""
+    M, K = A.shape
+    N = B.shape[0]
+    A, B = _c2(A, BITS_DTYPE[ta]), _c2(B, BITS_DTYPE[tb])
+    SA, SB = _c2(SA, np.uint8), _c2(SB, np.uint8)
+    Cc = None if beta == 0 else _c2(C, np.float32)
+    ii = np.ascontiguousarray(ii, np.int64)
+    jj = np.ascontiguousarray(jj, np.int64)
+    out = np.empty(ii.shape, np.float64)
+    S = np.empty(ii.shape, np.float64)
+    _check(lib().oracle_gemm_mx_f64_entries(ta, tb, M, N, K, float(alpha), _p(A), K, _p(SA), K // 32, _p(B), K,
+                                            _p(SB), K // 32, float(beta), _p(Cc), N, ii.size, _p(ii), _p(jj),
+                                            _p(out), _p(S)), "gemm_mx_f64_entries")
     return out, S
 
 

@@ -160,6 +160,95 @@ int oracle_gemm_dense_f64(int ta, int tb, int64_t M, int64_t N, int64_t K, doubl
     return rc;
 }
 
+/*
+ * Block-scaled ("microscaling", MX) GEMM -- beyond the pages, from the OCP
+ * Microscaling Formats specification: along K every block of 32 consecutive
+ * elements of a row of A (and of a column of B) shares one E8M0 scale, an
+ * unsigned 8-bit exponent with value 2^(e - 127) (e = 255 is NaN).  The
+ * product is
+ *   D[i][j] = alpha * sum_b 2^(SA[i][b] - 127) * 2^(SB[j][b] - 127)
+ *                         * sum_{k in block b} a[i][k] * b[k][j]  +  beta * C[i][j]
+ * summed exactly in fp64 (every term is a power-of-two multiple of an exact
+ * fp8 product).  SA is M x K/32 bytes (row pitch ldsa), SB is N x K/32 bytes
+ * (ldsb), both row-major; K must be a multiple of 32.  S receives
+ * sum |scaled product|, the error scale.  Rows [r0, r1) as in the dense oracle.
+ */
+static double e8m0(uint8_t e) { return e == 255 ? NAN : ldexp(1.0, (int)e - 127); }
+
+int oracle_gemm_mx_f64(int ta, int tb, int64_t M, int64_t N, int64_t K, double alpha,
+                       const void *A, int64_t lda, const uint8_t *SA, int64_t ldsa,
+                       const void *B, int64_t ldb, const uint8_t *SB, int64_t ldsb,
+                       double beta, const float *C, int64_t ldc,
+                       int64_t r0, int64_t r1, double *D, int64_t ldd, double *S, int64_t lds) {
+    if (bad_float_pair(ta, tb) || M < 0 || N < 0 || K < 0 || (K % 32) != 0 || r0 < 0 || r1 > M || r0 > r1) return -1;
+    if (beta != 0.0 && !C) return -1;
+    double *Bd = decode_b(tb, N, K, B, ldb);
+    if (!Bd) return -2;
+    const int64_t nb = K / 32;
+    int rc = 0;
+#pragma omp parallel
+    {
+        double *Ad = (double *)malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
+        if (!Ad) {
+#pragma omp atomic write
+            rc = -2;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t i = r0; i < r1; ++i) {
+                for (int64_t k = 0; k < K; ++k) Ad[k] = oracle_decode_one(ta, load_bits(ta, A, i * lda + k));
+                for (int64_t j = 0; j < N; ++j) {
+                    const double *bj = Bd + j * K;
+                    double acc = 0.0, sabs = 0.0;
+                    for (int64_t b = 0; b < nb; ++b) {
+                        const double scale = e8m0(SA[i * ldsa + b]) * e8m0(SB[j * ldsb + b]);
+                        for (int64_t k = 32 * b; k < 32 * b + 32; ++k) {
+                            double p = scale * (Ad[k] * bj[k]);
+                            acc += p;
+                            sabs += fabs(p);
+                        }
+                    }
+                    double d = alpha * acc;
+                    if (beta != 0.0) d += beta * (double)C[i * ldc + j];
+                    D[(i - r0) * ldd + j] = d;
+                    if (S) S[(i - r0) * lds + j] = sabs;
+                }
+            }
+            free(Ad);
+        }
+    }
+    free(Bd);
+    return rc;
+}
+
+/* The block-scaled GEMM at n individual output positions. */
+int oracle_gemm_mx_f64_entries(int ta, int tb, int64_t M, int64_t N, int64_t K, double alpha,
+                               const void *A, int64_t lda, const uint8_t *SA, int64_t ldsa,
+                               const void *B, int64_t ldb, const uint8_t *SB, int64_t ldsb,
+                               double beta, const float *C, int64_t ldc,
+                               int64_t n, const int64_t *ii, const int64_t *jj, double *out, double *S) {
+    if (bad_float_pair(ta, tb) || M < 0 || N < 0 || K < 0 || (K % 32) != 0) return -1;
+    if (beta != 0.0 && !C) return -1;
+    for (int64_t q = 0; q < n; ++q)
+        if (ii[q] < 0 || ii[q] >= M || jj[q] < 0 || jj[q] >= N) return -1;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t q = 0; q < n; ++q) {
+        const int64_t i = ii[q], j = jj[q];
+        double acc = 0.0, sabs = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double scale = e8m0(SA[i * ldsa + k / 32]) * e8m0(SB[j * ldsb + k / 32]);
+            double p = scale * (oracle_decode_one(ta, load_bits(ta, A, i * lda + k)) *
+                                oracle_decode_one(tb, load_bits(tb, B, j * ldb + k)));
+            acc += p;
+            sabs += fabs(p);
+        }
+        double d = alpha * acc;
+        if (beta != 0.0) d += beta * (double)C[i * ldc + j];
+        out[q] = d;
+        if (S) S[q] = sabs;
+    }
+    return 0;
+}
+
 /* Dense floating GEMM at n individual output positions (ii[q], jj[q]). */
 int oracle_gemm_dense_f64_entries(int ta, int tb, int64_t M, int64_t N, int64_t K, double alpha,
                                   const void *A, int64_t lda, const void *B, int64_t ldb,

@@ -524,3 +524,85 @@ def test_fp8_ties_and_saturation():
     out, _ = oracle.epilogue(np.array([[3.0, -500.0]]), np.array([0.25, 0.0], np.float32), oracle.ACT_NONE,
                              oracle.OUT_E4M3)
     assert out.dtype == np.uint8 and list(out[0]) == [0x45, 0xFE]      # 3.25 -> 3.25 (0x45), -500 -> -448
+
+
+# ------------------------------------------------------ block-scaled (MX) GEMM --
+# Not on the pages: the OCP microscaling definition (blocks of 32 along K, one
+# E8M0 scale 2^(e - 127) per block of a row of A and of a column of B).
+
+MX_PAIRS = [(E4M3, E4M3), (E4M3, E5M2), (E5M2, E4M3), (E5M2, E5M2)]
+
+
+def mx_inputs(ta, tb, M, N, K, seed, lo=117, hi=138):
+    g = np.random.default_rng(seed)
+    A = W.to_bits(g.standard_normal((M, K)), ta)
+    B = W.to_bits(g.standard_normal((N, K)), tb)
+    SA = g.integers(lo, hi, size=(M, K // 32)).astype(np.uint8)
+    SB = g.integers(lo, hi, size=(N, K // 32)).astype(np.uint8)
+    return A, B, SA, SB
+
+
+@pytest.mark.parametrize("ta,tb", MX_PAIRS)
+def test_mx_brute_force_fraction(ta, tb):
+    """Exact rational brute force (torch-decoded values, scales as Fractions)."""
+    M, N, K = 5, 4, 64
+    A, B, SA, SB = mx_inputs(ta, tb, M, N, K, ta * 10 + tb)
+    C = np.random.default_rng(1).standard_normal((M, N)).astype(np.float32)
+    D, S = oracle.gemm_mx(ta, tb, A, SA, B, SB, 0.75, -1.5, C)
+    Av, Bv = torch_decode(A, ta), torch_decode(B, tb)
+    for i in range(M):
+        for j in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                sc = Fraction(2) ** (int(SA[i, k // 32]) - 127) * Fraction(2) ** (int(SB[j, k // 32]) - 127)
+                acc += sc * Fraction(Av[i, k]) * Fraction(Bv[j, k])
+            want = Fraction(0.75) * acc + Fraction(-1.5) * Fraction(float(C[i, j]))
+            assert D[i, j] == float(want)
+
+
+@pytest.mark.parametrize("ta,tb", MX_PAIRS)
+def test_mx_unit_scales_equal_dense(ta, tb):
+    M, N, K = 9, 7, 96
+    A, B, _, _ = mx_inputs(ta, tb, M, N, K, 3)
+    ones_a = np.full((M, K // 32), 127, np.uint8)
+    ones_b = np.full((N, K // 32), 127, np.uint8)
+    D, S = oracle.gemm_mx(ta, tb, A, ones_a, B, ones_b)
+    D0, S0 = oracle.gemm_dense(ta, tb, A, B)
+    assert np.array_equal(D, D0) and np.array_equal(S, S0)
+
+
+def test_mx_block_scales_act_per_block():
+    """Raising one block's exponent by d multiplies exactly that block's contribution by 2^d;
+    the scale of a block of A acts on its row, that of B on its column; 255 is NaN."""
+    ta = tb = E4M3
+    M, N, K = 3, 2, 96
+    A, B, SA, SB = mx_inputs(ta, tb, M, N, K, 9, 127, 128)       # all scales 127
+    parts = []
+    for b in range(3):
+        keep = np.zeros((1, K), bool)
+        keep[0, 32 * b:32 * b + 32] = True
+        Ab = np.where(keep, A, W.zero_bits(ta)).astype(A.dtype)
+        parts.append(oracle.gemm_mx(ta, tb, Ab, SA, B, SB)[0])
+    SA2 = SA.copy()
+    SA2[1, 2] += 3
+    SB2 = SB.copy()
+    SB2[0, 0] -= 2
+    D, _ = oracle.gemm_mx(ta, tb, A, SA2, B, SB2)
+    want = parts[0] + parts[1] + parts[2]
+    want[1, :] += 7 * parts[2][1, :]                   # block 2 of row 1: x 2^3
+    want[:, 0] -= 0.75 * parts[0][:, 0]                # block 0 of column 0: x 2^-2
+    assert np.allclose(D, want, rtol=0, atol=1e-12)
+    SA2[2, 1] = 255
+    D, _ = oracle.gemm_mx(ta, tb, A, SA2, B, SB2)
+    assert np.isnan(D[2]).all() and np.isfinite(D[:2]).all()
+
+
+def test_mx_entries_match_full():
+    ta, tb = E5M2, E4M3
+    M, N, K = 40, 30, 128
+    A, B, SA, SB = mx_inputs(ta, tb, M, N, K, 4)
+    C = np.random.default_rng(2).standard_normal((M, N)).astype(np.float32)
+    D, S = oracle.gemm_mx(ta, tb, A, SA, B, SB, 1.5, 0.5, C)
+    ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    De, Se = oracle.gemm_mx_entries(ta, tb, A, SA, B, SB, ii.ravel(), jj.ravel(), 1.5, 0.5, C)
+    assert np.array_equal(De, D.ravel()) and np.array_equal(Se, S.ravel())
