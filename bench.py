@@ -361,6 +361,19 @@ def suite():
                     "workspace_MiB": round((0 if ws is None else ws.numel()) / 2 ** 20, 1)}
         del A, B, D, ws
 
+    # block-scaled (MX) fp8 x bf8 at 8192^3: E8M0 scales per 32-element block (scale words in the
+    # library's k-tile-major layout), 128 x 256 tiles
+    w = W.workload("fp8_8192")
+    M, N, K = w["M"], w["N"], w["K"]
+    A, B = to_dev(w["A"], w["ta"]), to_dev(w["B"], w["tb"])
+    SA = torch.full((K // 128, M), 0x7F7F7F7F, dtype=torch.int32, device=dev)
+    SB = torch.full((K // 128, N), 0x7F7F7F7F, dtype=torch.int32, device=dev)
+    D = torch.empty((M, N), dtype=torch.float32, device=dev)
+    ms = median_ms([lambda: mm.gemm_mx(A, SA, B, SB, D, a_type=w["ta"], b_type=w["tb"], stream=stream)], 20)
+    out["mx_fp8e4m3xbf8e5m2_8192^3"] = {"us": round(ms * 1e3, 1), "TFLOP/s": round(gemm_flops(M, N, K) / ms / 1e9, 1),
+                                         "shape": [M, N, K], "scales": "E8M0 per 32 along K"}
+    del A, B, SA, SB, D
+
     split_case(512, 512, 32768, W.BF16, "splitk_bf16_512x512x32768")
     split_case(256, 256, 65536, W.BF16, "splitk_bf16_256x256x65536")
     split_case(1024, 512, 8192, W.E4M3, "splitk_fp8e4m3_1024x512x8192")

@@ -267,6 +267,34 @@ mmac_status_t mmac_gemm_sparse24_ws(mmac_dtype_t a_type, mmac_dtype_t b_type,
                                     void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
+ * Block-scaled (MX) dense GEMM -- beyond the pages, which have no block
+ * scales; the format is the OCP Microscaling one: along K, every block of 32
+ * consecutive elements of a row of A (and of a column of B) shares one E8M0
+ * scale, an unsigned exponent e with value 2^(e - 127).  Computes
+ *   D = alpha * sum_b 2^(sa[i][b] - 127) * 2^(sb[j][b] - 127) * (A_b * B_b)[i][j] + beta * C
+ * with the gfx950 instruction v_mfma_scale_f32_32x32x64_f8f6f4, whose E8M0
+ * operands scale exactly these 32-element blocks.
+ *   a_type, b_type  FP8_E4M3 / BF8_E5M2, any pair.  K % 32 == 0.
+ *   A, B            as in mmac_gemm_dense.
+ *   SA              scale words of A: ceil(K/128) x ldsa 32-bit words,
+ *                   SA[t*ldsa + i] holds the exponents of blocks 4t .. 4t+3
+ *                   of row i in its bytes 0 .. 3 (byte q: block 4t + q,
+ *                   elements 32(4t+q) .. 32(4t+q)+31 along K).  ldsa >= M,
+ *                   ldsa % 4 == 0, SA 16-byte aligned.  Bytes of blocks at or
+ *                   past K/32 are ignored.
+ *   SB              the same for the N columns of B (ldsb >= N).
+ *   e = 255 (NaN in E8M0) in a block that is used gives unspecified results.
+ *   C, D, ep, stream and the error rules as in mmac_gemm_dense_ep.  Outputs
+ *   with M <= 32 rows use the tiled kernel (there is no skinny path here).
+ */
+mmac_status_t mmac_gemm_dense_mx(mmac_dtype_t a_type, mmac_dtype_t b_type,
+                                 int64_t M, int64_t N, int64_t K, double alpha,
+                                 const void *A, int64_t lda, const uint32_t *SA, int64_t ldsa,
+                                 const void *B, int64_t ldb, const uint32_t *SB, int64_t ldsb,
+                                 double beta, const void *C, int64_t ldc,
+                                 void *D, int64_t ldd, const mmac_epilogue_t *ep, void *stream);
+
+/*
  * Workspace bytes the _ws calls use for an M x N x K product with A of type
  * a_type (sparse != 0: mmac_gemm_sparse24_ws), under the current environment;
  * 0 when they would not split.  Host-only, no GPU work.

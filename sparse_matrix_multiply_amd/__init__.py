@@ -78,6 +78,9 @@ def lib():
         L.mmac_gemm_sparse24_ws.restype = i32
         L.mmac_gemm_sparse24_ws.argtypes = [i32, i32, i64, i64, i64, dbl, vp, i64, vp, i64, vp, i64, dbl, vp, i64,
                                             vp, i64, ep, vp, i64, vp]
+        L.mmac_gemm_dense_mx.restype = i32
+        L.mmac_gemm_dense_mx.argtypes = [i32, i32, i64, i64, i64, dbl, vp, i64, vp, i64, vp, i64, vp, i64, dbl, vp,
+                                         i64, vp, i64, ep, vp]
         L.mmac_gemm_workspace_bytes.restype = i64
         L.mmac_gemm_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
         L.mmac_status_string.restype = ctypes.c_char_p
@@ -201,6 +204,22 @@ def gemm_sparse24(Ac, idx, B, D, K=None, alpha=1.0, beta=0.0, C=None, a_type=Non
         _check(lib().mmac_gemm_sparse24(*args, _stream(stream)), "mmac_gemm_sparse24")
     else:
         _check(lib().mmac_gemm_sparse24_ep(*args, ctypes.byref(ep), _stream(stream)), "mmac_gemm_sparse24_ep")
+    return D
+
+
+def gemm_mx(A, SA, B, SB, D, alpha=1.0, beta=0.0, C=None, a_type=None, b_type=None, stream=None, bias=None,
+            act=ACT_NONE, d_type=None):
+    """Block-scaled (MX) GEMM: D = alpha * (A, SA) @ (B, SB) + beta * C.  A M x K and B N x K fp8;
+    SA and SB the E8M0 scale words (ceil(K/128) x >= M and ceil(K/128) x >= N int32 tensors,
+    four block exponents per word, see include/mmac.h).  Epilogue arguments as in gemm_dense."""
+    M, K = A.shape
+    N = B.shape[0]
+    ta, tb = _dtype(A, a_type), _dtype(B, b_type)
+    ep = _epilogue(D, bias, act, d_type)
+    st = lib().mmac_gemm_dense_mx(ta, tb, M, N, K, float(alpha), _ptr(A), _ld(A), _ptr(SA), _ld(SA), _ptr(B), _ld(B),
+                                  _ptr(SB), _ld(SB), float(beta), _ptr(C), _ld(C) if C is not None else 0, _ptr(D),
+                                  _ld(D), None if ep is None else ctypes.byref(ep), _stream(stream))
+    _check(st, "mmac_gemm_dense_mx")
     return D
 
 

@@ -302,6 +302,33 @@ mmac_status_t mmac_gemm_sparse24_ep(mmac_dtype_t a_type, mmac_dtype_t b_type, in
                                  ep, nullptr, 0, stream);
 }
 
+mmac_status_t mmac_gemm_dense_mx(mmac_dtype_t a_type, mmac_dtype_t b_type, int64_t M, int64_t N, int64_t K,
+                                 double alpha, const void *A, int64_t lda, const uint32_t *SA, int64_t ldsa,
+                                 const void *B, int64_t ldb, const uint32_t *SB, int64_t ldsb, double beta,
+                                 const void *C, int64_t ldc, void *D, int64_t ldd, const mmac_epilogue_t *ep_in,
+                                 void *stream) {
+    const mmac_epilogue_t ep = epilogue_of(ep_in);
+    if (valid_type(a_type) && valid_type(b_type) && (!is_fp8(a_type) || !is_fp8(b_type))) return MMAC_ERR_UNSUPPORTED;
+    if (K >= 0 && (K % 32) != 0) return MMAC_ERR_INVALID_ARG;
+    const mmac_status_t st = check_gemm(a_type, b_type, M, N, K, alpha, A, lda, K, B, ldb, beta, C, ldc, D, ldd, ep);
+    if (st != MMAC_OK) return st;
+    if ((K > 0 && (!SA || !SB)) || ldsa < M || ldsb < N || ldsa < 1 || ldsb < 1) return MMAC_ERR_INVALID_ARG;
+    const int64_t scale_rows = (K + 127) / 128;
+    if (scale_rows * std::max(ldsa, ldsb) * 4 >= ((int64_t)1 << 31)) return MMAC_ERR_UNSUPPORTED;
+    if ((ldsa % 4) || (ldsb % 4) || !aligned16(SA) || !aligned16(SB)) return MMAC_ERR_MISALIGNED;
+    if (M == 0 || N == 0) return MMAC_OK;
+    // the 8-wave 256 x 256 tile has no registers left for the scale words: its 128 x 256 half instead
+    TileShape shape = pick_shape(M, N, true);
+    if (shape == TILE_256) shape = TILE_128x256;
+    GemmParams p = make_params(a_type, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd, ep, shape);
+    p.sa = SA;
+    p.sb = SB;
+    p.ldsa = ldsa;
+    p.ldsb = ldsb;
+    p.scale_rows = (int)scale_rows;
+    return launched(launch_gemm_mx(a_type, b_type, shape, p, static_cast<hipStream_t>(stream)));
+}
+
 int64_t mmac_gemm_workspace_bytes(mmac_dtype_t a_type, int64_t M, int64_t N, int64_t K, int sparse) {
     if (!valid_type(a_type) || M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
     return plan_split(a_type, M, N, K, sparse != 0).bytes;

@@ -197,7 +197,8 @@ __device__ __forceinline__ i32x8 join(const Frag<32> &f) {
 
 // Dense bf16 / fp16: v_mfma_f32_32x32x16_{bf16,f16}, 8 elements (16 B) per lane.
 template <int DT> struct MmaDense16 {
-    static constexpr bool kSparse = false;
+    static constexpr bool kSparse = false, kScaled = false;
+    static constexpr int kScaleWords = 0;
     static constexpr int kEsize = 2, kAFrag = 16, kBFrag = 16, kKStep = 16;
     static constexpr int kBK = 64;                 // dense K per LDS k-tile
     static constexpr int kARowBytes = kBK * kEsize, kBRowBytes = kBK * kEsize;
@@ -218,7 +219,8 @@ template <int DT> struct MmaDense16 {
 
 // Dense int8: v_mfma_i32_32x32x32_i8, 16 elements (16 B) per lane.
 struct MmaDenseI8 {
-    static constexpr bool kSparse = false;
+    static constexpr bool kSparse = false, kScaled = false;
+    static constexpr int kScaleWords = 0;
     static constexpr int kEsize = 1, kAFrag = 16, kBFrag = 16, kKStep = 32;
     static constexpr int kBK = 128;
     static constexpr int kARowBytes = kBK, kBRowBytes = kBK;
@@ -234,7 +236,8 @@ struct MmaDenseI8 {
 // Dense fp8 / bf8 (OCP): v_mfma_f32_32x32x64_f8f6f4 with unit scales; the
 // format selectors name the A and B formats (0 = E4M3, 1 = E5M2).
 template <int FA, int FB> struct MmaDenseF8 {
-    static constexpr bool kSparse = false;
+    static constexpr bool kSparse = false, kScaled = false;
+    static constexpr int kScaleWords = 0;
     static constexpr int kEsize = 1, kAFrag = 32, kBFrag = 32, kKStep = 64;
     static constexpr int kBK = 128;
     static constexpr int kARowBytes = kBK, kBRowBytes = kBK;
@@ -244,6 +247,33 @@ template <int FA, int FB> struct MmaDenseF8 {
     __device__ __forceinline__ static constexpr int b_unit(int s, int g, int h) { return 4 * s + 2 * g + h; }
     __device__ __forceinline__ static acc_t mma(const Frag<32> &a, const Frag<32> &b, acc_t c, uint32_t) {
         return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(join(a), join(b), c, FA, FB, 0, 0, 0, 0);
+    }
+};
+
+// Block-scaled (MX) fp8 / bf8: v_mfma_scale_f32_32x32x64_f8f6f4 with E8M0
+// scale operands.  The instruction's own K order within its 64-K step puts
+// K 16g .. 16g+15 in the first 16 bytes of lane half g's operand and
+// K 32+16g .. 32+16g+15 in the second (the order the sparse B fragments
+// above also show), and scales its K block 32c .. 32c+31 with byte 0 of the
+// scale operand of lane half c.  So these fragments load, for lane half g of
+// step s, the 16-byte units 4s + g and 4s + 2 + g: the instruction's K order is
+// then the matrix's, and lane half g's scale byte is that of block 2s + g of
+// the k-tile.  Established on gfx950 with one-wave probes (lane-, row- and
+// column-dependent scales, byte select) and with one-block-scaled GEMMs
+// through this library (each block's exponent doubled in turn, K chunks
+// weighted by distinct powers of two); every MX parity test rechecks it.
+// (For the unscaled dense product the unit order does not matter: A and B
+// use the same one.)  Scale words come in per k-tile: kScaleWords words of
+// four block exponents per row of A and per column of B.
+template <int FA, int FB> struct MmaMX : MmaDenseF8<FA, FB> {
+    typedef typename MmaDenseF8<FA, FB>::acc_t acc_t;
+    static constexpr bool kScaled = true;
+    static constexpr int kScaleWords = MmaDenseF8<FA, FB>::kBK / 128;
+    __device__ __forceinline__ static constexpr int a_unit(int s, int g, int h) { return 4 * s + g + 2 * h; }
+    __device__ __forceinline__ static constexpr int b_unit(int s, int g, int h) { return 4 * s + g + 2 * h; }
+    __device__ __forceinline__ static acc_t mma_scaled(const Frag<32> &a, const Frag<32> &b, acc_t c, uint32_t sa,
+                                                       uint32_t sb) {
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(join(a), join(b), c, FA, FB, 0, (int)sa, 0, (int)sb);
     }
 };
 
@@ -261,7 +291,8 @@ template <int FA, int FB> struct MmaDenseF8 {
 // index bits (4 groups).  One index word covers the instruction's 32 dense K;
 // lane half g takes its bits [16g, 16g + 16).
 template <int DT> struct MmaSparse16 {
-    static constexpr bool kSparse = true;
+    static constexpr bool kSparse = true, kScaled = false;
+    static constexpr int kScaleWords = 0;
     static constexpr int kEsize = 2, kAFrag = 16, kBFrag = 32, kKStep = 32;
     static constexpr int kBK = 64;                 // 64-byte compressed A rows, 128-byte B rows
     static constexpr int kARowBytes = kBK / 2 * kEsize, kBRowBytes = kBK * kEsize;
@@ -296,7 +327,8 @@ template <int DT> struct MmaSparse16 {
 // compressed A bytes = 32 dense K, 32 dense B bytes, 32 index bits (8 groups).
 // The instruction's 64 dense K take two index words; lane half g takes word g.
 template <int DT_A, int DT_B> struct MmaSparse8 {
-    static constexpr bool kSparse = true;
+    static constexpr bool kSparse = true, kScaled = false;
+    static constexpr int kScaleWords = 0;
     static constexpr int kEsize = 1, kAFrag = 16, kBFrag = 32, kKStep = 64;
     static constexpr int kBK = 128;                // 64-byte compressed A rows, 128-byte B rows
     static constexpr int kARowBytes = kBK / 2, kBRowBytes = kBK;

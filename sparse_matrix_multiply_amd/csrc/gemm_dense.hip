@@ -20,4 +20,13 @@ hipError_t launch_gemm_dense(int a, int b, TileShape shape, GemmParams p, hipStr
     return hipErrorInvalidValue;
 }
 
+hipError_t launch_gemm_mx(int a, int b, TileShape shape, GemmParams p, hipStream_t s) {
+    // f8f6f4 format selectors: 0 = E4M3, 1 = E5M2
+    if (a == DT_E4M3 && b == DT_E4M3) return launch_dense_op<MmaMX<0, 0>>(shape, p, s);
+    if (a == DT_E4M3 && b == DT_E5M2) return launch_dense_op<MmaMX<0, 1>>(shape, p, s);
+    if (a == DT_E5M2 && b == DT_E4M3) return launch_dense_op<MmaMX<1, 0>>(shape, p, s);
+    if (a == DT_E5M2 && b == DT_E5M2) return launch_dense_op<MmaMX<1, 1>>(shape, p, s);
+    return hipErrorInvalidValue;
+}
+
 }  // namespace mmac

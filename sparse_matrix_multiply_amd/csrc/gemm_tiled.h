@@ -144,16 +144,27 @@ struct TiledGemm {
     static_assert(AUPW * NW == BM * AW && BUPW * NW == BN * BW && IUPW * NW * IES == BM * IW * 4,
                   "uneven copy split");
     static constexpr int AP = (AUPW + 63) / 64, BP = (BUPW + 63) / 64, IP = (IUPW + 63) / 64;  // passes
-    static constexpr int LPT = AP + BP + IP;        // copy instructions per wave per k-tile
+    // Block-scaled operands: SW scale words per row of A and per column of B
+    // per k-tile, copied as 16-byte units (four rows' words), one pass for A's
+    // and one for B's in every wave.
+    static constexpr bool SCALED = Op::kScaled;
+    static constexpr int SW = Op::kScaleWords;
+    static constexpr int SAUPW = SCALED ? BM * SW / 4 / NW : 0, SBUPW = SCALED ? BN * SW / 4 / NW : 0;
+    static_assert(!SCALED || (SAUPW * NW * 4 == BM * SW && SBUPW * NW * 4 == BN * SW && SAUPW >= 1 && SBUPW >= 1 &&
+                              SAUPW <= 64 && SBUPW <= 64), "scale copy split");
+    static constexpr int SP = SCALED ? 2 : 0;
+    static constexpr int LPT = AP + BP + IP + SP;   // copy instructions per wave per k-tile
     static constexpr int A_BYTES = BM * AW * 16, B_BYTES = BN * BW * 16, I_BYTES = BM * IW * 4;
-    static constexpr int STAGE = A_BYTES + B_BYTES + I_BYTES;
+    static constexpr int S_BYTES = SCALED ? (BM + BN) * SW * 4 : 0;
+    static constexpr int STAGE = A_BYTES + B_BYTES + I_BYTES + S_BYTES;
+    static constexpr int NSW = SCALED ? (TM + TN) * SW : 1;   // scale words a lane holds per k-tile
     static constexpr int LDS_BYTES = STAGES * STAGE;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 workgroup");
 
     const GemmParams &p;
     int wave, lane, g, l32, wm, wn, row0, col0;
     int tile, split, kt0;   // output tile number, K range, its first k-tile
-    rsrc_t ra, rb, rx;
+    rsrc_t ra, rb, rx, rsa, rsb;
     acc_t acc[TM][TN];
 
     __device__ __forceinline__ TiledGemm(const GemmParams &p_) : p(p_) {
@@ -175,6 +186,10 @@ struct TiledGemm {
         rb = make_rsrc(p.B + (int64_t)col0 * p.b_pitch, (uint32_t)(bcols * p.b_pitch));
         if constexpr (Op::kSparse)
             rx = make_rsrc(p.idx + (int64_t)row0 * p.idx_pitch, (uint32_t)(arows * p.idx_pitch * 4));
+        if constexpr (SCALED) {
+            rsa = make_rsrc(p.sa + row0, (uint32_t)((p.scale_rows * p.ldsa - row0) * 4));
+            rsb = make_rsrc(p.sb + col0, (uint32_t)((p.scale_rows * p.ldsb - col0) * 4));
+        }
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -196,7 +211,17 @@ struct TiledGemm {
         return (r * (uint32_t)p.idx_pitch + (kt + kt0) * IW) * 4 + byte % (IW * 4);
     }
 
-    // Copy instruction j (0 <= j < LPT: the A passes, then B, then the index)
+    // Byte offset (from the tile's first row / column) of 16-byte scale unit u
+    // of a k-tile: words 4u .. 4u + 3 of the tile's ROWS x SW words, laid out
+    // word-of-k-tile major, which are rows r .. r + 3 of scale-word row
+    // (kt + kt0) * SW + c of the source.
+    template <int ROWS>
+    __device__ __forceinline__ uint32_t scale_off(uint32_t u, int64_t ld, int kt) const {
+        const uint32_t w0 = 4 * u, c = w0 / ROWS, r = w0 % ROWS;
+        return (uint32_t)((((int64_t)(kt + kt0) * SW + c) * ld + r) * 4);
+    }
+
+    // Copy instruction j (0 <= j < LPT: the A passes, then B, then the index or the scales)
     // of k-tile kt into LDS stage `st`; each writes one contiguous run of LDS.
     __device__ __forceinline__ void dma_pass(uint8_t *st, int kt, int j) const {
         if (j < AP) {
@@ -215,6 +240,18 @@ struct TiledGemm {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     rx, (lds_void *)(st + A_BYTES + B_BYTES + (wave * IUPW + q * 64) * IES), IES,
                     idx_off(wave * IUPW + u, kt), 0, 0, 0);
+        } else if constexpr (SCALED) {
+            uint8_t *ss = st + A_BYTES + B_BYTES + I_BYTES;
+            if (j == AP + BP) {
+                if (lane < SAUPW)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void *)(ss + wave * SAUPW * 16), 16,
+                                                             scale_off<BM>(wave * SAUPW + lane, p.ldsa, kt), 0, 0, 0);
+            } else {
+                if (lane < SBUPW)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void *)(ss + BM * SW * 4 + wave * SBUPW * 16),
+                                                             16, scale_off<BN>(wave * SBUPW + lane, p.ldsb, kt), 0, 0,
+                                                             0);
+            }
         }
     }
 
@@ -260,8 +297,8 @@ struct TiledGemm {
 
     // Fragments of step s of the k-tile held in LDS stage `st`, and with step 0
     // the index words of every step of that k-tile (sparse A).
-    __device__ __forceinline__ void load_frags(FragA (&a)[TM], FragB (&b)[TN], IdxT (&ix)[TM], const uint8_t *st,
-                                               int s) const {
+    __device__ __forceinline__ void load_frags(FragA (&a)[TM], FragB (&b)[TN], IdxT (&ix)[TM], uint32_t (&sw)[NSW],
+                                               const uint8_t *st, int s) const {
         const uint8_t *sa = st, *sb = st + A_BYTES;
         const uint32_t *sx = reinterpret_cast<const uint32_t *>(st + A_BYTES + B_BYTES);
 #pragma unroll
@@ -279,11 +316,39 @@ struct TiledGemm {
             const uint32_t r = (wn * WTN + j * 32 + l32) * BW;
             lds_frag<BW>(b[j], sb, r + Op::b_unit(s, g, 0), r + Op::b_unit(s, g, 1));
         }
+        if constexpr (SCALED) {
+            if (s == 0) {   // this lane's row / column scale words of the whole k-tile
+                const uint32_t *ss = reinterpret_cast<const uint32_t *>(st + A_BYTES + B_BYTES + I_BYTES);
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int c = 0; c < SW; ++c) sw[i * SW + c] = ss[c * BM + wm * WTM + i * 32 + l32];
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int c = 0; c < SW; ++c) sw[(TM + j) * SW + c] = ss[BM * SW + c * BN + wn * WTN + j * 32 + l32];
+            }
+        }
+    }
+
+    // Scale bytes of blocks past K (in the ragged last k-tile) become 127
+    // (2^0): their elements are zero, and a 255 (NaN) there must not reach
+    // the sum.  `valid` = blocks of the k-tile that lie before K.
+    __device__ __forceinline__ static void mask_scales(uint32_t (&sw)[NSW], int valid) {
+        if constexpr (SCALED) {
+#pragma unroll
+            for (int w = 0; w < NSW; ++w) {
+                const int n = min(max(valid - 4 * (w % SW), 0), 4);
+                const uint32_t keep = n >= 4 ? 0xffffffffu : (1u << (8 * n)) - 1u;
+                sw[w] = (sw[w] & keep) | (0x7f7f7f7fu & ~keep);
+            }
+        }
     }
 
     // Instruction counts of one step, for the interleaving below.
     static constexpr int NMMA = TM * TN;
-    static constexpr int NREAD = TM * (Op::kAFrag / 16) + TN * (Op::kBFrag / 16) + (Op::kSparse ? TM : 0);
+    static constexpr int NREAD = TM * (Op::kAFrag / 16) + TN * (Op::kBFrag / 16) + (Op::kSparse ? TM : 0) +
+                                 (SCALED ? (TM + TN) * SW : 0);
 
     // Index operand of the matrix instruction of step s.
     __device__ __forceinline__ uint32_t step_idx(const IdxT &x, int s) const {
@@ -295,12 +360,25 @@ struct TiledGemm {
     // with the LDS reads (next step's fragments) and copy instructions issued
     // before them in the same region: one matrix instruction, then one read,
     // then one copy, so the reads and copies go out while the matrix unit works.
-    __device__ __forceinline__ void mma_step(const FragA (&a)[TM], const FragB (&b)[TN], const IdxT (&ix)[TM], int s,
-                                             int ncopies) {
+    __device__ __forceinline__ void mma_step(const FragA (&a)[TM], const FragB (&b)[TN], const IdxT (&ix)[TM],
+                                             const uint32_t (&sw)[NSW], int s, int ncopies) {
+        if constexpr (SCALED) {
+            // lane half g of step s holds block q = 2s + g of the k-tile (64 K per step): byte q % 4 of
+            // word q / 4 of its row's and column's scale words
+            const int q = 2 * s + g;
+            const uint32_t sh = 8 * (q & 3);
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] = Op::mma(a[i], b[j], acc[i][j], step_idx(ix[i], s));
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = Op::mma_scaled(a[i], b[j], acc[i][j], sw[i * SW + (q >> 2)] >> sh,
+                                               sw[(TM + j) * SW + (q >> 2)] >> sh);
+        } else {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i][j] = Op::mma(a[i], b[j], acc[i][j], step_idx(ix[i], s));
+        }
 #pragma unroll
         for (int k = 0; k < NMMA; ++k) {
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
@@ -313,6 +391,7 @@ struct TiledGemm {
     FragA a0[TM], a1[TM];
     FragB b0[TN], b1[TN];
     IdxT x0[TM], x1[TM];
+    uint32_t sw0[NSW], sw1[NSW];   // scale words of the current and the next k-tile
 
     // One k-tile: start the copy of k-tile kt + STAGES - 1 into the stage that
     // k-tile kt - 1 freed, then the STEPS steps of k-tile kt (in stage `cur`).
@@ -352,7 +431,7 @@ struct TiledGemm {
 #pragma unroll
         for (int s = 0; s < STEPS; ++s) {
             if (s + 1 < STEPS) {
-                load_frags(a1, b1, x1, sc, s + 1);
+                load_frags(a1, b1, x1, sw1, sc, s + 1);
             } else {
                 if constexpr (STEADY) {
                     wait_vm_lgkm0<STEADY_WAIT>();
@@ -370,14 +449,22 @@ struct TiledGemm {
                     if (pre < nk) dma(st_pre, pre);
                     else fill_masked(st_pre, pre);
                 }
-                load_frags(a1, b1, x1, sn, 0);   // past the last k-tile this reads a stale stage, unused
+                load_frags(a1, b1, x1, sw1, sn, 0);   // past the last k-tile this reads a stale stage, unused
+                if constexpr (SCALED && !STEADY)
+                    if (kt + 1 == nk && nkt > nk) mask_scales(sw1, p.K / 32 - (kt0 + nk) * 4 * SW);
             }
             const int ncopies = !STEADY ? 0 : (s + 1 == STEPS ? LPT - P0 : (s == 0 ? P0 : 0));
-            mma_step(a0, b0, x0, s, ncopies);
+            mma_step(a0, b0, x0, sw0, s, ncopies);
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 a0[i] = a1[i];
                 if (s + 1 == STEPS) x0[i] = x1[i];   // index words change once per k-tile
+            }
+            if constexpr (SCALED) {
+                if (s + 1 == STEPS) {
+#pragma unroll
+                    for (int w = 0; w < NSW; ++w) sw0[w] = sw1[w];
+                }
             }
 #pragma unroll
             for (int j = 0; j < TN; ++j) b0[j] = b1[j];
@@ -765,7 +852,9 @@ void gemm_tiled_kernel(GemmParams p) {
         wait_copies<T::LPT, T::AHEAD - 1>(after <= 0 || after >= nk ? 0 : after);
         block_barrier();
     }
-    if (nkt > 0) t.load_frags(t.a0, t.b0, t.x0, smem, 0);
+    if (nkt > 0) t.load_frags(t.a0, t.b0, t.x0, t.sw0, smem, 0);
+    if constexpr (T::SCALED)
+        if (nk == 0 && nkt > 0) t.mask_scales(t.sw0, p.K / 32 - t.kt0 * 4 * T::SW);
     int kt = 0, cur = 0;
     for (; kt + T::AHEAD < nk; ++kt) {
         t.template iteration<true>(smem, kt, cur, nk, nkt);

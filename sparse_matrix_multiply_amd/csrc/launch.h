@@ -15,6 +15,12 @@ struct GemmParams {
     int64_t b_pitch;
     const uint32_t *idx;
     int64_t idx_pitch;
+    // Block-scaled A and B (MX): E8M0 scale words, four 32-element blocks
+    // along K per word; word t of row i of A at sa[t * ldsa + i] (t < scale_rows
+    // = ceil(K / 128)), likewise sb for the columns of B.
+    const uint32_t *sa, *sb;
+    int64_t ldsa, ldsb;
+    int scale_rows;
     const void *C;
     int64_t ldc;
     void *D;
@@ -71,6 +77,7 @@ enum TileShape : int { TILE_256 = 0, TILE_128 = 1, TILE_64 = 2, TILE_SKINNY = 3,
 hipError_t launch_gemm_dense(int dt_a, int dt_b, TileShape shape, GemmParams p, hipStream_t s);
 hipError_t launch_gemm_sparse(int dt_a, int dt_b, TileShape shape, GemmParams p, hipStream_t s);
 hipError_t launch_gemm_skinny(int dt_a, int dt_b, GemmParams p, hipStream_t s);
+hipError_t launch_gemm_mx(int dt_a, int dt_b, TileShape shape, GemmParams p, hipStream_t s);
 hipError_t launch_compress(int dt, CompressParams p, bool prune, hipStream_t s);
 
 // Geometry of a tile shape.

@@ -1,4 +1,5 @@
-// Dense GEMM instantiations: bf16, fp16, int8 and the four OCP fp8/bf8 pairs.
+// Dense GEMM instantiations: bf16, fp16, int8, the four OCP fp8/bf8 pairs and
+// their block-scaled (MX) forms.
 // LDS stages of 128-byte rows: two for 256 x 256 tiles (64 KiB each; the next
 // copy goes out right after the barrier that frees a stage), three for the
 // 256 x 128 halves, four for the smaller tiles.
@@ -15,7 +16,11 @@ template <class Op>
 hipError_t launch_dense_op(TileShape shape, const GemmParams &p, hipStream_t s) {
     const dim3 grid(p.tiles_m * p.tiles_n * p.splits), block(256);   // one workgroup per tile and K range
     switch (shape) {
-    case TILE_256: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 256, 256, 2, 4, 2>), grid, dim3(512), 0, s, p); break;
+    case TILE_256:
+        // block-scaled operands: the 8-wave tile has no registers left for the scale words
+        if constexpr (Op::kScaled) return hipErrorInvalidValue;
+        else hipLaunchKernelGGL((gemm_tiled_kernel<Op, 256, 256, 2, 4, 2>), grid, dim3(512), 0, s, p);
+        break;
     case TILE_256x128: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 256, 128, 2, 2, 3>), grid, block, 0, s, p); break;
     case TILE_128x256: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 128, 256, 2, 2, 3>), grid, block, 0, s, p); break;
     case TILE_128: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 128, 128, 2, 2, 4>), grid, block, 0, s, p); break;

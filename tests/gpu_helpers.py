@@ -134,3 +134,19 @@ def sample_entries(M, N, n, seed, tiles=((0, 0),), tile=256):
     ii.append(g.integers(0, M, n))
     jj.append(g.integers(0, N, n))
     return np.concatenate(ii).astype(np.int64), np.concatenate(jj).astype(np.int64)
+
+
+def pack_mx_scales(S, ld=None, seed=0):
+    """Row-major E8M0 exponents (rows x K/32 bytes) -> the library's scale-word layout:
+    ceil(K/128) x ld int32 words, word (t, i) holding the exponents of blocks 4t .. 4t+3 of row i
+    in bytes 0 .. 3.  The bytes of blocks past K/32 and the pitch padding are filled with random
+    bytes (255 included): the library must ignore them."""
+    S = np.ascontiguousarray(S, np.uint8)
+    rows, nb = S.shape
+    t = (nb + 3) // 4
+    ld = ((rows + 3) // 4 * 4) if ld is None else ld
+    g = np.random.default_rng(seed)
+    full = g.integers(0, 256, size=(ld, 4 * t)).astype(np.uint8)
+    full[:rows, :nb] = S
+    words = full.view("<u4").reshape(ld, t).T                # (t, ld)
+    return torch.from_numpy(np.ascontiguousarray(words).view(np.int32)).to(dev())

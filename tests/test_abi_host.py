@@ -32,7 +32,8 @@ def L():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["mmac_gemm_dense", "mmac_gemm_dense_ep", "mmac_gemm_dense_ws",
+    assert declared_functions() == ["mmac_gemm_dense", "mmac_gemm_dense_ep", "mmac_gemm_dense_mx",
+                                    "mmac_gemm_dense_ws",
                                     "mmac_gemm_sparse24", "mmac_gemm_sparse24_ep", "mmac_gemm_sparse24_ws",
                                     "mmac_gemm_workspace_bytes", "mmac_sparse24_compress",
                                     "mmac_sparse24_prune_compress", "mmac_status_string"]
@@ -246,3 +247,34 @@ def test_workspace_argument_errors(L, ws, nbytes, code):
 def test_workspace_calls_validate_like_the_plain_ones(L):
     assert dense_ws(L, None, 0, ldd=1000) == mm.ERR_INVALID_ARG
     assert dense_ws(L, None, 0, M=0) == mm.OK
+
+
+def dense_mx(L, **kw):
+    a = dict(a=mm.FP8_E4M3, b=mm.BF8_E5M2, M=64, N=64, K=256, alpha=1.0, A=P, lda=256, SA=P, ldsa=64, B=P, ldb=256,
+             SB=P, ldsb=64, beta=0.0, C=None, ldc=64, D=P, ldd=64, stream=None)
+    a.update(kw)
+    return L.mmac_gemm_dense_mx(a["a"], a["b"], a["M"], a["N"], a["K"], a["alpha"], a["A"], a["lda"], a["SA"],
+                                a["ldsa"], a["B"], a["ldb"], a["SB"], a["ldsb"], a["beta"], a["C"], a["ldc"], a["D"],
+                                a["ldd"], None, a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(a=mm.BF16, b=mm.BF16), mm.ERR_UNSUPPORTED),
+    (dict(a=mm.I8, b=mm.I8), mm.ERR_UNSUPPORTED),
+    (dict(a=mm.FP8_E4M3, b=mm.BF16), mm.ERR_UNSUPPORTED),
+    (dict(K=48, lda=64, ldb=64), mm.ERR_INVALID_ARG),                 # K % 32 != 0
+    (dict(SA=None), mm.ERR_INVALID_ARG),
+    (dict(SB=None), mm.ERR_INVALID_ARG),
+    (dict(ldsa=60), mm.ERR_INVALID_ARG),                             # < M
+    (dict(ldsb=62, N=60, ldd=64), mm.ERR_MISALIGNED),                 # ldsb % 4
+    (dict(SA=P + 4), mm.ERR_MISALIGNED),
+    (dict(SB=P + 8), mm.ERR_MISALIGNED),
+    (dict(lda=200), mm.ERR_INVALID_ARG),
+])
+def test_mx_argument_errors(L, kw, code):
+    assert dense_mx(L, **kw) == code
+
+
+def test_mx_empty_is_a_no_op(L):
+    assert dense_mx(L, M=0) == mm.OK
+    assert dense_mx(L, N=0) == mm.OK

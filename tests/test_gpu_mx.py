@@ -1,0 +1,122 @@
+"""GPU parity of the block-scaled (MX) GEMM, mmac_gemm_dense_mx, against the oracle.
+
+Every fp8/bf8 pair and tile shape, ragged M, N and K (K a multiple of 32 but not of the
+128-element k-tile, so the last k-tile holds one to three blocks), scale exponents spread
+over 2^-20 .. 2^20, garbage (255 included) in the scale bytes past K and in the pitch
+padding, beta != 0, M <= 32; exact small-integer products with random power-of-two block
+scales (bit for bit); the epilogue variants on top; and the 8192^3 fp8 x bf8 shape against
+two whole 256 x 256 output tiles plus 20 000 sampled entries.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_matrix_multiply_amd as mm
+import workloads as W
+from gpu_helpers import assert_close, dev, env, out_tensor, pack_mx_scales, sample_entries, to_dev_bits
+from oracle import E4M3, E5M2
+
+pytestmark = pytest.mark.gpu
+
+PAIRS = [(E4M3, E4M3), (E4M3, E5M2), (E5M2, E4M3), (E5M2, E5M2)]
+
+
+def mx_problem(ta, tb, M, N, K, seed, integers=False, lo=107, hi=148):
+    g = np.random.default_rng(seed)
+    if integers:
+        A = W.to_bits(g.integers(-4, 5, size=(M, K)).astype(np.float64), ta)
+        B = W.to_bits(g.integers(-4, 5, size=(N, K)).astype(np.float64), tb)
+    else:
+        A = W.to_bits(g.standard_normal((M, K)), ta)
+        B = W.to_bits(g.standard_normal((N, K)), tb)
+    SA = g.integers(lo, hi, size=(M, K // 32)).astype(np.uint8)
+    SB = g.integers(lo, hi, size=(N, K // 32)).astype(np.uint8)
+    C = g.standard_normal((M, N)).astype(np.float32)
+    return A, B, SA, SB, C
+
+
+def run_mx(ta, tb, A, SA, B, SB, alpha, beta, C, D=None, ld_pad=0, **kw):
+    M, N = A.shape[0], B.shape[0]
+    if D is None:
+        D = out_tensor(M, N, False)
+    SAd = pack_mx_scales(SA, ld=(M + 3) // 4 * 4 + ld_pad, seed=1)
+    SBd = pack_mx_scales(SB, ld=(N + 3) // 4 * 4 + ld_pad, seed=2)
+    Cd = torch.from_numpy(np.ascontiguousarray(C)).to(dev()) if beta != 0 and C is not None else None
+    mm.gemm_mx(to_dev_bits(A, ta), SAd, to_dev_bits(B, tb), SBd, D, alpha, beta, Cd, a_type=ta, b_type=tb, **kw)
+    torch.cuda.synchronize()
+    return D
+
+
+@pytest.mark.parametrize("ta,tb", PAIRS)
+@pytest.mark.parametrize("tile", [256, 2561, 1282, 128, 64])
+@pytest.mark.parametrize("M,N,K", [(64, 64, 128), (300, 260, 32 * 37), (33, 300, 1024), (257, 130, 96), (5, 7, 32)])
+def test_mx_matches_oracle(ta, tb, tile, M, N, K):
+    A, B, SA, SB, C = mx_problem(ta, tb, M, N, K, M + 3 * N + K + 7 * ta + tb)
+    with env(MMAC_TILE=tile):
+        D = run_mx(ta, tb, A, SA, B, SB, 1.25, -0.5, C, ld_pad=4).cpu().numpy()
+    Dref, S = oracle.gemm_mx(ta, tb, A, SA, B, SB, 1.25, -0.5, C)
+    assert_close(D, Dref, S, ta, K, 1.25, -0.5, C, f"mx {ta},{tb} {M}x{N}x{K} tile {tile}")
+
+
+@pytest.mark.parametrize("ta,tb", PAIRS)
+def test_mx_small_integers_exact(ta, tb):
+    """|a|, |b| <= 4 with block exponents 2^-2 .. 2^2 on each side: every partial sum is a
+    multiple of 2^-4 below 2^18, exact in fp32 -- the GPU must give the oracle's bits."""
+    M, N, K = 130, 70, 32 * 21
+    A, B, SA, SB, C = mx_problem(ta, tb, M, N, K, 5 + ta + tb, integers=True, lo=125, hi=130)
+    C = np.round(C * 8) / 8
+    for tile in (1282, 64):
+        with env(MMAC_TILE=tile):
+            D = run_mx(ta, tb, A, SA, B, SB, 1.0, 1.0, C).cpu().numpy()
+        Dref, _ = oracle.gemm_mx(ta, tb, A, SA, B, SB, 1.0, 1.0, C)
+        assert np.array_equal(D.astype(np.float64), Dref), f"tile {tile}"
+
+
+def test_mx_epilogue_variant_exact():
+    """bfloat16 C and D, bias and ReLU after the block-scaled sum (integer data, exact)."""
+    ta, tb = E4M3, E5M2
+    M, N, K = 200, 136, 512
+    A, B, SA, SB, _ = mx_problem(ta, tb, M, N, K, 11, integers=True, lo=126, hi=129)
+    g = np.random.default_rng(12)
+    C = g.integers(-64, 65, size=(M, N)).astype(np.float32)
+    bias = g.integers(-300, 301, size=N).astype(np.float32)
+    Y, _ = oracle.gemm_mx(ta, tb, A, SA, B, SB, 1.0, 1.0, C)
+    ref, _ = oracle.epilogue(Y, bias, mm.ACT_RELU, oracle.OUT_BF16)
+    D = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev())
+    Cd = torch.from_numpy(C).to(dev()).to(torch.bfloat16)
+    mm.gemm_mx(to_dev_bits(A, ta), pack_mx_scales(SA), to_dev_bits(B, tb), pack_mx_scales(SB), D, 1.0, 1.0, Cd,
+               a_type=ta, b_type=tb, bias=torch.from_numpy(bias).to(dev()), act=mm.ACT_RELU)
+    torch.cuda.synchronize()
+    assert np.array_equal(D.view(torch.int16).cpu().numpy().view(np.uint16), ref)
+
+
+def test_mx_unit_scales_match_plain_fp8():
+    """All exponents 127: the block-scaled GEMM is the plain fp8 GEMM (same tile shape, same
+    summation order: the same bits)."""
+    ta, tb = E4M3, E5M2
+    M, N, K = 300, 270, 1024
+    A, B, _, _, C = mx_problem(ta, tb, M, N, K, 13)
+    ones_a = np.full((M, K // 32), 127, np.uint8)
+    ones_b = np.full((N, K // 32), 127, np.uint8)
+    with env(MMAC_TILE=1282):
+        D = run_mx(ta, tb, A, ones_a, B, ones_b, 1.0, 0.0, None).cpu().numpy()
+        D0 = out_tensor(M, N, False)
+        mm.gemm_dense(to_dev_bits(A, ta), to_dev_bits(B, tb), D0, a_type=ta, b_type=tb)
+        torch.cuda.synchronize()
+    assert np.array_equal(D.view(np.uint32), D0.cpu().numpy().view(np.uint32))
+
+
+def test_mx_8192_sampled():
+    """The 8192^3 fp8 x bf8 workload's operands with random block exponents, in the launch
+    configuration the library picks (128 x 256 tiles)."""
+    w = W.workload("fp8_8192")
+    ta, tb, M, N, K = w["ta"], w["tb"], w["M"], w["N"], w["K"]
+    g = np.random.default_rng(31)
+    SA = g.integers(117, 138, size=(M, K // 32)).astype(np.uint8)
+    SB = g.integers(117, 138, size=(N, K // 32)).astype(np.uint8)
+    D = run_mx(ta, tb, w["A"], SA, w["B"], SB, 1.0, 0.0, None)
+    ii, jj = sample_entries(M, N, 20000, 14, tiles=((0, 0), ((M - 1) // 256, (N - 1) // 256)))
+    ref, S = oracle.gemm_mx_entries(ta, tb, w["A"], SA, w["B"], SB, ii, jj)
+    got = D[torch.from_numpy(ii).to(dev()), torch.from_numpy(jj).to(dev())].cpu().numpy()
+    assert_close(got, ref, S, ta, K, 1.0, 0.0, None, "mx 8192^3")
