@@ -129,7 +129,11 @@ GemmParams make_params(int a, int64_t M, int64_t N, int64_t K, double alpha, con
             p.c_scale = alpha == beta ? 1.0f : (float)(beta / alpha);
         }
     }
+    // C is folded into the accumulator only for fp32 / int32 outputs (16- and
+    // 8-bit C is read in the epilogue)
+    if (ep.d_type != MMAC_OUT_ACC) p.fold_c = 0;
     p.vec_d = aligned16(D) && (ldd * out_size(ep)) % 16 == 0;
+    p.vec_c = p.use_c && aligned16(C) && (ldc * out_size(ep)) % 16 == 0;
     p.d_type = ep.d_type;
     p.act = ep.act;
     p.bias = ep.bias;

@@ -569,24 +569,31 @@ struct TiledGemm {
     // instructions over this tile's rows: elements outside M x N get an offset
     // past the end of the buffer, where loads return zero and stores are
     // dropped, so there are no branches and all loads of a row of instruction
-    // tiles are in flight together.
+    // tiles are in flight together.  fp32 / int32 D takes the unrolled paths
+    // below; 16- and 8-bit D the converted path after them.
     __device__ __forceinline__ void epilogue(uint8_t *smem) {
         if constexpr (std::is_same<out_t, float>::value) {
-            if (p.d_type == OUT_BF16) return epilogue_as<OUT_BF16>(smem);
-            if (p.d_type == OUT_F16) return epilogue_as<OUT_F16>(smem);
-            if (p.d_type == OUT_E4M3) return epilogue_as<OUT_E4M3>(smem);
-            if (p.d_type == OUT_E5M2) return epilogue_as<OUT_E5M2>(smem);
+            if (p.d_type != OUT_ACC) return epilogue_converted(smem);
         }
-        epilogue_as<OUT_ACC>(smem);
+        const int rows = min(BM, p.M - row0);
+        const rsrc_t rd = make_rsrc(reinterpret_cast<out_t *>(p.D) + (int64_t)row0 * p.ldd,
+                                    (uint32_t)(rows * p.ldd * 4));
+        float bias[TN];   // this lane's column of each instruction-tile column
+        const bool has_bias = load_bias(bias);
+        if (p.use_c && !p.fold_c) {
+            const rsrc_t rc = make_rsrc(reinterpret_cast<const out_t *>(p.C) + (int64_t)row0 * p.ldc,
+                                        (uint32_t)(rows * p.ldc * 4));
+            store_tiles<true>(rd, rc, bias, has_bias);
+        } else if (p.vec_d) {
+            store_tiles_lds(rd, smem, bias, has_bias);
+        } else {
+            store_tiles<false>(rd, rd, bias, has_bias);
+        }
     }
 
-    template <int OT>
-    __device__ __forceinline__ void epilogue_as(uint8_t *smem) {
-        constexpr int ES = out_esize<OT>();
-        const int rows = min(BM, p.M - row0);
-        const rsrc_t rd = make_rsrc(static_cast<uint8_t *>(p.D) + (int64_t)row0 * p.ldd * ES,
-                                    (uint32_t)(rows * p.ldd * ES));
-        float bias[TN];   // this lane's column of each instruction-tile column
+    // The bias of this lane's column of each instruction-tile column (floating
+    // D only); returns whether there is a bias.
+    __device__ __forceinline__ bool load_bias(float (&bias)[TN]) const {
         const bool has_bias = std::is_same<out_t, float>::value && p.bias != nullptr;
 #pragma unroll
         for (int j = 0; j < TN; ++j) bias[j] = 0.0f;
@@ -599,25 +606,17 @@ struct TiledGemm {
                                                         rb, col0 + c < p.N ? (uint32_t)c * 4 : kOutOfRange, 0, 0));
             }
         }
-        if (p.use_c && !p.fold_c) {
-            const rsrc_t rc = make_rsrc(static_cast<const uint8_t *>(p.C) + (int64_t)row0 * p.ldc * ES,
-                                        (uint32_t)(rows * p.ldc * ES));
-            store_tiles<true, OT>(rd, rc, bias, has_bias);
-        } else if (ES >= 2 && p.vec_d) {   // one-byte D: element stores
-            store_tiles_lds<OT>(rd, smem, bias, has_bias);
-        } else {
-            store_tiles<false, OT>(rd, rd, bias, has_bias);
-        }
+        return has_bias;
     }
 
-    // One output element's bits from its accumulator value and (USE_C) the
-    // stored bits of its C element.
-    template <bool USE_C, int OT, class A>
+    // One fp32 / int32 output element's bits from its accumulator value and
+    // (USE_C) the bits of its C element.
+    template <bool USE_C, class A>
     __device__ __forceinline__ uint32_t out_bits(A a, uint32_t c, float bias, bool has_bias) const {
         if constexpr (std::is_same<out_t, float>::value) {
             float v = p.alpha * a;
-            if constexpr (USE_C) v = fmaf(p.beta, from_out_bits<OT>(c), v);
-            return finish<OT>(v, bias, has_bias, p.act != 0);
+            if constexpr (USE_C) v = fmaf(p.beta, __builtin_bit_cast(float, c), v);
+            return finish<OUT_ACC>(v, bias, has_bias, p.act != 0);
         } else {
             uint32_t v = (uint32_t)p.ialpha * (uint32_t)a;
             if constexpr (USE_C) v += (uint32_t)p.ibeta * c;
@@ -627,24 +626,15 @@ struct TiledGemm {
 
     // The epilogue through LDS (free once the last k-tile is done: no copy is
     // in flight and no remaining read matters), so that D goes out with
-    // 16-byte stores, each instruction writing whole row segments of 128 bytes
-    // (fp32 / int32 D: 8 per instruction) or 64 bytes (16-bit D: 16) instead
-    // of 2 segments of 32 elements.  Each wave stages up to EPI_TILES of its
-    // 32 x 32 instruction tiles at a time in its own 4 KiB-per-tile region (no
-    // other wave touches it, so no barrier): lanes write their 16 registers in
-    // the accumulator layout, then read back row-contiguous 16-byte chunks.
-    //   32-bit D: 128-byte rows; lane L reads row 8q + L / 8 of the tile,
-    //   chunk L mod 8.  Row r sits at row slot r ^ ((r >> 2) & 1): rows r and
-    //   r + 4, written by the two lane halves together, then fall in opposite
-    //   halves of the 64 banks, and so do the two rows of each 16-lane read.
-    //   16-bit D: 64-byte rows.  For each pair of registers (rows r, r + 1 of
-    //   the lane's column) neighbouring lanes swap one value (DPP quad_perm
-    //   1,0,3,2): the even lane then writes the word of columns (L, L + 1) of
-    //   row r, the odd lane that of row r + 1, so the writes are whole words.
-    //   Row r sits at slot r ^ (2 * ((r >> 2) & 1)), which keeps the 64 lanes'
-    //   words (rows r, r+1 from one lane half, r+4, r+5 from the other) and each
-    //   16-lane read (four rows) on distinct banks; lane L reads row
-    //   16q + L / 4, chunk L mod 4.
+    // 16-byte stores, each instruction writing 8 whole 128-byte row segments
+    // instead of 2.  Each wave stages up to EPI_TILES of its 32 x 32 instruction
+    // tiles at a time in its own 4 KiB-per-tile region (no other wave touches
+    // it, so no barrier): lanes write their 16 registers in the accumulator
+    // layout, then read back row-contiguous 16-byte chunks (lane L: row
+    // 8q + L / 8 of the tile, chunk L mod 8).  Row r of a tile sits at row
+    // slot r ^ ((r >> 2) & 1): rows r and r + 4, written by the two lane halves
+    // together, then fall in opposite halves of the 64 banks, and so do the two
+    // rows of each 16-lane read.
     static constexpr int epi_tiles() {   // most instruction tiles per pass: fits and divides TM * TN
         int t = TM * TN;
         while (t > 1 && (t * 4096 * NW > LDS_BYTES || (TM * TN) % t != 0)) --t;
@@ -653,41 +643,26 @@ struct TiledGemm {
     static constexpr int EPI_TILES = epi_tiles();
     static_assert(EPI_TILES * 4096 * NW <= LDS_BYTES, "epilogue staging space");
 
-    template <int OT>
+    // Stage t of the current group: this lane's 16 values of instruction tile (i, j), as fp32 / int32 bits.
+    template <class F>
+    __device__ __forceinline__ void stage_tile(uint8_t *base, int i, int j, F bits_of) {
+#pragma unroll
+        for (int G = 0; G < 16; ++G) {
+            const int r = 8 * (G / 4) + 4 * g + (G % 4);
+            const int slot = r ^ ((r >> 2) & 1);
+            *reinterpret_cast<uint32_t *>(base + slot * 128 + l32 * 4) = bits_of(acc[i][j][G]);
+        }
+    }
+
     __device__ __forceinline__ void store_tiles_lds(rsrc_t rd, uint8_t *smem, const float *bias, bool has_bias) {
-        constexpr int ES = out_esize<OT>() < 2 ? 2 : out_esize<OT>();   // never called for one-byte D
-        constexpr int RB = 32 * ES;            // bytes of a staged row
-        constexpr int CPR = RB / 16;           // 16-byte chunks per row
-        constexpr int RPR = 64 / CPR;          // rows per read instruction
         uint8_t *region = smem + wave * EPI_TILES * 4096;
-        const bool odd = lane & 1;
 #pragma unroll
         for (int t0 = 0; t0 < TM * TN; t0 += EPI_TILES) {
 #pragma unroll
             for (int t = 0; t < EPI_TILES; ++t) {
                 const int i = (t0 + t) / TN, j = (t0 + t) % TN;
-                uint8_t *base = region + t * 4096;
-                if constexpr (ES == 4) {
-#pragma unroll
-                    for (int G = 0; G < 16; ++G) {
-                        const int r = 8 * (G / 4) + 4 * g + (G % 4);
-                        const int slot = r ^ ((r >> 2) & 1);
-                        *reinterpret_cast<uint32_t *>(base + slot * RB + l32 * 4) =
-                            out_bits<false, OT>(acc[i][j][G], 0u, bias[j], has_bias);
-                    }
-                } else {
-#pragma unroll
-                    for (int G = 0; G < 16; G += 2) {
-                        const uint32_t h0 = out_bits<false, OT>(acc[i][j][G], 0u, bias[j], has_bias);
-                        const uint32_t h1 = out_bits<false, OT>(acc[i][j][G + 1], 0u, bias[j], has_bias);
-                        const uint32_t recv =
-                            (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(odd ? h0 : h1), 0xB1, 0xF, 0xF, false);
-                        const uint32_t word = odd ? (recv | (h1 << 16)) : (h0 | (recv << 16));
-                        const int r = 8 * (G / 4) + 4 * g + (G % 4) + (odd ? 1 : 0);
-                        const int slot = r ^ (((r >> 2) & 1) << 1);
-                        *reinterpret_cast<uint32_t *>(base + slot * RB + (l32 >> 1) * 4) = word;
-                    }
-                }
+                stage_tile(region + t * 4096, i, j,
+                           [&](out_t a) { return out_bits<false>(a, 0u, bias[j], has_bias); });
             }
             __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's staging writes are done
             __builtin_amdgcn_sched_barrier(0);
@@ -696,27 +671,22 @@ struct TiledGemm {
                 const int i = (t0 + t) / TN, j = (t0 + t) % TN;
                 const uint8_t *base = region + t * 4096;
 #pragma unroll
-                for (int q = 0; q < 32 / RPR; ++q) {
-                    const int r = RPR * q + lane / CPR, c = lane % CPR;
-                    const int slot = ES == 4 ? r ^ ((r >> 2) & 1) : r ^ (((r >> 2) & 1) << 1);
-                    const i32x4 v = *reinterpret_cast<const i32x4 *>(base + slot * RB + c * 16);
-                    constexpr int PER = 16 / ES;                                  // elements per chunk
-                    const int tr = wm * WTM + i * 32 + r;                         // row within the block tile
-                    const int col = col0 + wn * WTN + j * 32 + PER * c;          // first of the chunk's columns
+                for (int q = 0; q < 4; ++q) {
+                    const int r = 8 * q + lane / 8, c = lane % 8;
+                    const int slot = r ^ ((r >> 2) & 1);
+                    const i32x4 v = *reinterpret_cast<const i32x4 *>(base + slot * 128 + c * 16);
+                    const int tr = wm * WTM + i * 32 + r;                    // row within the block tile
+                    const int col = col0 + wn * WTN + j * 32 + 4 * c;       // first of the 4 columns
                     const bool rin = row0 + tr < p.M;
-                    const uint32_t o = (uint32_t)((tr * p.ldd + col) * ES);
-                    if (col + PER - 1 < p.N) {
+                    const uint32_t o = (uint32_t)((tr * p.ldd + col) * 4);
+                    if (col + 3 < p.N) {
                         __builtin_amdgcn_raw_buffer_store_b128(v, rd, rin ? o : kOutOfRange, 0, kNonTemporal);
                     } else {
 #pragma unroll
-                        for (int e = 0; e < PER; ++e) {
-                            const uint32_t oe = rin && col + e < p.N ? o + ES * e : kOutOfRange;
-                            if constexpr (ES == 4)
-                                __builtin_amdgcn_raw_buffer_store_b32((uint32_t)v[e], rd, oe, 0, kNonTemporal);
-                            else
-                                __builtin_amdgcn_raw_buffer_store_b16(
-                                    (unsigned short)((uint32_t)v[e / 2] >> (16 * (e % 2))), rd, oe, 0, kNonTemporal);
-                        }
+                        for (int e = 0; e < 4; ++e)
+                            __builtin_amdgcn_raw_buffer_store_b32((uint32_t)v[e], rd,
+                                                                  rin && col + e < p.N ? o + 4 * e : kOutOfRange, 0,
+                                                                  kNonTemporal);
                     }
                 }
             }
@@ -725,25 +695,113 @@ struct TiledGemm {
         }
     }
 
-    // Folded beta * C: the accumulator starts as c_scale * C, read with the same
-    // branch-free buffer accesses as the epilogue.  Called right after the first
-    // copies are issued, so the two latencies overlap.
-    __device__ __forceinline__ void load_c_into_acc() {
+    // 16- and 8-bit C and D (floating inputs).  alpha * acc (plus the column
+    // bias, when given) is staged in LDS as fp32 in the layout above; then
+    // each lane reads back four consecutive columns of a row at a time and
+    // finishes them there: beta * C (C has D's type and is read here, four
+    // elements per load), ReLU and the rounding, in a loop unrolled only four
+    // times (one short body per output type, four C loads in flight).  Four outputs leave in one
+    // 8-byte (16-bit D) or 4-byte (8-bit D) store when D's rows allow (vec_d),
+    // else one by one.
+    __device__ __forceinline__ void epilogue_converted(uint8_t *smem) {
         if constexpr (std::is_same<out_t, float>::value) {
-            if (p.d_type == OUT_BF16) return load_c_as<OUT_BF16>();
-            if (p.d_type == OUT_F16) return load_c_as<OUT_F16>();
-            if (p.d_type == OUT_E4M3) return load_c_as<OUT_E4M3>();
-            if (p.d_type == OUT_E5M2) return load_c_as<OUT_E5M2>();
+            switch (p.d_type) {   // one copy of the loops per output type
+            case OUT_BF16: return converted_as<OUT_BF16>(smem);
+            case OUT_F16: return converted_as<OUT_F16>(smem);
+            case OUT_E4M3: return converted_as<OUT_E4M3>(smem);
+            default: return converted_as<OUT_E5M2>(smem);
+            }
         }
-        load_c_as<OUT_ACC>();
     }
 
     template <int OT>
-    __device__ __forceinline__ void load_c_as() {
-        constexpr int ES = out_esize<OT>();
+    __device__ __forceinline__ void converted_as(uint8_t *smem) {
+        constexpr int es = out_esize<OT>();
         const int rows = min(BM, p.M - row0);
-        const rsrc_t rc = make_rsrc(static_cast<const uint8_t *>(p.C) + (int64_t)row0 * p.ldc * ES,
-                                    (uint32_t)(rows * p.ldc * ES));
+        const rsrc_t rd = make_rsrc(static_cast<uint8_t *>(p.D) + (int64_t)row0 * p.ldd * es,
+                                    (uint32_t)(rows * p.ldd * es));
+        const rsrc_t rc = p.use_c ? make_rsrc(static_cast<const uint8_t *>(p.C) + (int64_t)row0 * p.ldc * es,
+                                              (uint32_t)(rows * p.ldc * es))
+                                  : rd;
+        const bool relu = p.act != 0;
+        float bias[TN];
+        const bool has_bias = load_bias(bias);
+        uint8_t *region = smem + wave * EPI_TILES * 4096;
+#pragma unroll
+        for (int t0 = 0; t0 < TM * TN; t0 += EPI_TILES) {
+#pragma unroll
+            for (int t = 0; t < EPI_TILES; ++t) {
+                const int j = (t0 + t) % TN;
+                stage_tile(region + t * 4096, (t0 + t) / TN, j, [&](float a) {
+                    const float v = p.alpha * a;
+                    return __builtin_bit_cast(uint32_t, has_bias ? v + bias[j] : v);
+                });
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the staging writes are done
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll 4
+            for (int k = 0; k < EPI_TILES * 4; ++k) {
+                const int t = k >> 2, q = k & 3, tt = t0 + t, i = tt / TN, j = tt % TN;
+                const int r = 8 * q + lane / 8, c = lane % 8;
+                const int slot = r ^ ((r >> 2) & 1);
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(region + t * 4096 + slot * 128 + c * 16);
+                const int tr = wm * WTM + i * 32 + r;                   // row within the block tile
+                const int cc = wn * WTN + j * 32 + 4 * c;              // first column within the block tile
+                if (row0 + tr >= p.M || col0 + cc >= p.N) continue;
+                const bool whole = col0 + cc + 3 < p.N;
+                const uint32_t od = (uint32_t)((tr * p.ldd + col0 + cc) * es);
+                float x[4] = {v[0], v[1], v[2], v[3]};
+                if (p.use_c) {
+                    const uint32_t oc = (uint32_t)((tr * p.ldc + col0 + cc) * es);
+                    uint32_t cb[4];
+                    if (whole && p.vec_c) {
+                        if constexpr (es == 2) {
+                            const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rc, oc, 0, kNonTemporal);
+                            cb[0] = w[0] & 0xffffu; cb[1] = w[0] >> 16;
+                            cb[2] = w[1] & 0xffffu; cb[3] = w[1] >> 16;
+                        } else {
+                            const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(rc, oc, 0, kNonTemporal);
+                            for (int e = 0; e < 4; ++e) cb[e] = (w >> (8 * e)) & 0xffu;
+                        }
+                    } else {
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t oe = col0 + cc + e < p.N ? oc + es * e : kOutOfRange;
+                            if constexpr (es == 2) cb[e] = __builtin_amdgcn_raw_buffer_load_b16(rc, oe, 0, kNonTemporal);
+                            else cb[e] = __builtin_amdgcn_raw_buffer_load_b8(rc, oe, 0, kNonTemporal);
+                        }
+                    }
+                    for (int e = 0; e < 4; ++e) x[e] = fmaf(p.beta, from_out_bits<OT>(cb[e]), x[e]);
+                }
+                uint32_t h[4];
+                for (int e = 0; e < 4; ++e) h[e] = finish<OT>(x[e], 0.0f, false, relu);
+                if (whole && p.vec_d) {
+                    if constexpr (es == 2) {
+                        const u32x2 w = {h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+                        __builtin_amdgcn_raw_buffer_store_b64(w, rd, od, 0, kNonTemporal);
+                    } else {
+                        __builtin_amdgcn_raw_buffer_store_b32(h[0] | (h[1] << 8) | (h[2] << 16) | (h[3] << 24), rd, od,
+                                                              0, kNonTemporal);
+                    }
+                } else {
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t oe = col0 + cc + e < p.N ? od + es * e : kOutOfRange;
+                        if constexpr (es == 2) __builtin_amdgcn_raw_buffer_store_b16((unsigned short)h[e], rd, oe, 0, kNonTemporal);
+                        else __builtin_amdgcn_raw_buffer_store_b8((unsigned char)h[e], rd, oe, 0, kNonTemporal);
+                    }
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // the reads are done before the region is written again
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // Folded beta * C (fp32 / int32 D): the accumulator starts as c_scale * C,
+    // read with the same branch-free buffer accesses as the epilogue.  Called
+    // right after the first copies are issued, so the two latencies overlap.
+    __device__ __forceinline__ void load_c_into_acc() {
+        const int rows = min(BM, p.M - row0);
+        const rsrc_t rc = make_rsrc(reinterpret_cast<const out_t *>(p.C) + (int64_t)row0 * p.ldc,
+                                    (uint32_t)(rows * p.ldc * 4));
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -753,10 +811,10 @@ struct TiledGemm {
                 for (int G = 0; G < 16; ++G) {
                     const int r = wm * WTM + i * 32 + 8 * (G / 4) + 4 * g + (G % 4);
                     const bool in = (row0 + r < p.M) && (col < p.N);
-                    const uint32_t oc = in ? (uint32_t)((r * p.ldc + col) * ES) : kOutOfRange;
-                    const uint32_t c = load_elem<ES>(rc, oc);
+                    const uint32_t oc = in ? (uint32_t)((r * p.ldc + col) * 4) : kOutOfRange;
+                    const uint32_t c = __builtin_amdgcn_raw_buffer_load_b32(rc, oc, 0, kNonTemporal);
                     if constexpr (std::is_same<out_t, float>::value)
-                        acc[i][j][G] = p.c_scale * from_out_bits<OT>(c);
+                        acc[i][j][G] = p.c_scale * __builtin_bit_cast(float, c);
                     else
                         acc[i][j][G] = (int32_t)((uint32_t)p.ibeta * c);
                 }
@@ -765,23 +823,8 @@ struct TiledGemm {
         }
     }
 
-    // One C element (ES bytes) / one D element, non-temporal.
-    template <int ES>
-    __device__ __forceinline__ static uint32_t load_elem(rsrc_t r, uint32_t off) {
-        if constexpr (ES == 4) return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kNonTemporal);
-        else if constexpr (ES == 2) return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kNonTemporal);
-        else return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, kNonTemporal);
-    }
-    template <int ES>
-    __device__ __forceinline__ static void store_elem(uint32_t v, rsrc_t r, uint32_t off) {
-        if constexpr (ES == 4) __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kNonTemporal);
-        else if constexpr (ES == 2) __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, off, 0, kNonTemporal);
-        else __builtin_amdgcn_raw_buffer_store_b8((unsigned char)v, r, off, 0, kNonTemporal);
-    }
-
-    template <bool USE_C, int OT>
+    template <bool USE_C>
     __device__ __forceinline__ void store_tiles(rsrc_t rd, rsrc_t rc, const float *bias, bool has_bias) {
-        constexpr int ES = out_esize<OT>();
         constexpr int JB = TN < 2 ? TN : 2;             // instruction tiles per batch of loads
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
@@ -796,21 +839,21 @@ struct TiledGemm {
                     for (int G = 0; G < 16; ++G) {
                         const int r = wm * WTM + i * 32 + 8 * (G / 4) + 4 * g + (G % 4);   // row within the tile
                         const bool in = (row0 + r < p.M) && (col < p.N);
-                        od[jj][G] = in ? (uint32_t)((r * p.ldd + col) * ES) : kOutOfRange;
+                        od[jj][G] = in ? (uint32_t)((r * p.ldd + col) * 4) : kOutOfRange;
                         c[jj][G] = 0;
                         if constexpr (USE_C) {
-                            const uint32_t oc = in ? (uint32_t)((r * p.ldc + col) * ES) : kOutOfRange;
-                            c[jj][G] = load_elem<ES>(rc, oc);
+                            const uint32_t oc = in ? (uint32_t)((r * p.ldc + col) * 4) : kOutOfRange;
+                            c[jj][G] = __builtin_amdgcn_raw_buffer_load_b32(rc, oc, 0, kNonTemporal);
                         }
                     }
                 }
 #pragma unroll
                 for (int jj = 0; jj < JB; ++jj) {
 #pragma unroll
-                    for (int G = 0; G < 16; ++G) {
-                        const uint32_t bits = out_bits<USE_C, OT>(acc[i][j0 + jj][G], c[jj][G], bias[j0 + jj], has_bias);
-                        store_elem<ES>(bits, rd, od[jj][G]);
-                    }
+                    for (int G = 0; G < 16; ++G)
+                        __builtin_amdgcn_raw_buffer_store_b32(
+                            out_bits<USE_C>(acc[i][j0 + jj][G], c[jj][G], bias[j0 + jj], has_bias), rd, od[jj][G], 0,
+                            kNonTemporal);
                 }
             }
         }

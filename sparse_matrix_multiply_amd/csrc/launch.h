@@ -38,9 +38,13 @@ struct GemmParams {
     // 16 bytes, so the epilogue may store 16 consecutive bytes of a row with
     // one access.
     int vec_d;
+    // vec_c: the same for C (16- and 8-bit C is read four elements at a time
+    // when it holds).
+    int vec_c;
     // Epilogue variant (floating inputs only): d_type is OUT_ACC (C and D are
-    // fp32), OUT_BF16 or OUT_F16 (C and D are of that type); bias is NULL or
-    // N fp32 values added per column; act 1 applies ReLU.
+    // fp32) or one of the 16- / 8-bit types (C and D are of that type; C is
+    // then never folded); bias is NULL or N fp32 values added per column;
+    // act 1 applies ReLU.
     int d_type;
     int act;
     const float *bias;
