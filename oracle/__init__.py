@@ -18,9 +18,10 @@ import numpy as np
 
 from . import build as _build
 
-F16, BF16, I8, E4M3, E5M2 = 1, 2, 3, 4, 5
+F16, BF16, I8, E4M3, E5M2, FP4 = 1, 2, 3, 4, 5, 6
 FLOAT_TYPES = (F16, BF16, E4M3, E5M2)
-BITS_DTYPE = {F16: np.uint16, BF16: np.uint16, I8: np.int8, E4M3: np.uint8, E5M2: np.uint8}
+BITS_DTYPE = {F16: np.uint16, BF16: np.uint16, I8: np.int8, E4M3: np.uint8, E5M2: np.uint8, FP4: np.uint8}
+# FP4 (OCP E2M1) arrays are packed: rows x K/2 bytes, element 2m in the low nibble of byte m.
 
 _lib = None
 
@@ -135,11 +136,18 @@ def gemm_dense_entries(ta, tb, A, B, ii, jj, alpha=1.0, beta=0.0, C=None):
     return out, S
 
 
+def _mx_k(t, X):
+    """Elements per row of an MX operand array (FP4 is packed two per byte)."""
+    return X.shape[1] * (2 if t == FP4 else 1)
+
+
 def gemm_mx(ta, tb, A, SA, B, SB, alpha=1.0, beta=0.0, C=None, rows=None):
-    """Block-scaled (MX) GEMM: A M x K, B N x K (fp8 bits), SA M x K/32 and SB N x K/32 E8M0
-    scale bytes; returns (D fp64, S fp64) for output rows [r0, r1)."""
-    M, K = A.shape
+    """Block-scaled (MX) GEMM: A M x K, B N x K (fp8 bits, or packed FP4 bytes M x K/2 and
+    N x K/2), SA M x K/32 and SB N x K/32 E8M0 scale bytes; returns (D fp64, S fp64) for
+    output rows [r0, r1)."""
+    M, K = A.shape[0], _mx_k(ta, A)
     N = B.shape[0]
+    assert _mx_k(tb, B) == K
     r0, r1 = (0, M) if rows is None else rows
     A, B = _c2(A, BITS_DTYPE[ta]), _c2(B, BITS_DTYPE[tb])
     SA, SB = _c2(SA, np.uint8), _c2(SB, np.uint8)
@@ -154,7 +162,7 @@ def gemm_mx(ta, tb, A, SA, B, SB, alpha=1.0, beta=0.0, C=None, rows=None):
 
 def gemm_mx_entries(ta, tb, A, SA, B, SB, ii, jj, alpha=1.0, beta=0.0, C=None):
     """Block-scaled GEMM at output positions (ii[q], jj[q]); returns (D, S) 1-D fp64."""
-    M, K = A.shape
+    M, K = A.shape[0], _mx_k(ta, A)
     N = B.shape[0]
     A, B = _c2(A, BITS_DTYPE[ta]), _c2(B, BITS_DTYPE[tb])
     SA, SB = _c2(SA, np.uint8), _c2(SB, np.uint8)

@@ -44,12 +44,17 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F16 = 1, OR_BF16 = 2, OR_I8 = 3, OR_E4M3 = 4, OR_E5M2 = 5 };
+enum { OR_F16 = 1, OR_BF16 = 2, OR_I8 = 3, OR_E4M3 = 4, OR_E5M2 = 5, OR_FP4 = 6 };
 
 static int elem_bytes(int t) { return (t == OR_F16 || t == OR_BF16) ? 2 : 1; }
-static int is_float_type(int t) { return t == OR_F16 || t == OR_BF16 || t == OR_E4M3 || t == OR_E5M2; }
+static int is_float_type(int t) {
+    return t == OR_F16 || t == OR_BF16 || t == OR_E4M3 || t == OR_E5M2 || t == OR_FP4;
+}
 
+/* Element `off` (counted in elements) of an array of type t.  FP4 packs two
+ * elements per byte, element 2m in bits 0-3 and element 2m+1 in bits 4-7. */
 static uint32_t load_bits(int t, const void *base, int64_t off) {
+    if (t == OR_FP4) return (((const uint8_t *)base)[off >> 1] >> (4 * (off & 1))) & 15u;
     if (elem_bytes(t) == 2) return ((const uint16_t *)base)[off];
     return ((const uint8_t *)base)[off];
 }
@@ -84,6 +89,9 @@ double oracle_decode_one(int t, uint32_t bits) {
         s = (bits >> 7) & 1u; e = (bits >> 2) & 31u; m = bits & 3u;
         if (e == 31u) return m ? NAN : (s ? -INFINITY : INFINITY);
         return from_fields(s, e, m, 2, 15);
+    case OR_FP4: /* OCP FP4 E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa; no infinities or NaN, max 6 */
+        s = (bits >> 3) & 1u; e = (bits >> 1) & 3u; m = bits & 1u;
+        return from_fields(s, e, m, 1, 1);
     case OR_I8: /* two's complement */
         return (double)(int8_t)(uint8_t)bits;
     default:
@@ -93,13 +101,13 @@ double oracle_decode_one(int t, uint32_t bits) {
 
 /* Decode n elements of type t into doubles.  Returns 0, or -1 on a bad type. */
 int oracle_decode(int t, int64_t n, const void *src, double *dst) {
-    if (t < OR_F16 || t > OR_E5M2) return -1;
+    if (t < OR_F16 || t > OR_FP4) return -1;
     for (int64_t q = 0; q < n; ++q) dst[q] = oracle_decode_one(t, load_bits(t, src, q));
     return 0;
 }
 
 static int bad_float_pair(int ta, int tb) {
-    if (ta == OR_F16 || ta == OR_BF16) return tb != ta;
+    if (ta == OR_F16 || ta == OR_BF16 || ta == OR_FP4) return tb != ta;
     if (ta == OR_E4M3 || ta == OR_E5M2) return !(tb == OR_E4M3 || tb == OR_E5M2);
     return 1;
 }

@@ -606,3 +606,39 @@ def test_mx_entries_match_full():
     ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
     De, Se = oracle.gemm_mx_entries(ta, tb, A, SA, B, SB, ii.ravel(), jj.ravel(), 1.5, 0.5, C)
     assert np.array_equal(De, D.ravel()) and np.array_equal(Se, S.ravel())
+
+
+# FP4 (OCP E2M1, two per byte, element 2m in the low nibble of byte m) for block-scaled GEMMs.
+FP4_VALUES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]          # codes 0..7; 8..15 are their negatives
+
+
+def fp4_unpack(P):
+    P = np.asarray(P, np.uint8)
+    lo, hi = P & 15, P >> 4
+    codes = np.stack([lo, hi], axis=-1).reshape(P.shape[0], -1)
+    mag = np.array(FP4_VALUES)[codes & 7]
+    return np.where(codes & 8, -mag, mag)
+
+
+def test_fp4_decode_every_code():
+    got = [oracle.decode_one(oracle.FP4, c) for c in range(16)]
+    want = FP4_VALUES + [-v for v in FP4_VALUES]
+    assert got == want and np.signbit(got[8])
+
+
+def test_mx_fp4_brute_force_fraction():
+    g = np.random.default_rng(41)
+    M, N, K = 4, 3, 64
+    A = g.integers(0, 256, size=(M, K // 2)).astype(np.uint8)
+    B = g.integers(0, 256, size=(N, K // 2)).astype(np.uint8)
+    SA = g.integers(120, 135, size=(M, K // 32)).astype(np.uint8)
+    SB = g.integers(120, 135, size=(N, K // 32)).astype(np.uint8)
+    D, S = oracle.gemm_mx(oracle.FP4, oracle.FP4, A, SA, B, SB, 2.0, 0.0)
+    Av, Bv = fp4_unpack(A), fp4_unpack(B)
+    for i in range(M):
+        for j in range(N):
+            acc = sum(Fraction(2) ** (int(SA[i, k // 32]) + int(SB[j, k // 32]) - 254) * Fraction(Av[i, k]) *
+                      Fraction(Bv[j, k]) for k in range(K))
+            assert D[i, j] == float(2 * acc)
+            assert S[i, j] == float(sum(abs(Fraction(2) ** (int(SA[i, k // 32]) + int(SB[j, k // 32]) - 254) *
+                                            Fraction(Av[i, k]) * Fraction(Bv[j, k])) for k in range(K)))
