@@ -373,6 +373,17 @@ def suite():
     out["mx_fp8e4m3xbf8e5m2_8192^3"] = {"us": round(ms * 1e3, 1), "TFLOP/s": round(gemm_flops(M, N, K) / ms / 1e9, 1),
                                          "shape": [M, N, K], "scales": "E8M0 per 32 along K"}
     del A, B, SA, SB, D
+    # block-scaled FP4 E2M1 x FP4 at 8192^3 (packed two per byte, random codes)
+    g = torch.Generator(device="cpu").manual_seed(5)
+    A = torch.randint(0, 256, (M, K // 2), dtype=torch.uint8, generator=g).to(dev)
+    B = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, generator=g).to(dev)
+    SA = torch.full((K // 128, M), 0x7F7F7F7F, dtype=torch.int32, device=dev)
+    SB = torch.full((K // 128, N), 0x7F7F7F7F, dtype=torch.int32, device=dev)
+    D = torch.empty((M, N), dtype=torch.float32, device=dev)
+    ms = median_ms([lambda: mm.gemm_mx(A, SA, B, SB, D, a_type=mm.FP4_E2M1, b_type=mm.FP4_E2M1, stream=stream)], 20)
+    out["mx_fp4e2m1_8192^3"] = {"us": round(ms * 1e3, 1), "TFLOP/s": round(gemm_flops(M, N, K) / ms / 1e9, 1),
+                                 "shape": [M, N, K], "scales": "E8M0 per 32 along K"}
+    del A, B, SA, SB, D
 
     split_case(512, 512, 32768, W.BF16, "splitk_bf16_512x512x32768")
     split_case(256, 256, 65536, W.BF16, "splitk_bf16_256x256x65536")

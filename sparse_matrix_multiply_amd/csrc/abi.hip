@@ -312,9 +312,18 @@ mmac_status_t mmac_gemm_dense_mx(mmac_dtype_t a_type, mmac_dtype_t b_type, int64
                                  const void *C, int64_t ldc, void *D, int64_t ldd, const mmac_epilogue_t *ep_in,
                                  void *stream) {
     const mmac_epilogue_t ep = epilogue_of(ep_in);
-    if (valid_type(a_type) && valid_type(b_type) && (!is_fp8(a_type) || !is_fp8(b_type))) return MMAC_ERR_UNSUPPORTED;
+    // FP4 (packed two per byte) only with FP4; the generic checks below then
+    // see it as a one-byte type with half the element counts
+    const bool fp4 = a_type == MMAC_FP4_E2M1 || b_type == MMAC_FP4_E2M1;
+    if (fp4 && a_type != b_type) return MMAC_ERR_UNSUPPORTED;
+    if (!fp4 && valid_type(a_type) && valid_type(b_type) && (!is_fp8(a_type) || !is_fp8(b_type)))
+        return MMAC_ERR_UNSUPPORTED;
     if (K >= 0 && (K % 32) != 0) return MMAC_ERR_INVALID_ARG;
-    const mmac_status_t st = check_gemm(a_type, b_type, M, N, K, alpha, A, lda, K, B, ldb, beta, C, ldc, D, ldd, ep);
+    if (fp4 && ((lda % 2) || (ldb % 2))) return MMAC_ERR_MISALIGNED;
+    const mmac_dtype_t ga = fp4 ? MMAC_FP8_E4M3 : a_type, gb = fp4 ? MMAC_FP8_E4M3 : b_type;
+    const int64_t kk = fp4 ? K / 2 : K;   // bytes of a row for FP4
+    const mmac_status_t st = check_gemm(ga, gb, M, N, kk, alpha, A, fp4 ? lda / 2 : lda, kk, B, fp4 ? ldb / 2 : ldb,
+                                        beta, C, ldc, D, ldd, ep);
     if (st != MMAC_OK) return st;
     if ((K > 0 && (!SA || !SB)) || ldsa < M || ldsb < N || ldsa < 1 || ldsb < 1) return MMAC_ERR_INVALID_ARG;
     const int64_t scale_rows = (K + 127) / 128;
@@ -324,7 +333,11 @@ mmac_status_t mmac_gemm_dense_mx(mmac_dtype_t a_type, mmac_dtype_t b_type, int64
     // the 8-wave 256 x 256 tile has no registers left for the scale words: its 128 x 256 half instead
     TileShape shape = pick_shape(M, N, true);
     if (shape == TILE_256) shape = TILE_128x256;
-    GemmParams p = make_params(a_type, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd, ep, shape);
+    GemmParams p = make_params(ga, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd, ep, shape);
+    if (fp4) {
+        p.a_pitch = lda / 2;
+        p.b_pitch = ldb / 2;
+    }
     p.sa = SA;
     p.sb = SB;
     p.ldsa = ldsa;

@@ -32,7 +32,7 @@ typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x16 __attribute__((ext_vector_type(16)));
 
-enum : int { DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3, DT_E4M3 = 4, DT_E5M2 = 5 };
+enum : int { DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3, DT_E4M3 = 4, DT_E5M2 = 5, DT_FP4 = 6 };
 
 // Word 3 of a gfx9 buffer descriptor for raw (untyped) 32-bit accesses.
 constexpr int kBufferWord3 = 0x00020000;
@@ -275,6 +275,30 @@ template <int FA, int FB> struct MmaMX : MmaDenseF8<FA, FB> {
     __device__ __forceinline__ static acc_t mma_scaled(const Frag<32> &a, const Frag<32> &b, acc_t c, uint32_t sa,
                                                        uint32_t sb) {
         return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(join(a), join(b), c, FA, FB, 0, (int)sa, 0, (int)sb);
+    }
+};
+
+// Block-scaled (MX) FP4 E2M1 x FP4: the same instruction with format 4 on
+// both sides.  A lane's operand is 16 bytes, 32 elements packed two per byte
+// (low nibble first); 128-byte LDS rows hold 256 elements per k-tile, so a
+// k-tile is four 64-K steps and two scale words per row.  Lane half g of
+// step s loads 16-byte unit 2s + g: K 64s + 32g .. 64s + 32g + 31, block
+// 2s + g.  Copies count bytes: kKPerByte = 2 elements per byte.
+struct MmaMX4 {
+    static constexpr bool kSparse = false, kScaled = true;
+    static constexpr int kEsize = 1, kKPerByte = 2, kAFrag = 16, kBFrag = 16, kKStep = 64;
+    static constexpr int kBK = 256;
+    static constexpr int kARowBytes = kBK / 2, kBRowBytes = kBK / 2;
+    static constexpr int kScaleWords = kBK / 128;
+    typedef f32x16 acc_t;
+    typedef float out_t;
+    __device__ __forceinline__ static constexpr int a_unit(int s, int g, int) { return 2 * s + g; }
+    __device__ __forceinline__ static constexpr int b_unit(int s, int g, int) { return 2 * s + g; }
+    __device__ __forceinline__ static acc_t mma_scaled(const Frag<16> &a, const Frag<16> &b, acc_t c, uint32_t sa,
+                                                       uint32_t sb) {
+        const i32x8 A = {a.v[0], a.v[1], a.v[2], a.v[3], 0, 0, 0, 0};
+        const i32x8 B = {b.v[0], b.v[1], b.v[2], b.v[3], 0, 0, 0, 0};
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, c, 4, 4, 0, (int)sa, 0, (int)sb);
     }
 };
 

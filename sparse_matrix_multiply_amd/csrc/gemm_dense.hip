@@ -26,6 +26,7 @@ hipError_t launch_gemm_mx(int a, int b, TileShape shape, GemmParams p, hipStream
     if (a == DT_E4M3 && b == DT_E5M2) return launch_dense_op<MmaMX<0, 1>>(shape, p, s);
     if (a == DT_E5M2 && b == DT_E4M3) return launch_dense_op<MmaMX<1, 0>>(shape, p, s);
     if (a == DT_E5M2 && b == DT_E5M2) return launch_dense_op<MmaMX<1, 1>>(shape, p, s);
+    if (a == DT_FP4 && b == DT_FP4) return launch_dense_op<MmaMX4>(shape, p, s);
     return hipErrorInvalidValue;
 }
 

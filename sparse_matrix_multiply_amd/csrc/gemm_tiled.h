@@ -118,6 +118,10 @@ __device__ __forceinline__ void wait_copies(int n) {
     }
 }
 
+// Elements per byte of an operand (packed FP4: 2).
+template <class O, class = void> struct KPerByte { static constexpr int value = 1; };
+template <class O> struct KPerByte<O, std::void_t<decltype(O::kKPerByte)>> { static constexpr int value = O::kKPerByte; };
+
 // Bytes of index words one copy lane moves (sparse A only).
 template <class O>
 constexpr int idx_copy_bytes() {
@@ -264,7 +268,8 @@ struct TiledGemm {
     // The ragged last k-tile: A and B through registers with elements past K set
     // to zero (the index words, if any, still by copy).
     __device__ __forceinline__ void fill_masked(uint8_t *st, int kt) const {
-        const int climit = Op::kSparse ? p.K / 2 : p.K;      // elements of A per row
+        constexpr int KB = KPerByte<Op>::value;
+        const int climit = (Op::kSparse ? p.K / 2 : p.K) / KB;   // copy elements of A per row
 #pragma unroll
         for (int q = 0; q < AP; ++q) {
             const int u = q * 64 + lane;
@@ -282,7 +287,7 @@ struct TiledGemm {
             if (BUPW % 64 == 0 || u < BUPW) {
                 const int e0 = ((kt + kt0) * BW * 16 + (int)(swz<BW>(P) % BW) * 16) / Op::kEsize;
                 *reinterpret_cast<i32x4 *>(st + A_BYTES + P * 16) =
-                    masked_unit<Op::kEsize>(rb, src_off<BW>(P, p.b_pitch, kt), e0, p.K);
+                    masked_unit<Op::kEsize>(rb, src_off<BW>(P, p.b_pitch, kt), e0, p.K / KB);
             }
         }
 #pragma unroll

@@ -270,6 +270,10 @@ def dense_mx(L, **kw):
     (dict(SA=P + 4), mm.ERR_MISALIGNED),
     (dict(SB=P + 8), mm.ERR_MISALIGNED),
     (dict(lda=200), mm.ERR_INVALID_ARG),
+    (dict(a=mm.FP4_E2M1, b=mm.FP8_E4M3), mm.ERR_UNSUPPORTED),         # FP4 only with FP4
+    (dict(a=mm.FP4_E2M1, b=mm.FP4_E2M1, lda=257, ldb=256), mm.ERR_MISALIGNED),   # odd element pitch
+    (dict(a=mm.FP4_E2M1, b=mm.FP4_E2M1, lda=264, ldb=256), mm.ERR_MISALIGNED),   # 132-byte rows
+    (dict(a=mm.FP4_E2M1, b=mm.FP4_E2M1, lda=128, ldb=256), mm.ERR_INVALID_ARG),  # lda < K
 ])
 def test_mx_argument_errors(L, kw, code):
     assert dense_mx(L, **kw) == code
@@ -278,3 +282,9 @@ def test_mx_argument_errors(L, kw, code):
 def test_mx_empty_is_a_no_op(L):
     assert dense_mx(L, M=0) == mm.OK
     assert dense_mx(L, N=0) == mm.OK
+    assert dense_mx(L, M=0, a=mm.FP4_E2M1, b=mm.FP4_E2M1) == mm.OK
+
+
+def test_fp4_is_only_for_block_scaled_gemm(L):
+    assert dense(L, a=mm.FP4_E2M1, b=mm.FP4_E2M1) == mm.ERR_UNSUPPORTED
+    assert compress(L, a=mm.FP4_E2M1) == mm.ERR_UNSUPPORTED

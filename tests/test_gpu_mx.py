@@ -120,3 +120,69 @@ def test_mx_8192_sampled():
     ref, S = oracle.gemm_mx_entries(ta, tb, w["A"], SA, w["B"], SB, ii, jj)
     got = D[torch.from_numpy(ii).to(dev()), torch.from_numpy(jj).to(dev())].cpu().numpy()
     assert_close(got, ref, S, ta, K, 1.0, 0.0, None, "mx 8192^3")
+
+
+# ----------------------------------------------------------------------- FP4 E2M1 --
+FP4 = oracle.FP4
+
+
+def fp4_problem(M, N, K, seed, lo=107, hi=148, small=False):
+    g = np.random.default_rng(seed)
+    if small:      # codes of magnitude <= 2 (0, 0.5, 1, 1.5, 2) and either sign
+        mag = g.integers(0, 5, size=(M + N, K))
+        sgn = g.integers(0, 2, size=(M + N, K)) << 3
+        codes = (mag | sgn).astype(np.uint8)
+    else:
+        codes = g.integers(0, 16, size=(M + N, K)).astype(np.uint8)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    A, B = packed[:M], packed[M:]
+    SA = g.integers(lo, hi, size=(M, K // 32)).astype(np.uint8)
+    SB = g.integers(lo, hi, size=(N, K // 32)).astype(np.uint8)
+    return A, B, SA, SB
+
+
+def run_fp4(A, SA, B, SB, alpha=1.0, beta=0.0, C=None, pad=0):
+    M, N = A.shape[0], B.shape[0]
+    def dev_packed(X):
+        buf = torch.zeros((X.shape[0], X.shape[1] + pad), dtype=torch.uint8, device=dev())
+        buf[:, :X.shape[1]] = torch.from_numpy(X).to(dev())
+        return buf[:, :X.shape[1]]
+    D = out_tensor(M, N, False)
+    Cd = torch.from_numpy(np.ascontiguousarray(C)).to(dev()) if beta != 0 else None
+    mm.gemm_mx(dev_packed(A), pack_mx_scales(SA, seed=3), dev_packed(B), pack_mx_scales(SB, seed=4), D, alpha, beta,
+               Cd, a_type=FP4, b_type=FP4)
+    torch.cuda.synchronize()
+    return D
+
+
+@pytest.mark.parametrize("tile", [256, 2561, 1282, 128, 64])
+@pytest.mark.parametrize("M,N,K", [(64, 64, 256), (300, 260, 32 * 37), (33, 300, 1024), (257, 130, 96), (5, 7, 32)])
+def test_mx_fp4_matches_oracle(tile, M, N, K):
+    A, B, SA, SB = fp4_problem(M, N, K, M + N + K)
+    C = np.random.default_rng(K).standard_normal((M, N)).astype(np.float32)
+    with env(MMAC_TILE=tile):
+        D = run_fp4(A, SA, B, SB, 0.75, 1.5, C, pad=16).cpu().numpy()
+    Dref, S = oracle.gemm_mx(FP4, FP4, A, SA, B, SB, 0.75, 1.5, C)
+    assert_close(D, Dref, S, E4M3, K, 0.75, 1.5, C, f"mx fp4 {M}x{N}x{K} tile {tile}")
+
+
+def test_mx_fp4_exact():
+    """|a|, |b| <= 2 with block exponents 2^-1 .. 2^1 on each side: multiples of 2^-4 below 2^16,
+    exact in fp32 -- the oracle's bits."""
+    M, N, K = 130, 70, 32 * 21
+    A, B, SA, SB = fp4_problem(M, N, K, 3, lo=126, hi=129, small=True)
+    for tile in (1282, 64):
+        with env(MMAC_TILE=tile):
+            D = run_fp4(A, SA, B, SB).cpu().numpy()
+        Dref, _ = oracle.gemm_mx(FP4, FP4, A, SA, B, SB)
+        assert np.array_equal(D.astype(np.float64), Dref), f"tile {tile}"
+
+
+def test_mx_fp4_8192_sampled():
+    M = N = K = 8192
+    A, B, SA, SB = fp4_problem(M, N, K, 77, lo=117, hi=138)
+    D = run_fp4(A, SA, B, SB)
+    ii, jj = sample_entries(M, N, 20000, 15, tiles=((0, 0), ((M - 1) // 256, (N - 1) // 256)))
+    ref, S = oracle.gemm_mx_entries(FP4, FP4, A, SA, B, SB, ii, jj)
+    got = D[torch.from_numpy(ii).to(dev()), torch.from_numpy(jj).to(dev())].cpu().numpy()
+    assert_close(got, ref, S, E4M3, K, 1.0, 0.0, None, "mx fp4 8192^3")
