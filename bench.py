@@ -385,6 +385,22 @@ def suite():
                                  "shape": [M, N, K], "scales": "E8M0 per 32 along K"}
     del A, B, SA, SB, D
 
+    # other operand layouts: the bf16 8192^3 workload (beta = 1) with A stored M-contiguous and / or
+    # B stored N-contiguous (transposed LDS reads)
+    w = W.workload("bf16_8192")
+    M, N, K = w["M"], w["N"], w["K"]
+    A, B = to_dev(w["A"], W.BF16), to_dev(w["B"], W.BF16)
+    At, Bt = A.t().contiguous(), B.t().contiguous()
+    C = torch.from_numpy(w["C"]).to(dev)
+    D = torch.empty((M, N), dtype=torch.float32, device=dev)
+    for ta, tb, key in ((True, False, "A_Mcontig"), (False, True, "B_Ncontig"), (True, True, "A_Mcontig_B_Ncontig")):
+        ms = median_ms([lambda: mm.gemm_layout(At if ta else A, Bt if tb else B, D, ta, tb, 1.0, 1.0, C,
+                                               stream=stream)], 20)
+        out["layout_bf16_8192^3_beta1_" + key] = {"us": round(ms * 1e3, 1),
+                                                  "TFLOP/s": round(gemm_flops(M, N, K) / ms / 1e9, 1)}
+    del A, B, At, Bt, C, D
+    torch.cuda.empty_cache()
+
     split_case(512, 512, 32768, W.BF16, "splitk_bf16_512x512x32768")
     split_case(256, 256, 65536, W.BF16, "splitk_bf16_256x256x65536")
     split_case(1024, 512, 8192, W.E4M3, "splitk_fp8e4m3_1024x512x8192")

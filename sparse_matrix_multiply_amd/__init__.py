@@ -81,6 +81,9 @@ def lib():
         L.mmac_gemm_dense_mx.restype = i32
         L.mmac_gemm_dense_mx.argtypes = [i32, i32, i64, i64, i64, dbl, vp, i64, vp, i64, vp, i64, vp, i64, dbl, vp,
                                          i64, vp, i64, ep, vp]
+        L.mmac_gemm_dense_layout.restype = i32
+        L.mmac_gemm_dense_layout.argtypes = [i32, i32, i32, i32, i64, i64, i64, dbl, vp, i64, vp, i64, dbl, vp, i64,
+                                             vp, i64, ep, vp]
         L.mmac_gemm_workspace_bytes.restype = i64
         L.mmac_gemm_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
         L.mmac_status_string.restype = ctypes.c_char_p
@@ -223,6 +226,23 @@ def gemm_mx(A, SA, B, SB, D, alpha=1.0, beta=0.0, C=None, a_type=None, b_type=No
                                   _ptr(SB), _ld(SB), float(beta), _ptr(C), _ld(C) if C is not None else 0, _ptr(D),
                                   _ld(D), None if ep is None else ctypes.byref(ep), _stream(stream))
     _check(st, "mmac_gemm_dense_mx")
+    return D
+
+
+def gemm_layout(A, B, D, trans_a=False, trans_b=False, alpha=1.0, beta=0.0, C=None, a_type=None, b_type=None,
+                stream=None, bias=None, act=ACT_NONE, d_type=None):
+    """D = alpha * op(A) @ op(B) + beta * C for 16-bit types.  trans_a: A is given as its K x M
+    transpose (M contiguous); trans_b: B is given as K x N (N contiguous).  Otherwise A is M x K and
+    B is N x K as in gemm_dense."""
+    M = A.shape[1] if trans_a else A.shape[0]
+    K = A.shape[0] if trans_a else A.shape[1]
+    N = B.shape[1] if trans_b else B.shape[0]
+    ta, tb = _dtype(A, a_type), _dtype(B, b_type)
+    ep = _epilogue(D, bias, act, d_type)
+    st = lib().mmac_gemm_dense_layout(ta, tb, int(bool(trans_a)), int(bool(trans_b)), M, N, K, float(alpha), _ptr(A),
+                                      _ld(A), _ptr(B), _ld(B), float(beta), _ptr(C), _ld(C) if C is not None else 0,
+                                      _ptr(D), _ld(D), None if ep is None else ctypes.byref(ep), _stream(stream))
+    _check(st, "mmac_gemm_dense_layout")
     return D
 
 

@@ -76,7 +76,8 @@ bool aligned_to(const void *p, int n) { return reinterpret_cast<uintptr_t>(p) % 
 // Common checks of the GEMM calls.  Returns MMAC_OK or the error.
 mmac_status_t check_gemm(int a, int b, int64_t M, int64_t N, int64_t K, double alpha, const void *A,
                          int64_t lda, int64_t a_cols, const void *B, int64_t ldb, double beta, const void *C,
-                         int64_t ldc, const void *D, int64_t ldd, const mmac_epilogue_t &ep) {
+                         int64_t ldc, const void *D, int64_t ldd, const mmac_epilogue_t &ep, int64_t b_cols = -1) {
+    if (b_cols < 0) b_cols = K;   // elements per memory row of B
     if (!supported_pair(a, b)) return MMAC_ERR_UNSUPPORTED;
     if (ep.d_type < MMAC_OUT_ACC || ep.d_type > MMAC_OUT_BF8_E5M2 || ep.act < MMAC_ACT_NONE || ep.act > MMAC_ACT_RELU)
         return MMAC_ERR_INVALID_ARG;
@@ -85,7 +86,7 @@ mmac_status_t check_gemm(int a, int b, int64_t M, int64_t N, int64_t K, double a
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return MMAC_ERR_INVALID_ARG;
     if ((K > 0 && (!A || !B)) || !D) return MMAC_ERR_INVALID_ARG;
     if (beta != 0.0 && !C) return MMAC_ERR_INVALID_ARG;
-    if (lda < a_cols || ldb < K || lda < 1 || ldb < 1 || ldd < N || (C && beta != 0.0 && ldc < N))
+    if (lda < a_cols || ldb < b_cols || lda < 1 || ldb < 1 || ldd < N || (C && beta != 0.0 && ldc < N))
         return MMAC_ERR_INVALID_ARG;
     if (!std::isfinite(alpha) || !std::isfinite(beta)) return MMAC_ERR_INVALID_ARG;
     if (a == MMAC_I8 && (!integral_i32(alpha) || !integral_i32(beta))) return MMAC_ERR_INVALID_ARG;
@@ -344,6 +345,27 @@ mmac_status_t mmac_gemm_dense_mx(mmac_dtype_t a_type, mmac_dtype_t b_type, int64
     p.ldsb = ldsb;
     p.scale_rows = (int)scale_rows;
     return launched(launch_gemm_mx(a_type, b_type, shape, p, static_cast<hipStream_t>(stream)));
+}
+
+mmac_status_t mmac_gemm_dense_layout(mmac_dtype_t a_type, mmac_dtype_t b_type, int trans_a, int trans_b, int64_t M,
+                                     int64_t N, int64_t K, double alpha, const void *A, int64_t lda, const void *B,
+                                     int64_t ldb, double beta, const void *C, int64_t ldc, void *D, int64_t ldd,
+                                     const mmac_epilogue_t *ep_in, void *stream) {
+    if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1)) return MMAC_ERR_INVALID_ARG;
+    if (!trans_a && !trans_b)
+        return mmac_gemm_dense_ep(a_type, b_type, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd, ep_in, stream);
+    const mmac_epilogue_t ep = epilogue_of(ep_in);
+    if (!((a_type == MMAC_BF16 || a_type == MMAC_F16) && b_type == a_type)) return MMAC_ERR_UNSUPPORTED;
+    const mmac_status_t st = check_gemm(a_type, b_type, M, N, K, alpha, A, lda, trans_a ? M : K, B, ldb, beta, C, ldc,
+                                        D, ldd, ep, trans_b ? N : K);
+    if (st != MMAC_OK) return st;
+    // a transposed operand is addressed with one buffer over all its K rows
+    if ((trans_a && K * lda * 2 >= ((int64_t)1 << 31)) || (trans_b && K * ldb * 2 >= ((int64_t)1 << 31)))
+        return MMAC_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return MMAC_OK;
+    const TileShape shape = pick_shape(M, N, true);
+    const GemmParams p = make_params(a_type, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd, ep, shape);
+    return launched(launch_gemm_layout(a_type, trans_a != 0, trans_b != 0, shape, p, static_cast<hipStream_t>(stream)));
 }
 
 int64_t mmac_gemm_workspace_bytes(mmac_dtype_t a_type, int64_t M, int64_t N, int64_t K, int sparse) {

@@ -302,6 +302,12 @@ struct MmaMX4 {
     }
 };
 
+// Dense 16-bit product with A stored M-contiguous (TA) and / or B stored
+// N-contiguous (TB): same instruction, fragments read transposed.
+template <class Base, bool TA, bool TB> struct Trans : Base {
+    static constexpr bool kTransA = TA, kTransB = TB;
+};
+
 // Sparse instructions, A side: lane half g holds the compressed values of
 // the g-th contiguous half of the instruction's dense K (in ascending order)
 // and the index nibbles of those groups.  B side: the 64-byte K step of a B

@@ -20,6 +20,20 @@ hipError_t launch_gemm_dense(int a, int b, TileShape shape, GemmParams p, hipStr
     return hipErrorInvalidValue;
 }
 
+template <int DT>
+static hipError_t launch_trans(bool ta, bool tb, TileShape shape, const GemmParams &p, hipStream_t s) {
+    if (ta && tb) return launch_dense_op<Trans<MmaDense16<DT>, true, true>>(shape, p, s);
+    if (ta) return launch_dense_op<Trans<MmaDense16<DT>, true, false>>(shape, p, s);
+    if (tb) return launch_dense_op<Trans<MmaDense16<DT>, false, true>>(shape, p, s);
+    return launch_dense_op<MmaDense16<DT>>(shape, p, s);
+}
+
+hipError_t launch_gemm_layout(int a, bool trans_a, bool trans_b, TileShape shape, GemmParams p, hipStream_t s) {
+    if (a == DT_BF16) return launch_trans<DT_BF16>(trans_a, trans_b, shape, p, s);
+    if (a == DT_F16) return launch_trans<DT_F16>(trans_a, trans_b, shape, p, s);
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_gemm_mx(int a, int b, TileShape shape, GemmParams p, hipStream_t s) {
     // f8f6f4 format selectors: 0 = E4M3, 1 = E5M2
     if (a == DT_E4M3 && b == DT_E4M3) return launch_dense_op<MmaMX<0, 0>>(shape, p, s);

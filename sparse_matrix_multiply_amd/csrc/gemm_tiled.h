@@ -122,6 +122,12 @@ __device__ __forceinline__ void wait_copies(int n) {
 template <class O, class = void> struct KPerByte { static constexpr int value = 1; };
 template <class O> struct KPerByte<O, std::void_t<decltype(O::kKPerByte)>> { static constexpr int value = O::kKPerByte; };
 
+// Operands stored with M (A) or N (B) contiguous instead of K (16-bit types).
+template <class O, class = void> struct TransOf { static constexpr bool a = false, b = false; };
+template <class O> struct TransOf<O, std::void_t<decltype(O::kTransA)>> {
+    static constexpr bool a = O::kTransA, b = O::kTransB;
+};
+
 // Bytes of index words one copy lane moves (sparse A only).
 template <class O>
 constexpr int idx_copy_bytes() {
@@ -162,6 +168,12 @@ struct TiledGemm {
     static constexpr int S_BYTES = SCALED ? (BM + BN) * SW * 4 : 0;
     static constexpr int STAGE = A_BYTES + B_BYTES + I_BYTES + S_BYTES;
     static constexpr int NSW = SCALED ? (TM + TN) * SW : 1;   // scale words a lane holds per k-tile
+    // Transposed operands (A stored M-contiguous, B N-contiguous; 16-bit
+    // types): the LDS tile is kBK rows of BM (BN) elements, copied row by row,
+    // 16-byte unit u of row r stored at u ^ tswz(r); fragments come out of it
+    // with ds_read_b64_tr_b16 (load_tr).
+    static constexpr bool TRANS_A = TransOf<Op>::a, TRANS_B = TransOf<Op>::b;
+    static_assert(!(TRANS_A || TRANS_B) || (Op::kEsize == 2 && !Op::kSparse && !SCALED), "16-bit dense only");
     static constexpr int LDS_BYTES = STAGES * STAGE;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 workgroup");
 
@@ -186,8 +198,10 @@ struct TiledGemm {
         row0 = tm * BM;
         col0 = tn * BN;
         const int arows = min(BM, p.M - row0), bcols = min(BN, p.N - col0);
-        ra = make_rsrc(p.A + (int64_t)row0 * p.a_pitch, (uint32_t)(arows * p.a_pitch));
-        rb = make_rsrc(p.B + (int64_t)col0 * p.b_pitch, (uint32_t)(bcols * p.b_pitch));
+        if constexpr (TRANS_A) ra = make_rsrc(p.A + row0 * 2, (uint32_t)(p.K * p.a_pitch - row0 * 2));
+        else ra = make_rsrc(p.A + (int64_t)row0 * p.a_pitch, (uint32_t)(arows * p.a_pitch));
+        if constexpr (TRANS_B) rb = make_rsrc(p.B + col0 * 2, (uint32_t)(p.K * p.b_pitch - col0 * 2));
+        else rb = make_rsrc(p.B + (int64_t)col0 * p.b_pitch, (uint32_t)(bcols * p.b_pitch));
         if constexpr (Op::kSparse)
             rx = make_rsrc(p.idx + (int64_t)row0 * p.idx_pitch, (uint32_t)(arows * p.idx_pitch * 4));
         if constexpr (SCALED) {
@@ -215,6 +229,27 @@ struct TiledGemm {
         return (r * (uint32_t)p.idx_pitch + (kt + kt0) * IW) * 4 + byte % (IW * 4);
     }
 
+    // Transposed tiles: XOR of the 16-byte unit index of row r (U units per
+    // row).  Each ds_read_b64_tr_b16 of load_tr reads, per 32 lanes, 4 rows x
+    // 64 bytes; rows r .. r+3 then land in distinct quarters of the 64 banks.
+    template <int U>
+    __device__ __forceinline__ static constexpr uint32_t tswz(uint32_t r) {
+        return (r % 4) * (U >= 16 ? 4 : U / 4);
+    }
+    // Source byte offset of physical unit P of a transposed tile of MN
+    // elements per row at k-tile kt (memory rows are K rows of pitch bytes).
+    template <int MN>
+    __device__ __forceinline__ uint32_t tsrc_off(uint32_t P, int64_t pitch, int kt) const {
+        constexpr int U = MN / 8;
+        const uint32_t r = P / U, u = (P % U) ^ tswz<U>(r);
+        return (uint32_t)(((int64_t)(kt + kt0) * Op::kBK + r) * pitch) + u * 16;
+    }
+    template <bool T, int MN, int W>
+    __device__ __forceinline__ uint32_t op_off(uint32_t P, int64_t pitch, int kt) const {
+        if constexpr (T) return tsrc_off<MN>(P, pitch, kt);
+        else return src_off<W>(P, pitch, kt);
+    }
+
     // Byte offset (from the tile's first row / column) of 16-byte scale unit u
     // of a k-tile: words 4u .. 4u + 3 of the tile's ROWS x SW words, laid out
     // word-of-k-tile major, which are rows r .. r + 3 of scale-word row
@@ -232,12 +267,14 @@ struct TiledGemm {
             const int u = j * 64 + lane;
             if (AUPW % 64 == 0 || u < AUPW)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(st + (wave * AUPW + j * 64) * 16), 16,
-                                                         src_off<AW>(wave * AUPW + u, p.a_pitch, kt), 0, 0, 0);
+                                                         op_off<TRANS_A, BM, AW>(wave * AUPW + u, p.a_pitch, kt), 0,
+                                                         0, 0);
         } else if (j < AP + BP) {
             const int q = j - AP, u = q * 64 + lane;
             if (BUPW % 64 == 0 || u < BUPW)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(st + A_BYTES + (wave * BUPW + q * 64) * 16),
-                                                         16, src_off<BW>(wave * BUPW + u, p.b_pitch, kt), 0, 0, 0);
+                                                         16, op_off<TRANS_B, BN, BW>(wave * BUPW + u, p.b_pitch, kt),
+                                                         0, 0, 0);
         } else if constexpr (Op::kSparse) {
             const int q = j - AP - BP, u = q * 64 + lane;
             if (IUPW % 64 == 0 || u < IUPW)
@@ -275,9 +312,16 @@ struct TiledGemm {
             const int u = q * 64 + lane;
             const uint32_t P = wave * AUPW + u;
             if (AUPW % 64 == 0 || u < AUPW) {
-                const int e0 = ((kt + kt0) * AW * 16 + (int)(swz<AW>(P) % AW) * 16) / Op::kEsize;
-                *reinterpret_cast<i32x4 *>(st + P * 16) =
-                    masked_unit<Op::kEsize>(ra, src_off<AW>(P, p.a_pitch, kt), e0, climit);
+                if constexpr (TRANS_A) {   // whole rows of K
+                    const bool in = (kt + kt0) * Op::kBK + (int)(P / (BM / 8)) < p.K;
+                    *reinterpret_cast<i32x4 *>(st + P * 16) =
+                        in ? __builtin_amdgcn_raw_buffer_load_b128(ra, tsrc_off<BM>(P, p.a_pitch, kt), 0, 0)
+                           : i32x4{0, 0, 0, 0};
+                } else {
+                    const int e0 = ((kt + kt0) * AW * 16 + (int)(swz<AW>(P) % AW) * 16) / Op::kEsize;
+                    *reinterpret_cast<i32x4 *>(st + P * 16) =
+                        masked_unit<Op::kEsize>(ra, src_off<AW>(P, p.a_pitch, kt), e0, climit);
+                }
             }
         }
 #pragma unroll
@@ -285,9 +329,16 @@ struct TiledGemm {
             const int u = q * 64 + lane;
             const uint32_t P = wave * BUPW + u;
             if (BUPW % 64 == 0 || u < BUPW) {
-                const int e0 = ((kt + kt0) * BW * 16 + (int)(swz<BW>(P) % BW) * 16) / Op::kEsize;
-                *reinterpret_cast<i32x4 *>(st + A_BYTES + P * 16) =
-                    masked_unit<Op::kEsize>(rb, src_off<BW>(P, p.b_pitch, kt), e0, p.K / KB);
+                if constexpr (TRANS_B) {
+                    const bool in = (kt + kt0) * Op::kBK + (int)(P / (BN / 8)) < p.K;
+                    *reinterpret_cast<i32x4 *>(st + A_BYTES + P * 16) =
+                        in ? __builtin_amdgcn_raw_buffer_load_b128(rb, tsrc_off<BN>(P, p.b_pitch, kt), 0, 0)
+                           : i32x4{0, 0, 0, 0};
+                } else {
+                    const int e0 = ((kt + kt0) * BW * 16 + (int)(swz<BW>(P) % BW) * 16) / Op::kEsize;
+                    *reinterpret_cast<i32x4 *>(st + A_BYTES + P * 16) =
+                        masked_unit<Op::kEsize>(rb, src_off<BW>(P, p.b_pitch, kt), e0, p.K / KB);
+                }
             }
         }
 #pragma unroll
@@ -309,7 +360,8 @@ struct TiledGemm {
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const uint32_t r = wm * WTM + i * 32 + l32;
-            lds_frag<AW>(a[i], sa, r * AW + Op::a_unit(s, g, 0), r * AW + Op::a_unit(s, g, 1));
+            if constexpr (TRANS_A) load_tr<BM>(a[i], sa, wm * WTM + i * 32, s);
+            else lds_frag<AW>(a[i], sa, r * AW + Op::a_unit(s, g, 0), r * AW + Op::a_unit(s, g, 1));
             if constexpr (Op::kSparse) {
                 if (s == 0) ix[i] = Op::load_idx(reinterpret_cast<const uint8_t *>(sx + r * IW), g);
             } else {
@@ -319,7 +371,8 @@ struct TiledGemm {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const uint32_t r = (wn * WTN + j * 32 + l32) * BW;
-            lds_frag<BW>(b[j], sb, r + Op::b_unit(s, g, 0), r + Op::b_unit(s, g, 1));
+            if constexpr (TRANS_B) load_tr<BN>(b[j], sb, wn * WTN + j * 32, s);
+            else lds_frag<BW>(b[j], sb, r + Op::b_unit(s, g, 0), r + Op::b_unit(s, g, 1));
         }
         if constexpr (SCALED) {
             if (s == 0) {   // this lane's row / column scale words of the whole k-tile
@@ -333,6 +386,33 @@ struct TiledGemm {
 #pragma unroll
                     for (int c = 0; c < SW; ++c) sw[(TM + j) * SW + c] = ss[BM * SW + c * BN + wn * WTN + j * 32 + l32];
             }
+        }
+    }
+
+    // Fragment of the 32 rows (A) or columns (B) mn0 .. mn0 + 31 of a
+    // transposed tile at step s, in the order lds_frag gives the
+    // K-contiguous tiles: lane half g holds K 16s + 8g .. 16s + 8g + 7.
+    // ds_read_b64_tr_b16 works on groups of 16 lanes: if lane l of a group
+    // addresses 4 consecutive elements S[l][0..3], lane i receives
+    // S[4e + i/4][i mod 4] for e = 0..3 (measured on gfx950).  So lane l
+    // addresses row k0 + l/4, elements n0 + 4(l mod 4) .. + 3, and lane i then
+    // holds rows k0 .. k0 + 3 of element n0 + i.  Group h of the wave takes
+    // elements n0 = mn0 + 16(h mod 2) and K half h / 2; two reads give 8 K.
+    template <int MN>
+    __device__ __forceinline__ void load_tr(Frag<16> &f, const uint8_t *tile, int mn0, int s) const {
+        constexpr int U = MN / 8;
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        const int h = lane >> 4, l = lane & 15;
+        const int n = mn0 + 16 * (h & 1) + 4 * (l & 3);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int k = 16 * s + 8 * (h >> 1) + 4 * c + (l >> 2);
+            const uint8_t *addr = tile + k * (MN * 2) + (((uint32_t)(n >> 3) ^ tswz<U>(k)) << 4) + (n & 7) * 2;
+            const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)addr);
+            const i32x2 w = __builtin_bit_cast(i32x2, v);
+            f.v[2 * c] = w[0];
+            f.v[2 * c + 1] = w[1];
         }
     }
 

@@ -32,7 +32,8 @@ def L():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["mmac_gemm_dense", "mmac_gemm_dense_ep", "mmac_gemm_dense_mx",
+    assert declared_functions() == ["mmac_gemm_dense", "mmac_gemm_dense_ep", "mmac_gemm_dense_layout",
+                                    "mmac_gemm_dense_mx",
                                     "mmac_gemm_dense_ws",
                                     "mmac_gemm_sparse24", "mmac_gemm_sparse24_ep", "mmac_gemm_sparse24_ws",
                                     "mmac_gemm_workspace_bytes", "mmac_sparse24_compress",
@@ -288,3 +289,32 @@ def test_mx_empty_is_a_no_op(L):
 def test_fp4_is_only_for_block_scaled_gemm(L):
     assert dense(L, a=mm.FP4_E2M1, b=mm.FP4_E2M1) == mm.ERR_UNSUPPORTED
     assert compress(L, a=mm.FP4_E2M1) == mm.ERR_UNSUPPORTED
+
+
+def dense_layout(L, **kw):
+    a = dict(a=mm.BF16, b=mm.BF16, ta=1, tb=0, M=64, N=64, K=64, alpha=1.0, A=P, lda=64, B=P, ldb=64, beta=0.0,
+             C=None, ldc=64, D=P, ldd=64, stream=None)
+    a.update(kw)
+    return L.mmac_gemm_dense_layout(a["a"], a["b"], a["ta"], a["tb"], a["M"], a["N"], a["K"], a["alpha"], a["A"],
+                                    a["lda"], a["B"], a["ldb"], a["beta"], a["C"], a["ldc"], a["D"], a["ldd"], None,
+                                    a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ta=2), mm.ERR_INVALID_ARG),
+    (dict(tb=-1), mm.ERR_INVALID_ARG),
+    (dict(a=mm.FP8_E4M3, b=mm.FP8_E4M3), mm.ERR_UNSUPPORTED),
+    (dict(a=mm.I8, b=mm.I8, ta=0, tb=1), mm.ERR_UNSUPPORTED),
+    (dict(M=100, lda=96), mm.ERR_INVALID_ARG),                        # trans A: lda >= M
+    (dict(ta=0, tb=1, N=100, ldb=96, ldd=100), mm.ERR_INVALID_ARG),     # trans B: ldb >= N
+    (dict(M=60, lda=60, ldd=64), mm.ERR_MISALIGNED),                  # 120-byte rows
+    (dict(K=1 << 20, lda=1 << 12, ldb=1 << 20), mm.ERR_UNSUPPORTED),   # 8 GiB of transposed A
+    (dict(ta=0, lda=32), mm.ERR_INVALID_ARG),                         # plain checks when not transposed
+])
+def test_layout_argument_errors(L, kw, code):
+    assert dense_layout(L, **kw) == code
+
+
+def test_layout_empty_is_a_no_op(L):
+    assert dense_layout(L, M=0) == mm.OK
+    assert dense_layout(L, N=0, tb=1) == mm.OK
