@@ -18,10 +18,13 @@ import numpy as np
 
 from . import build as _build
 
-F16, BF16, I8, E4M3, E5M2, FP4 = 1, 2, 3, 4, 5, 6
+F16, BF16, I8, E4M3, E5M2, FP4, FP6, BF6 = 1, 2, 3, 4, 5, 6, 7, 8
 FLOAT_TYPES = (F16, BF16, E4M3, E5M2)
-BITS_DTYPE = {F16: np.uint16, BF16: np.uint16, I8: np.int8, E4M3: np.uint8, E5M2: np.uint8, FP4: np.uint8}
+BITS_DTYPE = {F16: np.uint16, BF16: np.uint16, I8: np.int8, E4M3: np.uint8, E5M2: np.uint8, FP4: np.uint8,
+              FP6: np.uint8, BF6: np.uint8}
 # FP4 (OCP E2M1) arrays are packed: rows x K/2 bytes, element 2m in the low nibble of byte m.
+# FP6 (OCP E2M3 = FP6, E3M2 = BF6) arrays are packed: rows x 3K/4 bytes, element n of a row in
+# bits 6n .. 6n+5 of the row read as a little-endian bit string.
 
 _lib = None
 
@@ -137,13 +140,18 @@ def gemm_dense_entries(ta, tb, A, B, ii, jj, alpha=1.0, beta=0.0, C=None):
 
 
 def _mx_k(t, X):
-    """Elements per row of an MX operand array (FP4 is packed two per byte)."""
-    return X.shape[1] * (2 if t == FP4 else 1)
+    """Elements per row of an MX operand array (FP4 packs two per byte, FP6 four per three bytes)."""
+    if t == FP4:
+        return X.shape[1] * 2
+    if t in (FP6, BF6):
+        assert X.shape[1] % 3 == 0
+        return X.shape[1] // 3 * 4
+    return X.shape[1]
 
 
 def gemm_mx(ta, tb, A, SA, B, SB, alpha=1.0, beta=0.0, C=None, rows=None):
-    """Block-scaled (MX) GEMM: A M x K, B N x K (fp8 bits, or packed FP4 bytes M x K/2 and
-    N x K/2), SA M x K/32 and SB N x K/32 E8M0 scale bytes; returns (D fp64, S fp64) for
+    """Block-scaled (MX) GEMM: A M x K, B N x K (fp8 bits, packed FP4 bytes M x K/2 and N x K/2,
+    or packed FP6 bytes M x 3K/4 and N x 3K/4), SA M x K/32 and SB N x K/32 E8M0 scale bytes; returns (D fp64, S fp64) for
     output rows [r0, r1)."""
     M, K = A.shape[0], _mx_k(ta, A)
     N = B.shape[0]

@@ -44,17 +44,29 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F16 = 1, OR_BF16 = 2, OR_I8 = 3, OR_E4M3 = 4, OR_E5M2 = 5, OR_FP4 = 6 };
+enum { OR_F16 = 1, OR_BF16 = 2, OR_I8 = 3, OR_E4M3 = 4, OR_E5M2 = 5, OR_FP4 = 6, OR_FP6_E2M3 = 7, OR_BF6_E3M2 = 8 };
 
 static int elem_bytes(int t) { return (t == OR_F16 || t == OR_BF16) ? 2 : 1; }
 static int is_float_type(int t) {
-    return t == OR_F16 || t == OR_BF16 || t == OR_E4M3 || t == OR_E5M2 || t == OR_FP4;
+    return t == OR_F16 || t == OR_BF16 || t == OR_E4M3 || t == OR_E5M2 || t == OR_FP4 || t == OR_FP6_E2M3 ||
+           t == OR_BF6_E3M2;
 }
+static int is_fp6(int t) { return t == OR_FP6_E2M3 || t == OR_BF6_E3M2; }
 
 /* Element `off` (counted in elements) of an array of type t.  FP4 packs two
- * elements per byte, element 2m in bits 0-3 and element 2m+1 in bits 4-7. */
+ * elements per byte, element 2m in bits 0-3 and element 2m+1 in bits 4-7.
+ * FP6 packs four elements in three bytes: element n occupies bits 6n .. 6n+5
+ * of the array read as one little-endian bit string (bit b is bit b mod 8 of
+ * byte b / 8). */
 static uint32_t load_bits(int t, const void *base, int64_t off) {
     if (t == OR_FP4) return (((const uint8_t *)base)[off >> 1] >> (4 * (off & 1))) & 15u;
+    if (is_fp6(t)) {
+        const uint8_t *b = (const uint8_t *)base;
+        const int64_t bit = 6 * off;
+        uint32_t v = 0;
+        for (int q = 0; q < 6; ++q) v |= (uint32_t)((b[(bit + q) >> 3] >> ((bit + q) & 7)) & 1u) << q;
+        return v;
+    }
     if (elem_bytes(t) == 2) return ((const uint16_t *)base)[off];
     return ((const uint8_t *)base)[off];
 }
@@ -92,6 +104,12 @@ double oracle_decode_one(int t, uint32_t bits) {
     case OR_FP4: /* OCP FP4 E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa; no infinities or NaN, max 6 */
         s = (bits >> 3) & 1u; e = (bits >> 1) & 3u; m = bits & 1u;
         return from_fields(s, e, m, 1, 1);
+    case OR_FP6_E2M3: /* OCP FP6 E2M3: 1 sign, 2 exponent (bias 1), 3 mantissa; no infinities or NaN, max 7.5 */
+        s = (bits >> 5) & 1u; e = (bits >> 3) & 3u; m = bits & 7u;
+        return from_fields(s, e, m, 3, 1);
+    case OR_BF6_E3M2: /* OCP FP6 E3M2: 1 sign, 3 exponent (bias 3), 2 mantissa; no infinities or NaN, max 28 */
+        s = (bits >> 5) & 1u; e = (bits >> 2) & 7u; m = bits & 3u;
+        return from_fields(s, e, m, 2, 3);
     case OR_I8: /* two's complement */
         return (double)(int8_t)(uint8_t)bits;
     default:
@@ -101,7 +119,7 @@ double oracle_decode_one(int t, uint32_t bits) {
 
 /* Decode n elements of type t into doubles.  Returns 0, or -1 on a bad type. */
 int oracle_decode(int t, int64_t n, const void *src, double *dst) {
-    if (t < OR_F16 || t > OR_FP4) return -1;
+    if (t < OR_F16 || t > OR_BF6_E3M2) return -1;
     for (int64_t q = 0; q < n; ++q) dst[q] = oracle_decode_one(t, load_bits(t, src, q));
     return 0;
 }
@@ -109,6 +127,7 @@ int oracle_decode(int t, int64_t n, const void *src, double *dst) {
 static int bad_float_pair(int ta, int tb) {
     if (ta == OR_F16 || ta == OR_BF16 || ta == OR_FP4) return tb != ta;
     if (ta == OR_E4M3 || ta == OR_E5M2) return !(tb == OR_E4M3 || tb == OR_E5M2);
+    if (is_fp6(ta)) return !is_fp6(tb);
     return 1;
 }
 
@@ -177,7 +196,9 @@ int oracle_gemm_dense_f64(int ta, int tb, int64_t M, int64_t N, int64_t K, doubl
  *   D[i][j] = alpha * sum_b 2^(SA[i][b] - 127) * 2^(SB[j][b] - 127)
  *                         * sum_{k in block b} a[i][k] * b[k][j]  +  beta * C[i][j]
  * summed exactly in fp64 (every term is a power-of-two multiple of an exact
- * fp8 product).  SA is M x K/32 bytes (row pitch ldsa), SB is N x K/32 bytes
+ * product of two elements).  The elements are fp8 (E4M3 / E5M2, any pair),
+ * FP6 (E2M3 / E3M2, any pair) or FP4 (E2M1 with E2M1), the element formats
+ * of that specification.  SA is M x K/32 bytes (row pitch ldsa), SB is N x K/32 bytes
  * (ldsb), both row-major; K must be a multiple of 32.  S receives
  * sum |scaled product|, the error scale.  Rows [r0, r1) as in the dense oracle.
  */

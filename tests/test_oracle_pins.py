@@ -642,3 +642,75 @@ def test_mx_fp4_brute_force_fraction():
             assert D[i, j] == float(2 * acc)
             assert S[i, j] == float(sum(abs(Fraction(2) ** (int(SA[i, k // 32]) + int(SB[j, k // 32]) - 254) *
                                             Fraction(Av[i, k]) * Fraction(Bv[j, k])) for k in range(K)))
+
+
+# FP6 (OCP E2M3 and E3M2, four elements in three bytes: element n of a row in bits 6n .. 6n+5 of
+# the row read as a little-endian bit string) for block-scaled GEMMs.  Each format's 32 non-negative
+# codes run through its binades in order: subnormals, then equal steps inside each power of two.
+# The OCP microscaling specification fixes the end points checked here: E2M3 max 7.5, smallest
+# normal 1, smallest subnormal 1/8; E3M2 max 28, smallest normal 1/4, smallest subnormal 1/16.
+FP6_VALUES = np.concatenate([np.arange(0, 1, 1 / 8), np.arange(1, 2, 1 / 8), np.arange(2, 4, 1 / 4),
+                             np.arange(4, 8, 1 / 2)]).tolist()
+BF6_VALUES = np.concatenate([np.arange(0, 1 / 4, 1 / 16), np.arange(1 / 4, 1 / 2, 1 / 16),
+                             np.arange(1 / 2, 1, 1 / 8), np.arange(1, 2, 1 / 4), np.arange(2, 4, 1 / 2),
+                             np.arange(4, 8, 1), np.arange(8, 16, 2), np.arange(16, 32, 4)]).tolist()
+
+
+def fp6_unpack(P, t):
+    """Packed FP6 rows -> values, through numpy's own little-endian bit unpacking."""
+    P = np.asarray(P, np.uint8)
+    bits = np.unpackbits(P, axis=1, bitorder="little")                  # rows x 8 * bytes
+    codes = (bits.reshape(P.shape[0], -1, 6) * (1 << np.arange(6))).sum(axis=2)
+    table = np.array(FP6_VALUES if t == oracle.FP6 else BF6_VALUES)
+    mag = table[codes & 31]
+    return np.where(codes & 32, -mag, mag)
+
+
+@pytest.mark.parametrize("t,table,top,norm,sub", [(oracle.FP6, FP6_VALUES, 7.5, 1.0, 0.125),
+                                                 (oracle.BF6, BF6_VALUES, 28.0, 0.25, 0.0625)])
+def test_fp6_decode_every_code(t, table, top, norm, sub):
+    assert len(table) == 32 and table[-1] == top and table[1] == sub
+    mbits = 3 if t == oracle.FP6 else 2
+    assert table[1 << mbits] == norm                      # first code with a non-zero exponent field
+    got = [oracle.decode_one(t, c) for c in range(64)]
+    assert got == table + [-v for v in table] and np.signbit(got[32])
+
+
+@pytest.mark.parametrize("ta,tb", [(oracle.FP6, oracle.FP6), (oracle.FP6, oracle.BF6), (oracle.BF6, oracle.FP6),
+                                   (oracle.BF6, oracle.BF6)])
+def test_mx_fp6_brute_force_fraction(ta, tb):
+    g = np.random.default_rng(43 + 2 * ta + tb)
+    M, N, K = 4, 3, 96
+    A = g.integers(0, 256, size=(M, K * 3 // 4)).astype(np.uint8)
+    B = g.integers(0, 256, size=(N, K * 3 // 4)).astype(np.uint8)
+    SA = g.integers(120, 135, size=(M, K // 32)).astype(np.uint8)
+    SB = g.integers(120, 135, size=(N, K // 32)).astype(np.uint8)
+    C = g.standard_normal((M, N)).astype(np.float32)
+    D, S = oracle.gemm_mx(ta, tb, A, SA, B, SB, 0.5, 1.25, C)
+    Av, Bv = fp6_unpack(A, ta), fp6_unpack(B, tb)
+    assert Av.shape == (M, K)
+    for i in range(M):
+        for j in range(N):
+            terms = [Fraction(2) ** (int(SA[i, k // 32]) + int(SB[j, k // 32]) - 254) * Fraction(Av[i, k]) *
+                     Fraction(Bv[j, k]) for k in range(K)]
+            assert D[i, j] == float(Fraction(1, 2) * sum(terms) + Fraction(5, 4) * Fraction(float(C[i, j])))
+            assert S[i, j] == float(sum(abs(t) for t in terms))
+
+
+def test_mx_fp6_element_position():
+    """One non-zero code at element n of a packed row of A lands on k = n alone: against a B whose
+    column j holds 1 at k = j only, D[0][j] is non-zero exactly for j = n (every n of a 64-element row)."""
+    K = 64
+    one = 0b001000                                          # E2M3: exponent field 1, mantissa 0 -> 1.0
+    B = np.zeros((K, K * 3 // 4), np.uint8)
+    for j in range(K):                                      # column j of B: 1.0 at element j
+        bit = 6 * j
+        v = one << (bit % 8)
+        B[j, bit // 8] |= v & 255
+        if v >> 8:
+            B[j, bit // 8 + 1] |= v >> 8
+    ones = np.full((K, 2), 127, np.uint8)
+    for n in range(K):
+        A = B[n:n + 1].copy()
+        D, _ = oracle.gemm_mx(oracle.FP6, oracle.FP6, A, ones[:1], B, ones)
+        assert np.nonzero(D[0])[0].tolist() == [n] and D[0, n] == 1.0
