@@ -384,6 +384,17 @@ def suite():
     out["mx_fp4e2m1_8192^3"] = {"us": round(ms * 1e3, 1), "TFLOP/s": round(gemm_flops(M, N, K) / ms / 1e9, 1),
                                  "shape": [M, N, K], "scales": "E8M0 per 32 along K"}
     del A, B, SA, SB, D
+    # block-scaled FP6 E2M3 x BF6 E3M2 at 8192^3 (packed four per three bytes, random codes)
+    A = torch.randint(0, 256, (M, K // 4 * 3), dtype=torch.uint8, generator=g).to(dev)
+    B = torch.randint(0, 256, (N, K // 4 * 3), dtype=torch.uint8, generator=g).to(dev)
+    SA = torch.full((K // 128, M), 0x7F7F7F7F, dtype=torch.int32, device=dev)
+    SB = torch.full((K // 128, N), 0x7F7F7F7F, dtype=torch.int32, device=dev)
+    D = torch.empty((M, N), dtype=torch.float32, device=dev)
+    ms = median_ms([lambda: mm.gemm_mx(A, SA, B, SB, D, a_type=mm.FP6_E2M3, b_type=mm.BF6_E3M2, stream=stream)], 20)
+    out["mx_fp6e2m3xbf6e3m2_8192^3"] = {"us": round(ms * 1e3, 1),
+                                         "TFLOP/s": round(gemm_flops(M, N, K) / ms / 1e9, 1),
+                                         "shape": [M, N, K], "scales": "E8M0 per 32 along K"}
+    del A, B, SA, SB, D
 
     # other operand layouts: the bf16 8192^3 workload (beta = 1) with A stored M-contiguous and / or
     # B stored N-contiguous (transposed LDS reads)

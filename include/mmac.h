@@ -86,8 +86,11 @@ typedef enum {
     MMAC_I8 = 3,       /* signed 8-bit integer */
     MMAC_FP8_E4M3 = 4, /* OCP FP8 E4M3 */
     MMAC_BF8_E5M2 = 5, /* OCP BF8 E5M2 */
-    MMAC_FP4_E2M1 = 6  /* OCP FP4 E2M1, two per byte (element 2m in the low nibble of byte m);
+    MMAC_FP4_E2M1 = 6, /* OCP FP4 E2M1, two per byte (element 2m in the low nibble of byte m);
                           block-scaled GEMM only */
+    MMAC_FP6_E2M3 = 7, /* OCP FP6 E2M3 and BF6 E3M2, four elements per three bytes: element n of */
+    MMAC_BF6_E3M2 = 8  /* a row in bits 6n .. 6n+5 of the row read as a little-endian bit string
+                          (bit b = bit b mod 8 of byte b / 8); block-scaled GEMM only */
 } mmac_dtype_t;
 
 /*
@@ -276,11 +279,13 @@ mmac_status_t mmac_gemm_sparse24_ws(mmac_dtype_t a_type, mmac_dtype_t b_type,
  *   D = alpha * sum_b 2^(sa[i][b] - 127) * 2^(sb[j][b] - 127) * (A_b * B_b)[i][j] + beta * C
  * with the gfx950 instruction v_mfma_scale_f32_32x32x64_f8f6f4, whose E8M0
  * operands scale exactly these 32-element blocks.
- *   a_type, b_type  FP8_E4M3 / BF8_E5M2, any pair, or FP4_E2M1 x FP4_E2M1.
- *                   K % 32 == 0.
- *   A, B            as in mmac_gemm_dense; for FP4 the row pitches lda, ldb
- *                   count elements and must be even (each row starts on a
- *                   byte; the 16-byte pitch rule applies to lda / 2 bytes).
+ *   a_type, b_type  FP8_E4M3 / BF8_E5M2, any pair; FP6_E2M3 / BF6_E3M2, any
+ *                   pair; or FP4_E2M1 x FP4_E2M1.  K % 32 == 0.
+ *   A, B            as in mmac_gemm_dense; for FP4 and FP6 the row pitches
+ *                   lda, ldb count elements: even for FP4 (the 16-byte pitch
+ *                   rule applies to lda / 2 bytes), a multiple of 4 for FP6
+ *                   (rows of 3 lda / 4 bytes, which must be a multiple of 16,
+ *                   so lda % 64 == 0) -- MMAC_ERR_MISALIGNED otherwise.
  *   SA              scale words of A: ceil(K/128) x ldsa 32-bit words,
  *                   SA[t*ldsa + i] holds the exponents of blocks 4t .. 4t+3
  *                   of row i in its bytes 0 .. 3 (byte q: block 4t + q,

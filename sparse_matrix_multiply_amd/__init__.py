@@ -23,7 +23,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmmac.so")
 
-F16, BF16, I8, FP8_E4M3, BF8_E5M2, FP4_E2M1 = 1, 2, 3, 4, 5, 6
+F16, BF16, I8, FP8_E4M3, BF8_E5M2, FP4_E2M1, FP6_E2M3, BF6_E3M2 = 1, 2, 3, 4, 5, 6, 7, 8
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_HIP = 0, 1, 2, 3, 4
 
 OUT_ACC, OUT_BF16, OUT_F16, OUT_FP8_E4M3, OUT_BF8_E5M2 = 0, 1, 2, 3, 4
@@ -215,12 +215,22 @@ def gemm_mx(A, SA, B, SB, D, alpha=1.0, beta=0.0, C=None, a_type=None, b_type=No
     """Block-scaled (MX) GEMM: D = alpha * (A, SA) @ (B, SB) + beta * C.  A M x K and B N x K fp8;
     SA and SB the E8M0 scale words (ceil(K/128) x >= M and ceil(K/128) x >= N int32 tensors,
     four block exponents per word, see include/mmac.h).  For FP4_E2M1, A and B are uint8 tensors
-    of packed pairs (M x K/2, N x K/2).  Epilogue arguments as in gemm_dense."""
+    of packed pairs (M x K/2, N x K/2); for FP6_E2M3 / BF6_E3M2 uint8 tensors of packed
+    elements, four per three bytes (M x 3K/4, N x 3K/4).  Epilogue arguments as in gemm_dense."""
     M, K = A.shape
     N = B.shape[0]
     ta, tb = _dtype(A, a_type), _dtype(B, b_type)
-    per = 2 if ta == FP4_E2M1 else 1          # elements per stored byte
-    K, lda, ldb = K * per, _ld(A) * per, _ld(B) * (2 if tb == FP4_E2M1 else 1)
+
+    def elems(nbytes, t):                      # elements in nbytes stored bytes of type t
+        if t == FP4_E2M1:
+            return nbytes * 2
+        if t in (FP6_E2M3, BF6_E3M2):
+            if nbytes % 3:
+                raise ValueError("packed FP6 rows and pitches must be whole multiples of 3 bytes")
+            return nbytes // 3 * 4
+        return nbytes
+
+    K, lda, ldb = elems(K, ta), elems(_ld(A), ta), elems(_ld(B), tb)
     ep = _epilogue(D, bias, act, d_type)
     st = lib().mmac_gemm_dense_mx(ta, tb, M, N, K, float(alpha), _ptr(A), lda, _ptr(SA), _ld(SA), _ptr(B), ldb,
                                   _ptr(SB), _ld(SB), float(beta), _ptr(C), _ld(C) if C is not None else 0, _ptr(D),

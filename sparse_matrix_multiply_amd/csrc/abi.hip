@@ -313,18 +313,25 @@ mmac_status_t mmac_gemm_dense_mx(mmac_dtype_t a_type, mmac_dtype_t b_type, int64
                                  const void *C, int64_t ldc, void *D, int64_t ldd, const mmac_epilogue_t *ep_in,
                                  void *stream) {
     const mmac_epilogue_t ep = epilogue_of(ep_in);
-    // FP4 (packed two per byte) only with FP4; the generic checks below then
-    // see it as a one-byte type with half the element counts
+    // FP4 (packed two per byte) only with FP4, FP6 (four per three bytes) only
+    // with FP6; the generic checks below then see them as a one-byte type with
+    // the rows' byte counts
     const bool fp4 = a_type == MMAC_FP4_E2M1 || b_type == MMAC_FP4_E2M1;
+    const bool fp6a = a_type == MMAC_FP6_E2M3 || a_type == MMAC_BF6_E3M2;
+    const bool fp6b = b_type == MMAC_FP6_E2M3 || b_type == MMAC_BF6_E3M2;
+    const bool fp6 = fp6a || fp6b, packed = fp4 || fp6;
     if (fp4 && a_type != b_type) return MMAC_ERR_UNSUPPORTED;
-    if (!fp4 && valid_type(a_type) && valid_type(b_type) && (!is_fp8(a_type) || !is_fp8(b_type)))
+    if (fp6 && !(fp6a && fp6b)) return MMAC_ERR_UNSUPPORTED;
+    if (!packed && valid_type(a_type) && valid_type(b_type) && (!is_fp8(a_type) || !is_fp8(b_type)))
         return MMAC_ERR_UNSUPPORTED;
     if (K >= 0 && (K % 32) != 0) return MMAC_ERR_INVALID_ARG;
     if (fp4 && ((lda % 2) || (ldb % 2))) return MMAC_ERR_MISALIGNED;
-    const mmac_dtype_t ga = fp4 ? MMAC_FP8_E4M3 : a_type, gb = fp4 ? MMAC_FP8_E4M3 : b_type;
-    const int64_t kk = fp4 ? K / 2 : K;   // bytes of a row for FP4
-    const mmac_status_t st = check_gemm(ga, gb, M, N, kk, alpha, A, fp4 ? lda / 2 : lda, kk, B, fp4 ? ldb / 2 : ldb,
-                                        beta, C, ldc, D, ldd, ep);
+    if (fp6 && ((lda % 4) || (ldb % 4))) return MMAC_ERR_MISALIGNED;
+    const auto bytes = [&](int64_t n) { return fp4 ? n / 2 : fp6 ? n / 4 * 3 : n; };   // of n elements
+    const mmac_dtype_t ga = packed ? MMAC_FP8_E4M3 : a_type, gb = packed ? MMAC_FP8_E4M3 : b_type;
+    const int64_t kk = bytes(K);
+    const mmac_status_t st =
+        check_gemm(ga, gb, M, N, kk, alpha, A, bytes(lda), kk, B, bytes(ldb), beta, C, ldc, D, ldd, ep);
     if (st != MMAC_OK) return st;
     if ((K > 0 && (!SA || !SB)) || ldsa < M || ldsb < N || ldsa < 1 || ldsb < 1) return MMAC_ERR_INVALID_ARG;
     const int64_t scale_rows = (K + 127) / 128;
@@ -335,9 +342,9 @@ mmac_status_t mmac_gemm_dense_mx(mmac_dtype_t a_type, mmac_dtype_t b_type, int64
     TileShape shape = pick_shape(M, N, true);
     if (shape == TILE_256) shape = TILE_128x256;
     GemmParams p = make_params(ga, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd, ep, shape);
-    if (fp4) {
-        p.a_pitch = lda / 2;
-        p.b_pitch = ldb / 2;
+    if (packed) {
+        p.a_pitch = bytes(lda);
+        p.b_pitch = bytes(ldb);
     }
     p.sa = SA;
     p.sb = SB;

@@ -32,7 +32,7 @@ typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x16 __attribute__((ext_vector_type(16)));
 
-enum : int { DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3, DT_E4M3 = 4, DT_E5M2 = 5, DT_FP4 = 6 };
+enum : int { DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3, DT_E4M3 = 4, DT_E5M2 = 5, DT_FP4 = 6, DT_FP6 = 7, DT_BF6 = 8 };
 
 // Word 3 of a gfx9 buffer descriptor for raw (untyped) 32-bit accesses.
 constexpr int kBufferWord3 = 0x00020000;
@@ -172,11 +172,17 @@ __device__ __forceinline__ uint32_t finish(float v, float bias, bool has_bias, b
 // 256-byte bank row keep distinct positions, and successive bank rows are
 // XOR-rotated, so those 16 reads hit 16 different 16-byte bank groups.  The
 // map keeps the row and is its own inverse.
+// Rows of 7 units hold the 96 bytes of 128 packed FP6 elements and one unused
+// unit; they need no swizzle: 112-byte rows sit 28 banks apart, so 16
+// consecutive rows start on 16 distinct multiples of 4 banks.
 template <int W>
 __device__ __forceinline__ constexpr uint32_t swz(uint32_t L) {
-    static_assert(W == 2 || W == 4 || W == 8, "rows of 2, 4 or 8 units");
-    const uint32_t r = L / W;
-    return r * W + ((L % W) ^ ((r / (16 / W)) % W));
+    static_assert(W == 2 || W == 4 || W == 7 || W == 8, "rows of 2, 4, 7 or 8 units");
+    if constexpr (W == 7) return L;
+    else {
+        const uint32_t r = L / W;
+        return r * W + ((L % W) ^ ((r / (16 / W)) % W));
+    }
 }
 
 // ---- matrix-instruction wrappers -----------------------------------------
@@ -186,6 +192,8 @@ __device__ __forceinline__ constexpr uint32_t swz(uint32_t L) {
 template <int BYTES> struct Frag;
 template <> struct Frag<16> { i32x4 v; };
 template <> struct Frag<32> { i32x4 lo, hi; };
+typedef int i32x6 __attribute__((ext_vector_type(6)));
+template <> struct Frag<24> { i32x6 v; };
 
 __device__ __forceinline__ i32x8 join(const Frag<32> &f) {
     return i32x8{f.lo[0], f.lo[1], f.lo[2], f.lo[3], f.hi[0], f.hi[1], f.hi[2], f.hi[3]};
@@ -283,10 +291,10 @@ template <int FA, int FB> struct MmaMX : MmaDenseF8<FA, FB> {
 // (low nibble first); 128-byte LDS rows hold 256 elements per k-tile, so a
 // k-tile is four 64-K steps and two scale words per row.  Lane half g of
 // step s loads 16-byte unit 2s + g: K 64s + 32g .. 64s + 32g + 31, block
-// 2s + g.  Copies count bytes: kKPerByte = 2 elements per byte.
+// 2s + g.  Copies count bytes: 4 bits per element.
 struct MmaMX4 {
     static constexpr bool kSparse = false, kScaled = true;
-    static constexpr int kEsize = 1, kKPerByte = 2, kAFrag = 16, kBFrag = 16, kKStep = 64;
+    static constexpr int kEsize = 1, kElemBits = 4, kAFrag = 16, kBFrag = 16, kKStep = 64;
     static constexpr int kBK = 256;
     static constexpr int kARowBytes = kBK / 2, kBRowBytes = kBK / 2;
     static constexpr int kScaleWords = kBK / 128;
@@ -299,6 +307,31 @@ struct MmaMX4 {
         const i32x8 A = {a.v[0], a.v[1], a.v[2], a.v[3], 0, 0, 0, 0};
         const i32x8 B = {b.v[0], b.v[1], b.v[2], b.v[3], 0, 0, 0, 0};
         return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, c, 4, 4, 0, (int)sa, 0, (int)sb);
+    }
+};
+
+// Block-scaled FP6 (format 2 = E2M3, 3 = E3M2): one 32-element block of
+// packed elements (24 bytes, element e at bits 6e .. 6e+5) per lane, lane half
+// g holding block g of the instruction's 64 K (established on gfx950 with
+// one-hot operands: every element of lane half g took block g's scale, with
+// the value the packing gives).  K-tiles of 128 elements: 96 bytes per row
+// (kept in 112-byte LDS rows), blocks 2s and 2s+1 in step s; one scale word
+// per row per k-tile.
+template <int FA, int FB>
+struct MmaMX6 {
+    static constexpr bool kSparse = false, kScaled = true;
+    static constexpr int kEsize = 1, kElemBits = 6, kAFrag = 24, kBFrag = 24, kKStep = 64;
+    static constexpr int kBK = 128;
+    static constexpr int kARowBytes = kBK * 6 / 8, kBRowBytes = kBK * 6 / 8;
+    static constexpr int kScaleWords = kBK / 128;
+    typedef f32x16 acc_t;
+    typedef float out_t;
+    __device__ __forceinline__ static acc_t mma_scaled(const Frag<24> &a, const Frag<24> &b, acc_t c, uint32_t sa,
+                                                       uint32_t sb) {
+        // the instruction reads six registers for FP6 operands; the last two are don't-cares
+        const i32x8 A = __builtin_shufflevector(a.v, a.v, 0, 1, 2, 3, 4, 5, -1, -1);
+        const i32x8 B = __builtin_shufflevector(b.v, b.v, 0, 1, 2, 3, 4, 5, -1, -1);
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, c, FA, FB, 0, (int)sa, 0, (int)sb);
     }
 };
 

@@ -41,6 +41,11 @@ hipError_t launch_gemm_mx(int a, int b, TileShape shape, GemmParams p, hipStream
     if (a == DT_E5M2 && b == DT_E4M3) return launch_dense_op<MmaMX<1, 0>>(shape, p, s);
     if (a == DT_E5M2 && b == DT_E5M2) return launch_dense_op<MmaMX<1, 1>>(shape, p, s);
     if (a == DT_FP4 && b == DT_FP4) return launch_dense_op<MmaMX4>(shape, p, s);
+    // f8f6f4 format selectors: 2 = FP6 E2M3, 3 = BF6 E3M2
+    if (a == DT_FP6 && b == DT_FP6) return launch_dense_op<MmaMX6<2, 2>>(shape, p, s);
+    if (a == DT_FP6 && b == DT_BF6) return launch_dense_op<MmaMX6<2, 3>>(shape, p, s);
+    if (a == DT_BF6 && b == DT_FP6) return launch_dense_op<MmaMX6<3, 2>>(shape, p, s);
+    if (a == DT_BF6 && b == DT_BF6) return launch_dense_op<MmaMX6<3, 3>>(shape, p, s);
     return hipErrorInvalidValue;
 }
 

@@ -118,9 +118,9 @@ __device__ __forceinline__ void wait_copies(int n) {
     }
 }
 
-// Elements per byte of an operand (packed FP4: 2).
-template <class O, class = void> struct KPerByte { static constexpr int value = 1; };
-template <class O> struct KPerByte<O, std::void_t<decltype(O::kKPerByte)>> { static constexpr int value = O::kKPerByte; };
+// Bits per element of an operand (packed FP4: 4, packed FP6: 6).
+template <class O, class = void> struct ElemBits { static constexpr int value = 8 * O::kEsize; };
+template <class O> struct ElemBits<O, std::void_t<decltype(O::kElemBits)>> { static constexpr int value = O::kElemBits; };
 
 // Operands stored with M (A) or N (B) contiguous instead of K (16-bit types).
 template <class O, class = void> struct TransOf { static constexpr bool a = false, b = false; };
@@ -143,9 +143,17 @@ struct TiledGemm {
     static constexpr int STEPS = Op::kBK / Op::kKStep;
     static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 tiles");
-    static constexpr int AW = Op::kARowBytes / 16, BW = Op::kBRowBytes / 16;  // 16-byte units per LDS row
-    static_assert(AW == 2 || AW == 4 || AW == 8, "A LDS rows of 32, 64 or 128 bytes");
-    static_assert(BW == 4 || BW == 8, "B LDS rows of 64 or 128 bytes");
+    // 16-byte units per LDS row: the row's bytes of one k-tile, except that the
+    // 96 bytes of packed FP6 go in 7-unit rows (the last unit unused)
+    static constexpr int lds_units(int bytes) { return bytes == 96 ? 7 : bytes / 16; }
+    static constexpr int AW = lds_units(Op::kARowBytes), BW = lds_units(Op::kBRowBytes);
+    static_assert(AW == 2 || AW == 4 || AW == 7 || AW == 8, "A LDS rows of 32, 64, 112 or 128 bytes");
+    static_assert(BW == 4 || BW == 7 || BW == 8, "B LDS rows of 64, 112 or 128 bytes");
+    static_assert((AW != 7 && BW != 7) || Op::kAFrag == 24, "112-byte rows hold packed FP6 only");
+    // bytes of a row that one k-tile covers, and whether LDS slot P of a tile with
+    // W units per row holds data
+    static constexpr int row_bytes(int W) { return W == 7 ? 96 : W * 16; }
+    static constexpr bool data_slot(int W, uint32_t P) { return W != 7 || P % 7 != 6; }
     static constexpr int IW = Op::kSparse ? Op::kBK / 32 : 0;                  // index words per row
     static_assert(!Op::kSparse || STEPS == 2, "index words of a k-tile read once, for two steps");
     // copy units per wave: 16-byte units of A and B, 4-byte words of the index
@@ -219,7 +227,7 @@ struct TiledGemm {
     template <int W>
     __device__ __forceinline__ uint32_t src_off(uint32_t P, int64_t pitch, int kt) const {
         const uint32_t L = swz<W>(P);
-        return (L / W) * (uint32_t)pitch + (uint32_t)((kt + kt0) * W * 16) + (L % W) * 16;
+        return (L / W) * (uint32_t)pitch + (uint32_t)((kt + kt0) * row_bytes(W)) + (L % W) * 16;
     }
 
     // Byte offset of the source of index copy lane d (LDS bytes [d*IES,
@@ -265,13 +273,13 @@ struct TiledGemm {
     __device__ __forceinline__ void dma_pass(uint8_t *st, int kt, int j) const {
         if (j < AP) {
             const int u = j * 64 + lane;
-            if (AUPW % 64 == 0 || u < AUPW)
+            if ((AUPW % 64 == 0 || u < AUPW) && data_slot(AW, wave * AUPW + u))
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(st + (wave * AUPW + j * 64) * 16), 16,
                                                          op_off<TRANS_A, BM, AW>(wave * AUPW + u, p.a_pitch, kt), 0,
                                                          0, 0);
         } else if (j < AP + BP) {
             const int q = j - AP, u = q * 64 + lane;
-            if (BUPW % 64 == 0 || u < BUPW)
+            if ((BUPW % 64 == 0 || u < BUPW) && data_slot(BW, wave * BUPW + u))
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(st + A_BYTES + (wave * BUPW + q * 64) * 16),
                                                          16, op_off<TRANS_B, BN, BW>(wave * BUPW + u, p.b_pitch, kt),
                                                          0, 0, 0);
@@ -305,20 +313,22 @@ struct TiledGemm {
     // The ragged last k-tile: A and B through registers with elements past K set
     // to zero (the index words, if any, still by copy).
     __device__ __forceinline__ void fill_masked(uint8_t *st, int kt) const {
-        constexpr int KB = KPerByte<Op>::value;
-        const int climit = (Op::kSparse ? p.K / 2 : p.K) / KB;   // copy elements of A per row
+        constexpr int EB = ElemBits<Op>::value;
+        // bytes of A's (compressed) and B's rows before K, in units of kEsize
+        const int climit = (Op::kSparse ? p.K / 2 : p.K) * EB / 8 / Op::kEsize;
+        const int blimit = p.K * EB / 8 / Op::kEsize;
 #pragma unroll
         for (int q = 0; q < AP; ++q) {
             const int u = q * 64 + lane;
             const uint32_t P = wave * AUPW + u;
-            if (AUPW % 64 == 0 || u < AUPW) {
+            if ((AUPW % 64 == 0 || u < AUPW) && data_slot(AW, P)) {
                 if constexpr (TRANS_A) {   // whole rows of K
                     const bool in = (kt + kt0) * Op::kBK + (int)(P / (BM / 8)) < p.K;
                     *reinterpret_cast<i32x4 *>(st + P * 16) =
                         in ? __builtin_amdgcn_raw_buffer_load_b128(ra, tsrc_off<BM>(P, p.a_pitch, kt), 0, 0)
                            : i32x4{0, 0, 0, 0};
                 } else {
-                    const int e0 = ((kt + kt0) * AW * 16 + (int)(swz<AW>(P) % AW) * 16) / Op::kEsize;
+                    const int e0 = ((kt + kt0) * row_bytes(AW) + (int)(swz<AW>(P) % AW) * 16) / Op::kEsize;
                     *reinterpret_cast<i32x4 *>(st + P * 16) =
                         masked_unit<Op::kEsize>(ra, src_off<AW>(P, p.a_pitch, kt), e0, climit);
                 }
@@ -328,16 +338,16 @@ struct TiledGemm {
         for (int q = 0; q < BP; ++q) {
             const int u = q * 64 + lane;
             const uint32_t P = wave * BUPW + u;
-            if (BUPW % 64 == 0 || u < BUPW) {
+            if ((BUPW % 64 == 0 || u < BUPW) && data_slot(BW, P)) {
                 if constexpr (TRANS_B) {
                     const bool in = (kt + kt0) * Op::kBK + (int)(P / (BN / 8)) < p.K;
                     *reinterpret_cast<i32x4 *>(st + A_BYTES + P * 16) =
                         in ? __builtin_amdgcn_raw_buffer_load_b128(rb, tsrc_off<BN>(P, p.b_pitch, kt), 0, 0)
                            : i32x4{0, 0, 0, 0};
                 } else {
-                    const int e0 = ((kt + kt0) * BW * 16 + (int)(swz<BW>(P) % BW) * 16) / Op::kEsize;
+                    const int e0 = ((kt + kt0) * row_bytes(BW) + (int)(swz<BW>(P) % BW) * 16) / Op::kEsize;
                     *reinterpret_cast<i32x4 *>(st + A_BYTES + P * 16) =
-                        masked_unit<Op::kEsize>(rb, src_off<BW>(P, p.b_pitch, kt), e0, p.K / KB);
+                        masked_unit<Op::kEsize>(rb, src_off<BW>(P, p.b_pitch, kt), e0, blimit);
                 }
             }
         }
@@ -361,6 +371,7 @@ struct TiledGemm {
         for (int i = 0; i < TM; ++i) {
             const uint32_t r = wm * WTM + i * 32 + l32;
             if constexpr (TRANS_A) load_tr<BM>(a[i], sa, wm * WTM + i * 32, s);
+            else if constexpr (Op::kAFrag == 24) lds_frag6<AW>(a[i], sa, r, s);
             else lds_frag<AW>(a[i], sa, r * AW + Op::a_unit(s, g, 0), r * AW + Op::a_unit(s, g, 1));
             if constexpr (Op::kSparse) {
                 if (s == 0) ix[i] = Op::load_idx(reinterpret_cast<const uint8_t *>(sx + r * IW), g);
@@ -372,6 +383,7 @@ struct TiledGemm {
         for (int j = 0; j < TN; ++j) {
             const uint32_t r = (wn * WTN + j * 32 + l32) * BW;
             if constexpr (TRANS_B) load_tr<BN>(b[j], sb, wn * WTN + j * 32, s);
+            else if constexpr (Op::kBFrag == 24) lds_frag6<BW>(b[j], sb, wn * WTN + j * 32 + l32, s);
             else lds_frag<BW>(b[j], sb, r + Op::b_unit(s, g, 0), r + Op::b_unit(s, g, 1));
         }
         if constexpr (SCALED) {
@@ -387,6 +399,21 @@ struct TiledGemm {
                     for (int c = 0; c < SW; ++c) sw[(TM + j) * SW + c] = ss[BM * SW + c * BN + wn * WTN + j * 32 + l32];
             }
         }
+    }
+
+    // Packed FP6 fragment: the 24 bytes of block 2s + g of row r of a tile of
+    // 112-byte rows (bytes 48s + 24g .. + 23 of the row), read as three 8-byte
+    // pieces straight into operand order; only the row base is per lane, the
+    // rest are instruction offsets.
+    template <int W>
+    __device__ __forceinline__ void lds_frag6(Frag<24> &f, const uint8_t *base, uint32_t r, int s) const {
+        static_assert(W == 7, "112-byte rows");
+        const uint8_t *row = base + r * (W * 16) + 24 * g;
+        const i32x2 p0 = *reinterpret_cast<const i32x2 *>(row + 48 * s);
+        const i32x2 p1 = *reinterpret_cast<const i32x2 *>(row + 48 * s + 8);
+        const i32x2 p2 = *reinterpret_cast<const i32x2 *>(row + 48 * s + 16);
+        const i32x4 p01 = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+        f.v = __builtin_shufflevector(p01, __builtin_shufflevector(p2, p2, 0, 1, -1, -1), 0, 1, 2, 3, 4, 5);
     }
 
     // Fragment of the 32 rows (A) or columns (B) mn0 .. mn0 + 31 of a
@@ -430,9 +457,11 @@ struct TiledGemm {
         }
     }
 
+    // LDS read instructions per fragment (packed FP6: three 8-byte reads).
+    static constexpr int frag_reads(int bytes) { return bytes == 24 ? 3 : bytes / 16; }
     // Instruction counts of one step, for the interleaving below.
     static constexpr int NMMA = TM * TN;
-    static constexpr int NREAD = TM * (Op::kAFrag / 16) + TN * (Op::kBFrag / 16) + (Op::kSparse ? TM : 0) +
+    static constexpr int NREAD = TM * frag_reads(Op::kAFrag) + TN * frag_reads(Op::kBFrag) + (Op::kSparse ? TM : 0) +
                                  (SCALED ? (TM + TN) * SW : 0);
 
     // Index operand of the matrix instruction of step s.

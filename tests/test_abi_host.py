@@ -275,6 +275,13 @@ def dense_mx(L, **kw):
     (dict(a=mm.FP4_E2M1, b=mm.FP4_E2M1, lda=257, ldb=256), mm.ERR_MISALIGNED),   # odd element pitch
     (dict(a=mm.FP4_E2M1, b=mm.FP4_E2M1, lda=264, ldb=256), mm.ERR_MISALIGNED),   # 132-byte rows
     (dict(a=mm.FP4_E2M1, b=mm.FP4_E2M1, lda=128, ldb=256), mm.ERR_INVALID_ARG),  # lda < K
+    (dict(a=mm.FP6_E2M3, b=mm.FP8_E4M3), mm.ERR_UNSUPPORTED),         # FP6 only with FP6
+    (dict(a=mm.FP8_E4M3, b=mm.BF6_E3M2), mm.ERR_UNSUPPORTED),
+    (dict(a=mm.FP6_E2M3, b=mm.FP4_E2M1), mm.ERR_UNSUPPORTED),
+    (dict(a=mm.FP6_E2M3, b=mm.BF6_E3M2, lda=258), mm.ERR_MISALIGNED),   # not whole bytes
+    (dict(a=mm.BF6_E3M2, b=mm.FP6_E2M3, ldb=260), mm.ERR_MISALIGNED),   # 195-byte rows
+    (dict(a=mm.FP6_E2M3, b=mm.FP6_E2M3, lda=192), mm.ERR_INVALID_ARG),  # lda < K (144-byte rows)
+    (dict(a=mm.FP6_E2M3, b=mm.FP6_E2M3, K=240, lda=256, ldb=256), mm.ERR_INVALID_ARG),   # K % 32
 ])
 def test_mx_argument_errors(L, kw, code):
     assert dense_mx(L, **kw) == code
@@ -284,11 +291,15 @@ def test_mx_empty_is_a_no_op(L):
     assert dense_mx(L, M=0) == mm.OK
     assert dense_mx(L, N=0) == mm.OK
     assert dense_mx(L, M=0, a=mm.FP4_E2M1, b=mm.FP4_E2M1) == mm.OK
+    assert dense_mx(L, M=0, a=mm.FP6_E2M3, b=mm.BF6_E3M2) == mm.OK
 
 
-def test_fp4_is_only_for_block_scaled_gemm(L):
+def test_fp4_and_fp6_are_only_for_block_scaled_gemm(L):
     assert dense(L, a=mm.FP4_E2M1, b=mm.FP4_E2M1) == mm.ERR_UNSUPPORTED
     assert compress(L, a=mm.FP4_E2M1) == mm.ERR_UNSUPPORTED
+    for t in (mm.FP6_E2M3, mm.BF6_E3M2):
+        assert dense(L, a=t, b=t) == mm.ERR_UNSUPPORTED
+        assert compress(L, a=t) == mm.ERR_UNSUPPORTED
 
 
 def dense_layout(L, **kw):

@@ -186,3 +186,79 @@ def test_mx_fp4_8192_sampled():
     ref, S = oracle.gemm_mx_entries(FP4, FP4, A, SA, B, SB, ii, jj)
     got = D[torch.from_numpy(ii).to(dev()), torch.from_numpy(jj).to(dev())].cpu().numpy()
     assert_close(got, ref, S, E4M3, K, 1.0, 0.0, None, "mx fp4 8192^3")
+
+
+# ------------------------------------------------------------- FP6 E2M3 / BF6 E3M2 --
+FP6, BF6 = oracle.FP6, oracle.BF6
+FP6_PAIRS = [(FP6, FP6), (FP6, BF6), (BF6, FP6), (BF6, BF6)]
+
+
+def pack6(codes):
+    """rows x K six-bit codes -> rows x 3K/4 bytes, element n at bits 6n .. 6n+5 of the row."""
+    bits = ((codes[:, :, None] >> np.arange(6)) & 1).astype(np.uint8).reshape(codes.shape[0], -1)
+    return np.packbits(bits, axis=1, bitorder="little")
+
+
+def fp6_problem(M, N, K, seed, lo=107, hi=148, small=False):
+    g = np.random.default_rng(seed)
+    if small:      # magnitudes <= 2 in either format (codes 0 .. 16) and either sign
+        codes = g.integers(0, 17, size=(M + N, K)) | (g.integers(0, 2, size=(M + N, K)) << 5)
+    else:
+        codes = g.integers(0, 64, size=(M + N, K))
+    packed = pack6(codes)
+    SA = g.integers(lo, hi, size=(M, K // 32)).astype(np.uint8)
+    SB = g.integers(lo, hi, size=(N, K // 32)).astype(np.uint8)
+    return packed[:M], packed[M:], SA, SB
+
+
+def run_fp6(ta, tb, A, SA, B, SB, alpha=1.0, beta=0.0, C=None, pad=0):
+    M, N = A.shape[0], B.shape[0]
+
+    def dev_packed(X):
+        buf = torch.zeros((X.shape[0], X.shape[1] + pad), dtype=torch.uint8, device=dev())
+        buf[:, :X.shape[1]] = torch.from_numpy(X).to(dev())
+        return buf[:, :X.shape[1]]
+    D = out_tensor(M, N, False)
+    Cd = torch.from_numpy(np.ascontiguousarray(C)).to(dev()) if beta != 0 else None
+    mm.gemm_mx(dev_packed(A), pack_mx_scales(SA, seed=5), dev_packed(B), pack_mx_scales(SB, seed=6), D, alpha, beta,
+               Cd, a_type=ta, b_type=tb)
+    torch.cuda.synchronize()
+    return D
+
+
+@pytest.mark.parametrize("ta,tb", FP6_PAIRS)
+@pytest.mark.parametrize("tile", [2561, 1282, 128, 64])
+@pytest.mark.parametrize("M,N,K", [(64, 64, 128), (300, 260, 32 * 37), (33, 300, 1024), (257, 130, 96), (5, 7, 32)])
+def test_mx_fp6_matches_oracle(ta, tb, tile, M, N, K):
+    """Rows of 3K/4 bytes padded to a 48-byte multiple of the pitch (lda a multiple of 64 elements)."""
+    A, B, SA, SB = fp6_problem(M, N, K, M + N + K + 3 * ta + tb)
+    pad = (-(K * 3 // 4)) % 48 + 48
+    C = np.random.default_rng(K + 1).standard_normal((M, N)).astype(np.float32)
+    with env(MMAC_TILE=tile):
+        D = run_fp6(ta, tb, A, SA, B, SB, 0.75, 1.5, C, pad=pad).cpu().numpy()
+    Dref, S = oracle.gemm_mx(ta, tb, A, SA, B, SB, 0.75, 1.5, C)
+    assert_close(D, Dref, S, E4M3, K, 0.75, 1.5, C, f"mx fp6 {ta},{tb} {M}x{N}x{K} tile {tile}")
+
+
+@pytest.mark.parametrize("ta,tb", FP6_PAIRS)
+def test_mx_fp6_exact(ta, tb):
+    """|a|, |b| <= 2 with block exponents 2^0 .. 2^1: multiples of 2^-8 below 2^14, exact in fp32 --
+    the oracle's bits."""
+    M, N, K = 130, 70, 32 * 21
+    A, B, SA, SB = fp6_problem(M, N, K, 7 + ta + tb, lo=127, hi=129, small=True)
+    pad = (-(K * 3 // 4)) % 48
+    for tile in (1282, 64):
+        with env(MMAC_TILE=tile):
+            D = run_fp6(ta, tb, A, SA, B, SB, pad=pad).cpu().numpy()
+        Dref, _ = oracle.gemm_mx(ta, tb, A, SA, B, SB)
+        assert np.array_equal(D.astype(np.float64), Dref), f"tile {tile}"
+
+
+def test_mx_fp6_8192_sampled():
+    M = N = K = 8192
+    A, B, SA, SB = fp6_problem(M, N, K, 78, lo=117, hi=138)
+    D = run_fp6(FP6, BF6, A, SA, B, SB)
+    ii, jj = sample_entries(M, N, 20000, 16, tiles=((0, 0), ((M - 1) // 256, (N - 1) // 256)))
+    ref, S = oracle.gemm_mx_entries(FP6, BF6, A, SA, B, SB, ii, jj)
+    got = D[torch.from_numpy(ii).to(dev()), torch.from_numpy(jj).to(dev())].cpu().numpy()
+    assert_close(got, ref, S, E4M3, K, 1.0, 0.0, None, "mx fp6 8192^3")
