@@ -172,17 +172,16 @@ __device__ __forceinline__ uint32_t finish(float v, float bias, bool has_bias, b
 // 256-byte bank row keep distinct positions, and successive bank rows are
 // XOR-rotated, so those 16 reads hit 16 different 16-byte bank groups.  The
 // map keeps the row and is its own inverse.
-// Rows of 7 units hold the 96 bytes of 128 packed FP6 elements and one unused
-// unit; they need no swizzle: 112-byte rows sit 28 banks apart, so 16
-// consecutive rows start on 16 distinct multiples of 4 banks.
+// Rows of 6 units (96 bytes: 128 packed FP6 elements) sit 24 banks apart, so
+// 8 consecutive rows start on 8 distinct multiples of 8 banks; the units of
+// rows 8 .. 15 of every 16 swap in pairs (c ^ 1), which moves them to the 8
+// starts in between.
 template <int W>
 __device__ __forceinline__ constexpr uint32_t swz(uint32_t L) {
-    static_assert(W == 2 || W == 4 || W == 7 || W == 8, "rows of 2, 4, 7 or 8 units");
-    if constexpr (W == 7) return L;
-    else {
-        const uint32_t r = L / W;
-        return r * W + ((L % W) ^ ((r / (16 / W)) % W));
-    }
+    static_assert(W == 2 || W == 4 || W == 6 || W == 8, "rows of 2, 4, 6 or 8 units");
+    const uint32_t r = L / W;
+    if constexpr (W == 6) return r * W + ((L % W) ^ ((r >> 3) & 1));
+    else return r * W + ((L % W) ^ ((r / (16 / W)) % W));
 }
 
 // ---- matrix-instruction wrappers -----------------------------------------
@@ -314,9 +313,8 @@ struct MmaMX4 {
 // packed elements (24 bytes, element e at bits 6e .. 6e+5) per lane, lane half
 // g holding block g of the instruction's 64 K (established on gfx950 with
 // one-hot operands: every element of lane half g took block g's scale, with
-// the value the packing gives).  K-tiles of 128 elements: 96 bytes per row
-// (kept in 112-byte LDS rows), blocks 2s and 2s+1 in step s; one scale word
-// per row per k-tile.
+// the value the packing gives).  K-tiles of 128 elements: 96-byte LDS rows,
+// blocks 2s and 2s+1 in step s; one scale word per row per k-tile.
 template <int FA, int FB>
 struct MmaMX6 {
     static constexpr bool kSparse = false, kScaled = true;

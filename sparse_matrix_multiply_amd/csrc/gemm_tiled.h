@@ -143,17 +143,10 @@ struct TiledGemm {
     static constexpr int STEPS = Op::kBK / Op::kKStep;
     static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 tiles");
-    // 16-byte units per LDS row: the row's bytes of one k-tile, except that the
-    // 96 bytes of packed FP6 go in 7-unit rows (the last unit unused)
-    static constexpr int lds_units(int bytes) { return bytes == 96 ? 7 : bytes / 16; }
-    static constexpr int AW = lds_units(Op::kARowBytes), BW = lds_units(Op::kBRowBytes);
-    static_assert(AW == 2 || AW == 4 || AW == 7 || AW == 8, "A LDS rows of 32, 64, 112 or 128 bytes");
-    static_assert(BW == 4 || BW == 7 || BW == 8, "B LDS rows of 64, 112 or 128 bytes");
-    static_assert((AW != 7 && BW != 7) || Op::kAFrag == 24, "112-byte rows hold packed FP6 only");
-    // bytes of a row that one k-tile covers, and whether LDS slot P of a tile with
-    // W units per row holds data
-    static constexpr int row_bytes(int W) { return W == 7 ? 96 : W * 16; }
-    static constexpr bool data_slot(int W, uint32_t P) { return W != 7 || P % 7 != 6; }
+    static constexpr int AW = Op::kARowBytes / 16, BW = Op::kBRowBytes / 16;  // 16-byte units per LDS row
+    static_assert(AW == 2 || AW == 4 || AW == 6 || AW == 8, "A LDS rows of 32, 64, 96 or 128 bytes");
+    static_assert(BW == 4 || BW == 6 || BW == 8, "B LDS rows of 64, 96 or 128 bytes");
+    static_assert((AW != 6 && BW != 6) || Op::kAFrag == 24, "96-byte rows hold packed FP6 only");
     static constexpr int IW = Op::kSparse ? Op::kBK / 32 : 0;                  // index words per row
     static_assert(!Op::kSparse || STEPS == 2, "index words of a k-tile read once, for two steps");
     // copy units per wave: 16-byte units of A and B, 4-byte words of the index
@@ -162,6 +155,11 @@ struct TiledGemm {
     static_assert(AUPW * NW == BM * AW && BUPW * NW == BN * BW && IUPW * NW * IES == BM * IW * 4,
                   "uneven copy split");
     static constexpr int AP = (AUPW + 63) / 64, BP = (BUPW + 63) / 64, IP = (IUPW + 63) / 64;  // passes
+    // A partly filled copy pass of 96-byte rows (64 x 64 tiles) sits in a lane-divergent branch
+    // next to whole passes; the compiler then merges such copies into one whose LDS base (M0)
+    // it takes from the first active lane, which is wrong for the other lanes.  Those rows
+    // use whole passes only.
+    static_assert((AW != 6 || AUPW % 64 == 0) && (BW != 6 || BUPW % 64 == 0), "whole copy passes for 96-byte rows");
     // Block-scaled operands: SW scale words per row of A and per column of B
     // per k-tile, copied as 16-byte units (four rows' words), one pass for A's
     // and one for B's in every wave.
@@ -227,7 +225,7 @@ struct TiledGemm {
     template <int W>
     __device__ __forceinline__ uint32_t src_off(uint32_t P, int64_t pitch, int kt) const {
         const uint32_t L = swz<W>(P);
-        return (L / W) * (uint32_t)pitch + (uint32_t)((kt + kt0) * row_bytes(W)) + (L % W) * 16;
+        return (L / W) * (uint32_t)pitch + (uint32_t)((kt + kt0) * W * 16) + (L % W) * 16;
     }
 
     // Byte offset of the source of index copy lane d (LDS bytes [d*IES,
@@ -273,13 +271,13 @@ struct TiledGemm {
     __device__ __forceinline__ void dma_pass(uint8_t *st, int kt, int j) const {
         if (j < AP) {
             const int u = j * 64 + lane;
-            if ((AUPW % 64 == 0 || u < AUPW) && data_slot(AW, wave * AUPW + u))
+            if (AUPW % 64 == 0 || u < AUPW)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(st + (wave * AUPW + j * 64) * 16), 16,
                                                          op_off<TRANS_A, BM, AW>(wave * AUPW + u, p.a_pitch, kt), 0,
                                                          0, 0);
         } else if (j < AP + BP) {
             const int q = j - AP, u = q * 64 + lane;
-            if ((BUPW % 64 == 0 || u < BUPW) && data_slot(BW, wave * BUPW + u))
+            if (BUPW % 64 == 0 || u < BUPW)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(st + A_BYTES + (wave * BUPW + q * 64) * 16),
                                                          16, op_off<TRANS_B, BN, BW>(wave * BUPW + u, p.b_pitch, kt),
                                                          0, 0, 0);
@@ -321,14 +319,14 @@ struct TiledGemm {
         for (int q = 0; q < AP; ++q) {
             const int u = q * 64 + lane;
             const uint32_t P = wave * AUPW + u;
-            if ((AUPW % 64 == 0 || u < AUPW) && data_slot(AW, P)) {
+            if (AUPW % 64 == 0 || u < AUPW) {
                 if constexpr (TRANS_A) {   // whole rows of K
                     const bool in = (kt + kt0) * Op::kBK + (int)(P / (BM / 8)) < p.K;
                     *reinterpret_cast<i32x4 *>(st + P * 16) =
                         in ? __builtin_amdgcn_raw_buffer_load_b128(ra, tsrc_off<BM>(P, p.a_pitch, kt), 0, 0)
                            : i32x4{0, 0, 0, 0};
                 } else {
-                    const int e0 = ((kt + kt0) * row_bytes(AW) + (int)(swz<AW>(P) % AW) * 16) / Op::kEsize;
+                    const int e0 = ((kt + kt0) * AW * 16 + (int)(swz<AW>(P) % AW) * 16) / Op::kEsize;
                     *reinterpret_cast<i32x4 *>(st + P * 16) =
                         masked_unit<Op::kEsize>(ra, src_off<AW>(P, p.a_pitch, kt), e0, climit);
                 }
@@ -338,14 +336,14 @@ struct TiledGemm {
         for (int q = 0; q < BP; ++q) {
             const int u = q * 64 + lane;
             const uint32_t P = wave * BUPW + u;
-            if ((BUPW % 64 == 0 || u < BUPW) && data_slot(BW, P)) {
+            if (BUPW % 64 == 0 || u < BUPW) {
                 if constexpr (TRANS_B) {
                     const bool in = (kt + kt0) * Op::kBK + (int)(P / (BN / 8)) < p.K;
                     *reinterpret_cast<i32x4 *>(st + A_BYTES + P * 16) =
                         in ? __builtin_amdgcn_raw_buffer_load_b128(rb, tsrc_off<BN>(P, p.b_pitch, kt), 0, 0)
                            : i32x4{0, 0, 0, 0};
                 } else {
-                    const int e0 = ((kt + kt0) * row_bytes(BW) + (int)(swz<BW>(P) % BW) * 16) / Op::kEsize;
+                    const int e0 = ((kt + kt0) * BW * 16 + (int)(swz<BW>(P) % BW) * 16) / Op::kEsize;
                     *reinterpret_cast<i32x4 *>(st + A_BYTES + P * 16) =
                         masked_unit<Op::kEsize>(rb, src_off<BW>(P, p.b_pitch, kt), e0, blimit);
                 }
@@ -402,18 +400,20 @@ struct TiledGemm {
     }
 
     // Packed FP6 fragment: the 24 bytes of block 2s + g of row r of a tile of
-    // 112-byte rows (bytes 48s + 24g .. + 23 of the row), read as three 8-byte
-    // pieces straight into operand order; only the row base is per lane, the
-    // rest are instruction offsets.
+    // 96-byte rows, bytes 48s + 24g .. + 23 of the row.  Two whole-unit reads:
+    // unit 3s + 2g (lane half 0: operand bytes 0-15; half 1: bytes 8-23) and
+    // unit 3s + 1, whose low half ends block 2s and whose high half starts
+    // block 2s + 1; each half then puts the pieces in operand order.  (8-byte
+    // reads at the blocks' own offsets would need no reordering, but every 32
+    // lanes of such a read meet the same banks at least twice.)
     template <int W>
     __device__ __forceinline__ void lds_frag6(Frag<24> &f, const uint8_t *base, uint32_t r, int s) const {
-        static_assert(W == 7, "112-byte rows");
-        const uint8_t *row = base + r * (W * 16) + 24 * g;
-        const i32x2 p0 = *reinterpret_cast<const i32x2 *>(row + 48 * s);
-        const i32x2 p1 = *reinterpret_cast<const i32x2 *>(row + 48 * s + 8);
-        const i32x2 p2 = *reinterpret_cast<const i32x2 *>(row + 48 * s + 16);
-        const i32x4 p01 = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
-        f.v = __builtin_shufflevector(p01, __builtin_shufflevector(p2, p2, 0, 1, -1, -1), 0, 1, 2, 3, 4, 5);
+        static_assert(W == 6, "96-byte rows");
+        const i32x4 x = *reinterpret_cast<const i32x4 *>(base + swz<W>(r * W + 3 * s + 2 * g) * 16);
+        const i32x4 z = *reinterpret_cast<const i32x4 *>(base + swz<W>(r * W + 3 * s + 1) * 16);
+        const bool h = g != 0;
+        f.v = i32x6{h ? z[2] : x[0], h ? z[3] : x[1], h ? x[0] : x[2], h ? x[1] : x[3], h ? x[2] : z[0],
+                    h ? x[3] : z[1]};
     }
 
     // Fragment of the 32 rows (A) or columns (B) mn0 .. mn0 + 31 of a
@@ -457,8 +457,8 @@ struct TiledGemm {
         }
     }
 
-    // LDS read instructions per fragment (packed FP6: three 8-byte reads).
-    static constexpr int frag_reads(int bytes) { return bytes == 24 ? 3 : bytes / 16; }
+    // LDS read instructions per fragment (packed FP6: two 16-byte reads).
+    static constexpr int frag_reads(int bytes) { return bytes == 24 ? 2 : bytes / 16; }
     // Instruction counts of one step, for the interleaving below.
     static constexpr int NMMA = TM * TN;
     static constexpr int NREAD = TM * frag_reads(Op::kAFrag) + TN * frag_reads(Op::kBFrag) + (Op::kSparse ? TM : 0) +

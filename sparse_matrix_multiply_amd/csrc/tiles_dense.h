@@ -12,8 +12,16 @@ namespace mmac {
 // Kernels of one instruction class Op for every tile shape; each element-type
 // pair is instantiated in a source file of its own under inst/, so that the
 // build compiles them in parallel.
+// LDS stages of the 128 x 256 and 256 x 128 tiles: three, or four for the
+// 96-byte rows of packed FP6 (38 KiB a stage).
+template <class Op>
+constexpr int half_tile_stages() {
+    return Op::kARowBytes == 96 ? 4 : 3;
+}
+
 template <class Op>
 hipError_t launch_dense_op(TileShape shape, const GemmParams &p, hipStream_t s) {
+    constexpr int S2 = half_tile_stages<Op>();
     const dim3 grid(p.tiles_m * p.tiles_n * p.splits), block(256);   // one workgroup per tile and K range
     switch (shape) {
     case TILE_256:
@@ -21,10 +29,14 @@ hipError_t launch_dense_op(TileShape shape, const GemmParams &p, hipStream_t s) 
         if constexpr (Op::kScaled) return hipErrorInvalidValue;
         else hipLaunchKernelGGL((gemm_tiled_kernel<Op, 256, 256, 2, 4, 2>), grid, dim3(512), 0, s, p);
         break;
-    case TILE_256x128: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 256, 128, 2, 2, 3>), grid, block, 0, s, p); break;
-    case TILE_128x256: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 128, 256, 2, 2, 3>), grid, block, 0, s, p); break;
+    case TILE_256x128: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 256, 128, 2, 2, S2>), grid, block, 0, s, p); break;
+    case TILE_128x256: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 128, 256, 2, 2, S2>), grid, block, 0, s, p); break;
     case TILE_128: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 128, 128, 2, 2, 4>), grid, block, 0, s, p); break;
-    case TILE_64: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 64, 64, 2, 2, 4>), grid, block, 0, s, p); break;
+    case TILE_64:
+        // 96-byte rows of packed FP6 fill whole copy passes only from 128 rows on
+        if constexpr (Op::kARowBytes == 96) return hipErrorInvalidValue;
+        else hipLaunchKernelGGL((gemm_tiled_kernel<Op, 64, 64, 2, 2, 4>), grid, block, 0, s, p);
+        break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
