@@ -410,6 +410,17 @@ def suite():
         out["layout_bf16_8192^3_beta1_" + key] = {"us": round(ms * 1e3, 1),
                                                   "TFLOP/s": round(gemm_flops(M, N, K) / ms / 1e9, 1)}
     del A, B, At, Bt, C, D
+    # the same for the 8192^3 fp8 x bf8 workload (transposed 8-bit reads)
+    w = W.workload("fp8_8192")
+    A, B = to_dev(w["A"], w["ta"]), to_dev(w["B"], w["tb"])
+    At, Bt = A.t().contiguous(), B.t().contiguous()
+    D = torch.empty((M, N), dtype=torch.float32, device=dev)
+    for ta, tb, key in ((True, False, "A_Mcontig"), (False, True, "B_Ncontig"), (True, True, "A_Mcontig_B_Ncontig")):
+        ms = median_ms([lambda: mm.gemm_layout(At if ta else A, Bt if tb else B, D, ta, tb, a_type=w["ta"],
+                                               b_type=w["tb"], stream=stream)], 20)
+        out["layout_fp8e4m3xbf8e5m2_8192^3_" + key] = {"us": round(ms * 1e3, 1),
+                                                       "TFLOP/s": round(gemm_flops(M, N, K) / ms / 1e9, 1)}
+    del A, B, At, Bt, D
     torch.cuda.empty_cache()
 
     split_case(512, 512, 32768, W.BF16, "splitk_bf16_512x512x32768")

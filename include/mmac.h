@@ -306,17 +306,19 @@ mmac_status_t mmac_gemm_dense_mx(mmac_dtype_t a_type, mmac_dtype_t b_type,
                                  void *D, int64_t ldd, const mmac_epilogue_t *ep, void *stream);
 
 /*
- * Dense GEMM with other operand layouts (16-bit types).  trans_a = 1: A is
- * stored M-contiguous (column-major M x K: A[i + k*lda], lda >= M);
- * trans_b = 1: B is stored N-contiguous (row-major K x N: B[k*ldb + j],
- * ldb >= N).  trans_a = trans_b = 0 is mmac_gemm_dense_ep.  The kernels copy
- * such an operand into LDS as K rows and read its fragments with the gfx950
- * transposing LDS read (ds_read_b64_tr_b16).
- *   a_type = b_type = F16 or BF16 when a flag is set (MMAC_ERR_UNSUPPORTED
+ * Dense GEMM with other operand layouts.  trans_a = 1: A is stored
+ * M-contiguous (column-major M x K: A[i + k*lda], lda >= M); trans_b = 1: B
+ * is stored N-contiguous (row-major K x N: B[k*ldb + j], ldb >= N).
+ * trans_a = trans_b = 0 is mmac_gemm_dense_ep.  The kernels copy such an
+ * operand into LDS as K rows and read its fragments with the gfx950
+ * transposing LDS reads (ds_read_b64_tr_b16 for 16-bit elements,
+ * ds_read_b64_tr_b8 for 8-bit ones).
+ *   (a_type, b_type) as in mmac_gemm_dense (MMAC_ERR_UNSUPPORTED
  *   otherwise); a transposed operand's K rows must span less than 2 GiB
- *   (K * ld * 2 bytes; MMAC_ERR_UNSUPPORTED).  The 16-byte alignment and
- *   pitch rules, C, D, ep, stream and errors as in mmac_gemm_dense_ep.  Flags
- *   other than 0 / 1: MMAC_ERR_INVALID_ARG.
+ *   (K * ld * element size bytes; MMAC_ERR_UNSUPPORTED).  The 16-byte
+ *   alignment and pitch rules, C, D, ep, stream and errors as in
+ *   mmac_gemm_dense_ep.  Outputs with M <= 32 rows use the tiled kernel.
+ *   Flags other than 0 / 1: MMAC_ERR_INVALID_ARG.
  */
 mmac_status_t mmac_gemm_dense_layout(mmac_dtype_t a_type, mmac_dtype_t b_type, int trans_a, int trans_b,
                                      int64_t M, int64_t N, int64_t K, double alpha,

@@ -363,17 +363,18 @@ mmac_status_t mmac_gemm_dense_layout(mmac_dtype_t a_type, mmac_dtype_t b_type, i
     if (!trans_a && !trans_b)
         return mmac_gemm_dense_ep(a_type, b_type, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd, ep_in, stream);
     const mmac_epilogue_t ep = epilogue_of(ep_in);
-    if (!((a_type == MMAC_BF16 || a_type == MMAC_F16) && b_type == a_type)) return MMAC_ERR_UNSUPPORTED;
     const mmac_status_t st = check_gemm(a_type, b_type, M, N, K, alpha, A, lda, trans_a ? M : K, B, ldb, beta, C, ldc,
                                         D, ldd, ep, trans_b ? N : K);
     if (st != MMAC_OK) return st;
     // a transposed operand is addressed with one buffer over all its K rows
-    if ((trans_a && K * lda * 2 >= ((int64_t)1 << 31)) || (trans_b && K * ldb * 2 >= ((int64_t)1 << 31)))
+    const int64_t es = elem_size(a_type);
+    if ((trans_a && K * lda * es >= ((int64_t)1 << 31)) || (trans_b && K * ldb * es >= ((int64_t)1 << 31)))
         return MMAC_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return MMAC_OK;
     const TileShape shape = pick_shape(M, N, true);
     const GemmParams p = make_params(a_type, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd, ep, shape);
-    return launched(launch_gemm_layout(a_type, trans_a != 0, trans_b != 0, shape, p, static_cast<hipStream_t>(stream)));
+    return launched(
+        launch_gemm_layout(a_type, b_type, trans_a != 0, trans_b != 0, shape, p, static_cast<hipStream_t>(stream)));
 }
 
 int64_t mmac_gemm_workspace_bytes(mmac_dtype_t a_type, int64_t M, int64_t N, int64_t K, int sparse) {

@@ -20,17 +20,22 @@ hipError_t launch_gemm_dense(int a, int b, TileShape shape, GemmParams p, hipStr
     return hipErrorInvalidValue;
 }
 
-template <int DT>
+template <class Op>
 static hipError_t launch_trans(bool ta, bool tb, TileShape shape, const GemmParams &p, hipStream_t s) {
-    if (ta && tb) return launch_dense_op<Trans<MmaDense16<DT>, true, true>>(shape, p, s);
-    if (ta) return launch_dense_op<Trans<MmaDense16<DT>, true, false>>(shape, p, s);
-    if (tb) return launch_dense_op<Trans<MmaDense16<DT>, false, true>>(shape, p, s);
-    return launch_dense_op<MmaDense16<DT>>(shape, p, s);
+    if (ta && tb) return launch_dense_op<Trans<Op, true, true>>(shape, p, s);
+    if (ta) return launch_dense_op<Trans<Op, true, false>>(shape, p, s);
+    if (tb) return launch_dense_op<Trans<Op, false, true>>(shape, p, s);
+    return launch_dense_op<Op>(shape, p, s);
 }
 
-hipError_t launch_gemm_layout(int a, bool trans_a, bool trans_b, TileShape shape, GemmParams p, hipStream_t s) {
-    if (a == DT_BF16) return launch_trans<DT_BF16>(trans_a, trans_b, shape, p, s);
-    if (a == DT_F16) return launch_trans<DT_F16>(trans_a, trans_b, shape, p, s);
+hipError_t launch_gemm_layout(int a, int b, bool trans_a, bool trans_b, TileShape shape, GemmParams p, hipStream_t s) {
+    if (a == DT_BF16 && b == DT_BF16) return launch_trans<MmaDense16<DT_BF16>>(trans_a, trans_b, shape, p, s);
+    if (a == DT_F16 && b == DT_F16) return launch_trans<MmaDense16<DT_F16>>(trans_a, trans_b, shape, p, s);
+    if (a == DT_I8 && b == DT_I8) return launch_trans<MmaDenseI8>(trans_a, trans_b, shape, p, s);
+    if (a == DT_E4M3 && b == DT_E4M3) return launch_trans<MmaDenseF8<0, 0>>(trans_a, trans_b, shape, p, s);
+    if (a == DT_E4M3 && b == DT_E5M2) return launch_trans<MmaDenseF8<0, 1>>(trans_a, trans_b, shape, p, s);
+    if (a == DT_E5M2 && b == DT_E4M3) return launch_trans<MmaDenseF8<1, 0>>(trans_a, trans_b, shape, p, s);
+    if (a == DT_E5M2 && b == DT_E5M2) return launch_trans<MmaDenseF8<1, 1>>(trans_a, trans_b, shape, p, s);
     return hipErrorInvalidValue;
 }
 

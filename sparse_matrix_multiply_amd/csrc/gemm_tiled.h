@@ -122,7 +122,7 @@ __device__ __forceinline__ void wait_copies(int n) {
 template <class O, class = void> struct ElemBits { static constexpr int value = 8 * O::kEsize; };
 template <class O> struct ElemBits<O, std::void_t<decltype(O::kElemBits)>> { static constexpr int value = O::kElemBits; };
 
-// Operands stored with M (A) or N (B) contiguous instead of K (16-bit types).
+// Operands stored with M (A) or N (B) contiguous instead of K (16- and 8-bit types).
 template <class O, class = void> struct TransOf { static constexpr bool a = false, b = false; };
 template <class O> struct TransOf<O, std::void_t<decltype(O::kTransA)>> {
     static constexpr bool a = O::kTransA, b = O::kTransB;
@@ -179,7 +179,7 @@ struct TiledGemm {
     // 16-byte unit u of row r stored at u ^ tswz(r); fragments come out of it
     // with ds_read_b64_tr_b16 (load_tr).
     static constexpr bool TRANS_A = TransOf<Op>::a, TRANS_B = TransOf<Op>::b;
-    static_assert(!(TRANS_A || TRANS_B) || (Op::kEsize == 2 && !Op::kSparse && !SCALED), "16-bit dense only");
+    static_assert(!(TRANS_A || TRANS_B) || (!Op::kSparse && !SCALED), "plain dense products only");
     static constexpr int LDS_BYTES = STAGES * STAGE;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 workgroup");
 
@@ -204,9 +204,9 @@ struct TiledGemm {
         row0 = tm * BM;
         col0 = tn * BN;
         const int arows = min(BM, p.M - row0), bcols = min(BN, p.N - col0);
-        if constexpr (TRANS_A) ra = make_rsrc(p.A + row0 * 2, (uint32_t)(p.K * p.a_pitch - row0 * 2));
+        if constexpr (TRANS_A) ra = make_rsrc(p.A + row0 * Op::kEsize, (uint32_t)(p.K * p.a_pitch - row0 * Op::kEsize));
         else ra = make_rsrc(p.A + (int64_t)row0 * p.a_pitch, (uint32_t)(arows * p.a_pitch));
-        if constexpr (TRANS_B) rb = make_rsrc(p.B + col0 * 2, (uint32_t)(p.K * p.b_pitch - col0 * 2));
+        if constexpr (TRANS_B) rb = make_rsrc(p.B + col0 * Op::kEsize, (uint32_t)(p.K * p.b_pitch - col0 * Op::kEsize));
         else rb = make_rsrc(p.B + (int64_t)col0 * p.b_pitch, (uint32_t)(bcols * p.b_pitch));
         if constexpr (Op::kSparse)
             rx = make_rsrc(p.idx + (int64_t)row0 * p.idx_pitch, (uint32_t)(arows * p.idx_pitch * 4));
@@ -236,17 +236,25 @@ struct TiledGemm {
     }
 
     // Transposed tiles: XOR of the 16-byte unit index of row r (U units per
-    // row).  Each ds_read_b64_tr_b16 of load_tr reads, per 32 lanes, 4 rows x
-    // 64 bytes; rows r .. r+3 then land in distinct quarters of the 64 banks.
+    // row).  16-bit elements: each ds_read_b64_tr_b16 of load_tr reads, per 32
+    // lanes, 4 rows x 64 bytes; rows r .. r+3 then land in distinct quarters
+    // of the 64 banks.  8-bit elements: each ds_read_b64_tr_b8 of load_tr8
+    // reads, per 32 lanes, 8 rows x two adjacent units; the even XOR
+    // 2 * (row number within the rows that share a 256-byte bank row) gives
+    // those 16 units distinct bank groups.
     template <int U>
     __device__ __forceinline__ static constexpr uint32_t tswz(uint32_t r) {
-        return (r % 4) * (U >= 16 ? 4 : U / 4);
+        if constexpr (Op::kEsize == 2) return (r % 4) * (U >= 16 ? 4 : U / 4);
+        else {
+            static_assert(U >= 4 && U <= 16, "rows of 64 to 256 bytes");
+            return 2 * ((r / (16 / U)) % (U / 2));
+        }
     }
     // Source byte offset of physical unit P of a transposed tile of MN
     // elements per row at k-tile kt (memory rows are K rows of pitch bytes).
     template <int MN>
     __device__ __forceinline__ uint32_t tsrc_off(uint32_t P, int64_t pitch, int kt) const {
-        constexpr int U = MN / 8;
+        constexpr int U = MN * Op::kEsize / 16;
         const uint32_t r = P / U, u = (P % U) ^ tswz<U>(r);
         return (uint32_t)(((int64_t)(kt + kt0) * Op::kBK + r) * pitch) + u * 16;
     }
@@ -321,7 +329,7 @@ struct TiledGemm {
             const uint32_t P = wave * AUPW + u;
             if (AUPW % 64 == 0 || u < AUPW) {
                 if constexpr (TRANS_A) {   // whole rows of K
-                    const bool in = (kt + kt0) * Op::kBK + (int)(P / (BM / 8)) < p.K;
+                    const bool in = (kt + kt0) * Op::kBK + (int)(P / (BM * Op::kEsize / 16)) < p.K;
                     *reinterpret_cast<i32x4 *>(st + P * 16) =
                         in ? __builtin_amdgcn_raw_buffer_load_b128(ra, tsrc_off<BM>(P, p.a_pitch, kt), 0, 0)
                            : i32x4{0, 0, 0, 0};
@@ -338,7 +346,7 @@ struct TiledGemm {
             const uint32_t P = wave * BUPW + u;
             if (BUPW % 64 == 0 || u < BUPW) {
                 if constexpr (TRANS_B) {
-                    const bool in = (kt + kt0) * Op::kBK + (int)(P / (BN / 8)) < p.K;
+                    const bool in = (kt + kt0) * Op::kBK + (int)(P / (BN * Op::kEsize / 16)) < p.K;
                     *reinterpret_cast<i32x4 *>(st + A_BYTES + P * 16) =
                         in ? __builtin_amdgcn_raw_buffer_load_b128(rb, tsrc_off<BN>(P, p.b_pitch, kt), 0, 0)
                            : i32x4{0, 0, 0, 0};
@@ -368,7 +376,7 @@ struct TiledGemm {
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const uint32_t r = wm * WTM + i * 32 + l32;
-            if constexpr (TRANS_A) load_tr<BM>(a[i], sa, wm * WTM + i * 32, s);
+            if constexpr (TRANS_A) load_tr_any<BM>(a[i], sa, wm * WTM + i * 32, s);
             else if constexpr (Op::kAFrag == 24) lds_frag6<AW>(a[i], sa, r, s);
             else lds_frag<AW>(a[i], sa, r * AW + Op::a_unit(s, g, 0), r * AW + Op::a_unit(s, g, 1));
             if constexpr (Op::kSparse) {
@@ -380,7 +388,7 @@ struct TiledGemm {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const uint32_t r = (wn * WTN + j * 32 + l32) * BW;
-            if constexpr (TRANS_B) load_tr<BN>(b[j], sb, wn * WTN + j * 32, s);
+            if constexpr (TRANS_B) load_tr_any<BN>(b[j], sb, wn * WTN + j * 32, s);
             else if constexpr (Op::kBFrag == 24) lds_frag6<BW>(b[j], sb, wn * WTN + j * 32 + l32, s);
             else lds_frag<BW>(b[j], sb, r + Op::b_unit(s, g, 0), r + Op::b_unit(s, g, 1));
         }
@@ -441,6 +449,43 @@ struct TiledGemm {
             f.v[2 * c] = w[0];
             f.v[2 * c + 1] = w[1];
         }
+    }
+
+    // The same for 8-bit elements: lane half g holds the instruction's
+    // Op::kAFrag consecutive K of its row (column) in operand order, K
+    // s * kKStep + g * kAFrag + 0 .. kAFrag - 1, as lds_frag gives them.
+    // ds_read_b64_tr_b8 works on groups of 16 lanes: if lane l of a group
+    // addresses 8 consecutive elements S[l][0..7], lane i receives
+    // S[2e + i/8][i mod 8] for e = 0..7 (measured on gfx950).  So lane l
+    // addresses row k0 + l/2, elements n0 + 8(l mod 2) .. + 7, and lane i then
+    // holds rows k0 .. k0 + 7 of element n0 + i.  Group h of the wave takes
+    // elements n0 = mn0 + 16(h mod 2) and lane half h / 2; each read gives 8 K.
+    template <int MN, int BYTES>
+    __device__ __forceinline__ void load_tr8(Frag<BYTES> &f, const uint8_t *tile, int mn0, int s) const {
+        constexpr int U = MN / 16;
+        typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+        const int h = lane >> 4, l = lane & 15;
+        const int n = mn0 + 16 * (h & 1) + 8 * (l & 1);
+        int w[BYTES / 4];
+#pragma unroll
+        for (int c = 0; c < BYTES / 8; ++c) {
+            const int k = s * Op::kKStep + (h >> 1) * BYTES + 8 * c + (l >> 1);
+            const uint8_t *addr = tile + k * MN + (((uint32_t)(n >> 4) ^ tswz<U>(k)) << 4) + (n & 15);
+            const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)addr);
+            w[2 * c] = v[0];
+            w[2 * c + 1] = v[1];
+        }
+        if constexpr (BYTES == 16) {
+            f.v = i32x4{w[0], w[1], w[2], w[3]};
+        } else {
+            f.lo = i32x4{w[0], w[1], w[2], w[3]};
+            f.hi = i32x4{w[4], w[5], w[6], w[7]};
+        }
+    }
+    template <int MN, int BYTES>
+    __device__ __forceinline__ void load_tr_any(Frag<BYTES> &f, const uint8_t *tile, int mn0, int s) const {
+        if constexpr (Op::kEsize == 2) load_tr<MN>(f, tile, mn0, s);
+        else load_tr8<MN>(f, tile, mn0, s);
     }
 
     // Scale bytes of blocks past K (in the ragged last k-tile) become 127

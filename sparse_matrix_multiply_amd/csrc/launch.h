@@ -82,7 +82,8 @@ hipError_t launch_gemm_dense(int dt_a, int dt_b, TileShape shape, GemmParams p, 
 hipError_t launch_gemm_sparse(int dt_a, int dt_b, TileShape shape, GemmParams p, hipStream_t s);
 hipError_t launch_gemm_skinny(int dt_a, int dt_b, GemmParams p, hipStream_t s);
 hipError_t launch_gemm_mx(int dt_a, int dt_b, TileShape shape, GemmParams p, hipStream_t s);
-hipError_t launch_gemm_layout(int dt_a, bool trans_a, bool trans_b, TileShape shape, GemmParams p, hipStream_t s);
+hipError_t launch_gemm_layout(int dt_a, int dt_b, bool trans_a, bool trans_b, TileShape shape, GemmParams p,
+                              hipStream_t s);
 hipError_t launch_compress(int dt, CompressParams p, bool prune, hipStream_t s);
 
 // Geometry of a tile shape.

@@ -314,8 +314,12 @@ def dense_layout(L, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(ta=2), mm.ERR_INVALID_ARG),
     (dict(tb=-1), mm.ERR_INVALID_ARG),
-    (dict(a=mm.FP8_E4M3, b=mm.FP8_E4M3), mm.ERR_UNSUPPORTED),
-    (dict(a=mm.I8, b=mm.I8, ta=0, tb=1), mm.ERR_UNSUPPORTED),
+    (dict(a=mm.FP8_E4M3, b=mm.BF16), mm.ERR_UNSUPPORTED),
+    (dict(a=mm.I8, b=mm.FP8_E4M3, ta=0, tb=1), mm.ERR_UNSUPPORTED),
+    (dict(a=mm.FP4_E2M1, b=mm.FP4_E2M1), mm.ERR_UNSUPPORTED),         # block-scaled formats: MX entry only
+    (dict(a=mm.I8, b=mm.I8, alpha=1.5), mm.ERR_INVALID_ARG),          # int8: integer alpha
+    (dict(a=mm.I8, b=mm.I8, M=48, lda=56, ldd=64), mm.ERR_MISALIGNED),   # 56-byte rows of int8
+    (dict(a=mm.FP8_E4M3, b=mm.BF8_E5M2, K=1 << 21, lda=1 << 10, ldb=1 << 21), mm.ERR_UNSUPPORTED),  # 2 GiB of A
     (dict(M=100, lda=96), mm.ERR_INVALID_ARG),                        # trans A: lda >= M
     (dict(ta=0, tb=1, N=100, ldb=96, ldd=100), mm.ERR_INVALID_ARG),     # trans B: ldb >= N
     (dict(M=60, lda=60, ldd=64), mm.ERR_MISALIGNED),                  # 120-byte rows

@@ -93,3 +93,86 @@ def test_layout_8192_sampled():
     ref, S = oracle.gemm_dense_entries(t, t, w["A"], w["B"], ii, jj, w["alpha"], w["beta"], w["C"])
     got = D[torch.from_numpy(ii).to(dev()), torch.from_numpy(jj).to(dev())].cpu().numpy()
     assert_close(got, ref, S, t, K, w["alpha"], w["beta"], w["C"][ii, jj], "layout 8192^3")
+
+
+# ---------------------------------------------------------------- 8-bit elements --
+# int8 and the four OCP fp8 / bf8 pairs; the transposed operand's fragments come through
+# ds_read_b64_tr_b8.  int8 bit for bit (int32 wrap-around), fp8 within the fp8 gate.
+from oracle import E4M3, E5M2, I8  # noqa: E402
+
+PAIRS8 = [(I8, I8), (E4M3, E4M3), (E4M3, E5M2), (E5M2, E4M3), (E5M2, E5M2)]
+
+
+def dev8(bits, pad=16):
+    """Host bytes (rows x cols) -> device uint8 view with the row pitch padded to a multiple of 16."""
+    rows, cols = bits.shape
+    ld = (cols + 15) // 16 * 16 + pad
+    buf = torch.zeros((rows, ld), dtype=torch.uint8, device=dev())
+    buf[:, :cols] = torch.from_numpy(np.ascontiguousarray(bits).view(np.uint8)).to(dev())
+    return buf[:, :cols]
+
+
+def problem8(ta, tb, M, N, K, seed, small=False):
+    g = np.random.default_rng(seed)
+    if ta == I8:
+        A = g.integers(-128, 128, size=(M, K)).astype(np.int8)
+        B = g.integers(-128, 128, size=(N, K)).astype(np.int8)
+        C = g.integers(-1000, 1001, size=(M, N)).astype(np.int32)
+        return A, B, C, 3, -2
+    draw = (lambda shape: g.integers(-4, 5, size=shape).astype(np.float64)) if small else g.standard_normal
+    A = W.to_bits(draw((M, K)), ta)
+    B = W.to_bits(draw((N, K)), tb)
+    C = (np.round(g.standard_normal((M, N)) * 8) / 8 if small else g.standard_normal((M, N))).astype(np.float32)
+    return A, B, C, (1.0 if small else 1.5), (1.0 if small else -0.5)
+
+
+def run_layout8(ta, tb, A, B, trans_a, trans_b, alpha, beta, C, D=None):
+    M, N = A.shape[0], B.shape[0]
+    Ad = dev8(np.ascontiguousarray(A.T) if trans_a else A)
+    Bd = dev8(np.ascontiguousarray(B.T) if trans_b else B)
+    D = out_tensor(M, N, ta == I8) if D is None else D
+    Cd = torch.from_numpy(np.ascontiguousarray(C)).to(dev()) if beta != 0 else None
+    mm.gemm_layout(Ad, Bd, D, trans_a, trans_b, alpha, beta, Cd, a_type=ta, b_type=tb)
+    torch.cuda.synchronize()
+    return D
+
+
+@pytest.mark.parametrize("ta,tb", PAIRS8)
+@pytest.mark.parametrize("trans_a,trans_b", LAYOUTS)
+@pytest.mark.parametrize("tile", [256, 2561, 1282, 128, 64])
+@pytest.mark.parametrize("M,N,K", [(64, 64, 128), (300, 260, 333), (33, 300, 1000), (257, 130, 72)])
+def test_layout8_matches_oracle(ta, tb, trans_a, trans_b, tile, M, N, K):
+    A, B, C, alpha, beta = problem8(ta, tb, M, N, K, M + N + K + 10 * trans_a + 20 * trans_b + 3 * ta + tb)
+    with env(MMAC_TILE=tile):
+        D = run_layout8(ta, tb, A, B, trans_a, trans_b, alpha, beta, C).cpu().numpy()
+    what = f"layout8 {ta},{tb} {trans_a},{trans_b} {M}x{N}x{K} tile {tile}"
+    if ta == I8:
+        Dref, _ = oracle.gemm_dense(ta, tb, A, B, alpha, beta, C)
+        assert np.array_equal(D, Dref), what
+    else:
+        Dref, S = oracle.gemm_dense(ta, tb, A, B, alpha, beta, C)
+        assert_close(D, Dref, S, ta, K, alpha, beta, C, what)
+
+
+@pytest.mark.parametrize("ta,tb", PAIRS8[1:])
+@pytest.mark.parametrize("trans_a,trans_b", LAYOUTS)
+def test_layout8_small_integers_exact(ta, tb, trans_a, trans_b):
+    """|a|, |b| <= 4: every partial sum is exact in fp32 -- the oracle's bits."""
+    M, N, K = 130, 200, 520
+    A, B, C, alpha, beta = problem8(ta, tb, M, N, K, 7 + ta + tb, small=True)
+    Dref, _ = oracle.gemm_dense(ta, tb, A, B, alpha, beta, C)
+    for tile in (256, 64):
+        with env(MMAC_TILE=tile):
+            D = run_layout8(ta, tb, A, B, trans_a, trans_b, alpha, beta, C).cpu().numpy()
+        assert np.array_equal(D.astype(np.float64), Dref), f"tile {tile}"
+
+
+def test_layout8_8192_sampled():
+    """The 8192^3 fp8 x bf8 workload with A stored M-contiguous and B N-contiguous."""
+    w = W.workload("fp8_8192")
+    ta, tb, M, N, K = w["ta"], w["tb"], w["M"], w["N"], w["K"]
+    D = run_layout8(ta, tb, w["A"], w["B"], True, True, 1.0, 0.0, None)
+    ii, jj = sample_entries(M, N, 20000, 17, tiles=((0, 0), ((M - 1) // 256, (N - 1) // 256)))
+    ref, S = oracle.gemm_dense_entries(ta, tb, w["A"], w["B"], ii, jj)
+    got = D[torch.from_numpy(ii).to(dev()), torch.from_numpy(jj).to(dev())].cpu().numpy()
+    assert_close(got, ref, S, ta, K, 1.0, 0.0, None, "layout8 8192^3")
