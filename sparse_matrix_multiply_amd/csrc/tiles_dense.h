@@ -2,7 +2,7 @@
 // their block-scaled (MX) forms.
 // LDS stages of 128-byte rows: two for 256 x 256 tiles (64 KiB each; the next
 // copy goes out right after the barrier that frees a stage), three for the
-// 256 x 128 halves, four for the smaller tiles.
+// 256 x 128 halves (four for packed FP6), four for the smaller tiles.
 #pragma once
 
 #include "gemm_tiled.h"
@@ -21,7 +21,7 @@ constexpr int half_tile_stages() {
 
 template <class Op>
 constexpr bool eight_wave_halves() {
-    return Op::kScaled && Op::kARowBytes != 96;
+    return Op::kARowBytes != 96;
 }
 
 template <class Op>
@@ -34,9 +34,10 @@ hipError_t launch_dense_op(TileShape shape, const GemmParams &p, hipStream_t s) 
         if constexpr (Op::kScaled) return hipErrorInvalidValue;
         else hipLaunchKernelGGL((gemm_tiled_kernel<Op, 256, 256, 2, 4, 2>), grid, dim3(512), 0, s, p);
         break;
-    // Block-scaled fp8 and FP4 (not FP6, whose 96-byte rows would leave partly filled copy passes):
-    // eight waves of 64 x 64 on the halves of the 256 x 256 tile, two waves per SIMD to hide each
-    // other's waits (measured 11 % faster for fp8 and 6 % for FP4 than four waves of 64 x 128).
+    // The halves of the 256 x 256 tile: eight waves of 64 x 64, two per SIMD to hide each other's
+    // waits (measured against four waves of 64 x 128 on one GPU's 8192 x 1024 x 8192 share: bf16
+    // 7 % and fp8 12 % faster; block-scaled fp8 11 % and FP4 6 % at 8192^3).  Not for packed FP6,
+    // whose 96-byte rows would leave partly filled copy passes.
     case TILE_256x128:
         if constexpr (eight_wave_halves<Op>())
             hipLaunchKernelGGL((gemm_tiled_kernel<Op, 256, 128, 4, 2, S2>), grid, dim3(512), 0, s, p);

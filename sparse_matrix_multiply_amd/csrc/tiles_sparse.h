@@ -16,8 +16,9 @@ hipError_t launch_sparse_op(TileShape shape, const GemmParams &p, hipStream_t s)
     const dim3 grid(p.tiles_m * p.tiles_n * p.splits), block(256);   // one workgroup per tile and K range
     switch (shape) {
     case TILE_256: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 256, 256, 2, 4, 3>), grid, dim3(512), 0, s, p); break;
-    case TILE_256x128: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 256, 128, 2, 2, 4>), grid, block, 0, s, p); break;
-    case TILE_128x256: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 128, 256, 2, 2, 3>), grid, block, 0, s, p); break;
+    // the halves of the 256 x 256 tile: eight waves of 64 x 64, two per SIMD, as for the whole tile
+    case TILE_256x128: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 256, 128, 4, 2, 4>), grid, dim3(512), 0, s, p); break;
+    case TILE_128x256: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 128, 256, 2, 4, 3>), grid, dim3(512), 0, s, p); break;
     case TILE_128: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 128, 128, 2, 2, 3>), grid, block, 0, s, p); break;
     case TILE_64: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 64, 64, 2, 2, 3>), grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
