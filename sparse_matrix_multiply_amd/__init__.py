@@ -241,7 +241,7 @@ def gemm_mx(A, SA, B, SB, D, alpha=1.0, beta=0.0, C=None, a_type=None, b_type=No
 
 def gemm_layout(A, B, D, trans_a=False, trans_b=False, alpha=1.0, beta=0.0, C=None, a_type=None, b_type=None,
                 stream=None, bias=None, act=ACT_NONE, d_type=None):
-    """D = alpha * op(A) @ op(B) + beta * C for 16-bit types.  trans_a: A is given as its K x M
+    """D = alpha * op(A) @ op(B) + beta * C for every dense type pair.  trans_a: A is given as its K x M
     transpose (M contiguous); trans_b: B is given as K x N (N contiguous).  Otherwise A is M x K and
     B is N x K as in gemm_dense."""
     M = A.shape[1] if trans_a else A.shape[0]
