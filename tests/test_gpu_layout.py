@@ -176,3 +176,22 @@ def test_layout8_8192_sampled():
     ref, S = oracle.gemm_dense_entries(ta, tb, w["A"], w["B"], ii, jj)
     got = D[torch.from_numpy(ii).to(dev()), torch.from_numpy(jj).to(dev())].cpu().numpy()
     assert_close(got, ref, S, ta, K, 1.0, 0.0, None, "layout8 8192^3")
+
+
+@pytest.mark.parametrize("trans_a,trans_b", LAYOUTS)
+def test_layout8_epilogue_variant(trans_a, trans_b):
+    """fp8 x bf8 with transposed operands, bfloat16 D + bias + ReLU (integer products: exact)."""
+    ta, tb = E4M3, E5M2
+    M, N, K = 200, 136, 384
+    A, B, _, _, _ = problem8(ta, tb, M, N, K, 31, small=True)
+    g = np.random.default_rng(32)
+    bias = g.integers(-300, 301, size=N).astype(np.float32)
+    Y, _ = oracle.gemm_dense(ta, tb, A, B)
+    ref, _ = oracle.epilogue(Y, bias, mm.ACT_RELU, oracle.OUT_BF16)
+    D = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev())
+    Ad = dev8(np.ascontiguousarray(A.T) if trans_a else A)
+    Bd = dev8(np.ascontiguousarray(B.T) if trans_b else B)
+    mm.gemm_layout(Ad, Bd, D, trans_a, trans_b, a_type=ta, b_type=tb, bias=torch.from_numpy(bias).to(dev()),
+                   act=mm.ACT_RELU)
+    torch.cuda.synchronize()
+    assert np.array_equal(D.view(torch.int16).cpu().numpy().view(np.uint16), ref)

@@ -262,3 +262,25 @@ def test_mx_fp6_8192_sampled():
     ref, S = oracle.gemm_mx_entries(FP6, BF6, A, SA, B, SB, ii, jj)
     got = D[torch.from_numpy(ii).to(dev()), torch.from_numpy(jj).to(dev())].cpu().numpy()
     assert_close(got, ref, S, E4M3, K, 1.0, 0.0, None, "mx fp6 8192^3")
+
+
+@pytest.mark.parametrize("ta,tb", [(FP6, BF6), (FP4, FP4)])
+def test_mx_packed_epilogue_variant_exact(ta, tb):
+    """bfloat16 C and D, bias and ReLU after a packed FP6 / FP4 block-scaled sum (small values,
+    power-of-two scales: exact)."""
+    M, N, K = 200, 136, 512
+    if ta == FP4:
+        A, B, SA, SB = fp4_problem(M, N, K, 21, lo=126, hi=129, small=True)
+    else:
+        A, B, SA, SB = fp6_problem(M, N, K, 21, lo=127, hi=129, small=True)
+    g = np.random.default_rng(22)
+    C = g.integers(-64, 65, size=(M, N)).astype(np.float32)
+    bias = g.integers(-300, 301, size=N).astype(np.float32)
+    Y, _ = oracle.gemm_mx(ta, tb, A, SA, B, SB, 1.0, 1.0, C)
+    ref, _ = oracle.epilogue(Y, bias, mm.ACT_RELU, oracle.OUT_BF16)
+    D = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev())
+    Cd = torch.from_numpy(C).to(dev()).to(torch.bfloat16)
+    mm.gemm_mx(torch.from_numpy(A).to(dev()), pack_mx_scales(SA), torch.from_numpy(B).to(dev()), pack_mx_scales(SB),
+               D, 1.0, 1.0, Cd, a_type=ta, b_type=tb, bias=torch.from_numpy(bias).to(dev()), act=mm.ACT_RELU)
+    torch.cuda.synchronize()
+    assert np.array_equal(D.view(torch.int16).cpu().numpy().view(np.uint16), ref)
