@@ -295,8 +295,7 @@ mmac_status_t mmac_gemm_sparse24_ws(mmac_dtype_t a_type, mmac_dtype_t b_type,
  *   SB              the same for the N columns of B (ldsb >= N).
  *   e = 255 (NaN in E8M0) in a block that is used gives unspecified results.
  *   C, D, ep, stream and the error rules as in mmac_gemm_dense_ep.  Outputs
- *   with M <= 32 rows use the tiled kernel (there is no skinny path here);
- *   FP6 products use output tiles of 128 x 128 and up.
+ *   with M <= 32 rows use the tiled kernel (there is no skinny path here).
  */
 mmac_status_t mmac_gemm_dense_mx(mmac_dtype_t a_type, mmac_dtype_t b_type,
                                  int64_t M, int64_t N, int64_t K, double alpha,

@@ -341,7 +341,6 @@ mmac_status_t mmac_gemm_dense_mx(mmac_dtype_t a_type, mmac_dtype_t b_type, int64
     // the 8-wave 256 x 256 tile has no registers left for the scale words: its 128 x 256 half instead
     TileShape shape = pick_shape(M, N, true);
     if (shape == TILE_256) shape = TILE_128x256;
-    if (fp6 && shape == TILE_64) shape = TILE_128;   // FP6 tiles start at 128 x 128
     GemmParams p = make_params(ga, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd, ep, shape);
     if (packed) {
         p.a_pitch = bytes(lda);

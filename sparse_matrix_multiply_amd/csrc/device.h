@@ -172,16 +172,11 @@ __device__ __forceinline__ uint32_t finish(float v, float bias, bool has_bias, b
 // 256-byte bank row keep distinct positions, and successive bank rows are
 // XOR-rotated, so those 16 reads hit 16 different 16-byte bank groups.  The
 // map keeps the row and is its own inverse.
-// Rows of 6 units (96 bytes: 128 packed FP6 elements) sit 24 banks apart, so
-// 8 consecutive rows start on 8 distinct multiples of 8 banks; the units of
-// rows 8 .. 15 of every 16 swap in pairs (c ^ 1), which moves them to the 8
-// starts in between.
 template <int W>
 __device__ __forceinline__ constexpr uint32_t swz(uint32_t L) {
-    static_assert(W == 2 || W == 4 || W == 6 || W == 8, "rows of 2, 4, 6 or 8 units");
+    static_assert(W == 2 || W == 4 || W == 8, "rows of 2, 4 or 8 units");
     const uint32_t r = L / W;
-    if constexpr (W == 6) return r * W + ((L % W) ^ ((r >> 3) & 1));
-    else return r * W + ((L % W) ^ ((r / (16 / W)) % W));
+    return r * W + ((L % W) ^ ((r / (16 / W)) % W));
 }
 
 // ---- matrix-instruction wrappers -----------------------------------------
@@ -313,8 +308,9 @@ struct MmaMX4 {
 // packed elements (24 bytes, element e at bits 6e .. 6e+5) per lane, lane half
 // g holding block g of the instruction's 64 K (established on gfx950 with
 // one-hot operands: every element of lane half g took block g's scale, with
-// the value the packing gives).  K-tiles of 128 elements: 96-byte LDS rows,
-// blocks 2s and 2s+1 in step s; one scale word per row per k-tile.
+// the value the packing gives).  K-tiles of 128 elements: 96 bytes of a row
+// (kept in a 128-byte LDS row), blocks 2s and 2s+1 in step s; one scale word
+// per row per k-tile.
 template <int FA, int FB>
 struct MmaMX6 {
     static constexpr bool kSparse = false, kScaled = true;

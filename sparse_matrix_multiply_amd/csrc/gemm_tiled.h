@@ -143,10 +143,16 @@ struct TiledGemm {
     static constexpr int STEPS = Op::kBK / Op::kKStep;
     static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 tiles");
-    static constexpr int AW = Op::kARowBytes / 16, BW = Op::kBRowBytes / 16;  // 16-byte units per LDS row
-    static_assert(AW == 2 || AW == 4 || AW == 6 || AW == 8, "A LDS rows of 32, 64, 96 or 128 bytes");
-    static_assert(BW == 4 || BW == 6 || BW == 8, "B LDS rows of 64, 96 or 128 bytes");
-    static_assert((AW != 6 && BW != 6) || Op::kAFrag == 24, "96-byte rows hold packed FP6 only");
+    // Bytes of a row that one k-tile covers (ARB, BRB) and 16-byte units per LDS
+    // row (AW, BW): the same, except that the 96 bytes of packed FP6 sit in
+    // 128-byte LDS rows whose last two units stay unused, so that FP6 tiles
+    // copy, swizzle and read like the other 128-byte rows.
+    static constexpr int ARB = Op::kARowBytes, BRB = Op::kBRowBytes;
+    static constexpr int lds_units(int bytes) { return bytes == 96 ? 8 : bytes / 16; }
+    static constexpr int AW = lds_units(ARB), BW = lds_units(BRB);
+    static_assert(AW == 2 || AW == 4 || AW == 8, "A LDS rows of 32, 64 or 128 bytes");
+    static_assert(BW == 4 || BW == 8, "B LDS rows of 64 or 128 bytes");
+    static_assert((ARB != 96 && BRB != 96) || Op::kAFrag == 24, "96-byte rows hold packed FP6 only");
     static constexpr int IW = Op::kSparse ? Op::kBK / 32 : 0;                  // index words per row
     static_assert(!Op::kSparse || STEPS == 2, "index words of a k-tile read once, for two steps");
     // copy units per wave: 16-byte units of A and B, 4-byte words of the index
@@ -155,11 +161,6 @@ struct TiledGemm {
     static_assert(AUPW * NW == BM * AW && BUPW * NW == BN * BW && IUPW * NW * IES == BM * IW * 4,
                   "uneven copy split");
     static constexpr int AP = (AUPW + 63) / 64, BP = (BUPW + 63) / 64, IP = (IUPW + 63) / 64;  // passes
-    // A partly filled copy pass of 96-byte rows (64 x 64 tiles) sits in a lane-divergent branch
-    // next to whole passes; the compiler then merges such copies into one whose LDS base (M0)
-    // it takes from the first active lane, which is wrong for the other lanes.  Those rows
-    // use whole passes only.
-    static_assert((AW != 6 || AUPW % 64 == 0) && (BW != 6 || BUPW % 64 == 0), "whole copy passes for 96-byte rows");
     // Block-scaled operands: SW scale words per row of A and per column of B
     // per k-tile, copied as 16-byte units (four rows' words), one pass for A's
     // and one for B's in every wave.
@@ -222,10 +223,17 @@ struct TiledGemm {
 
     // Physical LDS unit P of a W-unit-wide tile -> byte offset of its source in
     // the row-major source buffer at k-tile kt.
-    template <int W>
+    template <int W, int RB>
     __device__ __forceinline__ uint32_t src_off(uint32_t P, int64_t pitch, int kt) const {
         const uint32_t L = swz<W>(P);
-        return (L / W) * (uint32_t)pitch + (uint32_t)((kt + kt0) * W * 16) + (L % W) * 16;
+        return (L / W) * (uint32_t)pitch + (uint32_t)((kt + kt0) * RB) + (L % W) * 16;
+    }
+    // Whether physical unit P of a tile of W-unit LDS rows holding RB bytes each
+    // carries data (packed FP6: units 6 and 7 of a row do not).
+    template <int W, int RB>
+    __device__ __forceinline__ static constexpr bool data_slot(uint32_t P) {
+        if constexpr (W * 16 == RB) return true;
+        else return (swz<W>(P) % W) * 16 < (uint32_t)RB;
     }
 
     // Byte offset of the source of index copy lane d (LDS bytes [d*IES,
@@ -258,10 +266,10 @@ struct TiledGemm {
         const uint32_t r = P / U, u = (P % U) ^ tswz<U>(r);
         return (uint32_t)(((int64_t)(kt + kt0) * Op::kBK + r) * pitch) + u * 16;
     }
-    template <bool T, int MN, int W>
+    template <bool T, int MN, int W, int RB>
     __device__ __forceinline__ uint32_t op_off(uint32_t P, int64_t pitch, int kt) const {
         if constexpr (T) return tsrc_off<MN>(P, pitch, kt);
-        else return src_off<W>(P, pitch, kt);
+        else return src_off<W, RB>(P, pitch, kt);
     }
 
     // Byte offset (from the tile's first row / column) of 16-byte scale unit u
@@ -279,15 +287,16 @@ struct TiledGemm {
     __device__ __forceinline__ void dma_pass(uint8_t *st, int kt, int j) const {
         if (j < AP) {
             const int u = j * 64 + lane;
-            if (AUPW % 64 == 0 || u < AUPW)
+            if ((AUPW % 64 == 0 || u < AUPW) && data_slot<AW, ARB>(wave * AUPW + u))
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(st + (wave * AUPW + j * 64) * 16), 16,
-                                                         op_off<TRANS_A, BM, AW>(wave * AUPW + u, p.a_pitch, kt), 0,
-                                                         0, 0);
+                                                         op_off<TRANS_A, BM, AW, ARB>(wave * AUPW + u, p.a_pitch, kt),
+                                                         0, 0, 0);
         } else if (j < AP + BP) {
             const int q = j - AP, u = q * 64 + lane;
-            if (BUPW % 64 == 0 || u < BUPW)
+            if ((BUPW % 64 == 0 || u < BUPW) && data_slot<BW, BRB>(wave * BUPW + u))
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(st + A_BYTES + (wave * BUPW + q * 64) * 16),
-                                                         16, op_off<TRANS_B, BN, BW>(wave * BUPW + u, p.b_pitch, kt),
+                                                         16,
+                                                         op_off<TRANS_B, BN, BW, BRB>(wave * BUPW + u, p.b_pitch, kt),
                                                          0, 0, 0);
         } else if constexpr (Op::kSparse) {
             const int q = j - AP - BP, u = q * 64 + lane;
@@ -327,16 +336,16 @@ struct TiledGemm {
         for (int q = 0; q < AP; ++q) {
             const int u = q * 64 + lane;
             const uint32_t P = wave * AUPW + u;
-            if (AUPW % 64 == 0 || u < AUPW) {
+            if ((AUPW % 64 == 0 || u < AUPW) && data_slot<AW, ARB>(P)) {
                 if constexpr (TRANS_A) {   // whole rows of K
                     const bool in = (kt + kt0) * Op::kBK + (int)(P / (BM * Op::kEsize / 16)) < p.K;
                     *reinterpret_cast<i32x4 *>(st + P * 16) =
                         in ? __builtin_amdgcn_raw_buffer_load_b128(ra, tsrc_off<BM>(P, p.a_pitch, kt), 0, 0)
                            : i32x4{0, 0, 0, 0};
                 } else {
-                    const int e0 = ((kt + kt0) * AW * 16 + (int)(swz<AW>(P) % AW) * 16) / Op::kEsize;
+                    const int e0 = ((kt + kt0) * ARB + (int)(swz<AW>(P) % AW) * 16) / Op::kEsize;
                     *reinterpret_cast<i32x4 *>(st + P * 16) =
-                        masked_unit<Op::kEsize>(ra, src_off<AW>(P, p.a_pitch, kt), e0, climit);
+                        masked_unit<Op::kEsize>(ra, src_off<AW, ARB>(P, p.a_pitch, kt), e0, climit);
                 }
             }
         }
@@ -344,16 +353,16 @@ struct TiledGemm {
         for (int q = 0; q < BP; ++q) {
             const int u = q * 64 + lane;
             const uint32_t P = wave * BUPW + u;
-            if (BUPW % 64 == 0 || u < BUPW) {
+            if ((BUPW % 64 == 0 || u < BUPW) && data_slot<BW, BRB>(P)) {
                 if constexpr (TRANS_B) {
                     const bool in = (kt + kt0) * Op::kBK + (int)(P / (BN * Op::kEsize / 16)) < p.K;
                     *reinterpret_cast<i32x4 *>(st + A_BYTES + P * 16) =
                         in ? __builtin_amdgcn_raw_buffer_load_b128(rb, tsrc_off<BN>(P, p.b_pitch, kt), 0, 0)
                            : i32x4{0, 0, 0, 0};
                 } else {
-                    const int e0 = ((kt + kt0) * BW * 16 + (int)(swz<BW>(P) % BW) * 16) / Op::kEsize;
+                    const int e0 = ((kt + kt0) * BRB + (int)(swz<BW>(P) % BW) * 16) / Op::kEsize;
                     *reinterpret_cast<i32x4 *>(st + A_BYTES + P * 16) =
-                        masked_unit<Op::kEsize>(rb, src_off<BW>(P, p.b_pitch, kt), e0, blimit);
+                        masked_unit<Op::kEsize>(rb, src_off<BW, BRB>(P, p.b_pitch, kt), e0, blimit);
                 }
             }
         }
@@ -408,7 +417,7 @@ struct TiledGemm {
     }
 
     // Packed FP6 fragment: the 24 bytes of block 2s + g of row r of a tile of
-    // 96-byte rows, bytes 48s + 24g .. + 23 of the row.  Two whole-unit reads:
+    // 96 data bytes per row, bytes 48s + 24g .. + 23 of the row.  Two whole-unit reads:
     // unit 3s + 2g (lane half 0: operand bytes 0-15; half 1: bytes 8-23) and
     // unit 3s + 1, whose low half ends block 2s and whose high half starts
     // block 2s + 1; each half then puts the pieces in operand order.  (8-byte
@@ -416,7 +425,7 @@ struct TiledGemm {
     // lanes of such a read meet the same banks at least twice.)
     template <int W>
     __device__ __forceinline__ void lds_frag6(Frag<24> &f, const uint8_t *base, uint32_t r, int s) const {
-        static_assert(W == 6, "96-byte rows");
+        static_assert(W == 8, "96 data bytes in 128-byte LDS rows");
         const i32x4 x = *reinterpret_cast<const i32x4 *>(base + swz<W>(r * W + 3 * s + 2 * g) * 16);
         const i32x4 z = *reinterpret_cast<const i32x4 *>(base + swz<W>(r * W + 3 * s + 1) * 16);
         const bool h = g != 0;

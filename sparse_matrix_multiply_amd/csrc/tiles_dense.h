@@ -2,7 +2,7 @@
 // their block-scaled (MX) forms.
 // LDS stages of 128-byte rows: two for 256 x 256 tiles (64 KiB each; the next
 // copy goes out right after the barrier that frees a stage), three for the
-// 256 x 128 halves (four for packed FP6), four for the smaller tiles.
+// 256 x 128 halves, four for the smaller tiles.
 #pragma once
 
 #include "gemm_tiled.h"
@@ -12,21 +12,8 @@ namespace mmac {
 // Kernels of one instruction class Op for every tile shape; each element-type
 // pair is instantiated in a source file of its own under inst/, so that the
 // build compiles them in parallel.
-// LDS stages of the 128 x 256 and 256 x 128 tiles: three, or four for the
-// 96-byte rows of packed FP6 (38 KiB a stage).
-template <class Op>
-constexpr int half_tile_stages() {
-    return Op::kARowBytes == 96 ? 4 : 3;
-}
-
-template <class Op>
-constexpr bool eight_wave_halves() {
-    return Op::kARowBytes != 96;
-}
-
 template <class Op>
 hipError_t launch_dense_op(TileShape shape, const GemmParams &p, hipStream_t s) {
-    constexpr int S2 = half_tile_stages<Op>();
     const dim3 grid(p.tiles_m * p.tiles_n * p.splits), block(256);   // one workgroup per tile and K range
     switch (shape) {
     case TILE_256:
@@ -36,24 +23,11 @@ hipError_t launch_dense_op(TileShape shape, const GemmParams &p, hipStream_t s) 
         break;
     // The halves of the 256 x 256 tile: eight waves of 64 x 64, two per SIMD to hide each other's
     // waits (measured against four waves of 64 x 128 on one GPU's 8192 x 1024 x 8192 share: bf16
-    // 7 % and fp8 12 % faster; block-scaled fp8 11 % and FP4 6 % at 8192^3).  Not for packed FP6,
-    // whose 96-byte rows would leave partly filled copy passes.
-    case TILE_256x128:
-        if constexpr (eight_wave_halves<Op>())
-            hipLaunchKernelGGL((gemm_tiled_kernel<Op, 256, 128, 4, 2, S2>), grid, dim3(512), 0, s, p);
-        else hipLaunchKernelGGL((gemm_tiled_kernel<Op, 256, 128, 2, 2, S2>), grid, block, 0, s, p);
-        break;
-    case TILE_128x256:
-        if constexpr (eight_wave_halves<Op>())
-            hipLaunchKernelGGL((gemm_tiled_kernel<Op, 128, 256, 2, 4, S2>), grid, dim3(512), 0, s, p);
-        else hipLaunchKernelGGL((gemm_tiled_kernel<Op, 128, 256, 2, 2, S2>), grid, block, 0, s, p);
-        break;
+    // 7 % and fp8 12 % faster; block-scaled fp8 11 % and FP4 6 % at 8192^3).
+    case TILE_256x128: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 256, 128, 4, 2, 3>), grid, dim3(512), 0, s, p); break;
+    case TILE_128x256: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 128, 256, 2, 4, 3>), grid, dim3(512), 0, s, p); break;
     case TILE_128: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 128, 128, 2, 2, 4>), grid, block, 0, s, p); break;
-    case TILE_64:
-        // 96-byte rows of packed FP6 fill whole copy passes only from 128 rows on
-        if constexpr (Op::kARowBytes == 96) return hipErrorInvalidValue;
-        else hipLaunchKernelGGL((gemm_tiled_kernel<Op, 64, 64, 2, 2, 4>), grid, block, 0, s, p);
-        break;
+    case TILE_64: hipLaunchKernelGGL((gemm_tiled_kernel<Op, 64, 64, 2, 2, 4>), grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
