@@ -287,17 +287,24 @@ struct TiledGemm {
     __device__ __forceinline__ void dma_pass(uint8_t *st, int kt, int j) const {
         if (j < AP) {
             const int u = j * 64 + lane;
-            if ((AUPW % 64 == 0 || u < AUPW) && data_slot<AW, ARB>(wave * AUPW + u))
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(st + (wave * AUPW + j * 64) * 16), 16,
-                                                         op_off<TRANS_A, BM, AW, ARB>(wave * AUPW + u, p.a_pitch, kt),
+            if (AUPW % 64 == 0 || u < AUPW) {
+                // an unused unit of a packed-FP6 row loads from past the buffer (zero, no memory
+                // access) instead of branching around the copy
+                const uint32_t P = wave * AUPW + u;
+                const uint32_t off =
+                    data_slot<AW, ARB>(P) ? op_off<TRANS_A, BM, AW, ARB>(P, p.a_pitch, kt) : kOutOfRange;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(st + (wave * AUPW + j * 64) * 16), 16, off,
                                                          0, 0, 0);
+            }
         } else if (j < AP + BP) {
             const int q = j - AP, u = q * 64 + lane;
-            if ((BUPW % 64 == 0 || u < BUPW) && data_slot<BW, BRB>(wave * BUPW + u))
+            if (BUPW % 64 == 0 || u < BUPW) {
+                const uint32_t P = wave * BUPW + u;
+                const uint32_t off =
+                    data_slot<BW, BRB>(P) ? op_off<TRANS_B, BN, BW, BRB>(P, p.b_pitch, kt) : kOutOfRange;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(st + A_BYTES + (wave * BUPW + q * 64) * 16),
-                                                         16,
-                                                         op_off<TRANS_B, BN, BW, BRB>(wave * BUPW + u, p.b_pitch, kt),
-                                                         0, 0, 0);
+                                                         16, off, 0, 0, 0);
+            }
         } else if constexpr (Op::kSparse) {
             const int q = j - AP - BP, u = q * 64 + lane;
             if (IUPW % 64 == 0 || u < IUPW)
