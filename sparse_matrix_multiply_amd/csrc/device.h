@@ -396,11 +396,13 @@ template <int DT_A, int DT_B> struct MmaSparse8 {
     typedef typename std::conditional<kInt, int32_t, float>::type out_t;
     __device__ __forceinline__ static constexpr int a_unit(int s, int g, int) { return 2 * s + g; }
     __device__ __forceinline__ static constexpr int b_unit(int s, int g, int h) { return 4 * s + g + 2 * h; }
-    // Index words in LDS: the k-tile's four words of each row (16 bytes, one
-    // copy lane per row), read by each lane with one 16-byte read, so 16
+    // Index words in LDS: the k-tile's four words of each row (16 bytes),
+    // copied 4 bytes per lane so that every copy pass is whole (a partly
+    // filled pass would sit in a branch that splits the interleaved schedule
+    // of the main loop), read by each lane with one 16-byte read, so 16
     // consecutive rows fill the 64 banks once; lane half g takes word g for
     // step 0 and word 2 + g for step 1.
-    static constexpr int kIdxCopyBytes = 16;
+    static constexpr int kIdxCopyBytes = 4;
     typedef i32x4 idx_t;
     __device__ __forceinline__ static idx_t load_idx(const uint8_t *row, int) {
         return *reinterpret_cast<const i32x4 *>(row);
