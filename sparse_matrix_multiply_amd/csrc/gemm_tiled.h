@@ -162,17 +162,20 @@ struct TiledGemm {
                   "uneven copy split");
     static constexpr int AP = (AUPW + 63) / 64, BP = (BUPW + 63) / 64, IP = (IUPW + 63) / 64;  // passes
     // Block-scaled operands: SW scale words per row of A and per column of B
-    // per k-tile, copied as 16-byte units (four rows' words), one pass for A's
-    // and one for B's in every wave.
+    // per k-tile, (BM + BN) * SW words in all, copied 4 bytes per lane in whole
+    // passes of 64 words; pass t of wave w is the tile's pass w + t * NW.  A
+    // wave left without a pass copies nothing (an offset past the buffer) into
+    // a spare region of its own after the stages, so that every wave issues the
+    // same number of copies and no copy sits in a branch.
     static constexpr bool SCALED = Op::kScaled;
     static constexpr int SW = Op::kScaleWords;
-    static constexpr int SAUPW = SCALED ? BM * SW / 4 / NW : 0, SBUPW = SCALED ? BN * SW / 4 / NW : 0;
-    static_assert(!SCALED || (SAUPW * NW * 4 == BM * SW && SBUPW * NW * 4 == BN * SW && SAUPW >= 1 && SBUPW >= 1 &&
-                              SAUPW <= 64 && SBUPW <= 64), "scale copy split");
-    static constexpr int SP = SCALED ? 2 : 0;
+    static constexpr int S_WORDS = SCALED ? (BM + BN) * SW : 0, S_PASSES = S_WORDS / 64;
+    static_assert(!SCALED || (BM * SW % 64 == 0 && BN * SW % 64 == 0), "whole scale copy passes");
+    static constexpr int SP = SCALED ? (S_PASSES + NW - 1) / NW : 0;
     static constexpr int LPT = AP + BP + IP + SP;   // copy instructions per wave per k-tile
     static constexpr int A_BYTES = BM * AW * 16, B_BYTES = BN * BW * 16, I_BYTES = BM * IW * 4;
-    static constexpr int S_BYTES = SCALED ? (BM + BN) * SW * 4 : 0;
+    static constexpr int S_BYTES = S_WORDS * 4;
+    static constexpr int SPARE_BYTES = SCALED && SP * NW > S_PASSES ? NW * 256 : 0;
     static constexpr int STAGE = A_BYTES + B_BYTES + I_BYTES + S_BYTES;
     static constexpr int NSW = SCALED ? (TM + TN) * SW : 1;   // scale words a lane holds per k-tile
     // Transposed operands (A stored M-contiguous, B N-contiguous; 16-bit
@@ -181,12 +184,13 @@ struct TiledGemm {
     // with ds_read_b64_tr_b16 (load_tr).
     static constexpr bool TRANS_A = TransOf<Op>::a, TRANS_B = TransOf<Op>::b;
     static_assert(!(TRANS_A || TRANS_B) || (!Op::kSparse && !SCALED), "plain dense products only");
-    static constexpr int LDS_BYTES = STAGES * STAGE;
+    static constexpr int LDS_BYTES = STAGES * STAGE + SPARE_BYTES;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 workgroup");
 
     const GemmParams &p;
     int wave, lane, g, l32, wm, wn, row0, col0;
     int tile, split, kt0;   // output tile number, K range, its first k-tile
+    uint8_t *spare = nullptr;   // this wave's spare LDS region (block-scaled copies)
     rsrc_t ra, rb, rx, rsa, rsb;
     acc_t acc[TM][TN];
 
@@ -272,16 +276,6 @@ struct TiledGemm {
         else return src_off<W, RB>(P, pitch, kt);
     }
 
-    // Byte offset (from the tile's first row / column) of 16-byte scale unit u
-    // of a k-tile: words 4u .. 4u + 3 of the tile's ROWS x SW words, laid out
-    // word-of-k-tile major, which are rows r .. r + 3 of scale-word row
-    // (kt + kt0) * SW + c of the source.
-    template <int ROWS>
-    __device__ __forceinline__ uint32_t scale_off(uint32_t u, int64_t ld, int kt) const {
-        const uint32_t w0 = 4 * u, c = w0 / ROWS, r = w0 % ROWS;
-        return (uint32_t)((((int64_t)(kt + kt0) * SW + c) * ld + r) * 4);
-    }
-
     // Copy instruction j (0 <= j < LPT: the A passes, then B, then the index or the scales)
     // of k-tile kt into LDS stage `st`; each writes one contiguous run of LDS.
     __device__ __forceinline__ void dma_pass(uint8_t *st, int kt, int j) const {
@@ -312,17 +306,16 @@ struct TiledGemm {
                     rx, (lds_void *)(st + A_BYTES + B_BYTES + (wave * IUPW + q * 64) * IES), IES,
                     idx_off(wave * IUPW + u, kt), 0, 0, 0);
         } else if constexpr (SCALED) {
-            uint8_t *ss = st + A_BYTES + B_BYTES + I_BYTES;
-            if (j == AP + BP) {
-                if (lane < SAUPW)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void *)(ss + wave * SAUPW * 16), 16,
-                                                             scale_off<BM>(wave * SAUPW + lane, p.ldsa, kt), 0, 0, 0);
-            } else {
-                if (lane < SBUPW)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void *)(ss + BM * SW * 4 + wave * SBUPW * 16),
-                                                             16, scale_off<BN>(wave * SBUPW + lane, p.ldsb, kt), 0, 0,
-                                                             0);
-            }
+            // scale word w of the k-tile: A's words first (w = c * BM + r: word c of row r), then B's;
+            // source word ((kt + kt0) * SW + c) * ld + r of the operand's scale array
+            const int gp = wave + (j - AP - BP) * NW;   // the tile's scale pass (wave-uniform)
+            const bool real = gp < S_PASSES, on_a = gp * 64 < BM * SW;
+            const int w = gp * 64 + lane - (on_a ? 0 : BM * SW);
+            const int c = on_a ? w / BM : w / BN, r = on_a ? w % BM : w % BN;
+            const int64_t ld = on_a ? p.ldsa : p.ldsb;
+            const uint32_t off = real ? (uint32_t)((((int64_t)(kt + kt0) * SW + c) * ld + r) * 4) : kOutOfRange;
+            uint8_t *dst = real ? st + A_BYTES + B_BYTES + I_BYTES + gp * 256 : spare;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(on_a ? rsa : rsb, (lds_void *)dst, 4, off, 0, 0, 0);
         }
     }
 
@@ -812,11 +805,11 @@ struct TiledGemm {
     // rows of each 16-lane read.
     static constexpr int epi_tiles() {   // most instruction tiles per pass: fits and divides TM * TN
         int t = TM * TN;
-        while (t > 1 && (t * 4096 * NW > LDS_BYTES || (TM * TN) % t != 0)) --t;
+        while (t > 1 && (t * 4096 * NW > STAGES * STAGE || (TM * TN) % t != 0)) --t;
         return t;
     }
     static constexpr int EPI_TILES = epi_tiles();
-    static_assert(EPI_TILES * 4096 * NW <= LDS_BYTES, "epilogue staging space");
+    static_assert(EPI_TILES * 4096 * NW <= STAGES * STAGE, "epilogue staging space (the stages, not the spare)");
 
     // Stage t of the current group: this lane's 16 values of instruction tile (i, j), as fp32 / int32 bits.
     template <class F>
@@ -1043,6 +1036,7 @@ void gemm_tiled_kernel(GemmParams p) {
     typedef TiledGemm<Op, BM, BN, WM, WN, STAGES> T;
     __shared__ __attribute__((aligned(16))) uint8_t smem[T::LDS_BYTES];
     T t(p);
+    if constexpr (T::SPARE_BYTES > 0) t.spare = smem + T::STAGES * T::STAGE + t.wave * 256;
 
     // this workgroup's K range: k-tiles [kt0, kt0 + nkt) of the matrix, the
     // first nk of them whole (a ragged k-tile can only be the matrix's last)
