@@ -329,7 +329,7 @@ struct MmaMX6 {
     }
 };
 
-// Dense 16-bit product with A stored M-contiguous (TA) and / or B stored
+// Dense product (16- or 8-bit elements) with A stored M-contiguous (TA) and / or B stored
 // N-contiguous (TB): same instruction, fragments read transposed.
 template <class Base, bool TA, bool TB> struct Trans : Base {
     static constexpr bool kTransA = TA, kTransB = TB;

@@ -178,10 +178,10 @@ struct TiledGemm {
     static constexpr int SPARE_BYTES = SCALED && SP * NW > S_PASSES ? NW * 256 : 0;
     static constexpr int STAGE = A_BYTES + B_BYTES + I_BYTES + S_BYTES;
     static constexpr int NSW = SCALED ? (TM + TN) * SW : 1;   // scale words a lane holds per k-tile
-    // Transposed operands (A stored M-contiguous, B N-contiguous; 16-bit
-    // types): the LDS tile is kBK rows of BM (BN) elements, copied row by row,
-    // 16-byte unit u of row r stored at u ^ tswz(r); fragments come out of it
-    // with ds_read_b64_tr_b16 (load_tr).
+    // Transposed operands (A stored M-contiguous, B N-contiguous; 16- and
+    // 8-bit types): the LDS tile is kBK rows of BM (BN) elements, copied row by
+    // row, 16-byte unit u of row r stored at u ^ tswz(r); fragments come out of
+    // it with ds_read_b64_tr_b16 (load_tr) or ds_read_b64_tr_b8 (load_tr8).
     static constexpr bool TRANS_A = TransOf<Op>::a, TRANS_B = TransOf<Op>::b;
     static_assert(!(TRANS_A || TRANS_B) || (!Op::kSparse && !SCALED), "plain dense products only");
     static constexpr int LDS_BYTES = STAGES * STAGE + SPARE_BYTES;
