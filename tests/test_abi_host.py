@@ -333,3 +333,17 @@ def test_layout_argument_errors(L, kw, code):
 def test_layout_empty_is_a_no_op(L):
     assert dense_layout(L, M=0) == mm.OK
     assert dense_layout(L, N=0, tb=1) == mm.OK
+
+
+def test_binding_rejects_partial_fp6_rows():
+    """The Python binding counts packed-FP6 rows and pitches in whole 3-byte groups of four
+    elements; anything else is refused before the library is called."""
+    import torch
+    A = torch.zeros((4, 50), dtype=torch.uint8)            # 50 bytes: not a whole number of elements
+    B = torch.zeros((4, 48), dtype=torch.uint8)
+    S = torch.zeros((1, 4), dtype=torch.int32)
+    D = torch.zeros((4, 4), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        mm.gemm_mx(A, S, B, S, D, a_type=mm.FP6_E2M3, b_type=mm.FP6_E2M3)
+    with pytest.raises(ValueError):
+        mm.gemm_mx(B, S, A, S, D, a_type=mm.BF6_E3M2, b_type=mm.FP6_E2M3)
