@@ -187,7 +187,11 @@ template <int BYTES> struct Frag;
 template <> struct Frag<16> { i32x4 v; };
 template <> struct Frag<32> { i32x4 lo, hi; };
 typedef int i32x6 __attribute__((ext_vector_type(6)));
-template <> struct Frag<24> { i32x6 v; };
+// Packed FP6 operand as read from LDS: the lane half's own 16-byte unit x and
+// the 16-byte unit z that its block shares with the other half's (the
+// operand is put together at the instruction, so the reads need not be
+// waited for before then).
+template <> struct Frag<24> { i32x4 x, z; };
 
 __device__ __forceinline__ i32x8 join(const Frag<32> &f) {
     return i32x8{f.lo[0], f.lo[1], f.lo[2], f.lo[3], f.hi[0], f.hi[1], f.hi[2], f.hi[3]};
@@ -320,11 +324,17 @@ struct MmaMX6 {
     static constexpr int kScaleWords = kBK / 128;
     typedef f32x16 acc_t;
     typedef float out_t;
+    // Operand bytes of lane half g: half 0 holds its block's bytes 0-15 in x and 16-23 in the low
+    // half of z; half 1 its bytes 0-7 in the high half of z and 8-23 in x.
+    __device__ __forceinline__ static i32x8 operand(const Frag<24> &f) {
+        const bool h = (threadIdx.x & 32) != 0;
+        return i32x8{h ? f.z[2] : f.x[0], h ? f.z[3] : f.x[1], h ? f.x[0] : f.x[2], h ? f.x[1] : f.x[3],
+                     h ? f.x[2] : f.z[0], h ? f.x[3] : f.z[1], 0, 0};
+    }
     __device__ __forceinline__ static acc_t mma_scaled(const Frag<24> &a, const Frag<24> &b, acc_t c, uint32_t sa,
                                                        uint32_t sb) {
         // the instruction reads six registers for FP6 operands; the last two are don't-cares
-        const i32x8 A = __builtin_shufflevector(a.v, a.v, 0, 1, 2, 3, 4, 5, -1, -1);
-        const i32x8 B = __builtin_shufflevector(b.v, b.v, 0, 1, 2, 3, 4, 5, -1, -1);
+        const i32x8 A = operand(a), B = operand(b);
         return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, c, FA, FB, 0, (int)sa, 0, (int)sb);
     }
 };

@@ -426,11 +426,8 @@ struct TiledGemm {
     template <int W>
     __device__ __forceinline__ void lds_frag6(Frag<24> &f, const uint8_t *base, uint32_t r, int s) const {
         static_assert(W == 8, "96 data bytes in 128-byte LDS rows");
-        const i32x4 x = *reinterpret_cast<const i32x4 *>(base + swz<W>(r * W + 3 * s + 2 * g) * 16);
-        const i32x4 z = *reinterpret_cast<const i32x4 *>(base + swz<W>(r * W + 3 * s + 1) * 16);
-        const bool h = g != 0;
-        f.v = i32x6{h ? z[2] : x[0], h ? z[3] : x[1], h ? x[0] : x[2], h ? x[1] : x[3], h ? x[2] : z[0],
-                    h ? x[3] : z[1]};
+        f.x = *reinterpret_cast<const i32x4 *>(base + swz<W>(r * W + 3 * s + 2 * g) * 16);
+        f.z = *reinterpret_cast<const i32x4 *>(base + swz<W>(r * W + 3 * s + 1) * 16);
     }
 
     // Fragment of the 32 rows (A) or columns (B) mn0 .. mn0 + 31 of a
