@@ -36,6 +36,12 @@
  *   - beta == 0 means C is not read (C may be NULL; NaNs in C do not leak).
  *     D may be the same buffer as C when ldd == ldc; other overlaps between
  *     outputs and inputs are not allowed.
+ *   - Floating inputs: alpha and beta are applied in fp32 (rounded to
+ *     nearest from the double given); a value that is not finite or whose
+ *     magnitude exceeds FLT_MAX (3.40282347e38) is MMAC_ERR_INVALID_ARG, and a
+ *     beta that rounds to zero in fp32 reads no C.  beta * C enters the fp32
+ *     sum unscaled by any ratio beta / alpha, so every finite pair of scales
+ *     is exact to fp32 rounding (alpha = 2^-100 with beta = 2^100 included).
  *   - int8: alpha and beta must be integers that fit in int32.
  *   - M == 0 or N == 0: nothing is done.  K == 0: D = beta * C (A, B, Ac and
  *     idx are not read and may be NULL).

@@ -101,10 +101,37 @@ def _ptr(t):
 
 
 def _ld(t):
-    """Row pitch (elements) of a 2-D tensor whose last dimension is contiguous."""
+    """Row pitch (elements) of a 2-D tensor whose last dimension is contiguous and whose rows do not
+    overlap (a broadcast or overlapping view would make the kernels write past or over its rows)."""
     if t.dim() != 2 or (t.stride(1) != 1 and t.shape[1] > 1):
         raise ValueError("expected a 2-D tensor with a contiguous last dimension")
+    if t.shape[0] > 1 and t.stride(0) < t.shape[1]:
+        raise ValueError(f"rows of a {tuple(t.shape)} tensor with row stride {t.stride(0)} overlap")
     return max(t.stride(0), t.shape[1], 1)
+
+
+def _shape(t, rows, cols, name, min_cols=False):
+    """Check that a 2-D tensor has `rows` rows and `cols` columns (at least `cols` with min_cols)."""
+    if t is None:
+        return
+    if t.dim() != 2 or t.shape[0] != rows or (t.shape[1] < cols if min_cols else t.shape[1] != cols):
+        want = f"({rows}, {'>= ' if min_cols else ''}{cols})"
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {want}")
+
+
+def _same_device(*tensors):
+    """Every tensor given lives on one CUDA device (the library's kernels address them all)."""
+    devs = {t.device for t in tensors if t is not None}
+    if any(d.type != "cuda" for d in devs):
+        raise ValueError("every tensor must be in GPU memory")
+    if len(devs) > 1:
+        raise ValueError(f"tensors on different devices: {sorted(str(d) for d in devs)}")
+
+
+def _bias(bias, N):
+    if bias is not None and (bias.dtype != torch.float32 or bias.dim() != 1 or bias.numel() < N or
+                             (bias.numel() > 1 and bias.stride(0) != 1)):
+        raise ValueError(f"bias must be a contiguous float32 vector of at least N = {N} values")
 
 
 def _stream(stream):
@@ -122,9 +149,17 @@ def _check(status, what):
         raise MmacError(status, what)
 
 
-def _epilogue(D, bias, act, d_type):
-    """The mmac_epilogue_t of a call, or None for the plain call."""
-    d_type = OUT_OF.get(D.dtype, OUT_ACC) if d_type is None else d_type
+def _epilogue(D, bias, act, d_type, C=None):
+    """The mmac_epilogue_t of a call, or None for the plain call.  D (and C) must have the element
+    size of the output type the call writes."""
+    if d_type is None:
+        if D.dtype not in OUT_OF:
+            raise ValueError(f"D has dtype {D.dtype}; expected one of {sorted(str(t) for t in OUT_OF)}")
+        d_type = OUT_OF[D.dtype]
+    size = {OUT_ACC: 4, OUT_BF16: 2, OUT_F16: 2, OUT_FP8_E4M3: 1, OUT_BF8_E5M2: 1}.get(d_type)
+    for t, name in ((D, "D"), (C, "C")):
+        if size is not None and t is not None and t.element_size() != size:
+            raise ValueError(f"{name} has {t.element_size()}-byte elements; the output type writes {size}")
     if d_type == OUT_ACC and bias is None and act == ACT_NONE:
         return None
     return Epilogue(d_type, act, None if bias is None else bias.data_ptr())
@@ -151,10 +186,15 @@ def gemm_dense(A, B, D, alpha=1.0, beta=0.0, C=None, a_type=None, b_type=None, s
     workspace tensor (see workspace()) it is mmac_gemm_dense_ws, which may split K."""
     M, K = A.shape
     N = B.shape[0]
+    _shape(B, N, K, "B")
+    _shape(D, M, N, "D")
+    _shape(C, M, N, "C")
+    _bias(bias, N)
+    _same_device(A, B, C, D, bias, workspace)
     ta, tb = _dtype(A, a_type), _dtype(B, b_type)
     args = (ta, tb, M, N, K, float(alpha), _ptr(A), _ld(A), _ptr(B), _ld(B), float(beta),
             _ptr(C), _ld(C) if C is not None else 0, _ptr(D), _ld(D))
-    ep = _epilogue(D, bias, act, d_type)
+    ep = _epilogue(D, bias, act, d_type, C)
     if workspace is not None:
         _check(lib().mmac_gemm_dense_ws(*args, None if ep is None else ctypes.byref(ep), _ptr(workspace),
                                         workspace.numel() * workspace.element_size(), _stream(stream)),
@@ -166,9 +206,21 @@ def gemm_dense(A, B, D, alpha=1.0, beta=0.0, C=None, a_type=None, b_type=None, s
     return D
 
 
+def _compress_shapes(A, Ac, idx, bad_groups):
+    M, K = A.shape
+    _shape(Ac, M, K // 2, "Ac")
+    _shape(idx, M, (K + 31) // 32, "idx")
+    if idx.element_size() != 4:
+        raise ValueError("idx must hold 32-bit words")
+    if bad_groups is not None and (bad_groups.numel() < 1 or bad_groups.element_size() != 4):
+        raise ValueError("bad_groups must hold at least one 32-bit counter")
+    _same_device(A, Ac, idx, bad_groups)
+
+
 def sparse24_compress(A, Ac, idx, bad_groups=None, a_type=None, stream=None):
     """Compress a 4:2 A (M x K) into Ac (M x K/2) and idx (M x ceil(K/32) words)."""
     M, K = A.shape
+    _compress_shapes(A, Ac, idx, bad_groups)
     ta = _dtype(A, a_type)
     st = lib().mmac_sparse24_compress(ta, M, K, _ptr(A), _ld(A), _ptr(Ac), _ld(Ac), _ptr(idx), _ld(idx),
                                       _ptr(bad_groups), _stream(stream))
@@ -180,6 +232,7 @@ def sparse24_prune_compress(A, Ac, idx, bad_groups=None, a_type=None, stream=Non
     """Prune a dense A (M x K) to 4:2 by magnitude (two largest |a| per group of four) and
     compress it into Ac (M x K/2) and idx (M x ceil(K/32) words), in one pass."""
     M, K = A.shape
+    _compress_shapes(A, Ac, idx, bad_groups)
     ta = _dtype(A, a_type)
     st = lib().mmac_sparse24_prune_compress(ta, M, K, _ptr(A), _ld(A), _ptr(Ac), _ld(Ac), _ptr(idx), _ld(idx),
                                             _ptr(bad_groups), _stream(stream))
@@ -195,10 +248,19 @@ def gemm_sparse24(Ac, idx, B, D, K=None, alpha=1.0, beta=0.0, C=None, a_type=Non
     M = Ac.shape[0]
     N, KB = B.shape
     K = KB if K is None else K
+    _shape(Ac, M, K // 2, "Ac")
+    _shape(B, N, K, "B")
+    _shape(idx, M, (K + 31) // 32, "idx", min_cols=True)
+    if idx.element_size() != 4:
+        raise ValueError("idx must hold 32-bit words")
+    _shape(D, M, N, "D")
+    _shape(C, M, N, "C")
+    _bias(bias, N)
+    _same_device(Ac, idx, B, C, D, bias, workspace)
     ta, tb = _dtype(Ac, a_type), _dtype(B, b_type)
     args = (ta, tb, M, N, K, float(alpha), _ptr(Ac), _ld(Ac), _ptr(idx), _ld(idx), _ptr(B), _ld(B), float(beta),
             _ptr(C), _ld(C) if C is not None else 0, _ptr(D), _ld(D))
-    ep = _epilogue(D, bias, act, d_type)
+    ep = _epilogue(D, bias, act, d_type, C)
     if workspace is not None:
         _check(lib().mmac_gemm_sparse24_ws(*args, None if ep is None else ctypes.byref(ep), _ptr(workspace),
                                            workspace.numel() * workspace.element_size(), _stream(stream)),
@@ -231,7 +293,17 @@ def gemm_mx(A, SA, B, SB, D, alpha=1.0, beta=0.0, C=None, a_type=None, b_type=No
         return nbytes
 
     K, lda, ldb = elems(K, ta), elems(_ld(A), ta), elems(_ld(B), tb)
-    ep = _epilogue(D, bias, act, d_type)
+    if elems(B.shape[1], tb) != K:
+        raise ValueError(f"B has {elems(B.shape[1], tb)} elements per row, A has {K}")
+    _shape(SA, (K + 127) // 128, M, "SA", min_cols=True)
+    _shape(SB, (K + 127) // 128, N, "SB", min_cols=True)
+    if SA.element_size() != 4 or SB.element_size() != 4:
+        raise ValueError("SA and SB must hold 32-bit scale words")
+    _shape(D, M, N, "D")
+    _shape(C, M, N, "C")
+    _bias(bias, N)
+    _same_device(A, SA, B, SB, C, D, bias)
+    ep = _epilogue(D, bias, act, d_type, C)
     st = lib().mmac_gemm_dense_mx(ta, tb, M, N, K, float(alpha), _ptr(A), lda, _ptr(SA), _ld(SA), _ptr(B), ldb,
                                   _ptr(SB), _ld(SB), float(beta), _ptr(C), _ld(C) if C is not None else 0, _ptr(D),
                                   _ld(D), None if ep is None else ctypes.byref(ep), _stream(stream))
@@ -247,8 +319,14 @@ def gemm_layout(A, B, D, trans_a=False, trans_b=False, alpha=1.0, beta=0.0, C=No
     M = A.shape[1] if trans_a else A.shape[0]
     K = A.shape[0] if trans_a else A.shape[1]
     N = B.shape[1] if trans_b else B.shape[0]
+    if (B.shape[0] if trans_b else B.shape[1]) != K:
+        raise ValueError(f"B has shape {tuple(B.shape)}, which does not hold K = {K} for this layout")
+    _shape(D, M, N, "D")
+    _shape(C, M, N, "C")
+    _bias(bias, N)
+    _same_device(A, B, C, D, bias)
     ta, tb = _dtype(A, a_type), _dtype(B, b_type)
-    ep = _epilogue(D, bias, act, d_type)
+    ep = _epilogue(D, bias, act, d_type, C)
     st = lib().mmac_gemm_dense_layout(ta, tb, int(bool(trans_a)), int(bool(trans_b)), M, N, K, float(alpha), _ptr(A),
                                       _ld(A), _ptr(B), _ld(B), float(beta), _ptr(C), _ld(C) if C is not None else 0,
                                       _ptr(D), _ld(D), None if ep is None else ctypes.byref(ep), _stream(stream))

@@ -1,6 +1,7 @@
 // C ABI of libmmac: argument validation on the host, kernel selection, launch
 // on the caller's stream.  The public contract is in include/mmac.h.
 #include <algorithm>
+#include <cfloat>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -88,7 +89,10 @@ mmac_status_t check_gemm(int a, int b, int64_t M, int64_t N, int64_t K, double a
     if (beta != 0.0 && !C) return MMAC_ERR_INVALID_ARG;
     if (lda < a_cols || ldb < b_cols || lda < 1 || ldb < 1 || ldd < N || (C && beta != 0.0 && ldc < N))
         return MMAC_ERR_INVALID_ARG;
-    if (!std::isfinite(alpha) || !std::isfinite(beta)) return MMAC_ERR_INVALID_ARG;
+    // alpha and beta are used in fp32 (the epilogue's precision): they must be finite there
+    if (!std::isfinite(alpha) || !std::isfinite(beta) || std::fabs(alpha) > (double)FLT_MAX ||
+        std::fabs(beta) > (double)FLT_MAX)
+        return MMAC_ERR_INVALID_ARG;
     if (a == MMAC_I8 && (!integral_i32(alpha) || !integral_i32(beta))) return MMAC_ERR_INVALID_ARG;
     if (C == D && beta != 0.0 && ldc != ldd) return MMAC_ERR_INVALID_ARG;
     const int es = elem_size(a);
@@ -110,7 +114,6 @@ GemmParams make_params(int a, int64_t M, int64_t N, int64_t K, double alpha, con
     p.a_pitch = lda * es;
     p.B = static_cast<const uint8_t *>(B);
     p.b_pitch = ldb * es;
-    p.C = beta != 0.0 ? C : nullptr;
     p.ldc = ldc;
     p.D = D;
     p.ldd = ldd;
@@ -121,13 +124,23 @@ GemmParams make_params(int a, int64_t M, int64_t N, int64_t K, double alpha, con
     p.beta = (float)beta;
     p.ialpha = a == MMAC_I8 ? (int)alpha : 0;
     p.ibeta = a == MMAC_I8 ? (int)beta : 0;
-    p.use_c = beta != 0.0 ? 1 : 0;
+    // C is read only when beta is non-zero in the precision it is applied in
+    p.use_c = (a == MMAC_I8 ? beta != 0.0 : p.beta != 0.0f) ? 1 : 0;
+    p.C = p.use_c ? C : nullptr;
     if (p.use_c) {
+        // beta * C folded into the accumulator's start value only where that adds no scaling of its
+        // own: with alpha == 1 the start value is beta * C (the unfolded epilogue's product), with
+        // alpha == beta it is C and the epilogue's alpha scales both terms.  Any other ratio would
+        // start from (beta / alpha) * C, which can overflow or underflow fp32 while beta * C and
+        // the result do not (alpha = 2^-100, beta = 2^100, say), so C is then read in the epilogue.
         if (a == MMAC_I8) {
             p.fold_c = alpha == 1.0;
-        } else if (alpha != 0.0) {
+        } else if (p.alpha == p.beta) {
             p.fold_c = 1;
-            p.c_scale = alpha == beta ? 1.0f : (float)(beta / alpha);
+            p.c_scale = 1.0f;
+        } else if (p.alpha == 1.0f) {
+            p.fold_c = 1;
+            p.c_scale = p.beta;
         }
     }
     // C is folded into the accumulator only for fp32 / int32 outputs (16- and

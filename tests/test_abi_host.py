@@ -98,6 +98,9 @@ def compress(L, entry="mmac_sparse24_compress", **kw):
     (dict(beta=1.0, C=P + 4096, ldc=32), mm.ERR_INVALID_ARG),
     (dict(beta=1.0, C=P, ldc=64, ldd=128), mm.ERR_INVALID_ARG),        # in place needs ldc == ldd
     (dict(alpha=float("nan")), mm.ERR_INVALID_ARG),
+    (dict(alpha=float("inf")), mm.ERR_INVALID_ARG),
+    (dict(alpha=3.5e38), mm.ERR_INVALID_ARG),                           # finite double, beyond fp32
+    (dict(beta=-1e300, C=P + 4096), mm.ERR_INVALID_ARG),
     (dict(a=mm.I8, b=mm.I8, alpha=1.5), mm.ERR_INVALID_ARG),
     (dict(a=mm.I8, b=mm.I8, beta=2.0 ** 31, C=P + 4096), mm.ERR_INVALID_ARG),
     (dict(A=P + 8), mm.ERR_MISALIGNED),
@@ -347,3 +350,50 @@ def test_binding_rejects_partial_fp6_rows():
         mm.gemm_mx(A, S, B, S, D, a_type=mm.FP6_E2M3, b_type=mm.FP6_E2M3)
     with pytest.raises(ValueError):
         mm.gemm_mx(B, S, A, S, D, a_type=mm.BF6_E3M2, b_type=mm.FP6_E2M3)
+
+
+def test_binding_checks_shapes_before_any_launch():
+    """The binding rejects tensors whose shapes, strides or element sizes do not match the call
+    (the kernels would otherwise write outside the caller's buffers); host tensors suffice, since
+    every check runs before the library is called."""
+    import torch
+    A = torch.zeros((64, 128), dtype=torch.bfloat16)
+    B = torch.zeros((32, 128), dtype=torch.bfloat16)
+    D = torch.zeros((64, 32), dtype=torch.float32)
+    bad = [
+        dict(D=torch.zeros((63, 32))),                                 # too few rows of D
+        dict(D=torch.zeros((64, 31))),
+        dict(D=torch.zeros((64, 32), dtype=torch.int16)),              # 2-byte D for a 4-byte output
+        dict(D=torch.zeros((64, 32), dtype=torch.float64)),
+        dict(C=torch.zeros((32, 32)), beta=1.0),
+        dict(B=torch.zeros((32, 64), dtype=torch.bfloat16)),           # K mismatch
+        dict(bias=torch.zeros(16)),                                    # bias shorter than N
+        dict(bias=torch.zeros(32, dtype=torch.float16)),
+        dict(D=torch.zeros((1, 32)).expand(64, 32)),                   # rows overlap (stride 0)
+    ]
+    for kw in bad:
+        args = dict(A=A, B=B, D=D)
+        args.update(kw)
+        with pytest.raises(ValueError):
+            mm.gemm_dense(**args)
+    with pytest.raises(ValueError):                                    # host memory
+        mm.gemm_dense(A, B, D)
+
+    Ac = torch.zeros((64, 64), dtype=torch.float16)
+    idx = torch.zeros((64, 4), dtype=torch.int32)
+    Bs = torch.zeros((32, 128), dtype=torch.float16)
+    for kw in (dict(Ac=torch.zeros((64, 32), dtype=torch.float16)), dict(idx=torch.zeros((63, 4), dtype=torch.int32)),
+               dict(idx=torch.zeros((64, 3), dtype=torch.int32)), dict(idx=torch.zeros((64, 8), dtype=torch.int16)),
+               dict(D=torch.zeros((64, 16)))):
+        args = dict(Ac=Ac, idx=idx, B=Bs, D=D)
+        args.update(kw)
+        with pytest.raises(ValueError):
+            mm.gemm_sparse24(args["Ac"], args["idx"], args["B"], args["D"], K=128)
+    A16 = torch.zeros((64, 128), dtype=torch.float16)
+    for Acx, idxx, badx in ((torch.zeros((64, 32), dtype=torch.float16), idx, None),
+                            (Ac, torch.zeros((64, 3), dtype=torch.int32), None),
+                            (Ac, idx, torch.zeros(0, dtype=torch.int32))):
+        with pytest.raises(ValueError):
+            mm.sparse24_compress(A16, Acx, idxx, badx)
+        with pytest.raises(ValueError):
+            mm.sparse24_prune_compress(A16, Acx, idxx, badx)

@@ -176,3 +176,29 @@ def test_alpha_beta_combinations(ta, alpha, beta, tile):
         assert np.array_equal(D, Dref)
     else:
         assert_close(D, Dref, aux, ta, K, alpha, beta, C, f"alpha {alpha} beta {beta}")
+
+
+# (alpha, beta, A all zero): scale ratios far outside fp32 (2^+-200), a subnormal fp32 alpha, and
+# equal extreme scales.  beta * C must keep its exact fp32 value whatever alpha is.
+EXTREME_SCALES = [(2.0 ** -100, 2.0 ** 100, False), (2.0 ** 100, 2.0 ** -100, True), (1e-39, 1.0, False),
+                  (2.0 ** -100, 2.0 ** -100, False), (1.0, 2.0 ** -120, False), (-3.0, 2.0 ** 60, False)]
+
+
+@pytest.mark.parametrize("alpha,beta,a_zero", EXTREME_SCALES)
+@pytest.mark.parametrize("tile", [256, 64])
+@pytest.mark.parametrize("ta,tb", [(BF16, BF16), (E4M3, E5M2)])
+def test_extreme_alpha_beta_ratios(ta, tb, alpha, beta, a_zero, tile):
+    """alpha * A*B + beta * C for scales whose ratio leaves fp32's range.  The oracle gets alpha and
+    beta as the fp32 values the library applies (the ABI rounds them once to fp32)."""
+    M, N, K = 300, 270, 160
+    A, B, C, _, _ = inputs(ta, tb, M, N, K, 37)
+    if a_zero:
+        A = np.zeros_like(A)
+    with tile_shape(tile):
+        D = run_dense(ta, tb, A, B, alpha, beta, C)
+    a32, b32 = float(np.float32(alpha)), float(np.float32(beta))
+    Dref, S = oracle.gemm_dense(ta, tb, A, B, a32, b32, C)
+    assert np.isfinite(Dref).all()
+    assert_close(D, Dref, S, ta, K, a32, b32, C, f"alpha {alpha} beta {beta}")
+    if a_zero:                                    # D = beta * C exactly
+        assert np.array_equal(D.astype(np.float64), Dref)

@@ -199,3 +199,25 @@ def test_share_shape_is_not_split():
     """One GPU's 8192 x 1024 x 8192 share already has a tile per compute unit (128 x 256 tiles)."""
     assert mm.workspace_bytes(BF16, 8192, 1024, 8192) == 0
     assert mm.workspace_bytes(E4M3, 8192, 1024, 8192, True) == 0
+
+
+@pytest.mark.parametrize("alpha,beta,a_zero", [(2.0 ** -100, 2.0 ** 100, False), (2.0 ** 100, 2.0 ** -100, True),
+                                               (1e-39, 1.0, False)])
+@pytest.mark.parametrize("ta,tb", [(BF16, BF16), (E4M3, E5M2)])
+def test_extreme_alpha_beta_ratios_split(ta, tb, alpha, beta, a_zero):
+    """The same scale pairs under a forced split into three ranges (C then reaches the result in
+    the workgroup that finishes the tile, or in range 0's partial)."""
+    M, N, K = 300, 260, 1000
+    A, B, C, _, _ = inputs(ta, tb, M, N, K, 41)
+    if a_zero:
+        A = np.zeros_like(A)
+    with env(MMAC_SPLITK=3, MMAC_TILE=64):
+        ws = mm.workspace(ta, M, N, K)
+        assert ws is not None
+        D = run(ta, tb, A, B, alpha, beta, C, ws).cpu().numpy()
+        assert counters_zero(ws, M, N, 64)
+    a32, b32 = float(np.float32(alpha)), float(np.float32(beta))
+    Dref, S = oracle.gemm_dense(ta, tb, A, B, a32, b32, C)
+    assert_close(D, Dref, S, ta, K, a32, b32, C, f"split alpha {alpha} beta {beta}")
+    if a_zero:
+        assert np.array_equal(D.astype(np.float64), Dref)

@@ -66,6 +66,18 @@ def float32_normal(shape, workload_id, operand):
     return rng(workload_id, operand).standard_normal(size=shape).astype(np.float32)
 
 
+def small_int(shape, t, workload_id, operand, lo=-2, hi=2):
+    """Integers drawn uniformly from [lo, hi], stored exactly in format t (fp16, bf16 and the
+    fp8 formats hold every integer of magnitude <= 8 exactly).  Products of such inputs, and
+    their sums while below 2^24, are exact in fp32 whatever the order of the additions."""
+    x = rng(workload_id, operand).integers(lo, hi + 1, size=shape).astype(np.float64)
+    return to_bits(x, t)
+
+
+def int_valued_float32(shape, workload_id, operand, lo=-8, hi=8):
+    return rng(workload_id, operand).integers(lo, hi + 1, size=shape).astype(np.float32)
+
+
 # The six ways of keeping two of four positions, in the order the pattern draw uses.
 PATTERNS = ((0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3))
 
@@ -140,4 +152,29 @@ def workload(name):
         A = normal((M, K), E4M3, 5, "A") if name == "fp8_8192" else sparse24_normal(M, K, E4M3, 5, False)
         return dict(ta=E4M3, tb=E5M2, M=M, N=N, K=K, alpha=1.0, beta=0.0,
                     A=A, B=normal((N, K), E5M2, 5, "B"), C=None)
+    # Exact-input forms of the large workloads: the same shapes, types, alpha / beta and
+    # sparsity structure, with small integers as values, so that every fp32 partial sum is an
+    # exact integer (|sum| <= K * 4 + 8 < 2^24) and the GPU must equal the oracle bit for bit.
+    if name in ("bf16_4096_int", "bf16_8192_int", "bf16_skinny_int"):
+        M, N, K = {"bf16_4096_int": (4096, 4096, 4096), "bf16_8192_int": (8192, 8192, 8192),
+                   "bf16_skinny_int": (16, 4096, 4096)}[name]
+        wid = {"bf16_4096_int": 13, "bf16_8192_int": 16, "bf16_skinny_int": 17}[name]
+        return dict(ta=BF16, tb=BF16, M=M, N=N, K=K, alpha=1.0, beta=1.0,
+                    A=small_int((M, K), BF16, wid, "A"), B=small_int((N, K), BF16, wid, "B"),
+                    C=int_valued_float32((M, N), wid, "C"))
+    if name == "f16_sparse_int":
+        M, N, K = 4096, 4096, 8192
+        # kept values from {-2, -1, 1, 2}: exactly two non-zeros in every group
+        keep = prune_mask(M, K, 14)
+        mag = rng(14, "A").integers(1, 3, size=(M, K)) * rng(14, "C").choice([-1.0, 1.0], size=(M, K))
+        A = np.where(keep, to_bits(mag, F16), zero_bits(F16))
+        return dict(ta=F16, tb=F16, M=M, N=N, K=K, alpha=1.0, beta=0.0, A=np.ascontiguousarray(A),
+                    B=small_int((N, K), F16, 14, "B"), C=None)
+    if name in ("fp8_8192_int", "fp8_8192_int_sparse"):
+        M = N = K = 8192
+        A = small_int((M, K), E4M3, 15, "A")
+        if name == "fp8_8192_int_sparse":      # random 2-of-4 pruning of the dense A (kept zeros stay)
+            A = np.ascontiguousarray(np.where(prune_mask(M, K, 15), A, zero_bits(E4M3)))
+        return dict(ta=E4M3, tb=E5M2, M=M, N=N, K=K, alpha=1.0, beta=0.0,
+                    A=A, B=small_int((N, K), E5M2, 15, "B"), C=None)
     raise KeyError(name)
