@@ -52,7 +52,8 @@
  *     row pitch of A, B, Ac, C and D must be at most 8 MiB and that of idx
  *     at most 8 MiB / 4 words (MMAC_ERR_UNSUPPORTED otherwise).
  *   - Memory: every pointer is device memory on the current HIP device, owned
- *     by the caller; the library never allocates, frees or keeps a pointer.
+ *     by the caller; the library never allocates, frees or keeps a pointer
+ *     (its only device memory of its own is mmac_gemm_dense_static's array).
  *     Buffers must stay valid until the work on `stream` has finished.
  *   - Asynchrony: each call validates its arguments on the host, then enqueues
  *     kernels on `stream` (a hipStream_t; NULL is the default stream) and
@@ -61,7 +62,7 @@
  *   - Errors: no exception crosses this interface.  Argument errors are
  *     detected before any GPU work is enqueued; nothing is written then.
  *   - Thread safety: calls are re-entrant; the library keeps no state between
- *     calls.
+ *     calls (except mmac_gemm_dense_static's fixed scratch array, see there).
  *   - Tuning: two environment variables, read on every call, override the
  *     tile choice: MMAC_TILE (256, 128 or 64 forces that square output tile,
  *     2561 forces 256 x 128 and 1282 forces 128 x 256; 16 forces the
@@ -83,7 +84,8 @@ typedef enum {
     MMAC_ERR_INVALID_ARG = 1, /* negative or oversized dims, bad ld, NULL pointer, bad alpha/beta */
     MMAC_ERR_UNSUPPORTED = 2, /* element-type pair not supported */
     MMAC_ERR_MISALIGNED = 3,  /* alignment rule above broken */
-    MMAC_ERR_HIP = 4          /* the HIP runtime refused the launch */
+    MMAC_ERR_HIP = 4,         /* the HIP runtime refused the launch */
+    MMAC_ERR_SCRATCH = 5      /* mmac_gemm_dense_static: more scratch needed than its fixed array holds */
 } mmac_status_t;
 
 typedef enum {
@@ -276,6 +278,33 @@ mmac_status_t mmac_gemm_sparse24_ws(mmac_dtype_t a_type, mmac_dtype_t b_type,
                                     double beta, const void *C, int64_t ldc,
                                     void *D, int64_t ldd, const mmac_epilogue_t *ep,
                                     void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * Allocation-free split-K dense GEMM, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The same operation, arguments, rules and kernels as
+ * mmac_gemm_dense_ws, except that the split-K workspace is the library's own
+ * fixed device array of MMAC_STATIC_SCRATCH_BYTES (8 MiB): one copy per GPU,
+ * created when the library is loaded and held until the process ends.  The
+ * call allocates nothing and frees nothing.
+ *   - The first call on a device looks up that device's copy and enqueues one
+ *     small kernel on `stream` that zeroes it (the tile counters must start at
+ *     zero; every complete call leaves them zero again).
+ *   - A product whose split-K plan needs more than the array holds (only
+ *     possible when MMAC_TILE / MMAC_SPLITK force a large plan; every plan the
+ *     library picks by itself needs at most 4 MiB) returns MMAC_ERR_SCRATCH
+ *     before any GPU work; a product that does not split uses no scratch.
+ *   - All calls on one GPU share its array: calls that may overlap in time on
+ *     one GPU (different streams, or different host threads without ordering)
+ *     race on it and give undefined results.  Calls in one stream are safe.
+ */
+#define MMAC_STATIC_SCRATCH_BYTES (8 << 20)
+mmac_status_t mmac_gemm_dense_static(mmac_dtype_t a_type, mmac_dtype_t b_type,
+                                     int64_t M, int64_t N, int64_t K, double alpha,
+                                     const void *A, int64_t lda,
+                                     const void *B, int64_t ldb,
+                                     double beta, const void *C, int64_t ldc,
+                                     void *D, int64_t ldd, const mmac_epilogue_t *ep, void *stream);
 
 /*
  * Block-scaled (MX) dense GEMM -- beyond the pages, which have no block

@@ -24,7 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmmac.so")
 
 F16, BF16, I8, FP8_E4M3, BF8_E5M2, FP4_E2M1, FP6_E2M3, BF6_E3M2 = 1, 2, 3, 4, 5, 6, 7, 8
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_HIP = 0, 1, 2, 3, 4
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_HIP, ERR_SCRATCH = 0, 1, 2, 3, 4, 5
 
 OUT_ACC, OUT_BF16, OUT_F16, OUT_FP8_E4M3, OUT_BF8_E5M2 = 0, 1, 2, 3, 4
 ACT_NONE, ACT_RELU = 0, 1
@@ -75,6 +75,9 @@ def lib():
         L.mmac_gemm_dense_ws.restype = i32
         L.mmac_gemm_dense_ws.argtypes = [i32, i32, i64, i64, i64, dbl, vp, i64, vp, i64, dbl, vp, i64, vp, i64, ep,
                                          vp, i64, vp]
+        L.mmac_gemm_dense_static.restype = i32
+        L.mmac_gemm_dense_static.argtypes = [i32, i32, i64, i64, i64, dbl, vp, i64, vp, i64, dbl, vp, i64, vp, i64,
+                                             ep, vp]
         L.mmac_gemm_sparse24_ws.restype = i32
         L.mmac_gemm_sparse24_ws.argtypes = [i32, i32, i64, i64, i64, dbl, vp, i64, vp, i64, vp, i64, dbl, vp, i64,
                                             vp, i64, ep, vp, i64, vp]
@@ -215,6 +218,26 @@ def _compress_shapes(A, Ac, idx, bad_groups):
     if bad_groups is not None and (bad_groups.numel() < 1 or bad_groups.element_size() != 4):
         raise ValueError("bad_groups must hold at least one 32-bit counter")
     _same_device(A, Ac, idx, bad_groups)
+
+
+def gemm_dense_static(A, B, D, alpha=1.0, beta=0.0, C=None, a_type=None, b_type=None, stream=None, bias=None,
+                      act=ACT_NONE, d_type=None):
+    """gemm_dense with split-K through the library's fixed scratch array (mmac_gemm_dense_static):
+    no workspace argument, nothing allocated."""
+    M, K = A.shape
+    N = B.shape[0]
+    _shape(B, N, K, "B")
+    _shape(D, M, N, "D")
+    _shape(C, M, N, "C")
+    _bias(bias, N)
+    _same_device(A, B, C, D, bias)
+    ta, tb = _dtype(A, a_type), _dtype(B, b_type)
+    ep = _epilogue(D, bias, act, d_type, C)
+    _check(lib().mmac_gemm_dense_static(ta, tb, M, N, K, float(alpha), _ptr(A), _ld(A), _ptr(B), _ld(B), float(beta),
+                                        _ptr(C), _ld(C) if C is not None else 0, _ptr(D), _ld(D),
+                                        None if ep is None else ctypes.byref(ep), _stream(stream)),
+           "mmac_gemm_dense_static")
+    return D
 
 
 def sparse24_compress(A, Ac, idx, bad_groups=None, a_type=None, stream=None):

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 
 #include "launch.h"
 #include "mmac.h"
@@ -239,9 +240,80 @@ mmac_status_t compress_call(mmac_dtype_t a_type, int64_t M, int64_t K, const voi
     return launched(launch_compress(a_type, p, prune, static_cast<hipStream_t>(stream)));
 }
 
+// ---- the allocation-free split-K call ----------------------------------
+// The split-K workspace of mmac_gemm_dense_static: one fixed array per GPU
+// (tile counters first, then the partial tiles), held from the library's
+// load until the process ends.  Host code never passes the array's name to a
+// kernel or a copy: that is a host-side stand-in, not a device address.  It
+// uses the address hipGetSymbolAddress gives for the current device.
+constexpr int64_t kScratchBytes = MMAC_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+__global__ void zero_fill(uint4 *p, int64_t n) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = uint4{0u, 0u, 0u, 0u};
+}
+
+constexpr int kMaxDevices = 64;
+struct DeviceScratch {
+    std::once_flag once;
+    void *ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+DeviceScratch g_scratch[kMaxDevices];
+
+// This device's copy of `scratch`, set up once per device with that device
+// current: its address (hipGetSymbolAddress, return code checked) and one
+// fill kernel on `stream` that zeroes it, since the tile counters must start
+// at zero (every complete call leaves them zero again).  A fill kernel, not a
+// memset, so that a call captured into a HIP graph records only kernels.
+// Returns NULL (and the error) if the address cannot be had.
+void *device_scratch(hipStream_t stream, hipError_t *err) {
+    int dev = -1;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    DeviceScratch &d = g_scratch[dev];
+    std::call_once(d.once, [&] {
+        void *ptr = nullptr;
+        d.err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (d.err == hipSuccess) {
+            hipLaunchKernelGGL(zero_fill, dim3(256), dim3(256), 0, stream, static_cast<uint4 *>(ptr),
+                               kScratchBytes / 16);
+            d.err = hipGetLastError();
+        }
+        if (d.err == hipSuccess) d.ptr = ptr;
+    });
+    *err = d.err;
+    return d.ptr;
+}
+
 }  // namespace
 
 extern "C" {
+
+mmac_status_t mmac_gemm_dense_static(mmac_dtype_t a_type, mmac_dtype_t b_type, int64_t M, int64_t N, int64_t K,
+                                     double alpha, const void *A, int64_t lda, const void *B, int64_t ldb,
+                                     double beta, const void *C, int64_t ldc, void *D, int64_t ldd,
+                                     const mmac_epilogue_t *ep_in, void *stream) {
+    const mmac_epilogue_t ep = epilogue_of(ep_in);
+    const mmac_status_t st = check_gemm(a_type, b_type, M, N, K, alpha, A, lda, K, B, ldb, beta, C, ldc, D, ldd, ep);
+    if (st != MMAC_OK) return st;
+    if (M == 0 || N == 0) return MMAC_OK;
+    const int64_t need = pick_shape(M, N) == TILE_SKINNY ? 0 : plan_split(a_type, M, N, K, false).bytes;
+    if (need > kScratchBytes) return MMAC_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (need > 0) {
+        hipError_t e;
+        ws = device_scratch(static_cast<hipStream_t>(stream), &e);
+        if (!ws) return MMAC_ERR_HIP;
+    }
+    return mmac_gemm_dense_ws(a_type, b_type, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd, ep_in, ws,
+                              ws ? kScratchBytes : 0, stream);
+}
 
 mmac_status_t mmac_gemm_dense_ws(mmac_dtype_t a_type, mmac_dtype_t b_type, int64_t M, int64_t N, int64_t K,
                                  double alpha, const void *A, int64_t lda, const void *B, int64_t ldb, double beta,
@@ -409,6 +481,8 @@ const char *mmac_status_string(mmac_status_t s) {
     case MMAC_ERR_UNSUPPORTED: return "MMAC_ERR_UNSUPPORTED: unsupported element types or sizes";
     case MMAC_ERR_MISALIGNED: return "MMAC_ERR_MISALIGNED: pointer or row pitch not aligned as required";
     case MMAC_ERR_HIP: return "MMAC_ERR_HIP: the HIP runtime refused the launch";
+    case MMAC_ERR_SCRATCH:
+        return "MMAC_ERR_SCRATCH: the split-K plan needs more than the library's fixed scratch array (8 MiB)";
     default: return "unknown mmac status";
     }
 }

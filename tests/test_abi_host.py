@@ -33,7 +33,7 @@ def L():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["mmac_gemm_dense", "mmac_gemm_dense_ep", "mmac_gemm_dense_layout",
-                                    "mmac_gemm_dense_mx",
+                                    "mmac_gemm_dense_mx", "mmac_gemm_dense_static",
                                     "mmac_gemm_dense_ws",
                                     "mmac_gemm_sparse24", "mmac_gemm_sparse24_ep", "mmac_gemm_sparse24_ws",
                                     "mmac_gemm_workspace_bytes", "mmac_sparse24_compress",
@@ -46,9 +46,9 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for s in range(5):
+    for s in range(6):
         assert mm.string(s).startswith(["MMAC_OK", "MMAC_ERR_INVALID_ARG", "MMAC_ERR_UNSUPPORTED",
-                                        "MMAC_ERR_MISALIGNED", "MMAC_ERR_HIP"][s])
+                                        "MMAC_ERR_MISALIGNED", "MMAC_ERR_HIP", "MMAC_ERR_SCRATCH"][s])
     assert mm.string(99) == "unknown mmac status"
 
 
@@ -397,3 +397,42 @@ def test_binding_checks_shapes_before_any_launch():
             mm.sparse24_compress(A16, Acx, idxx, badx)
         with pytest.raises(ValueError):
             mm.sparse24_prune_compress(A16, Acx, idxx, badx)
+
+
+def static_dense(L, **kw):
+    a = dict(a=mm.BF16, b=mm.BF16, M=64, N=64, K=64, alpha=1.0, A=P, lda=64, B=P, ldb=64, beta=0.0,
+             C=None, ldc=64, D=P, ldd=64, ep=None, stream=None)
+    a.update(kw)
+    return L.mmac_gemm_dense_static(a["a"], a["b"], a["M"], a["N"], a["K"], a["alpha"], a["A"], a["lda"], a["B"],
+                                    a["ldb"], a["beta"], a["C"], a["ldc"], a["D"], a["ldd"], a["ep"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(a=mm.BF16, b=mm.F16), mm.ERR_UNSUPPORTED),
+    (dict(M=-1), mm.ERR_INVALID_ARG),
+    (dict(A=None), mm.ERR_INVALID_ARG),
+    (dict(beta=1.0, C=None), mm.ERR_INVALID_ARG),
+    (dict(alpha=3.5e38), mm.ERR_INVALID_ARG),
+    (dict(lda=68), mm.ERR_MISALIGNED),
+    (dict(M=0), mm.OK),
+])
+def test_static_entry_validates_like_the_workspace_call(L, kw, code):
+    assert static_dense(L, **kw) == code
+
+
+def test_static_entry_rejects_plans_beyond_its_scratch(L, monkeypatch):
+    """A forced plan larger than the fixed array is refused before any GPU work (the pointers here
+    are fake, so a launch would fault); the library's own plans fit."""
+    monkeypatch.setenv("MMAC_TILE", "256")
+    monkeypatch.setenv("MMAC_SPLITK", "8")
+    M, N, K = 1024, 1024, 65536                   # 16 tiles x 8 ranges x 256 KiB > 8 MiB
+    assert mm.workspace_bytes(mm.BF16, M, N, K) > (8 << 20)
+    assert static_dense(L, M=M, N=N, K=K, lda=K, ldb=K, ldd=N) == mm.ERR_SCRATCH
+    monkeypatch.delenv("MMAC_TILE")
+    monkeypatch.delenv("MMAC_SPLITK")
+    worst = 0
+    for M, N, K in ((64, 64, 1 << 20), (512, 512, 32768), (1024, 1024, 65536), (2048, 512, 65536),
+                    (1000, 1000, 100000), (64, 8192, 65536)):
+        for t in (mm.BF16, mm.I8, mm.FP8_E4M3):
+            worst = max(worst, mm.workspace_bytes(t, M, N, K))
+    assert 0 < worst <= (8 << 20)
