@@ -8,10 +8,18 @@ One step is one pass of the whole path over one batch of synthetic input:
 The inputs are resident in HBM before timing starts.  `value` is the step's
 work (2*M*N*K per GEMM, dense-equivalent K for the sparse one) divided by the
 wall time of the step.  Each kernel is also timed with HIP events on the
-stream it runs on, and the slowest one is reported against its roofline.  The
-CPU oracle is timed on a bounded slice of the bf16 GEMM for scale.
+stream it runs on, and the slowest one is reported against its roofline: the
+published peak, and the sustained rate of its matrix instruction measured on
+this GPU by the rate microbenchmark (`matrix_rates`), with the shader clock
+amd-smi reports while that GEMM runs.  The CPU oracle is timed on a bounded
+slice of the bf16 GEMM (`cpu_baseline`).  `configs` gives every smaller
+workload at its full size -- 256^3 bf16, 1024^3 int8, 4096^3 bf16,
+16x4096x4096 bf16 and the 4:2 fp16 4096x4096x8192 compress + GEMM -- with its
+GPU time, a full comparison with the oracle, and the oracle's own wall time on
+the host cores (the first two also on one thread).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-check]
+                       [--no-configs] [--no-rates] [--suite]
 """
 import argparse
 import json
@@ -84,6 +92,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration section (GPU time, full oracle check and oracle time of "
+                         "the 256^3, 1024^3 int8, 4096^3, 16x4096x4096 and 4:2 fp16 workloads)")
+    ap.add_argument("--no-rates", action="store_true", help="skip the matrix-instruction rate microbenchmark")
     ap.add_argument("--cpu-rows", type=int, default=0, help="rows of the oracle slice (0 = calibrate)")
     ap.add_argument("--suite", action="store_true",
                     help="instead of the step, time every workload once (one JSON line with a 'suite' object)")
@@ -226,9 +238,30 @@ def main():
     if tr:
         roof["traffic_detail"] = tr
 
+    # the sustained rate of the dominant kernel's instruction, measured on this GPU, beside the published peak
+    rates = None
+    if not args.no_rates:
+        rates = matrix_rates()
+        key = {"dense_bf16": "bf16_mfma", "dense_fp8": "fp8_mfma", "sparse_fp8": "fp8_smfmac"}.get(dominant)
+        if key in rates:
+            sus = rates[key]["TFLOP/s"] / (2 if dominant == "sparse_fp8" else 1)
+            roof["sustained_peak"] = round(sus, 1)
+            roof["frac_of_sustained"] = round(roof["achieved"] / sus, 4)
+    roof["sclk_MHz"] = sample_sclk(lambda: mm.gemm_dense(Ab, Bb, Db, 1.0, 1.0, Cb, a_type=BF16, b_type=BF16,
+                                                         stream=stream))
+
     check = None
     if not args.no_check:
         check = spot_check(wb, w8, ws, Db, D8, Ds, Ac, idx, dev)
+    del Ab, Bb, Cb, A8, B8, As, Db, D8, Ds, Ac, idx
+    torch.cuda.empty_cache()
+    configs = None
+    if not args.no_configs:
+        configs = configs_report(dev, stream, cpu=not args.no_cpu_baseline)
+        for p in ("sparse_fp8", "dense_bf16", "dense_fp8", "compress_fp8"):
+            configs[{"sparse_fp8": "5s 8192^3 4:2 fp8xbf8 (in the step)", "dense_bf16": "H 8192^3 bf16 beta=1 (in the step)",
+                     "dense_fp8": "5d 8192^3 fp8xbf8 (in the step)",
+                     "compress_fp8": "5c 8192^2 fp8 4:2 compress (in the step)"}[p]] = report[p]
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -241,7 +274,8 @@ def main():
         "dtype": "bf16,fp8e4m3xbf8e5m2", "data": "synthetic",
         "config": {"workload": "8192^3: 4:2 compress fp8 A + sparse fp8xbf8 GEMM + dense bf16 GEMM "
                                "(beta=1) + dense fp8xbf8 GEMM, fp32 out", "M": M, "N": N, "K": K},
-        "parts": report, "roofline": roof, "cpu_baseline": cpu, "check": check,
+        "parts": report, "roofline": roof, "cpu_baseline": cpu, "check": check, "configs": configs,
+        "matrix_rates": rates,
     }
     print(json.dumps(line), flush=True)
 
@@ -463,6 +497,181 @@ def suite():
         torch.cuda.empty_cache()
     print(json.dumps({"suite": out, "note": "median of repeated single launches (HIP events); skinny GEMM and "
                       "compressors rotate through copies larger than the 256 MB Infinity Cache"}), flush=True)
+
+
+def matrix_rates():
+    """Sustained rate of the matrix instructions the GEMM kernels use, each issued back to back on
+    every compute unit for about 150 ms (libmmac_rate.so): the ceiling this GPU reaches at the clock
+    it holds, beside the published peaks."""
+    from sparse_matrix_multiply_amd import rate
+    out = {}
+    for key, instr, peak in (("bf16_mfma", rate.MFMA_BF16, PEAK_TFLOPS["bf16"]), ("fp8_mfma", rate.MFMA_FP8, PEAK_TFLOPS["fp8"]),
+                             ("i8_mfma", rate.MFMA_I8, PEAK_TFLOPS["int8"]),
+                             ("fp16_smfmac", rate.SMFMAC_F16, 2 * PEAK_TFLOPS["fp16"]),
+                             ("fp8_smfmac", rate.SMFMAC_FP8, 2 * PEAK_TFLOPS["fp8"])):
+        r = rate.measure(instr)
+        out[key] = {"instr": r["instr"], "TFLOP/s": round(r["TFLOP/s"], 1), "frac_published": round(r["TFLOP/s"] / peak, 4),
+                    "seconds": round(r["seconds"], 3)}
+    return out
+
+
+def sample_sclk(fn, seconds=1.5):
+    """Shader clock (MHz, mean over the XCDs) that amd-smi reports while `fn` runs back to back for
+    about `seconds`; None if amd-smi is not there or says nothing usable."""
+    import re
+    import shutil
+    import subprocess
+    import threading
+    import torch
+    tool = shutil.which("amd-smi")
+    if not tool:
+        return None
+    got = {}
+
+    def sample():
+        time.sleep(0.3 * seconds)
+        try:
+            r = subprocess.run([tool, "metric", "-g", "0", "-c"], capture_output=True, text=True, timeout=20)
+            got["text"] = r.stdout
+        except (OSError, subprocess.SubprocessError):
+            pass
+
+    th = threading.Thread(target=sample)
+    th.start()
+    t0 = time.perf_counter()
+    while th.is_alive() or time.perf_counter() - t0 < 0.5:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 > 30:
+            break
+    th.join()
+    clks = [int(m) for m in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", got.get("text", ""))]
+    return round(sum(clks) / len(clks)) if clks else None
+
+
+def configs_report(dev, stream, cpu=True):
+    """The smaller workloads at their full sizes: GPU time (mean of back-to-back launches between HIP
+    events on the launch stream; the HBM-bound ones rotate through copies larger than the 256 MB
+    Infinity Cache), a full comparison with the oracle, and the oracle's own wall time on the host's
+    cores (the 256^3 and 1024^3 int8 workloads also on one thread)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import sparse_matrix_multiply_amd as mm
+    import workloads as W
+
+    threads = oracle.num_threads()
+    U = 2.0 ** -24
+
+    def to_dev(bits, t):
+        if t == W.I8:
+            return torch.from_numpy(np.ascontiguousarray(bits)).to(dev)
+        host = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16 if bits.dtype == np.uint16 else np.int8))
+        return host.to(dev).view({W.BF16: torch.bfloat16, W.F16: torch.float16, W.E4M3: torch.float8_e4m3fn,
+                                  W.E5M2: torch.float8_e5m2}[t])
+
+    def mean_ms(fns, reps):
+        for f in fns[:2]:
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for r in range(reps):
+            fns[r % len(fns)]()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def timed_oracle(fn, one_thread=False):
+        if not cpu:
+            return None, None
+        t = time.perf_counter()
+        res = fn()
+        out = {"seconds": round(time.perf_counter() - t, 3), "threads": threads}
+        if one_thread:
+            oracle.set_num_threads(1)
+            t = time.perf_counter()
+            fn()
+            out["seconds_1_thread"] = round(time.perf_counter() - t, 3)
+            oracle.set_num_threads(threads)
+        return res, out
+
+    def gate(D, ref, S, K, alpha, beta, C):
+        """normwise and element-wise errors of the float gates (the parity tests' bound; no narrow
+        format here), and whether both pass."""
+        D, ref = np.asarray(D, np.float64), np.asarray(ref, np.float64)
+        scale = abs(alpha) * S + (abs(beta) * np.abs(C.astype(np.float64)) if beta != 0 else 0.0)
+        e = oracle.normwise_error(D, ref, S, alpha, beta, C if beta != 0 else None)
+        emax = float(np.max(np.abs(D - ref) / np.where(scale > 0, scale, 1.0)))
+        ok = e <= 8 * U * np.sqrt(K) and emax <= 2 * (K + 2) * U
+        return {"normwise": float(f"{e:.3e}"), "elementwise": float(f"{emax:.3e}"), "pass": bool(ok)}
+
+    out = {}
+    if cpu:
+        oracle.lib()
+    for name, key, reps, rot in (("bf16_256", "1 bf16 256^3", 200, 1), ("i8_1024", "2 int8 1024^3", 200, 1),
+                                 ("bf16_4096", "3a bf16 4096^3 beta=1", 20, 1),
+                                 ("bf16_skinny", "3b bf16 16x4096x4096 beta=1", 200, 16)):
+        w = W.workload(name)
+        M, N, K, ta = w["M"], w["N"], w["K"], w["ta"]
+        integer = ta == W.I8
+        A = to_dev(w["A"], ta)
+        Bs = [to_dev(w["B"], w["tb"])]
+        Bs += [Bs[0].clone() for _ in range(rot - 1)]
+        odt = torch.int32 if integer else torch.float32
+        C = torch.from_numpy(w["C"]).to(dev) if w["beta"] != 0 else None
+        Ds = [torch.empty((M, N), dtype=odt, device=dev) for _ in range(rot)]
+        fns = [lambda i=i: mm.gemm_dense(A, Bs[i], Ds[i], w["alpha"], w["beta"], C, a_type=ta, b_type=w["tb"],
+                                         stream=stream) for i in range(rot)]
+        ms = mean_ms(fns, reps)
+        torch.cuda.synchronize()
+        D = Ds[0].cpu().numpy()
+        byt = (M + N) * K * (2 if ta == W.BF16 else 1) + M * N * 4 * (2 if w["beta"] != 0 else 1)
+        r = {"shape": [M, N, K], "us": round(ms * 1e3, 2), ("TOP/s" if integer else "TFLOP/s"): round(gemm_flops(M, N, K) / ms / 1e9, 1),
+             "GB/s": round(byt / ms / 1e6, 1)}
+        if rot > 1:
+            r["rotated_copies"] = rot
+        res, r["oracle"] = timed_oracle(lambda: oracle.gemm_dense(ta, w["tb"], w["A"], w["B"], w["alpha"], w["beta"], w["C"]),
+                                        one_thread=name in ("bf16_256", "i8_1024"))
+        if res is not None:
+            ref, aux = res
+            r["check"] = {"bit_exact": bool(np.array_equal(D, ref))} if integer else gate(D, ref, aux, K, w["alpha"], w["beta"], w["C"])
+        out[key] = r
+        del A, Bs, C, Ds
+        torch.cuda.empty_cache()
+
+    # 4:2 fp16 4096 x 4096 x 8192: compression of the dense A (rotated), then the sparse GEMM
+    w = W.workload("f16_sparse")
+    M, N, K, ta = w["M"], w["N"], w["K"], w["ta"]
+    As = [to_dev(w["A"], ta)]
+    As += [As[0].clone() for _ in range(7)]
+    Acs = [torch.empty((M, K // 2), dtype=torch.float16, device=dev) for _ in range(8)]
+    idxs = [torch.empty((M, K // 32), dtype=torch.int32, device=dev) for _ in range(8)]
+    cms = mean_ms([lambda i=i: mm.sparse24_compress(As[i], Acs[i], idxs[i], a_type=ta, stream=stream) for i in range(8)], 40)
+    B = to_dev(w["B"], w["tb"])
+    D = torch.empty((M, N), dtype=torch.float32, device=dev)
+    gms = mean_ms([lambda: mm.gemm_sparse24(Acs[0], idxs[0], B, D, K=K, a_type=ta, b_type=w["tb"], stream=stream)], 20)
+    torch.cuda.synchronize()
+    cbytes = M * K * 2 + M * (K // 2) * 2 + M * (K // 32) * 4
+    r = {"shape": [M, N, K], "compress_us": round(cms * 1e3, 2), "compress_GB/s": round(cbytes / cms / 1e6, 1),
+         "gemm_us": round(gms * 1e3, 2), "TFLOP/s_dense_equivalent": round(gemm_flops(M, N, K) / gms / 1e9, 1),
+         "TFLOP/s_effective": round(gemm_flops(M, N, K) / 2 / gms / 1e9, 1)}
+    Acg = Acs[0].view(torch.int16).cpu().numpy().view(np.uint16)
+    idxg = idxs[0].cpu().numpy().view(np.uint32)
+    Dg = D.cpu().numpy()
+    res, r["oracle_compress"] = timed_oracle(lambda: oracle.compress24(ta, w["A"]))
+    if res is not None:
+        Ac_ref, idx_ref, _ = res
+        r["check_compress"] = {"bit_exact": bool(np.array_equal(Acg, Ac_ref) and np.array_equal(idxg, idx_ref))}
+        res, r["oracle"] = timed_oracle(lambda: oracle.gemm_sparse24(ta, w["tb"], Ac_ref, idx_ref, w["B"]))
+        ref, S = res
+        r["check"] = gate(Dg, ref, S, K, 1.0, 0.0, None)
+    out["4 fp16 4:2 4096x4096x8192"] = r
+    del As, Acs, idxs, B, D
+    torch.cuda.empty_cache()
+    return out
 
 
 def spot_check(wb, w8, ws, Db, D8, Ds, Ac, idx, dev):

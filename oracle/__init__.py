@@ -62,6 +62,8 @@ def lib():
         L.oracle_gemm_mx_f64_entries.argtypes = [ip, ip, i64, i64, i64, dbl, vp, i64, vp, i64, vp, i64, vp, i64,
                                                  dbl, vp, i64, i64, vp, vp, vp, vp]
         L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        L.oracle_set_num_threads.restype = None
         _lib = L
     return _lib
 
@@ -69,6 +71,11 @@ def lib():
 def num_threads():
     """Threads the oracle's OpenMP loops use."""
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n):
+    """Threads for later oracle calls (timing only: results do not depend on it)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def _p(a):

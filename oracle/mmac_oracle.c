@@ -719,3 +719,8 @@ int oracle_is_float_type(int t) { return is_float_type(t); }
 
 /* Number of threads the oracle's parallel loops use. */
 int oracle_num_threads(void) { return omp_get_max_threads(); }
+
+/* Set the thread count of later oracle calls (n >= 1); timing only, results do not depend on it. */
+void oracle_set_num_threads(int n) {
+    if (n >= 1) omp_set_num_threads(n);
+}

@@ -3,7 +3,8 @@
 Every HIP source (csrc/*.hip and the per-type-pair kernel instantiations in
 csrc/inst/*.hip) is compiled with hipcc for --offload-arch=gfx950 into
 sparse_matrix_multiply_amd/_build/, in parallel, then linked into
-sparse_matrix_multiply_amd/libmmac.so.  Usage: python -m sparse_matrix_multiply_amd.build
+sparse_matrix_multiply_amd/libmmac.so; the matrix-instruction rate
+microbenchmark (csrc/rate/) becomes libmmac_rate.so.  Usage: python -m sparse_matrix_multiply_amd.build
 """
 import concurrent.futures as cf
 import os
@@ -15,6 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmmac.so")
+RATE_LIB = os.path.join(HERE, "libmmac_rate.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -61,6 +63,15 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    # the matrix-instruction rate microbenchmark: a library of its own (measurement only)
+    rate_src = os.path.join(CSRC, "rate", "matrix_rate.hip")
+    cmd = [HIPCC] + FLAGS + ["-shared", rate_src, "-o", RATE_LIB + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {rate_src}:\n{r.stdout}")
+    os.replace(RATE_LIB + ".tmp", RATE_LIB)
     return LIB
 
 

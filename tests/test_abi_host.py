@@ -436,3 +436,26 @@ def test_static_entry_rejects_plans_beyond_its_scratch(L, monkeypatch):
         for t in (mm.BF16, mm.I8, mm.FP8_E4M3):
             worst = max(worst, mm.workspace_bytes(t, M, N, K))
     assert 0 < worst <= (8 << 20)
+
+
+def test_rate_library_exports_its_header():
+    """libmmac_rate.so (the matrix-instruction rate microbenchmark) exports what include/mmac_rate.h
+    declares, and its host-side queries answer without a GPU."""
+    import ctypes
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "mmac_rate.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(mmac_rate_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["mmac_rate_name", "mmac_rate_ops", "mmac_rate_run"]
+    from sparse_matrix_multiply_amd import rate
+    if not os.path.exists(rate.LIB_PATH):
+        from sparse_matrix_multiply_amd import build
+        build.build()
+    L = rate.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.mmac_rate_ops(rate.MFMA_BF16) == 2 * 32 * 32 * 16
+    assert L.mmac_rate_ops(rate.SMFMAC_FP8) == 2 * 32 * 32 * 64          # dense-equivalent K
+    assert L.mmac_rate_ops(99) == 0 and L.mmac_rate_name(99) is None
+    assert rate.name(rate.MFMA_FP8).startswith("v_mfma_scale_f32_32x32x64_f8f6f4")
+    # argument errors return before any launch (fake pointers)
+    assert L.mmac_rate_run(99, 1, 1, ctypes.c_void_p(P), ctypes.c_void_p(P), None) == -1
+    assert L.mmac_rate_run(0, 0, 1, ctypes.c_void_p(P), ctypes.c_void_p(P), None) == -1
