@@ -96,9 +96,14 @@ def parse():
                     help="skip the per-configuration section (GPU time, full oracle check and oracle time of "
                          "the 256^3, 1024^3 int8, 4096^3, 16x4096x4096 and 4:2 fp16 workloads)")
     ap.add_argument("--no-rates", action="store_true", help="skip the matrix-instruction rate microbenchmark")
+    ap.add_argument("--no-sclk", action="store_true", help="skip sampling the shader clock during the bf16 GEMM")
     ap.add_argument("--cpu-rows", type=int, default=0, help="rows of the oracle slice (0 = calibrate)")
     ap.add_argument("--suite", action="store_true",
                     help="instead of the step, time every workload once (one JSON line with a 'suite' object)")
+    ap.add_argument("--only", choices=["skinny", "compress_fp8", "rates"], default=None,
+                    help="only run one kernel --steps times after --warmup (for counter runs): the 16x4096x4096 "
+                         "bf16 skinny GEMM (beta = 1, B and D rotated through 16 copies past the Infinity Cache), "
+                         "the 8192^2 fp8 4:2 compressor (8 copies rotated), or the matrix-rate microbenchmark")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain elementwise copy of this many MiB (fp32) three times: the known-size "
                          "kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters")
@@ -123,6 +128,9 @@ def main():
         return
     if args.suite:
         suite()
+        return
+    if args.only:
+        only(args.only, args.steps, args.warmup)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -235,6 +243,9 @@ def main():
     roof["kernel"] = dominant
     tr = measured_traffic(dominant)
     roof["traffic"] = tr["bytes"] if tr else None
+    roof["traffic_kind"] = ("bytes the L2 caches read from and wrote to the memory fabric per launch (TCC FETCH_SIZE and "
+                            "WRITE_SIZE, calibrated on a 1 GiB copy); Infinity Cache hits are included: no counter on "
+                            "gfx950 separates HBM from Infinity Cache traffic")
     if tr:
         roof["traffic_detail"] = tr
 
@@ -247,8 +258,9 @@ def main():
             sus = rates[key]["TFLOP/s"] / (2 if dominant == "sparse_fp8" else 1)
             roof["sustained_peak"] = round(sus, 1)
             roof["frac_of_sustained"] = round(roof["achieved"] / sus, 4)
-    roof["sclk_MHz"] = sample_sclk(lambda: mm.gemm_dense(Ab, Bb, Db, 1.0, 1.0, Cb, a_type=BF16, b_type=BF16,
-                                                         stream=stream))
+    if not args.no_sclk:
+        roof["sclk_MHz"] = sample_sclk(lambda: mm.gemm_dense(Ab, Bb, Db, 1.0, 1.0, Cb, a_type=BF16, b_type=BF16,
+                                                             stream=stream))
 
     check = None
     if not args.no_check:
@@ -497,6 +509,58 @@ def suite():
         torch.cuda.empty_cache()
     print(json.dumps({"suite": out, "note": "median of repeated single launches (HIP events); skinny GEMM and "
                       "compressors rotate through copies larger than the 256 MB Infinity Cache"}), flush=True)
+
+
+def only(which, steps, warmup):
+    """One kernel by itself, for counter runs: mean time per launch of `steps` back-to-back launches
+    after `warmup` (HIP events on the launch stream), as one JSON line."""
+    import numpy as np
+    import torch
+
+    import sparse_matrix_multiply_amd as mm
+    import workloads as W
+    mm.lib()
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    if which == "rates":
+        print(json.dumps({"only": which, "matrix_rates": matrix_rates()}), flush=True)
+        return
+
+    def to_dev(bits, t):
+        host = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16 if bits.dtype == np.uint16 else np.int8))
+        return host.to(dev).view({W.BF16: torch.bfloat16, W.E4M3: torch.float8_e4m3fn}[t])
+
+    if which == "skinny":
+        w = W.workload("bf16_skinny")
+        M, N, K = w["M"], w["N"], w["K"]
+        A = to_dev(w["A"], W.BF16)
+        Bs = [to_dev(w["B"], W.BF16)]
+        Bs += [Bs[0].clone() for _ in range(15)]
+        C = torch.from_numpy(w["C"]).to(dev)
+        Ds = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in range(16)]
+        fns = [lambda i=i: mm.gemm_dense(A, Bs[i], Ds[i], 1.0, 1.0, C, stream=stream) for i in range(16)]
+        nbytes = (M + N) * K * 2 + 2 * M * N * 4
+    else:
+        w = W.workload("fp8_8192_sparse")
+        M, K = w["M"], w["K"]
+        As = [to_dev(w["A"], W.E4M3)]
+        As += [As[0].clone() for _ in range(7)]
+        Acs = [torch.empty((M, K // 2), dtype=torch.float8_e4m3fn, device=dev) for _ in range(8)]
+        idxs = [torch.empty((M, K // 32), dtype=torch.int32, device=dev) for _ in range(8)]
+        fns = [lambda i=i: mm.sparse24_compress(As[i], Acs[i], idxs[i], a_type=W.E4M3, stream=stream) for i in range(8)]
+        nbytes = M * K + M * (K // 2) + M * (K // 32) * 4
+    for r in range(warmup):
+        fns[r % len(fns)]()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for r in range(steps):
+        fns[r % len(fns)]()
+    e1.record(stream)
+    e1.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    print(json.dumps({"only": which, "launches": steps, "us": round(us, 2), "algorithmic_bytes": nbytes,
+                      "GB/s": round(nbytes / us / 1e3, 1)}), flush=True)
 
 
 def matrix_rates():
