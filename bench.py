@@ -59,21 +59,51 @@ _KNAME = {"dense_bf16": ("dense", "gemm_tiled_kernel<mmac::MmaDense16<2>, 256, 2
           "compress_fp8": ("compress", "compress_kernel<4, false>")}
 
 
+def _code_only(text):
+    """C/C++ source without its comments and with whitespace runs collapsed: what the compiler sees,
+    so that a change to a comment does not count as a change of the kernel."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
+def source_hash(files):
+    """First 16 hex digits of the SHA-256 of the files' code (comments and layout ignored)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(part):
     """HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE) recorded by the last counter runs,
     or None when the kernel's sources changed since (or nothing was recorded)."""
-    import hashlib
     kind, name = _KNAME[part]
     try:
         kernels = json.load(open(os.path.join(ROOT, "profiles", "traffic_8192.json")))["kernels"]
         rec = next(v for k, v in kernels.items() if k.startswith(name))
     except (OSError, KeyError, ValueError, StopIteration):
         return None
-    h = hashlib.sha256()
-    for f in _KSRC[kind]:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    if h.hexdigest()[:16] != rec["source_hash"]:
+    if source_hash(_KSRC[kind]) != rec["source_hash"]:
         return None
     return {"bytes": rec["fetch_bytes"] + rec["write_bytes"], "read_bytes": rec["fetch_bytes"],
             "write_bytes": rec["write_bytes"],

@@ -72,8 +72,8 @@ struct CompressParams {
 
 // Tile shapes the host can pick from.
 // 256 x 256 tiles run 8 waves (2 per SIMD, 128 x 64 each); 256 x 128 and
-// 128 x 256 tiles run 4 waves of 128 x 64 or 64 x 128 (one per SIMD); 128 and
-// 64 run 4 waves.
+// 128 x 256 tiles run 8 waves of 64 x 64 (2 per SIMD); 128 x 128 and 64 x 64
+// tiles run 4 waves (one per SIMD, 64 x 64 and 32 x 32 each).
 enum TileShape : int { TILE_256 = 0, TILE_128 = 1, TILE_64 = 2, TILE_SKINNY = 3, TILE_256x128 = 4, TILE_128x256 = 5 };
 
 // Launchers (defined in the kernel files).  `dt_a`/`dt_b` use the public

@@ -459,3 +459,12 @@ def test_rate_library_exports_its_header():
     # argument errors return before any launch (fake pointers)
     assert L.mmac_rate_run(99, 1, 1, ctypes.c_void_p(P), ctypes.c_void_p(P), None) == -1
     assert L.mmac_rate_run(0, 0, 1, ctypes.c_void_p(P), ctypes.c_void_p(P), None) == -1
+
+
+def test_kernel_source_hash_ignores_comments_only():
+    """The recorded counter traffic stays valid across comment edits and lapses on a code edit."""
+    import bench
+    code = 'int a = 1; // note\n/* block\n comment */ const char *s = "x // y /* z */";\nchar q = \'"\';  int  b;'
+    assert bench._code_only(code) == 'int a = 1; const char *s = "x // y /* z */"; char q = \'"\'; int b;'
+    assert bench._code_only(code) == bench._code_only(code.replace("// note", "// other words"))
+    assert bench._code_only(code) != bench._code_only(code.replace("int a = 1", "int a = 2"))
