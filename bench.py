@@ -371,7 +371,7 @@ def suite():
 
     out = {}
 
-    def dense_case(name, key, reps=20, rotate=1, n_share=None, bf16_out=False):
+    def dense_case(name, key, reps=20, rotate=1, n_share=None, bf16_out=False, graph=False):
         """n_share: keep only the first n_share columns of B, C and D (one GPU's share when N is
         split across GPUs).  bf16_out: the epilogue variant with bfloat16 C and D, a per-column
         bias and ReLU."""
@@ -388,9 +388,11 @@ def suite():
         act = mm.ACT_RELU if bf16_out else mm.ACT_NONE
         Ds = [torch.empty((w["M"], w["N"]), dtype=odt, device=dev) for _ in range(rotate)]
         Bs = [B] + [B.clone() for _ in range(rotate - 1)]
-        fns = [lambda i=i: mm.gemm_dense(A, Bs[i], Ds[i], w["alpha"], w["beta"], C, a_type=w["ta"], b_type=w["tb"],
-                                         stream=stream, bias=bias, act=act) for i in range(rotate)]
+        fns = [lambda s=stream, i=i: mm.gemm_dense(A, Bs[i], Ds[i], w["alpha"], w["beta"], C, a_type=w["ta"],
+                                                   b_type=w["tb"], stream=s, bias=bias, act=act)
+               for i in range(rotate)]
         ms = median_ms(fns, reps)
+        gms = graph_ms(fns, reps) if graph else None
         f = gemm_flops(w["M"], w["N"], w["K"])
         es = 2 if w["ta"] in (W.BF16, W.F16) else 1
         oes = 2 if bf16_out else 4
@@ -399,6 +401,8 @@ def suite():
                     ("TOP/s" if integer else "TFLOP/s"): round(f / ms / 1e9, 1),
                     "GB/s": round(byt / ms / 1e6, 1), "shape": [w["M"], w["N"], w["K"]], "alpha": w["alpha"],
                     "beta": w["beta"]}
+        if gms is not None:
+            out[key]["graph_us"] = round(gms * 1e3, 1)
         if bf16_out:
             out[key]["epilogue"] = "bf16 C/D, bias, ReLU"
         del A, B, Bs, C, Ds
@@ -412,10 +416,10 @@ def suite():
     out["reference_copy_32.6MiB"] = {"us": round(cms * 1e3, 1), "GB/s": round(2 * n * 4 / cms / 1e6, 1)}
     del srcs, dsts
 
-    dense_case("bf16_256", "bf16_256^3", reps=200)
-    dense_case("i8_1024", "int8_1024^3", reps=200)
+    dense_case("bf16_256", "bf16_256^3", reps=200, graph=True)
+    dense_case("i8_1024", "int8_1024^3", reps=200, graph=True)
     dense_case("bf16_4096", "bf16_4096^3_beta1")
-    dense_case("bf16_skinny", "bf16_16x4096x4096_beta1", reps=200, rotate=16)
+    dense_case("bf16_skinny", "bf16_16x4096x4096_beta1", reps=200, rotate=16, graph=True)
     dense_case("bf16_8192", "bf16_8192^3_beta1")
     dense_case("fp8_8192", "fp8e4m3xbf8e5m2_8192^3")
     # one GPU's share of the 8192^3 GEMMs split 8 ways along N
@@ -537,8 +541,11 @@ def suite():
 
         del As, Acs, idxs, B, D
         torch.cuda.empty_cache()
-    print(json.dumps({"suite": out, "note": "median of repeated single launches (HIP events); skinny GEMM and "
-                      "compressors rotate through copies larger than the 256 MB Infinity Cache"}), flush=True)
+    print(json.dumps({"suite": out, "note": "us: mean of back-to-back launches issued from Python (HIP events on "
+                      "the launch stream); single_launch_us: median of single launches, each between events; "
+                      "graph_us: back-to-back launches replayed from a HIP graph (no host cost per call); the "
+                      "skinny GEMM and the compressors rotate through copies larger than the 256 MB Infinity "
+                      "Cache"}), flush=True)
 
 
 def only(which, steps, warmup):
@@ -644,11 +651,35 @@ def sample_sclk(fn, seconds=1.5):
     return round(sum(clks) / len(clks)) if clks else None
 
 
+def graph_ms(fns, reps):
+    """Mean time of one launch when `reps` calls (the fns round-robin; each takes the stream to launch
+    on) are captured in one HIP graph and the graph is replayed: the GPU's back-to-back time without
+    the host's cost per call, which for a small GEMM is as long as the kernel itself.  Median of
+    three timed replays after one untimed one."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = torch.cuda.current_stream()
+        for r in range(reps):
+            fns[r % len(fns)](cap)
+    times = []
+    for _ in range(4):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) / reps)
+    del g
+    return sorted(times[1:])[1]
+
+
 def configs_report(dev, stream, cpu=True):
-    """The smaller workloads at their full sizes: GPU time (mean of back-to-back launches between HIP
-    events on the launch stream; the HBM-bound ones rotate through copies larger than the 256 MB
-    Infinity Cache), a full comparison with the oracle, and the oracle's own wall time on the host's
-    cores (the 256^3 and 1024^3 int8 workloads also on one thread)."""
+    """The smaller workloads at their full sizes: GPU time ("us": back-to-back launches replayed from
+    a HIP graph; "us_eager": the same launches issued one by one from Python, between HIP events on
+    the launch stream; the HBM-bound ones rotate through copies larger than the 256 MB Infinity
+    Cache), a full comparison with the oracle, and the oracle's own wall time on the host's cores
+    (the 256^3 and 1024^3 int8 workloads also on one thread)."""
     import numpy as np
     import torch
 
@@ -717,14 +748,17 @@ def configs_report(dev, stream, cpu=True):
         odt = torch.int32 if integer else torch.float32
         C = torch.from_numpy(w["C"]).to(dev) if w["beta"] != 0 else None
         Ds = [torch.empty((M, N), dtype=odt, device=dev) for _ in range(rot)]
-        fns = [lambda i=i: mm.gemm_dense(A, Bs[i], Ds[i], w["alpha"], w["beta"], C, a_type=ta, b_type=w["tb"],
-                                         stream=stream) for i in range(rot)]
-        ms = mean_ms(fns, reps)
+        fns = [lambda s=stream, i=i: mm.gemm_dense(A, Bs[i], Ds[i], w["alpha"], w["beta"], C, a_type=ta,
+                                                   b_type=w["tb"], stream=s) for i in range(rot)]
+        eager = mean_ms(fns, reps)
         torch.cuda.synchronize()
         D = Ds[0].cpu().numpy()
+        ms = graph_ms(fns, reps)
+        replay_same = bool(np.array_equal(Ds[0].cpu().numpy(), D))
         byt = (M + N) * K * (2 if ta == W.BF16 else 1) + M * N * 4 * (2 if w["beta"] != 0 else 1)
-        r = {"shape": [M, N, K], "us": round(ms * 1e3, 2), ("TOP/s" if integer else "TFLOP/s"): round(gemm_flops(M, N, K) / ms / 1e9, 1),
-             "GB/s": round(byt / ms / 1e6, 1)}
+        r = {"shape": [M, N, K], "us": round(ms * 1e3, 2), "us_eager": round(eager * 1e3, 2),
+             ("TOP/s" if integer else "TFLOP/s"): round(gemm_flops(M, N, K) / ms / 1e9, 1),
+             "GB/s": round(byt / ms / 1e6, 1), "graph_replay_matches_eager": replay_same}
         if rot > 1:
             r["rotated_copies"] = rot
         res, r["oracle"] = timed_oracle(lambda: oracle.gemm_dense(ta, w["tb"], w["A"], w["B"], w["alpha"], w["beta"], w["C"]),

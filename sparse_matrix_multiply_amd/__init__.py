@@ -106,11 +106,12 @@ def _ptr(t):
 def _ld(t):
     """Row pitch (elements) of a 2-D tensor whose last dimension is contiguous and whose rows do not
     overlap (a broadcast or overlapping view would make the kernels write past or over its rows)."""
-    if t.dim() != 2 or (t.stride(1) != 1 and t.shape[1] > 1):
+    st, sh = t.stride(), t.shape
+    if len(sh) != 2 or (st[1] != 1 and sh[1] > 1):
         raise ValueError("expected a 2-D tensor with a contiguous last dimension")
-    if t.shape[0] > 1 and t.stride(0) < t.shape[1]:
-        raise ValueError(f"rows of a {tuple(t.shape)} tensor with row stride {t.stride(0)} overlap")
-    return max(t.stride(0), t.shape[1], 1)
+    if sh[0] > 1 and st[0] < sh[1]:
+        raise ValueError(f"rows of a {tuple(sh)} tensor with row stride {st[0]} overlap")
+    return max(st[0], sh[1], 1)
 
 
 def _shape(t, rows, cols, name, min_cols=False):
@@ -137,8 +138,15 @@ def _bias(bias, N):
         raise ValueError(f"bias must be a contiguous float32 vector of at least N = {N} values")
 
 
+# The current stream's handle without building a Stream object (a few microseconds per call, which
+# is as long as a small GEMM): torch's own accessor where it has one.
+_raw_current_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream):
     if stream is None:
+        if _raw_current_stream is not None:
+            return ctypes.c_void_p(_raw_current_stream(torch.cuda.current_device()))
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
 

@@ -90,14 +90,73 @@ __device__ __forceinline__ void load_frag16(typename Op::frag_t &f, rsrc_t r, ui
     }
 }
 
-// MB row blocks of 16 (M <= 16*MB), CB column blocks of 16 per workgroup, WK waves along K,
-// U instruction steps per batch of loads.
-template <class Op, int MB, int CB, int WK, int U>
+// s_waitcnt on gfx9: vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt
+// [11:8].  Waits until at most VM vector-memory instructions of this wave are
+// outstanding and every LDS access has completed.
+template <int VM>
+__device__ __forceinline__ void skinny_wait() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));
+    asm volatile("" ::: "memory");
+}
+// The same with the count n (0 <= n <= MAXN, in units of PER instructions) known only at run time.
+template <int PER, int MAXN>
+__device__ __forceinline__ void skinny_wait_n(int n) {
+    if constexpr (MAXN <= 0) {
+        skinny_wait<0>();
+    } else {
+        if (n >= MAXN) skinny_wait<MAXN * PER>();
+        else skinny_wait_n<PER, MAXN - 1>(n);
+    }
+}
+
+// Every LDS access of this wave has completed (outstanding memory loads may remain).
+__device__ __forceinline__ void skinny_wait_lds() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+    asm volatile("" ::: "memory");
+}
+
+// 16-byte unit u of row r of a 16-row block sits at unit u ^ ((r / 2) mod 8) of
+// its 128-byte LDS row: the 16 lanes that read one unit of all 16 rows then
+// meet 16 different 16-byte bank groups.
+__device__ __forceinline__ int skinny_swz(int r) { return (r >> 1) & 7; }
+
+// MB row blocks of 16 (M <= 16*MB), CB column blocks of 16 per workgroup, WK
+// waves along K, NSLOT chunks of loads in flight per wave.
+//
+// The rows of A and B are read in chunks of 128 bytes, one cache line per row
+// (64 16-bit or 128 8-bit elements: two instruction steps, or one for fp8).
+// A copy instruction moves 8 rows x 128 bytes straight into LDS (lane l: row
+// l/8, unit l mod 8), so every line is requested once.  Loaded into registers
+// in the instructions' own fragment layout (16 rows x 4 lanes of 16 bytes)
+// each line would be requested twice, half of it each time, and that request
+// rate, not HBM, would set the time.  Each wave streams its own contiguous
+// range of whole chunks through a private ring of NSLOT LDS slots and reads its
+// fragments back from there (no barrier: a wave reads only what it copied); the
+// chunk that K ends inside goes through registers, with the elements past K
+// set to zero.  Lane (r, q) = (lane mod 16, lane / 16) takes unit 4v + q of a
+// chunk in step v (16-byte fragments) or units 2q, 2q+1 (fp8's 32-byte ones):
+// the K order of the plain register loads.
+template <class Op, int MB, int CB, int WK, int NSLOT>
 __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(GemmParams p) {
     typedef typename Op::acc_t acc_t;
     typedef typename Op::out_t out_t;
     typedef typename Op::frag_t frag_t;
-    constexpr int KS = Op::kKStep;
+    constexpr int KS = Op::kKStep, ES = Op::kEsize;
+    constexpr int CE = 128 / ES;                  // K elements per chunk
+    constexpr int SPC = CE / KS;                  // instruction steps per chunk
+    constexpr int BLOCKS = MB + CB;               // 16-row blocks per chunk: B's first, then A's
+    constexpr int IPC = 2 * BLOCKS;               // copy instructions per chunk (8 rows each)
+    constexpr int SLOT = BLOCKS * 16 * 128;       // bytes of one chunk in LDS
+    constexpr int RED = WK * MB * CB * 4 * 64 * 4;
+    constexpr int LDS_BYTES = WK * NSLOT * SLOT > RED ? WK * NSLOT * SLOT : RED;
+    static_assert(SPC >= 1 && SPC * KS == CE, "whole steps per chunk");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r16 = lane & 15, q = lane >> 4;
     const int col0 = blockIdx.x * 16 * CB;
     const int bcols = min(16 * CB, p.N - col0);
@@ -133,48 +192,102 @@ __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(GemmParams p) {
                                              make_rsrc(p.bias + col0, (uint32_t)(bcols * 4)),
                                              oin ? (uint32_t)(ocol - col0) * 4 : kOutOfRange, 0, 0));
 
-    // contiguous range of K steps for this wave
-    const int nsteps = (p.K + KS - 1) / KS;
-    const int per_wave = (nsteps + WK - 1) / WK;
-    const int s0 = wave * per_wave, s1 = min(s0 + per_wave, nsteps);
-
     acc_t acc[MB][CB];
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
         for (int c = 0; c < CB; ++c) acc[m][c] = acc_t{};
 
-    uint32_t aoff[MB], boff[CB];
-#pragma unroll
-    for (int m = 0; m < MB; ++m) aoff[m] = (uint32_t)(m * 16 + r16) * (uint32_t)p.a_pitch;
-#pragma unroll
-    for (int c = 0; c < CB; ++c) boff[c] = (uint32_t)(c * 16 + r16) * (uint32_t)p.b_pitch;
+    // whole chunks: a contiguous range per wave
+    const int nfull = p.K / CE;
+    const int per = (nfull + WK - 1) / WK;
+    const int c0 = min(wave * per, nfull), c1 = min(c0 + per, nfull);
+    uint8_t *ring = smem + wave * NSLOT * SLOT;
 
-    for (int s = s0; s < s1; s += U) {
-        frag_t a[U][MB], b[U][CB];
+    // copy instruction j of chunk c into slot `slot`: block j / 2 (B's blocks, then A's),
+    // rows 8 (j mod 2) .. + 7 of it; rows past M or N read as zero (offsets past the buffer)
+    auto issue = [&](int c, int slot) {
+        const int r = lane >> 3;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int k0 = (s + u < s1) ? (s + u) * KS : p.K;   // past this wave's range: all zero
-#pragma unroll
-            for (int c = 0; c < CB; ++c) load_frag16<Op>(b[u][c], rb, boff[c], k0, p.K, q);
+        for (int j = 0; j < IPC; ++j) {
+            const int blk = j >> 1, row = 8 * (j & 1) + r;
+            const uint32_t unit = (uint32_t)((lane & 7) ^ skinny_swz(row));
+            const uint32_t kb = (uint32_t)c * 128u + unit * 16u;
+            uint8_t *dst = ring + slot * SLOT + j * 1024;
+            if (blk < CB)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rb, (lds_void *)dst, 16, (uint32_t)(blk * 16 + row) * (uint32_t)p.b_pitch + kb, 0, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    ra, (lds_void *)dst, 16, (uint32_t)((blk - CB) * 16 + row) * (uint32_t)p.a_pitch + kb, 0, 0,
+                    0);
         }
-        // A after B: B streams from HBM (long latency), A comes from L2
+    };
+    // unit u of row r16 of block blk in slot `slot`
+    auto unit_at = [&](int slot, int blk, int u) -> i32x4 {
+        return *reinterpret_cast<const i32x4 *>(ring + slot * SLOT + blk * 2048 + r16 * 128 +
+                                               ((u ^ skinny_swz(r16)) << 4));
+    };
+
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int k0 = (s + u < s1) ? (s + u) * KS : p.K;
+    for (int i = 0; i < NSLOT; ++i)
+        if (c0 + i < c1) issue(c0 + i, i);
+    for (int c = c0; c < c1; ++c) {
+        const int slot = (c - c0) % NSLOT;
+        // chunk c has landed once at most the chunks issued after it are outstanding
+        skinny_wait_n<IPC, NSLOT - 1>(min(NSLOT - 1, c1 - 1 - c));
+        frag_t a[SPC][MB], b[SPC][CB];
 #pragma unroll
-            for (int m = 0; m < MB; ++m) load_frag16<Op>(a[u][m], ra, aoff[m], k0, p.K, q);
+        for (int v = 0; v < SPC; ++v) {
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                if constexpr (Op::kFrag == 16) b[v][cb] = unit_at(slot, cb, 4 * v + q);
+                else { b[v][cb].lo = unit_at(slot, cb, 2 * q); b[v][cb].hi = unit_at(slot, cb, 2 * q + 1); }
+            }
+#pragma unroll
+            for (int m = 0; m < MB; ++m) {
+                if constexpr (Op::kFrag == 16) a[v][m] = unit_at(slot, CB + m, 4 * v + q);
+                else { a[v][m].lo = unit_at(slot, CB + m, 2 * q); a[v][m].hi = unit_at(slot, CB + m, 2 * q + 1); }
+            }
         }
+        skinny_wait_lds();   // the slot's reads are done before new data is copied into it
+        if (c + NSLOT < c1) issue(c + NSLOT, slot);
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int v = 0; v < SPC; ++v)
 #pragma unroll
             for (int m = 0; m < MB; ++m)
 #pragma unroll
-                for (int c = 0; c < CB; ++c) acc[m][c] = Op::mma(a[u][m], b[u][c], acc[m][c]);
+                for (int cb = 0; cb < CB; ++cb) acc[m][cb] = Op::mma(a[v][m], b[v][cb], acc[m][cb]);
+    }
+
+    // the chunk K ends inside (if any): the last wave, through registers, elements past K zero
+    if (wave == WK - 1 && nfull * CE < p.K) {
+        uint32_t aoff[MB], boff[CB];
+#pragma unroll
+        for (int m = 0; m < MB; ++m) aoff[m] = (uint32_t)(m * 16 + r16) * (uint32_t)p.a_pitch;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) boff[cb] = (uint32_t)(cb * 16 + r16) * (uint32_t)p.b_pitch;
+#pragma unroll
+        for (int v = 0; v < SPC; ++v) {
+            const int k0 = nfull * CE + v * KS;
+            if (k0 < p.K) {
+                frag_t a[MB], b[CB];
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) load_frag16<Op>(b[cb], rb, boff[cb], k0, p.K, q);
+#pragma unroll
+                for (int m = 0; m < MB; ++m) load_frag16<Op>(a[m], ra, aoff[m], k0, p.K, q);
+#pragma unroll
+                for (int m = 0; m < MB; ++m)
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) acc[m][cb] = Op::mma(a[m], b[cb], acc[m][cb]);
+            }
+        }
     }
 
     // combine the WK partial tiles in LDS, in wave order; each thread then owns one output
-    __shared__ out_t red[WK][MB][CB][4][64];
+    // (in the LDS of the chunk rings, once every wave is done with its ring)
+    __syncthreads();
+    out_t(*red)[MB][CB][4][64] = reinterpret_cast<out_t(*)[MB][CB][4][64]>(smem);
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
@@ -223,10 +336,11 @@ __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(GemmParams p) {
 template <int DA, int DB>
 static hipError_t launch_types(const GemmParams &p, hipStream_t s) {
     typedef Mma16<DA, DB> Op;
-    constexpr int CB = 1, WK = 8, U = 8;   // 8 waves x 8 steps of loads in flight per workgroup
+    // 8 waves, each with 4 chunks (16 KiB) of copies in flight; 3 chunks (18 KiB) when A has 32 rows
+    constexpr int CB = 1, WK = 8;
     const dim3 grid((p.N + 16 * CB - 1) / (16 * CB)), block(WK * 64);
-    if (p.M <= 16) hipLaunchKernelGGL((gemm_skinny_kernel<Op, 1, CB, WK, U>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((gemm_skinny_kernel<Op, 2, CB, WK, U>), grid, block, 0, s, p);
+    if (p.M <= 16) hipLaunchKernelGGL((gemm_skinny_kernel<Op, 1, CB, WK, 4>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((gemm_skinny_kernel<Op, 2, CB, WK, 3>), grid, block, 0, s, p);
     return hipGetLastError();
 }
 

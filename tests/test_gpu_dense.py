@@ -145,9 +145,12 @@ def test_deterministic(ta, tb):
 
 
 @pytest.mark.parametrize("ta,tb", PAIRS)
-@pytest.mark.parametrize("M,N,K", [(1, 64, 64), (5, 100, 333), (16, 130, 1000), (17, 77, 200), (32, 300, 4100)])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 64), (5, 100, 333), (16, 130, 1000), (17, 77, 200), (32, 300, 4100),
+                                   (7, 40, 8192), (32, 33, 2176)])
 def test_skinny_path_matches_oracle(ta, tb, M, N, K):
-    """M <= 32 runs the skinny kernel (B streamed once, split K, fixed-order reduction)."""
+    """M <= 32 runs the skinny kernel (B streamed once, split K, fixed-order reduction).  The shapes
+    cover K below one 128-byte chunk, a ragged last chunk, chunk counts below and far above the
+    wave count (each wave's LDS ring wrapping many times), 32-row A and ragged N."""
     A, B, C, alpha, beta = inputs(ta, tb, M, N, K, M * 5 + N + K + ta + tb)
     with tile_shape(16):
         D = run_dense(ta, tb, A, B, alpha, beta, C)
