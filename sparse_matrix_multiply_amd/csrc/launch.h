@@ -30,8 +30,9 @@ struct GemmParams {
     int ialpha, ibeta;
     int use_c;       // beta != 0
     // fold_c: the accumulator starts as c_scale * C and the epilogue only
-    // scales by alpha (float: c_scale = beta / alpha, alpha != 0; int32:
-    // alpha == 1 and c_scale = beta, exact modulo 2^32).
+    // scales by alpha (float: c_scale = 1 when alpha == beta, c_scale = beta
+    // when alpha == 1; int32: alpha == 1 and c_scale = beta, exact modulo
+    // 2^32).  Other pairs read C in the epilogue.
     int fold_c;
     float c_scale;
     // vec_d: D starts on a 16-byte boundary and its row pitch is a multiple of
