@@ -415,6 +415,13 @@ def suite():
     cms = median_ms([lambda i=i: dsts[i].copy_(srcs[i]) for i in range(16)], 200)
     out["reference_copy_32.6MiB"] = {"us": round(cms * 1e3, 1), "GB/s": round(2 * n * 4 / cms / 1e6, 1)}
     del srcs, dsts
+    # and of the 8192^2 fp8 compressor's bytes (64 MiB read, 40 MiB written: 52 MiB copied), 8 copies
+    n = (64 + 40) * 2 ** 20 // 2 // 4
+    srcs = [torch.ones(n, dtype=torch.float32, device=dev) for _ in range(8)]
+    dsts = [torch.empty_like(x) for x in srcs]
+    cms = median_ms([lambda i=i: dsts[i].copy_(srcs[i]) for i in range(8)], 80)
+    out["reference_copy_52MiB"] = {"us": round(cms * 1e3, 1), "GB/s": round(2 * n * 4 / cms / 1e6, 1)}
+    del srcs, dsts
 
     dense_case("bf16_256", "bf16_256^3", reps=200, graph=True)
     dense_case("i8_1024", "int8_1024^3", reps=200, graph=True)
