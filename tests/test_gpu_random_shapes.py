@@ -1,5 +1,5 @@
-"""Randomised shapes against the CPU oracle: dense and 4:2-sparse GEMMs, the operand-layout
-variants and the block-scaled GEMMs, with sizes drawn
+"""Randomised shapes against the CPU oracle: dense and 4:2-sparse GEMMs, the skinny (M <= 32)
+path, the operand-layout variants and the block-scaled GEMMs, with sizes drawn
 from a fixed seed (1..700 rows/columns, K from 1 (dense) or 4 (sparse) to 1200), every
 element-type pair, the library's own tile choice, random alpha/beta (beta = 0 included,
 int8 with integer alpha/beta) and, for some draws, padded row pitches.  The draws are
@@ -67,6 +67,27 @@ def test_random_dense(case):
     torch.cuda.synchronize()
     Dref, aux = oracle.gemm_dense(ta, tb, A, B, alpha, beta, C)
     check(D.cpu().numpy(), Dref, aux, ta, K, alpha, beta, C, f"dense case {case}: {ta},{tb} {M}x{N}x{K} "
+          f"alpha {alpha} beta {beta} pad {pad}")
+
+
+@pytest.mark.parametrize("case", range(28))
+def test_random_skinny(case):
+    """M <= 32 (the skinny kernel: whole-line copies into per-wave LDS rings, a masked last
+    chunk): random M 1..32, N 1..700, K 1..5000 (so 0 to 78 whole 128-byte chunks per row),
+    padded pitches, every pair."""
+    g, ta, tb, _, N, _, alpha, beta, pad = draw(case + 100, False)
+    M = int(g.integers(1, 33))
+    K = int(g.integers(1, 5001))
+    A, B, C = host_inputs(g, ta, tb, M, N, K, False)
+    es = 2 if ta in (F16, BF16) else 1
+    Ad = to_dev_bits(A, ta, padded(K, ta) + pad * (16 // es) // 4 * 4 if pad else None)
+    Bd = to_dev_bits(B, tb, padded(K, tb) + pad * (16 // es) // 4 * 4 if pad else None)
+    D = out_tensor(M, N, ta == I8, N + pad if pad else None)
+    Cd = torch.from_numpy(C).to(dev()) if beta != 0 else None
+    mm.gemm_dense(Ad, Bd, D, alpha, beta, Cd, a_type=ta, b_type=tb)
+    torch.cuda.synchronize()
+    Dref, aux = oracle.gemm_dense(ta, tb, A, B, alpha, beta, C)
+    check(D.cpu().numpy(), Dref, aux, ta, K, alpha, beta, C, f"skinny case {case}: {ta},{tb} {M}x{N}x{K} "
           f"alpha {alpha} beta {beta} pad {pad}")
 
 
