@@ -685,9 +685,11 @@ def configs_report(dev, stream, cpu=True):
     """The smaller workloads at their full sizes: GPU time per launch of back-to-back launches, timed
     two ways ("us_graph": replayed from a HIP graph; "us_eager": issued one by one from Python, which
     for the smallest kernels takes longer than the kernel; HIP events on the launch stream; "us" is
-    the lower; the HBM-bound ones rotate through copies larger than the 256 MB Infinity Cache), a
-    full comparison with the oracle, and the oracle's own wall time on the host's cores (the 256^3
-    and 1024^3 int8 workloads also on one thread)."""
+    the lower; "us_single_median" / "us_single_min": launches one at a time, each between its own
+    events; the HBM-bound ones rotate through copies larger than the 256 MB Infinity Cache, and
+    "us_warm" repeats one copy, resident in that cache), a full comparison with the oracle, and the
+    oracle's own wall time on the host's cores (the 256^3 and 1024^3 int8 workloads also on one
+    thread)."""
     import numpy as np
     import torch
 
@@ -716,6 +718,19 @@ def configs_report(dev, stream, cpu=True):
         e1.record(stream)
         e1.synchronize()
         return e0.elapsed_time(e1) / reps
+
+    def single_ms(fns, reps):
+        """(median, min) of single launches, each between its own pair of HIP events."""
+        times = []
+        for r in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fns[r % len(fns)]()
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        times.sort()
+        return times[len(times) // 2], times[0]
 
     def timed_oracle(fn, one_thread=False):
         if not cpu:
@@ -765,12 +780,18 @@ def configs_report(dev, stream, cpu=True):
         replay_same = bool(np.array_equal(Ds[0].cpu().numpy(), D))
         ms = min(graph, eager)
         byt = (M + N) * K * (2 if ta == W.BF16 else 1) + M * N * 4 * (2 if w["beta"] != 0 else 1)
+        med, mn = single_ms(fns, reps)
         r = {"shape": [M, N, K], "us": round(ms * 1e3, 2), "us_graph": round(graph * 1e3, 2),
-             "us_eager": round(eager * 1e3, 2),
+             "us_eager": round(eager * 1e3, 2), "us_single_median": round(med * 1e3, 2),
+             "us_single_min": round(mn * 1e3, 2),
              ("TOP/s" if integer else "TFLOP/s"): round(gemm_flops(M, N, K) / ms / 1e9, 1),
              "GB/s": round(byt / ms / 1e6, 1), "graph_replay_matches_eager": replay_same}
         if rot > 1:
+            # the same launches without rotation: B stays resident in the 256 MB Infinity Cache
             r["rotated_copies"] = rot
+            warm = mean_ms(fns[:1], reps)
+            r["us_warm"] = round(warm * 1e3, 2)
+            r["GB/s_warm"] = round(byt / warm / 1e6, 1)
         res, r["oracle"] = timed_oracle(lambda: oracle.gemm_dense(ta, w["tb"], w["A"], w["B"], w["alpha"], w["beta"], w["C"]),
                                         one_thread=name in ("bf16_256", "i8_1024"))
         if res is not None:
@@ -787,13 +808,16 @@ def configs_report(dev, stream, cpu=True):
     As += [As[0].clone() for _ in range(7)]
     Acs = [torch.empty((M, K // 2), dtype=torch.float16, device=dev) for _ in range(8)]
     idxs = [torch.empty((M, K // 32), dtype=torch.int32, device=dev) for _ in range(8)]
-    cms = mean_ms([lambda i=i: mm.sparse24_compress(As[i], Acs[i], idxs[i], a_type=ta, stream=stream) for i in range(8)], 40)
+    cfns = [lambda i=i: mm.sparse24_compress(As[i], Acs[i], idxs[i], a_type=ta, stream=stream) for i in range(8)]
+    cms = mean_ms(cfns, 40)
+    cwarm = mean_ms(cfns[:1], 40)
     B = to_dev(w["B"], w["tb"])
     D = torch.empty((M, N), dtype=torch.float32, device=dev)
     gms = mean_ms([lambda: mm.gemm_sparse24(Acs[0], idxs[0], B, D, K=K, a_type=ta, b_type=w["tb"], stream=stream)], 20)
     torch.cuda.synchronize()
     cbytes = M * K * 2 + M * (K // 2) * 2 + M * (K // 32) * 4
     r = {"shape": [M, N, K], "compress_us": round(cms * 1e3, 2), "compress_GB/s": round(cbytes / cms / 1e6, 1),
+         "compress_us_warm": round(cwarm * 1e3, 2), "compress_GB/s_warm": round(cbytes / cwarm / 1e6, 1),
          "gemm_us": round(gms * 1e3, 2), "TFLOP/s_dense_equivalent": round(gemm_flops(M, N, K) / gms / 1e9, 1),
          "TFLOP/s_effective": round(gemm_flops(M, N, K) / 2 / gms / 1e9, 1)}
     Acg = Acs[0].view(torch.int16).cpu().numpy().view(np.uint16)
