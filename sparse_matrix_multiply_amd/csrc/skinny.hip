@@ -3,10 +3,10 @@
 // With at most 32 rows of A the product does 2*M flops per byte of B, far
 // below the chip's flop/byte ridge, so the time is set by reading B from HBM.
 // Each workgroup owns 16*CB columns of D and all M rows; its WK waves split K
-// (a fixed, contiguous range each), read their A and B fragments straight
-// from memory into registers with 128-bit buffer loads (B exactly once, A from
-// L2), run 16 x 16 matrix instructions, and combine their partial tiles in LDS
-// in a fixed wave order, so the result does not depend on timing.
+// (a fixed, contiguous range each), copy their rows of B (read exactly once)
+// and A (from L2) into LDS a whole cache line at a time, run 16 x 16 matrix
+// instructions on fragments read back from LDS, and combine their partial
+// tiles in LDS in a fixed wave order, so the result does not depend on timing.
 //
 // The 16 x 16 accumulator follows the one-block 16x16 layout of "CDNA dense
 // MFMA builtins", "Accumulator layout": element (i, j) is register i mod 4 of
@@ -76,6 +76,9 @@ __device__ __forceinline__ i32x4 load_unit(rsrc_t r, uint32_t off, int e0, int l
     return i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
 }
 
+// The fragment of one K step (starting at element k0) of the row at row_off,
+// straight into registers, elements past K zero: the masked path for the
+// chunk that K ends inside.
 template <class Op>
 __device__ __forceinline__ void load_frag16(typename Op::frag_t &f, rsrc_t r, uint32_t row_off, int k0, int K,
                                             int q) {
