@@ -371,7 +371,14 @@ def suite():
 
     batch = []
 
-    out = {}
+    class Progress(dict):
+        """The results, with a progress line on stderr as each one comes in (long suite runs under
+        a profiler stay visibly alive)."""
+        def __setitem__(self, k, v):
+            super().__setitem__(k, v)
+            print(f"# suite: {k}", file=sys.stderr, flush=True)
+
+    out = Progress()
 
     def dense_case(name, key, reps=20, rotate=1, n_share=None, bf16_out=False, graph=False):
         """n_share: keep only the first n_share columns of B, C and D (one GPU's share when N is
