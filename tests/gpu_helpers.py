@@ -170,6 +170,10 @@ def compress_dev(t, Ad, M, K, prune=False):
     return Ac, idx, bad
 
 
+# Random output entries a full-size sampled check compares beside its whole tiles.
+SAMPLED_ENTRIES = 65536
+
+
 def sample_entries(M, N, n, seed, tiles=((0, 0),), tile=256):
     """Output positions for sampled checks: whole tile x tile blocks at the given tile
     coordinates (every lane / register / wave position) plus n random entries."""

@@ -4,7 +4,7 @@ The pages' operation is an accumulation over K in panels, the caller looping
 over K ("CDNA dense MFMA builtins", section "Naming convention"); the mistake
 that loop invites is a lost panel.  Here the oracle computes, at the full
 8192^3 workloads and on exactly the output positions the GPU parity tests
-sample (two whole 256 x 256 tiles plus 20 000 random entries), both the true
+sample (two whole 256 x 256 tiles plus 65 536 random entries), both the true
 result and the result of a kernel that skipped one k-tile -- every output
 missing the same k-tile, or only the last output tile missing the last
 k-tile.  The gate must accept the true result rounded to fp32 and reject
@@ -16,13 +16,14 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_helpers import elementwise_tolerance, gate_errors, gate_passes, sample_entries, tolerance
+from gpu_helpers import (SAMPLED_ENTRIES, elementwise_tolerance, gate_errors, gate_passes, sample_entries,
+                         tolerance)
 
 KTILE = {W.BF16: 64, W.E4M3: 128}      # dense K per k-tile of the tiled kernels
 
 
 def _sampled(M, N, seed):
-    return sample_entries(M, N, 20000, seed, tiles=((0, 0), ((M - 1) // 256, (N - 1) // 256)))
+    return sample_entries(M, N, SAMPLED_ENTRIES, seed, tiles=((0, 0), ((M - 1) // 256, (N - 1) // 256)))
 
 
 def _entries(w, A, ii, jj):

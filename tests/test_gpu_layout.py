@@ -10,7 +10,7 @@ import torch
 import oracle
 import sparse_matrix_multiply_amd as mm
 import workloads as W
-from gpu_helpers import assert_close, dev, env, out_tensor, sample_entries
+from gpu_helpers import SAMPLED_ENTRIES, assert_close, dev, env, out_tensor, sample_entries
 from oracle import BF16, F16
 
 pytestmark = pytest.mark.gpu
@@ -89,7 +89,7 @@ def test_layout_8192_sampled():
     w = W.workload("bf16_8192")
     t, M, N, K = w["ta"], w["M"], w["N"], w["K"]
     D = run_layout(t, w["A"], w["B"], False, True, w["alpha"], w["beta"], w["C"])
-    ii, jj = sample_entries(M, N, 20000, 16, tiles=((0, 0), ((M - 1) // 256, (N - 1) // 256)))
+    ii, jj = sample_entries(M, N, SAMPLED_ENTRIES, 16, tiles=((0, 0), ((M - 1) // 256, (N - 1) // 256)))
     ref, S = oracle.gemm_dense_entries(t, t, w["A"], w["B"], ii, jj, w["alpha"], w["beta"], w["C"])
     got = D[torch.from_numpy(ii).to(dev()), torch.from_numpy(jj).to(dev())].cpu().numpy()
     assert_close(got, ref, S, t, K, w["alpha"], w["beta"], w["C"][ii, jj], "layout 8192^3")
@@ -172,7 +172,7 @@ def test_layout8_8192_sampled():
     w = W.workload("fp8_8192")
     ta, tb, M, N, K = w["ta"], w["tb"], w["M"], w["N"], w["K"]
     D = run_layout8(ta, tb, w["A"], w["B"], True, True, 1.0, 0.0, None)
-    ii, jj = sample_entries(M, N, 20000, 17, tiles=((0, 0), ((M - 1) // 256, (N - 1) // 256)))
+    ii, jj = sample_entries(M, N, SAMPLED_ENTRIES, 17, tiles=((0, 0), ((M - 1) // 256, (N - 1) // 256)))
     ref, S = oracle.gemm_dense_entries(ta, tb, w["A"], w["B"], ii, jj)
     got = D[torch.from_numpy(ii).to(dev()), torch.from_numpy(jj).to(dev())].cpu().numpy()
     assert_close(got, ref, S, ta, K, 1.0, 0.0, None, "layout8 8192^3")

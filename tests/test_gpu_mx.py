@@ -5,7 +5,7 @@ Every fp8/bf8 pair and tile shape, ragged M, N and K (K a multiple of 32 but not
 over 2^-20 .. 2^20, garbage (255 included) in the scale bytes past K and in the pitch
 padding, beta != 0, M <= 32; exact small-integer products with random power-of-two block
 scales (bit for bit); the epilogue variants on top; and the 8192^3 fp8 x bf8 shape against
-two whole 256 x 256 output tiles plus 20 000 sampled entries.
+two whole 256 x 256 output tiles plus 65 536 sampled entries.
 """
 import numpy as np
 import pytest
@@ -14,7 +14,8 @@ import torch
 import oracle
 import sparse_matrix_multiply_amd as mm
 import workloads as W
-from gpu_helpers import assert_close, dev, env, out_tensor, pack_mx_scales, sample_entries, to_dev_bits
+from gpu_helpers import (SAMPLED_ENTRIES, assert_close, dev, env, out_tensor, pack_mx_scales, sample_entries,
+                         to_dev_bits)
 from oracle import E4M3, E5M2
 
 pytestmark = pytest.mark.gpu
@@ -116,7 +117,7 @@ def test_mx_8192_sampled():
     SA = g.integers(117, 138, size=(M, K // 32)).astype(np.uint8)
     SB = g.integers(117, 138, size=(N, K // 32)).astype(np.uint8)
     D = run_mx(ta, tb, w["A"], SA, w["B"], SB, 1.0, 0.0, None)
-    ii, jj = sample_entries(M, N, 20000, 14, tiles=((0, 0), ((M - 1) // 256, (N - 1) // 256)))
+    ii, jj = sample_entries(M, N, SAMPLED_ENTRIES, 14, tiles=((0, 0), ((M - 1) // 256, (N - 1) // 256)))
     ref, S = oracle.gemm_mx_entries(ta, tb, w["A"], SA, w["B"], SB, ii, jj)
     got = D[torch.from_numpy(ii).to(dev()), torch.from_numpy(jj).to(dev())].cpu().numpy()
     assert_close(got, ref, S, ta, K, 1.0, 0.0, None, "mx 8192^3")
@@ -182,7 +183,7 @@ def test_mx_fp4_8192_sampled():
     M = N = K = 8192
     A, B, SA, SB = fp4_problem(M, N, K, 77, lo=117, hi=138)
     D = run_fp4(A, SA, B, SB)
-    ii, jj = sample_entries(M, N, 20000, 15, tiles=((0, 0), ((M - 1) // 256, (N - 1) // 256)))
+    ii, jj = sample_entries(M, N, SAMPLED_ENTRIES, 15, tiles=((0, 0), ((M - 1) // 256, (N - 1) // 256)))
     ref, S = oracle.gemm_mx_entries(FP4, FP4, A, SA, B, SB, ii, jj)
     got = D[torch.from_numpy(ii).to(dev()), torch.from_numpy(jj).to(dev())].cpu().numpy()
     assert_close(got, ref, S, E4M3, K, 1.0, 0.0, None, "mx fp4 8192^3")
@@ -258,7 +259,7 @@ def test_mx_fp6_8192_sampled():
     M = N = K = 8192
     A, B, SA, SB = fp6_problem(M, N, K, 78, lo=117, hi=138)
     D = run_fp6(FP6, BF6, A, SA, B, SB)
-    ii, jj = sample_entries(M, N, 20000, 16, tiles=((0, 0), ((M - 1) // 256, (N - 1) // 256)))
+    ii, jj = sample_entries(M, N, SAMPLED_ENTRIES, 16, tiles=((0, 0), ((M - 1) // 256, (N - 1) // 256)))
     ref, S = oracle.gemm_mx_entries(FP6, BF6, A, SA, B, SB, ii, jj)
     got = D[torch.from_numpy(ii).to(dev()), torch.from_numpy(jj).to(dev())].cpu().numpy()
     assert_close(got, ref, S, E4M3, K, 1.0, 0.0, None, "mx fp6 8192^3")

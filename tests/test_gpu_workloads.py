@@ -20,8 +20,8 @@ import torch
 import oracle
 import sparse_matrix_multiply_amd as mm
 import workloads as W
-from gpu_helpers import (assert_bits_equal, assert_close, compress_dev, dev, dev_bits_to_host, out_tensor,
-                         sample_entries, to_dev_bits)
+from gpu_helpers import (SAMPLED_ENTRIES, assert_bits_equal, assert_close, compress_dev, dev, dev_bits_to_host,
+                         out_tensor, sample_entries, to_dev_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,10 +37,10 @@ def dense_on_gpu(w):
 
 
 def check_sampled(D, w, fn_entries, seed, exact=False):
-    """The first and the last 256 x 256 output tile plus 20 000 random entries against the oracle:
+    """The first and the last 256 x 256 output tile plus 65 536 random entries against the oracle:
     within the gates, or (exact inputs) bit for bit."""
     M, N, K = w["M"], w["N"], w["K"]
-    ii, jj = sample_entries(M, N, 20000, seed, tiles=((0, 0), ((M - 1) // 256, (N - 1) // 256)))
+    ii, jj = sample_entries(M, N, SAMPLED_ENTRIES, seed, tiles=((0, 0), ((M - 1) // 256, (N - 1) // 256)))
     ref, S = fn_entries(ii, jj)
     got = D[torch.from_numpy(ii).to(dev()), torch.from_numpy(jj).to(dev())].cpu().numpy()
     if exact:
