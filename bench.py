@@ -10,8 +10,9 @@ work (2*M*N*K per GEMM, dense-equivalent K for the sparse one) divided by the
 wall time of the step.  Each kernel is also timed with HIP events on the
 stream it runs on, and the slowest one is reported against its roofline: the
 published peak, and the sustained rate of its matrix instruction measured on
-this GPU by the rate microbenchmark (`matrix_rates`), with the shader clock
-amd-smi reports while that GEMM runs.  The CPU oracle is timed on a bounded
+this GPU by the rate microbenchmark (`matrix_rates`) with random operands, as
+the GEMM's are (the chip holds a lower clock for them than for constant ones;
+both rates and clocks are in the line).  The CPU oracle is timed on a bounded
 slice of the bf16 GEMM (`cpu_baseline`).  `configs` gives every smaller
 workload at its full size -- 256^3 bf16, 1024^3 int8, 4096^3 bf16,
 16x4096x4096 bf16 and the 4:2 fp16 4096x4096x8192 compress + GEMM -- with its
@@ -126,7 +127,6 @@ def parse():
                     help="skip the per-configuration section (GPU time, full oracle check and oracle time of "
                          "the 256^3, 1024^3 int8, 4096^3, 16x4096x4096 and 4:2 fp16 workloads)")
     ap.add_argument("--no-rates", action="store_true", help="skip the matrix-instruction rate microbenchmark")
-    ap.add_argument("--no-sclk", action="store_true", help="skip sampling the shader clock during the bf16 GEMM")
     ap.add_argument("--cpu-rows", type=int, default=0, help="rows of the oracle slice (0 = calibrate)")
     ap.add_argument("--suite", action="store_true",
                     help="instead of the step, time every workload once (one JSON line with a 'suite' object)")
@@ -279,18 +279,22 @@ def main():
     if tr:
         roof["traffic_detail"] = tr
 
-    # the sustained rate of the dominant kernel's instruction, measured on this GPU, beside the published peak
+    # the sustained rate of the dominant kernel's instruction on random operands (as the GEMM's inputs
+    # are), measured on this GPU, beside the published peak; the constant-operand rate for reference
     rates = None
     if not args.no_rates:
         rates = matrix_rates()
         key = {"dense_bf16": "bf16_mfma", "dense_fp8": "fp8_mfma", "sparse_fp8": "fp8_smfmac"}.get(dominant)
         if key in rates:
-            sus = rates[key]["TFLOP/s"] / (2 if dominant == "sparse_fp8" else 1)
-            roof["sustained_peak"] = round(sus, 1)
-            roof["frac_of_sustained"] = round(roof["achieved"] / sus, 4)
-    if not args.no_sclk:
-        roof["sclk_MHz"] = sample_sclk(lambda: mm.gemm_dense(Ab, Bb, Db, 1.0, 1.0, Cb, a_type=BF16, b_type=BF16,
-                                                             stream=stream))
+            half = 2 if dominant == "sparse_fp8" else 1
+            rnd, cst = rates[key]["random_operands"], rates[key]["constant_operands"]
+            roof["sustained_peak"] = round(rnd["TFLOP/s"] / half, 1)
+            roof["sustained_sclk_MHz"] = rnd["sclk_MHz"]
+            roof["frac_of_sustained"] = round(roof["achieved"] / roof["sustained_peak"], 4)
+            roof["sustained_peak_constant_operands"] = round(cst["TFLOP/s"] / half, 1)
+            roof["sustained_note"] = ("sustained_peak: the instruction alone, back to back on every SIMD, on random "
+                                      "operands that change from one instruction to the next; the chip's power "
+                                      "management holds a lower clock for them than for constant operands")
 
     check = None
     if not args.no_check:
@@ -618,53 +622,22 @@ def only(which, steps, warmup):
 
 def matrix_rates():
     """Sustained rate of the matrix instructions the GEMM kernels use, each issued back to back on
-    every compute unit for about 150 ms (libmmac_rate.so): the ceiling this GPU reaches at the clock
-    it holds, beside the published peaks."""
+    every compute unit for about 150 ms (libmmac_rate.so), once on constant operands and once on
+    random ones that change from one instruction to the next (as a GEMM's fragments do), with the
+    shader clock each run holds: the ceiling this GPU reaches, beside the published peaks."""
     from sparse_matrix_multiply_amd import rate
     out = {}
     for key, instr, peak in (("bf16_mfma", rate.MFMA_BF16, PEAK_TFLOPS["bf16"]), ("fp8_mfma", rate.MFMA_FP8, PEAK_TFLOPS["fp8"]),
                              ("i8_mfma", rate.MFMA_I8, PEAK_TFLOPS["int8"]),
                              ("fp16_smfmac", rate.SMFMAC_F16, 2 * PEAK_TFLOPS["fp16"]),
                              ("fp8_smfmac", rate.SMFMAC_FP8, 2 * PEAK_TFLOPS["fp8"])):
-        r = rate.measure(instr)
-        out[key] = {"instr": r["instr"], "TFLOP/s": round(r["TFLOP/s"], 1), "frac_published": round(r["TFLOP/s"] / peak, 4),
-                    "seconds": round(r["seconds"], 3)}
+        out[key] = {"instr": rate.name(instr)}
+        for kind, rnd in (("constant_operands", False), ("random_operands", True)):
+            r = rate.measure(instr, random=rnd)
+            out[key][kind] = {"TFLOP/s": round(r["TFLOP/s"], 1), "frac_published": round(r["TFLOP/s"] / peak, 4),
+                              "sclk_MHz": round(r["sclk_GHz"] * 1000), "cycles_per_instr": round(r["cycles_per_instr"], 2),
+                              "seconds": round(r["seconds"], 3)}
     return out
-
-
-def sample_sclk(fn, seconds=1.5):
-    """Shader clock (MHz, mean over the XCDs) that amd-smi reports while `fn` runs back to back for
-    about `seconds`; None if amd-smi is not there or says nothing usable."""
-    import re
-    import shutil
-    import subprocess
-    import threading
-    import torch
-    tool = shutil.which("amd-smi")
-    if not tool:
-        return None
-    got = {}
-
-    def sample():
-        time.sleep(0.3 * seconds)
-        try:
-            r = subprocess.run([tool, "metric", "-g", "0", "-c"], capture_output=True, text=True, timeout=20)
-            got["text"] = r.stdout
-        except (OSError, subprocess.SubprocessError):
-            pass
-
-    th = threading.Thread(target=sample)
-    th.start()
-    t0 = time.perf_counter()
-    while th.is_alive() or time.perf_counter() - t0 < 0.5:
-        for _ in range(20):
-            fn()
-        torch.cuda.synchronize()
-        if time.perf_counter() - t0 > 30:
-            break
-    th.join()
-    clks = [int(m) for m in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", got.get("text", ""))]
-    return round(sum(clks) / len(clks)) if clks else None
 
 
 def graph_ms(fns, reps):

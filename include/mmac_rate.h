@@ -58,6 +58,25 @@ const char *mmac_rate_name(int instr);
 #define MMAC_RATE_CHAINS 4
 int mmac_rate_run(int instr, int64_t iters, int blocks, uint64_t *clocks, float *sink, void *stream);
 
+/*
+ * The same with a choice of operand data.  random_operands = 0: constant
+ * operands (as mmac_rate_run: every instruction multiplies the same small
+ * values); 1: random operands, drawn once per wave at the start (random sign
+ * and mantissa, exponents around 1 for the floating formats, raw bits for
+ * int8 and the 4- / 6-bit formats), each instruction of a loop trip taking A
+ * operand c of MMAC_RATE_CHAINS and B operand c mod 2, so the matrix unit's
+ * inputs change from one instruction to the next as a GEMM's fragments do.
+ * The chip's power management sets a lower clock for switching data than
+ * for constant data; this measures the rate a GEMM on random inputs can
+ * reach.  Returns as mmac_rate_run; -1 also for random_operands not 0 or 1.
+ */
+int mmac_rate_run_data(int instr, int random_operands, int64_t iters, int blocks, uint64_t *clocks, float *sink,
+                       void *stream);
+
+/* Rate of the constant-rate clock behind the wall ticks (kHz) of the current device; -1 on a HIP
+ * error.  A workgroup's shader clock is then cycles / ticks * this rate. */
+int64_t mmac_rate_wall_clock_khz(void);
+
 #ifdef __cplusplus
 }
 #endif

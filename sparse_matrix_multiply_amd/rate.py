@@ -4,7 +4,9 @@ measure(instr) issues one matrix instruction back to back on every compute
 unit for a fixed time (default 150 ms) and returns its sustained rate and the
 shader clock meanwhile: the ceiling a GEMM kernel built on that instruction
 can reach on this chip at the clock it actually holds, next to the published
-peak (operations per cycle times 2.4 GHz).  Measurement only.
+peak (operations per cycle times 2.4 GHz).  With random=True the operands are
+random and change from one instruction to the next, as a GEMM's do; the chip
+then holds a lower clock than for constant operands.  Measurement only.
 """
 import ctypes
 import os
@@ -35,6 +37,11 @@ def lib():
         L.mmac_rate_run.restype = ctypes.c_int
         L.mmac_rate_run.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_void_p]
+        L.mmac_rate_wall_clock_khz.restype = ctypes.c_int64
+        L.mmac_rate_wall_clock_khz.argtypes = []
+        L.mmac_rate_run_data.restype = ctypes.c_int
+        L.mmac_rate_run_data.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -43,13 +50,14 @@ def name(instr):
     return lib().mmac_rate_name(instr).decode()
 
 
-def measure(instr, seconds=0.15, device=None):
-    """Sustained rate of one instruction on the whole GPU.  Returns a dict: TFLOP/s (TOP/s for
-    int8; dense-equivalent for sparse), the shader clock in GHz (clock64 cycles over the event-timed
-    duration), cycles per instruction per SIMD, and the duration."""
+def measure(instr, seconds=0.15, device=None, random=False):
+    """Sustained rate of one instruction on the whole GPU, multiplying constant operands or (random)
+    random ones that change from one instruction to the next.  Returns a dict: TFLOP/s (TOP/s for
+    int8; dense-equivalent for sparse), the shader clock in GHz (each workgroup's clock64 cycles over
+    its wall-clock ticks), cycles per instruction per SIMD at that clock, and the duration."""
     dev = torch.device("cuda", 0) if device is None else device
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    blocks = 4 * cus                     # four waves per SIMD, all resident at once
+    blocks = 4 * cus                     # four waves per SIMD once all are resident
     clocks = torch.zeros(2 * blocks, dtype=torch.int64, device=dev)
     sink = torch.empty(blocks * 64 * WAVES, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -58,10 +66,10 @@ def measure(instr, seconds=0.15, device=None):
     def run(iters):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        rc = L.mmac_rate_run(instr, iters, blocks, ctypes.c_void_p(clocks.data_ptr()),
-                             ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+        rc = L.mmac_rate_run_data(instr, 1 if random else 0, iters, blocks, ctypes.c_void_p(clocks.data_ptr()),
+                                  ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
         if rc != 0:
-            raise RuntimeError(f"mmac_rate_run({instr}) failed: {rc}")
+            raise RuntimeError(f"mmac_rate_run_data({instr}, {int(random)}) failed: {rc}")
         e1.record(stream)
         e1.synchronize()
         return e0.elapsed_time(e1) * 1e-3
@@ -72,8 +80,10 @@ def measure(instr, seconds=0.15, device=None):
     t = run(iters)
     c = clocks.view(blocks, 2).double().cpu()
     ops = L.mmac_rate_ops(instr) * iters * CHAINS * WAVES * blocks
-    simd_waves = WAVES * blocks / (4 * cus)          # waves sharing one SIMD
-    cycles = float(c[:, 0].mean())
-    return {"instr": name(instr), "TFLOP/s": ops / t / 1e12, "sclk_GHz": cycles / t / 1e9,
-            "cycles_per_instr": cycles / (iters * CHAINS * simd_waves), "seconds": t,
-            "wall_ticks_per_s": float(c[:, 1].mean()) / t}
+    # the workgroups do not all start at once, so the clock comes from each one's own cycles over its
+    # own constant-rate ticks, not from the event-timed duration
+    khz = L.mmac_rate_wall_clock_khz()
+    sclk = float((c[:, 0] / c[:, 1]).mean()) * khz * 1e3 if khz > 0 else float("nan")
+    instr_per_simd = iters * CHAINS * WAVES * blocks / (4 * cus)
+    return {"instr": name(instr), "TFLOP/s": ops / t / 1e12, "sclk_GHz": sclk / 1e9,
+            "cycles_per_instr": sclk * t / instr_per_simd, "seconds": t, "random_operands": bool(random)}

@@ -444,7 +444,7 @@ def test_rate_library_exports_its_header():
     import ctypes
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "mmac_rate.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(mmac_rate_[a-z0-9_]+)\s*\(", text)))
-    assert names == ["mmac_rate_name", "mmac_rate_ops", "mmac_rate_run"]
+    assert names == ["mmac_rate_name", "mmac_rate_ops", "mmac_rate_run", "mmac_rate_run_data", "mmac_rate_wall_clock_khz"]
     from sparse_matrix_multiply_amd import rate
     if not os.path.exists(rate.LIB_PATH):
         from sparse_matrix_multiply_amd import build
@@ -459,6 +459,8 @@ def test_rate_library_exports_its_header():
     # argument errors return before any launch (fake pointers)
     assert L.mmac_rate_run(99, 1, 1, ctypes.c_void_p(P), ctypes.c_void_p(P), None) == -1
     assert L.mmac_rate_run(0, 0, 1, ctypes.c_void_p(P), ctypes.c_void_p(P), None) == -1
+    assert L.mmac_rate_run_data(0, 2, 1, 1, ctypes.c_void_p(P), ctypes.c_void_p(P), None) == -1   # data flag 0 or 1
+    assert L.mmac_rate_run_data(0, 1, 0, 1, ctypes.c_void_p(P), ctypes.c_void_p(P), None) == -1
 
 
 def test_kernel_source_hash_ignores_comments_only():
