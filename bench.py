@@ -783,6 +783,17 @@ def configs_report(dev, stream, cpu=True):
         del A, Bs, C, Ds
         torch.cuda.empty_cache()
 
+    # the floor under the small cases: a one-element fill (torch's, the least a kernel can do) and the
+    # library's smallest GEMM (64 x 64 x 64 bf16, one k-tile: prologue, one step, epilogue), replayed
+    # from a HIP graph like the small cases above
+    one = torch.zeros(1, device=dev)
+    a64 = torch.zeros((64, 64), dtype=torch.bfloat16, device=dev)
+    d64 = torch.empty((64, 64), dtype=torch.float32, device=dev)
+    out["launch_floor"] = {
+        "us_graph_one_element_fill": round(graph_ms([lambda s: one.fill_(0.0)], 200) * 1e3, 2),
+        "us_graph_gemm_64x64x64_bf16": round(graph_ms([lambda s: mm.gemm_dense(a64, a64, d64, stream=s)], 200) * 1e3, 2)}
+    del one, a64, d64
+
     # 4:2 fp16 4096 x 4096 x 8192: compression of the dense A (rotated), then the sparse GEMM
     w = W.workload("f16_sparse")
     M, N, K, ta = w["M"], w["N"], w["K"], w["ta"]
