@@ -130,10 +130,11 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=0, help="rows of the oracle slice (0 = calibrate)")
     ap.add_argument("--suite", action="store_true",
                     help="instead of the step, time every workload once (one JSON line with a 'suite' object)")
-    ap.add_argument("--only", choices=["skinny", "compress_fp8", "rates"], default=None,
+    ap.add_argument("--only", choices=["skinny", "compress_fp8", "rates", "bf16_8192", "bf16_8192_ones"], default=None,
                     help="only run one kernel --steps times after --warmup (for counter runs): the 16x4096x4096 "
                          "bf16 skinny GEMM (beta = 1, B and D rotated through 16 copies past the Infinity Cache), "
-                         "the 8192^2 fp8 4:2 compressor (8 copies rotated), or the matrix-rate microbenchmark")
+                         "the 8192^2 fp8 4:2 compressor (8 copies rotated), the matrix-rate microbenchmark, or the "
+                         "8192^3 bf16 GEMM (beta = 1) on its random inputs or on all-ones A and B")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain elementwise copy of this many MiB (fp32) three times: the known-size "
                          "kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters")
@@ -295,6 +296,23 @@ def main():
             roof["sustained_note"] = ("sustained_peak: the instruction alone, back to back on every SIMD, on random "
                                       "operands that change from one instruction to the next; the chip's power "
                                       "management holds a lower clock for them than for constant operands")
+    # the same bf16 GEMM (same shape, beta = 1, same C) on all-ones A and B: the kernel is unchanged,
+    # only the data the matrix units switch is; context for the power-limited clock, not the metric
+    if dominant == "dense_bf16":
+        ones_a = torch.ones((M, K), dtype=torch.bfloat16, device=dev)
+        ones_b = torch.ones((N, K), dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            mm.gemm_dense(ones_a, ones_b, Db, 1.0, 1.0, Cb, a_type=BF16, b_type=BF16, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            mm.gemm_dense(ones_a, ones_b, Db, 1.0, 1.0, Cb, a_type=BF16, b_type=BF16, stream=stream)
+        e1.record(stream)
+        e1.synchronize()
+        ones_tf = gemm_flops(M, N, K) / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e12
+        roof["achieved_constant_operands"] = round(ones_tf, 1)
+        roof["frac_constant_operands"] = round(ones_tf / roof["peak"], 4)
+        del ones_a, ones_b
 
     check = None
     if not args.no_check:
@@ -587,7 +605,20 @@ def only(which, steps, warmup):
         host = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16 if bits.dtype == np.uint16 else np.int8))
         return host.to(dev).view({W.BF16: torch.bfloat16, W.E4M3: torch.float8_e4m3fn}[t])
 
-    if which == "skinny":
+    if which in ("bf16_8192", "bf16_8192_ones"):
+        # the step's bf16 GEMM (beta = 1) alone, on its random inputs or on all-ones A and B
+        w = W.workload("bf16_8192")
+        M, N, K = w["M"], w["N"], w["K"]
+        if which == "bf16_8192":
+            A, B = to_dev(w["A"], W.BF16), to_dev(w["B"], W.BF16)
+        else:
+            A = torch.ones((M, K), dtype=torch.bfloat16, device=dev)
+            B = torch.ones((N, K), dtype=torch.bfloat16, device=dev)
+        C = torch.from_numpy(w["C"]).to(dev)
+        D = torch.empty((M, N), dtype=torch.float32, device=dev)
+        fns = [lambda: mm.gemm_dense(A, B, D, 1.0, 1.0, C, stream=stream)]
+        nbytes = (M + N) * K * 2 + 2 * M * N * 4
+    elif which == "skinny":
         w = W.workload("bf16_skinny")
         M, N, K = w["M"], w["N"], w["K"]
         A = to_dev(w["A"], W.BF16)
@@ -616,8 +647,11 @@ def only(which, steps, warmup):
     e1.record(stream)
     e1.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
-    print(json.dumps({"only": which, "launches": steps, "us": round(us, 2), "algorithmic_bytes": nbytes,
-                      "GB/s": round(nbytes / us / 1e3, 1)}), flush=True)
+    out = {"only": which, "launches": steps, "us": round(us, 2), "algorithmic_bytes": nbytes,
+           "GB/s": round(nbytes / us / 1e3, 1)}
+    if which.startswith("bf16_8192"):
+        out["TFLOP/s"] = round(gemm_flops(M, N, K) / us / 1e6, 1)
+    print(json.dumps(out), flush=True)
 
 
 def matrix_rates():
