@@ -96,10 +96,14 @@ mmac_status_t check_gemm(int a, int b, int64_t M, int64_t N, int64_t K, double a
         return MMAC_ERR_INVALID_ARG;
     if (a == MMAC_I8 && (!integral_i32(alpha) || !integral_i32(beta))) return MMAC_ERR_INVALID_ARG;
     if (C == D && beta != 0.0 && ldc != ldd) return MMAC_ERR_INVALID_ARG;
+    // pitch limits compared by division, so that no leading dimension, however large, overflows
     const int es = elem_size(a);
-    if (lda * es > kMaxPitchBytes || ldb * es > kMaxPitchBytes) return MMAC_ERR_UNSUPPORTED;
+    if (lda > kMaxPitchBytes / es || ldb > kMaxPitchBytes / es) return MMAC_ERR_UNSUPPORTED;
     const int oes = out_size(ep);
-    if (ldd * oes > kMaxPitchBytes || (C && beta != 0.0 && ldc * oes > kMaxPitchBytes)) return MMAC_ERR_UNSUPPORTED;
+    if (ldd > kMaxPitchBytes / oes || (C && beta != 0.0 && ldc > kMaxPitchBytes / oes)) return MMAC_ERR_UNSUPPORTED;
+    // the grid (one workgroup per tile and K range) must fit a 32-bit count at the smallest tile
+    // and the most ranges; only an output of terabytes comes near this
+    if (((M + 63) / 64) * ((N + 63) / 64) > (int64_t)INT32_MAX / 8) return MMAC_ERR_UNSUPPORTED;
     if (!aligned16(A) || !aligned16(B) || (lda * es) % 16 || (ldb * es) % 16) return MMAC_ERR_MISALIGNED;
     if (!aligned_to(D, oes) || (C && beta != 0.0 && !aligned_to(C, oes))) return MMAC_ERR_MISALIGNED;
     if (ep.bias && !aligned4(ep.bias)) return MMAC_ERR_MISALIGNED;
@@ -224,6 +228,8 @@ mmac_status_t compress_call(mmac_dtype_t a_type, int64_t M, int64_t K, const voi
     const int64_t words = (K + 31) / 32;
     if (lda < K || ldac < K / 2 || ldidx < words || lda < 1 || ldac < 1 || ldidx < 1) return MMAC_ERR_INVALID_ARG;
     const int es = elem_size(a_type);
+    if (lda > kMaxPitchBytes / es || ldac > kMaxPitchBytes / es || ldidx > kMaxPitchBytes / 4)
+        return MMAC_ERR_UNSUPPORTED;
     if (!aligned16(A) || !aligned16(Ac) || (lda * es) % 16 || (ldac * es) % 16) return MMAC_ERR_MISALIGNED;
     if (!aligned4(idx) || (bad_groups && !aligned4(bad_groups))) return MMAC_ERR_MISALIGNED;
     if (M == 0 || K == 0) return MMAC_OK;
@@ -370,7 +376,7 @@ mmac_status_t mmac_gemm_sparse24_ws(mmac_dtype_t a_type, mmac_dtype_t b_type, in
         check_gemm(a_type, b_type, M, N, K, alpha, Ac, ldac, K / 2, B, ldb, beta, C, ldc, D, ldd, ep);
     if (st != MMAC_OK) return st;
     if ((K > 0 && !idx) || ldidx < (K + 31) / 32 || ldidx < 1) return MMAC_ERR_INVALID_ARG;
-    if (ldidx * 4 * 256 > ((int64_t)1 << 31)) return MMAC_ERR_UNSUPPORTED;
+    if (ldidx > kMaxPitchBytes / 4) return MMAC_ERR_UNSUPPORTED;   // 256 rows of index words below 2^31 bytes
     if (!aligned4(idx)) return MMAC_ERR_MISALIGNED;
     if (workspace_bytes < 0) return MMAC_ERR_INVALID_ARG;
     if (workspace && !aligned16(workspace)) return MMAC_ERR_MISALIGNED;
@@ -420,7 +426,9 @@ mmac_status_t mmac_gemm_dense_mx(mmac_dtype_t a_type, mmac_dtype_t b_type, int64
     if (st != MMAC_OK) return st;
     if ((K > 0 && (!SA || !SB)) || ldsa < M || ldsb < N || ldsa < 1 || ldsb < 1) return MMAC_ERR_INVALID_ARG;
     const int64_t scale_rows = (K + 127) / 128;
-    if (scale_rows * std::max(ldsa, ldsb) * 4 >= ((int64_t)1 << 31)) return MMAC_ERR_UNSUPPORTED;
+    // scale arrays of scale_rows rows of ld words below 2^31 bytes (compared by division: no overflow)
+    if (scale_rows > 0 && std::max(ldsa, ldsb) > ((((int64_t)1 << 31) - 1) / 4) / scale_rows)
+        return MMAC_ERR_UNSUPPORTED;
     if ((ldsa % 4) || (ldsb % 4) || !aligned16(SA) || !aligned16(SB)) return MMAC_ERR_MISALIGNED;
     if (M == 0 || N == 0) return MMAC_OK;
     // the 8-wave 256 x 256 tile has no registers left for the scale words: its 128 x 256 half instead

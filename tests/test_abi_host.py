@@ -470,3 +470,41 @@ def test_kernel_source_hash_ignores_comments_only():
     assert bench._code_only(code) == 'int a = 1; const char *s = "x // y /* z */"; char q = \'"\'; int b;'
     assert bench._code_only(code) == bench._code_only(code.replace("// note", "// other words"))
     assert bench._code_only(code) != bench._code_only(code.replace("int a = 1", "int a = 2"))
+
+
+HUGE = [(1 << 62), (1 << 62) + 16, (1 << 63) - 16]     # leading dimensions whose byte pitch overflows int64
+
+
+@pytest.mark.parametrize("ld", HUGE)
+def test_huge_leading_dimensions_are_rejected_without_overflow(L, ld):
+    """A leading dimension so large that ld * element size overflows a 64-bit integer is refused
+    with MMAC_ERR_UNSUPPORTED (the pitch limit is compared by division), on every entry point, before
+    anything is launched (the pointers here are not device memory)."""
+    U = mm.ERR_UNSUPPORTED
+    for kw in (dict(lda=ld), dict(ldb=ld), dict(ldd=ld), dict(beta=1.0, C=P + 4096, ldc=ld, ldd=64)):
+        assert dense(L, **kw) == U, kw
+        assert static_dense(L, **kw) == U, kw
+        assert dense_layout(L, **kw) == U, kw
+    for kw in (dict(ldac=ld), dict(ldidx=ld), dict(ldb=ld), dict(ldd=ld)):
+        assert sparse(L, **kw) == U, kw
+    for entry in ("mmac_sparse24_compress", "mmac_sparse24_prune_compress"):
+        for kw in (dict(lda=ld), dict(ldac=ld), dict(ldidx=ld)):
+            assert compress(L, entry, **kw) == U, (entry, kw)
+    for kw in (dict(lda=ld), dict(ldb=ld), dict(ldsa=ld), dict(ldsb=ld)):
+        assert dense_mx(L, **kw) == U, kw
+
+
+def test_compressor_pitch_limit(L):
+    """The compressor takes the row-pitch limit of the other calls: 8 MiB for A and Ac, 2 Mi words
+    for idx; one step past it is MMAC_ERR_UNSUPPORTED."""
+    for entry in ("mmac_sparse24_compress", "mmac_sparse24_prune_compress"):
+        assert compress(L, entry, lda=(1 << 22) + 8) == mm.ERR_UNSUPPORTED       # f16: 8 MiB + 16 bytes
+        assert compress(L, entry, ldac=(1 << 22) + 8) == mm.ERR_UNSUPPORTED
+        assert compress(L, entry, ldidx=(1 << 21) + 1) == mm.ERR_UNSUPPORTED
+        assert compress(L, entry, a=mm.FP8_E4M3, lda=(1 << 23) + 16) == mm.ERR_UNSUPPORTED
+
+
+def test_grid_count_limit(L):
+    """An output so large that its tile count would overflow the 32-bit grid is refused (only a
+    product of terabytes comes near it; the pointers here are not device memory)."""
+    assert dense(L, M=(1 << 31) - 1, N=(1 << 21) - 64, K=16, lda=16, ldb=16, ldd=(1 << 21) - 64) == mm.ERR_UNSUPPORTED

@@ -2,10 +2,10 @@
 (or 16-row) slab of an operand with one buffer resource and 32-bit offsets, so the library caps
 row pitches at 8 MiB (2 Mi words for the 4:2 index) and a transposed operand at K rows below
 2 GiB; here every operand and output sits at that cap, where a 256-row tile spans the whole
-2 GiB a 32-bit offset reaches.  The compressor addresses rows with 64-bit pointers and has no
-cap: it runs at a 16 MiB pitch, so its last rows lie beyond 4 GiB.  Small M, N and K keep the
-oracle quick; the pitches make the buffers several GiB of (zeroed) GPU memory.  One step past
-the caps the calls return MMAC_ERR_UNSUPPORTED (tests/test_abi_host.py)."""
+2 GiB a 32-bit offset reaches.  The compressor, under the same cap, addresses rows with 64-bit
+pointers: with 600 rows at the largest pitch its last rows lie beyond 4 GiB.  Small M, N and K
+keep the oracle quick; the pitches make the buffers several GiB of (zeroed) GPU memory.  One
+step past the caps the calls return MMAC_ERR_UNSUPPORTED (tests/test_abi_host.py)."""
 import numpy as np
 import pytest
 import torch
@@ -109,8 +109,8 @@ def test_layout_at_max_transposed_span(ta, tb):
 
 @pytest.mark.parametrize("t", [F16, E4M3])
 def test_compress_beyond_4gib(t):
-    M, K = 260, 1024
-    pitch = 2 * MAX_PITCH
+    M, K = 600, 1024
+    pitch = MAX_PITCH
     A = sparse_a(t, M, K, 21 + t, violate=0.02)
     Ac_ref, idx_ref, bad_ref = oracle.compress24(t, A)
     Ad = to_dev_bits(A, t, pitch // ESIZE[t])
