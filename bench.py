@@ -126,7 +126,9 @@ def parse():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-configuration section (GPU time, full oracle check and oracle time of "
                          "the 256^3, 1024^3 int8, 4096^3, 16x4096x4096 and 4:2 fp16 workloads)")
-    ap.add_argument("--no-rates", action="store_true", help="skip the matrix-instruction rate microbenchmark")
+    ap.add_argument("--no-rates", action="store_true",
+                    help="skip the matrix-instruction rate microbenchmark and the all-ones run of the bf16 GEMM "
+                         "(the context beside the roofline; counter runs of the step use this)")
     ap.add_argument("--cpu-rows", type=int, default=0, help="rows of the oracle slice (0 = calibrate)")
     ap.add_argument("--suite", action="store_true",
                     help="instead of the step, time every workload once (one JSON line with a 'suite' object)")
@@ -298,7 +300,7 @@ def main():
                                       "management holds a lower clock for them than for constant operands")
     # the same bf16 GEMM (same shape, beta = 1, same C) on all-ones A and B: the kernel is unchanged,
     # only the data the matrix units switch is; context for the power-limited clock, not the metric
-    if dominant == "dense_bf16":
+    if dominant == "dense_bf16" and not args.no_rates:
         ones_a = torch.ones((M, K), dtype=torch.bfloat16, device=dev)
         ones_b = torch.ones((N, K), dtype=torch.bfloat16, device=dev)
         for _ in range(3):
