@@ -315,6 +315,20 @@ def main():
         roof["achieved_constant_operands"] = round(ones_tf, 1)
         roof["frac_constant_operands"] = round(ones_tf / roof["peak"], 4)
         del ones_a, ones_b
+        # the vendor library on the same A and B, for comparison: torch.mm (hipBLASLt), bf16 out, no C
+        # (a lighter job than this GEMM's fp32 D with beta = 1); B transposed into a contiguous copy first
+        bt = Bb.t().contiguous()
+        for _ in range(3):
+            torch.mm(Ab, bt)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(10):
+            torch.mm(Ab, bt)
+        e1.record(stream)
+        e1.synchronize()
+        roof["vendor_library"] = {"call": "torch.mm (hipBLASLt): the same bf16 A and B, bf16 D, no C",
+                                  "TFLOP/s": round(gemm_flops(M, N, K) / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e12, 1)}
+        del bt
 
     check = None
     if not args.no_check:
