@@ -2,7 +2,8 @@
 //
 // One workgroup computes a BM x BN tile of D; its WM x WN waves each own a
 // (BM/WM) x (BN/WN) sub-tile made of 32 x 32 instruction tiles.  K is walked
-// in k-tiles of Op::kBK dense elements.  Each k-tile of A (or compressed A),
+// in k-tiles of Op::kBK dense elements, from a per-tile starting k-tile (see
+// the kernel) with wrap-around.  Each k-tile of A (or compressed A),
 // B and, for sparse A, the index words is copied from memory straight into
 // LDS by buffer loads with an LDS destination (no register staging).  There
 // are STAGES LDS stages: while the waves run the matrix instructions of
@@ -1053,7 +1054,7 @@ void gemm_tiled_kernel(GemmParams p) {
     // column) mod 4 and wraps around.  Of the tiles an XCD runs at once (eight tile rows by four
     // tile columns), those sharing a k-slice of A or of B then fetch it at different times, the later
     // ones from that XCD's L2 rather than all of them together from the fabric.  Measured at 8192^3:
-    // fp8 x bf8 3-4 % and 4:2 fp8 5 % faster, bf16 unchanged.  A tile's order depends only on its
+    // bf16 1 %, fp8 x bf8 3-4 % and 4:2 fp8 4-5 % faster.  A tile's order depends only on its
     // coordinates, so results stay deterministic, and exact sums are unchanged.
     if (p.splits == 1 && nkt == nk && nk >= 4) {
         t.rot = (t.tm + t.tn) & 3;
