@@ -34,7 +34,7 @@ if ROOT not in sys.path:
 
 METRIC = "GEMM TFLOP/s + % MFMA peak, bf16/fp8 dense and 4:2 sparse at 8192³, 1 GPU"
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
-PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp8": 5000.0, "int8": 5000.0}
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp8": 5000.0, "int8": 5000.0, "fp6": 10100.0, "fp4": 10100.0}
 PEAK_HBM_GBS = 8000.0
 
 
@@ -680,7 +680,9 @@ def matrix_rates():
     for key, instr, peak in (("bf16_mfma", rate.MFMA_BF16, PEAK_TFLOPS["bf16"]), ("fp8_mfma", rate.MFMA_FP8, PEAK_TFLOPS["fp8"]),
                              ("i8_mfma", rate.MFMA_I8, PEAK_TFLOPS["int8"]),
                              ("fp16_smfmac", rate.SMFMAC_F16, 2 * PEAK_TFLOPS["fp16"]),
-                             ("fp8_smfmac", rate.SMFMAC_FP8, 2 * PEAK_TFLOPS["fp8"])):
+                             ("fp8_smfmac", rate.SMFMAC_FP8, 2 * PEAK_TFLOPS["fp8"]),
+                             ("fp6_mfma_scaled", rate.MFMA_FP6, PEAK_TFLOPS["fp6"]),
+                             ("fp4_mfma_scaled", rate.MFMA_FP4, PEAK_TFLOPS["fp4"])):
         out[key] = {"instr": rate.name(instr)}
         for kind, rnd in (("constant_operands", False), ("random_operands", True)):
             r = rate.measure(instr, random=rnd)
