@@ -56,8 +56,8 @@
  *     (its only device memory of its own is mmac_gemm_dense_static's array).
  *     Buffers must stay valid until the work on `stream` has finished.
  *   - Asynchrony: each call validates its arguments on the host, then enqueues
- *     kernels on `stream` (a hipStream_t; NULL is the default stream) and
- *     returns without synchronising.  A kernel fault shows up at the caller's
+ *     kernels on `stream` (a hipStream_t of the current device; NULL is the
+ *     default stream) and returns without synchronising.  A kernel fault shows up at the caller's
  *     next synchronisation.
  *   - Errors: no exception crosses this interface.  Argument errors are
  *     detected before any GPU work is enqueued; nothing is written then.
